@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the paged KV-cache library on one MI355X.
+
+A step is one decode step of the whole model: for every layer, the cache-append
+scatter of the step's new token (paged_kv_append), decode attention
+(paged_attention_decode), and the log-sum-exp merge (paged_attention_reduce) when
+the workload runs split-context partitions.  The default workload is the
+Llama-2-7B attention shape: 128 sequences with lognormal lengths (P90 287),
+32 layers, 32 heads, head_dim 128, block_size 32, fp16.
+
+Inputs are seeded synthetic data already resident in HBM when timing starts.  To
+keep the last-level cache (256 MB) from serving repeated reads, the step cycles
+through R distinct per-layer pools with distinct data (8 for the default workload,
+about 2.9 GB of K/V touched per cycle); the block tables are shared by all layers.
+
+Prints ONE JSON line.  `value` is decode tokens/s over the whole step (sequences /
+step time); the line also carries the algorithmic HBM rate of the step, the
+roofline of the dominant kernel (decode attention) timed per launch with HIP
+events, and the fp64 CPU oracle timed on a bounded sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("decode attention tokens/s and achieved HBM GB/s (% of MI355X peak), 1 GPU")
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+
+
+def algorithmic_bytes(cfg, lengths, tables_entries):
+    """Bytes one layer of the step must move at minimum, split per kernel."""
+    e = cfg.elem_bytes
+    S, Hq, Hkv, D = cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+    kv = int(np.sum(lengths)) * 2 * Hkv * D * e        # K and V rows attended
+    qo = 2 * S * Hq * D * e                             # q read + output write
+    meta = 4 * int(tables_entries) + 4 * S              # table entries + lengths
+    append = 2 * S * 2 * Hkv * D * e                    # new K/V rows read + written
+    decode = kv + qo + meta
+    return {"decode": decode, "append": append + 4 * S + 4 * S, "layer": decode + append}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c3", help="workload key (c1a c1b c2 c3 c4 c5)")
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="override the workload's split-context partition size (0 = single pass)")
+    ap.add_argument("--distinct", type=int, default=None, help="override distinct layer pools")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="approximate CPU time budget of the oracle sample")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_09_amd as pkv
+    from workloads import get_config, make_workload
+
+    cfg = get_config(args.config)
+    P = cfg.bench_partition_size if args.partition_size is None else args.partition_size
+    R = min(cfg.num_layers, args.distinct or cfg.bench_distinct_layers)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tdt = {"fp16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
+    scale = float(np.float32(1.0 / math.sqrt(cfg.head_dim)))
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(tdt)
+
+    # ---- set-up: R distinct layers of pools, q, new rows (not timed) --------------
+    t_setup = time.time()
+    layers = []
+    w0 = None
+    for d in range(R):
+        w = make_workload(cfg, layer=d)
+        if w0 is None:
+            w0 = w
+        shape = w.pool_shape()
+        kp = torch.empty(shape, dtype=tdt, device=dev)
+        vp = torch.empty(shape, dtype=tdt, device=dev)
+        sentinel = int(np.array([w.nan_bits], np.uint16).view(np.int16)[0])
+        kp.view(torch.int16).fill_(sentinel)
+        vp.view(torch.int16).fill_(sentinel)
+        tabs = torch.from_numpy(w.tables).to(dev)
+        if w.total_history_tokens():
+            pkv.paged_kv_append_tokens(kp, vp, up(w.k_src), up(w.v_src),
+                                       torch.from_numpy(w.seg_cu).to(dev),
+                                       torch.from_numpy(w.seg_start).to(dev),
+                                       torch.from_numpy(w.seg_tables).to(dev))
+        layers.append(dict(k=kp, v=vp, q=up(w.q), kn=up(w.k_new), vn=up(w.v_new)))
+        torch.cuda.synchronize()
+        del tabs
+    tables = torch.from_numpy(w0.tables).to(dev)
+    lens = torch.from_numpy(w0.lengths).to(dev)
+    S, Hq, D = cfg.num_seqs, cfg.num_q_heads, cfg.head_dim
+    out = torch.empty((cfg.num_layers, S, Hq, D), dtype=tdt, device=dev)
+    mp = pkv.max_partitions(cfg.max_blocks_per_seq, cfg.block_size, P) if P else 0
+    part_o = torch.empty((S, Hq, mp, D), dtype=torch.float32, device=dev) if P else None
+    part_lse = torch.empty((S, Hq, mp), dtype=torch.float32, device=dev) if P else None
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+
+    def step(events=None):
+        for li in range(cfg.num_layers):
+            L = layers[li % R]
+            pkv.paged_kv_append(L["k"], L["v"], L["kn"], L["vn"], tables, lens)
+            if events is not None:
+                events[li][0].record()
+            if P:
+                pkv.paged_attention_decode(None, L["q"], L["k"], L["v"], tables, lens,
+                                           scale=scale, partition_size=P, part_o=part_o,
+                                           part_lse=part_lse)
+            else:
+                pkv.paged_attention_decode(out[li], L["q"], L["k"], L["v"], tables, lens,
+                                           scale=scale)
+            if events is not None:
+                events[li][1].record()
+            if P:
+                pkv.paged_attention_reduce(out[li], part_o, part_lse, lens, P)
+
+    # ---- timed region ------------------------------------------------------------
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # ---- per-launch duration of the dominant kernel (same launches, HIP events) ---
+    durs = []
+    for _ in range(max(1, min(args.steps, 10))):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(cfg.num_layers)]
+        step(ev)
+        torch.cuda.synchronize()
+        durs += [a.elapsed_time(b) for a, b in ev]
+    decode_ms = float(np.mean(durs))
+
+    assert bool(torch.isfinite(out.float()).all()), "non-finite attention output"
+
+    # ---- accounting -------------------------------------------------------------------
+    nblk = int(np.sum(-(-w0.lengths.astype(np.int64) // cfg.block_size)))
+    ab = algorithmic_bytes(cfg, w0.lengths, nblk)
+    step_bytes = ab["layer"] * cfg.num_layers
+    gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+    tokens_per_s = S / (ms_per_step * 1e-3)
+    dec_gbps = ab["decode"] / (decode_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded; N(0,1) x %g values, %s lengths)" % (cfg.value_scale,
+                                                                      cfg.length_kind),
+        "config": {
+            "workload": f"{cfg.key}: {cfg.title}",
+            "num_seqs": S, "layers": cfg.num_layers, "q_heads": Hq,
+            "kv_heads": cfg.num_kv_heads, "head_dim": D, "block_size": cfg.block_size,
+            "mean_context": round(float(np.mean(w0.lengths)), 2),
+            "max_context": int(np.max(w0.lengths)),
+            "pool_blocks_per_layer": int(w0.num_blocks),
+            "distinct_layer_pools": R,
+            "partition_size": P,
+            "accumulate": "fp32",
+        },
+        "hbm_gbps": round(gbps, 1),
+        "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "step_algorithmic_bytes": step_bytes,
+        "roofline": {
+            "kernel": "paged_attention_decode",
+            "bound": "hbm",
+            "achieved": round(dec_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "bytes_per_launch": ab["decode"],
+            "avg_launch_ms": round(decode_ms, 5),
+        },
+        "setup_s": round(setup_s, 1),
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w0, cfg, scale, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, cfg, scale, budget_s):
+    """Time the fp64 oracle on one layer of the same workload (append + attention of
+    every sequence and head), repeated until about `budget_s` seconds of CPU time,
+    and scale to the whole step (all layers)."""
+    from oracle import oracle as O
+    c = cfg
+    kp, vp = O.new_pools(w.num_blocks, c.num_kv_heads, c.block_size, c.head_dim, w.nan_bits)
+    O.append_tokens(kp, vp, w.k_src, w.v_src, w.seg_cu, w.seg_start, w.seg_tables,
+                    c.block_size, w.num_blocks)
+    threads = O.max_threads(0)
+    reps, spent = 0, 0.0
+    while reps == 0 or (spent < budget_s and reps < 50):
+        t = time.perf_counter()
+        O.append(kp, vp, w.k_new, w.v_new, w.tables, w.lengths, c.block_size, w.num_blocks)
+        O.attention(w.q, kp, vp, w.tables, w.lengths, c.num_kv_heads, c.block_size,
+                    w.num_blocks, scale, c.dtype, threads)
+        spent += time.perf_counter() - t
+        reps += 1
+    per_layer = spent / reps
+    step_s = per_layer * c.num_layers
+    return {
+        "value": round(c.num_seqs / step_s, 3),
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"layer 0 of {c.num_layers} ({c.num_seqs} sequences x {c.num_q_heads} heads, "
+                   f"append + fp64 attention), {reps} repetitions, {spent:.1f} s; "
+                   f"step time = per-layer time x {c.num_layers}"),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,171 @@
+/*
+ * paged_kv.h -- C ABI of the MI355X (gfx950) paged KV-cache decode library
+ * (libpagedkv.so).
+ *
+ * The library implements the decode-step hot path of PagedAttention: the KV cache
+ * of every sequence lives in fixed-size physical blocks of one pre-allocated pool,
+ * and a per-sequence block table maps logical block i to a physical block id
+ * (page "显存虚拟化革命：PagedAttention 内存池管理与显存碎片终结", blog.llmgo.top,
+ * §二.1 and §三.1; page "端侧 SLM 显存保活术：在 4GB 内存板卡上实现轻量
+ * PagedAttention 与 KV 缓存分块", pwwt.cn, section "注意力寻址").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory. Every pointer argument except `stream` is a DEVICE pointer, allocated
+ *   and owned by the caller.  The library allocates nothing and keeps no state
+ *   between calls; calls on different streams are independent.
+ * Asynchrony. Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *   stream) and the call returns without synchronising.  The return value only
+ *   reports argument errors and launch failures.
+ * Data types. `dtype` is PKV_FP16 (IEEE binary16) or PKV_BF16 (bfloat16) and
+ *   applies to the pools, q, the new K/V rows and the output.  Arithmetic is
+ *   fp32; outputs are rounded to `dtype` with round-to-nearest-even.
+ * Pool layout. One K pool and one V pool per layer, each
+ *     [num_blocks][num_kv_heads][block_size][head_dim]
+ *   row-major with head_dim contiguous, 16-byte aligned.  Token t of a sequence
+ *   lives in physical block table[t / block_size] at offset t % block_size.
+ * Block tables. int32 [num_seqs][max_blocks_per_seq], row-major (the flat 2-D
+ *   int32 tensor of the kernel sketch in §五.1 of the blog.llmgo.top page).  Only
+ *   entries of blocks that hold tokens are read; other entries may be anything
+ *   (-1 is conventional).
+ * Context lengths. int32 [num_seqs]: n = the number of tokens the step attends
+ *   to, INCLUDING the token appended in the same step (it sits at position n-1).
+ *   n = 0 marks a padding sequence.
+ * Caller contract (not checked unless PKV_DEBUG_CHECK=1 is set in the
+ *   environment): 0 <= n <= max_blocks_per_seq * block_size; table entries of
+ *   blocks 0 .. ceil(n/block_size)-1 lie in [0, num_blocks); no two sequences
+ *   append to the same slot in one call.  With PKV_DEBUG_CHECK=1 each call first
+ *   runs a device-side check of these, synchronises `stream`, and returns
+ *   PKV_EDEVICE if one fails.
+ * Supported shapes: head_dim = 128; block_size in {16, 32, 64, 128, 256};
+ *   num_q_heads a multiple of num_kv_heads with a group of at most 16 query
+ *   heads per KV head.  Others give PKV_ENOTSUP.
+ */
+#ifndef PAGED_KV_H
+#define PAGED_KV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define PKV_OK 0
+#define PKV_EINVAL (-1)     /* null pointer, non-positive size, bad ratio or alignment */
+#define PKV_ENOTSUP (-2)    /* valid but unsupported shape or dtype */
+#define PKV_EWORKSPACE (-3) /* partition workspace missing or too small */
+#define PKV_ELAUNCH (-4)    /* the HIP runtime rejected a kernel launch */
+#define PKV_EDEVICE (-5)    /* PKV_DEBUG_CHECK found a caller-contract violation */
+
+/* storage formats */
+#define PKV_FP16 0
+#define PKV_BF16 1
+
+/* Human-readable text of a status code (static storage). */
+const char *pkv_status_string(int status);
+
+/*
+ * paged_kv_append -- the cache-append scatter of one decode step.
+ *
+ * For each sequence s with n = context_lens[s] >= 1, writes the new token's rows
+ * k_new[s][h][:] and v_new[s][h][:] (all heads h) to position t = n-1, i.e. to
+ * offset t % block_size of physical block block_tables[s][t / block_size] of
+ * k_pool / v_pool.  A token that opens a new block lands at offset 0 of the block
+ * the host has just appended to the table (blog.llmgo.top page, §三, sequence
+ * diagram; hnwysp.cn KV-Cache/BlockManager page, §4.5, write_kv).  Bit copy.
+ *
+ *   k_pool, v_pool  [num_blocks][num_kv_heads][block_size][head_dim], written
+ *   k_new, v_new    [num_seqs][num_kv_heads][head_dim]
+ *   slot_out        optional (may be NULL), int64 [num_seqs]: receives
+ *                   phys * block_size + offset, or -1 when n == 0
+ * Sequences with n == 0 write nothing.
+ */
+int paged_kv_append(void *k_pool, void *v_pool, const void *k_new, const void *v_new,
+                    const int32_t *block_tables, const int32_t *context_lens, int64_t *slot_out,
+                    int num_seqs, int num_kv_heads, int head_dim, int block_size,
+                    int max_blocks_per_seq, int64_t num_blocks, int dtype, void *stream);
+
+/*
+ * paged_kv_append_tokens -- scatter runs of consecutive tokens (a prompt, a
+ * prefill chunk, or any history) into their blocks.
+ *
+ * Run r writes rows src_cu[r] .. src_cu[r+1]-1 of k_src / v_src to logical
+ * positions start_pos[r], start_pos[r]+1, ... of table row r (a 38-token prompt
+ * written to blocks [7, 3, 12] leaves block 12 holding 6 tokens: blog.llmgo.top
+ * page, §三).  Bit copy with the same walk as paged_kv_append.
+ *
+ *   k_src, v_src   [total_tokens][num_kv_heads][head_dim]
+ *   src_cu         int64 [num_runs + 1], src_cu[0] = 0, non-decreasing,
+ *                  src_cu[num_runs] = total_tokens (host value passed as well)
+ *   start_pos      int32 [num_runs], >= 0
+ *   block_tables   int32 [num_runs][max_blocks_per_seq]
+ * Positions past max_blocks_per_seq * block_size are a caller error.
+ */
+int paged_kv_append_tokens(void *k_pool, void *v_pool, const void *k_src, const void *v_src,
+                           const int64_t *src_cu, const int32_t *start_pos,
+                           const int32_t *block_tables, int num_runs, int64_t total_tokens,
+                           int num_kv_heads, int head_dim, int block_size,
+                           int max_blocks_per_seq, int64_t num_blocks, int dtype, void *stream);
+
+/*
+ * paged_attention_decode -- decode attention over the paged pools.
+ *
+ * For every sequence s and query head h (KV head g = h / (num_q_heads /
+ * num_kv_heads)):  out[s][h] = sum_t softmax_t(scale * q[s][h] . K_t) V_t over the
+ * logical tokens t = 0 .. n-1, each fetched through the block table (the kernel
+ * sketch of §五.1 of the blog.llmgo.top page: loop over logical blocks, look up
+ * the physical block, load its K/V tile, accumulate QK^T with a running softmax,
+ * normalise, store).  The result equals ordinary attention over the contiguous
+ * logical sequence.
+ *
+ *   out            [num_seqs][num_q_heads][head_dim], dtype (single-pass mode)
+ *   q              [num_seqs][num_q_heads][head_dim], dtype
+ *   scale          softmax scale, usually 1/sqrt(head_dim)
+ *   partition_size 0: single pass, each (sequence, KV head) is handled whole and
+ *                  `out` is written; part_o/part_lse/max_partitions are ignored.
+ *                  > 0: split-context mode; must be a multiple of block_size and
+ *                  of 32.  Partition p covers tokens [p*P, min(n, (p+1)*P)) and
+ *                  writes part_o[s][h][p][:] (fp32, that partition's normalised
+ *                  attention output) and part_lse[s][h][p] (fp32, natural-log
+ *                  log-sum-exp of the partition's scaled scores).  Partitions
+ *                  p >= ceil(n/P) are not written, and `out` is not touched:
+ *                  call paged_attention_reduce afterwards.
+ *   max_partitions row stride of the workspace; must be at least
+ *                  ceil(max_blocks_per_seq * block_size / partition_size),
+ *                  else PKV_EWORKSPACE.
+ *   part_o         fp32 [num_seqs][num_q_heads][max_partitions][head_dim]
+ *   part_lse       fp32 [num_seqs][num_q_heads][max_partitions]
+ * n == 0 gives an all-zero output row in single-pass mode.
+ */
+int paged_attention_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
+                           const int32_t *block_tables, const int32_t *context_lens,
+                           int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                           int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                           float scale, int partition_size, int max_partitions, float *part_o,
+                           float *part_lse, int dtype, void *stream);
+
+/*
+ * paged_attention_reduce -- log-sum-exp merge of split-context partitions.
+ *
+ * For each (s, h) with P = partition_size and np = ceil(n/P) partitions:
+ *   M = max_p part_lse[s][h][p],  w_p = exp(part_lse[s][h][p] - M),
+ *   out[s][h][:] = sum_p w_p part_o[s][h][p][:] / sum_p w_p   (p < np),
+ * rounded to dtype; n == 0 gives zeros.  Exact in real arithmetic: softmax over
+ * a union of token ranges is the lse-weighted mean of the per-range softmaxes
+ * (not on the pages; the pages describe no partitioning).
+ */
+int paged_attention_reduce(void *out, const float *part_o, const float *part_lse,
+                           const int32_t *context_lens, int num_seqs, int num_q_heads,
+                           int head_dim, int partition_size, int max_partitions, int dtype,
+                           void *stream);
+
+/* Smallest valid max_partitions for a table width and partition size (0 if the
+ * arguments are invalid). */
+int pkv_max_partitions(int max_blocks_per_seq, int block_size, int partition_size);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_KV_H */

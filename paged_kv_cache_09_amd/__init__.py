@@ -1,0 +1,22 @@
+"""MI355X (gfx950) paged KV-cache decode library: Python binding of libpagedkv.so.
+
+The functions here only marshal torch tensors into the C ABI declared in
+include/paged_kv.h (device pointers, sizes, the current HIP stream); every step of
+the computation runs in the library's HIP kernels.  Importing this package does
+not load the library; the first call does, and fails loudly if it is not built.
+"""
+from ._lib import (  # noqa: F401
+    PKV_BF16,
+    PKV_FP16,
+    PagedKVError,
+    exported_symbols,
+    header_symbols,
+    lib_path,
+    load,
+    max_partitions,
+    paged_attention_decode,
+    paged_attention_reduce,
+    paged_kv_append,
+    paged_kv_append_tokens,
+    status_string,
+)

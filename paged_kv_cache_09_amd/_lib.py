@@ -1,0 +1,195 @@
+"""ctypes binding of libpagedkv.so: the C ABI of include/paged_kv.h with torch
+tensors as arguments.  Argument marshalling only -- shapes are read from the
+tensors, pointers and the current HIP stream are passed through, and a non-zero
+status becomes a PagedKVError.  There is no CPU fallback: tensors must live on a
+GPU and the library must be built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+import os
+import re
+from typing import List, Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_ROOT = os.path.dirname(_HERE)
+_LIB = os.path.join(_HERE, "libpagedkv.so")
+_HEADER = os.path.join(_ROOT, "include", "paged_kv.h")
+
+PKV_FP16, PKV_BF16 = 0, 1
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+def load():
+    """Load libpagedkv.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        raise ImportError(f"{_LIB} is not built; run: python -m paged_kv_cache_09_amd.build")
+    L = C.CDLL(_LIB)
+    P, i32, i64, f32 = C.c_void_p, C.c_int, C.c_int64, C.c_float
+    L.pkv_status_string.argtypes = [i32]
+    L.pkv_status_string.restype = C.c_char_p
+    L.pkv_max_partitions.argtypes = [i32, i32, i32]
+    L.pkv_max_partitions.restype = i32
+    L.paged_kv_append.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i64, i32, P]
+    L.paged_kv_append.restype = i32
+    L.paged_kv_append_tokens.argtypes = [P, P, P, P, P, P, P, i32, i64, i32, i32, i32, i32, i64,
+                                         i32, P]
+    L.paged_kv_append_tokens.restype = i32
+    L.paged_attention_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i64, f32,
+                                         i32, i32, P, P, i32, P]
+    L.paged_attention_decode.restype = i32
+    L.paged_attention_reduce.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, P]
+    L.paged_attention_reduce.restype = i32
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    try:
+        return load().pkv_status_string(status).decode()
+    except ImportError:
+        return str(status)
+
+
+def header_symbols() -> List[str]:
+    """Function names declared in include/paged_kv.h."""
+    with open(_HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def exported_symbols() -> List[str]:
+    L = load()
+    return [s for s in header_symbols() if hasattr(L, s)]
+
+
+def max_partitions(max_blocks_per_seq: int, block_size: int, partition_size: int) -> int:
+    return load().pkv_max_partitions(max_blocks_per_seq, block_size, partition_size)
+
+
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return PKV_FP16
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float16 or bfloat16")
+
+
+def _dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU (no CPU path exists)")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("tensors are on different devices")
+    return dev
+
+
+def _p(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return C.c_void_p(_torch().cuda.current_stream(dev).cuda_stream)
+
+
+def _int(t, dtype, name):
+    torch = _torch()
+    want = {"i32": torch.int32, "i64": torch.int64}[dtype]
+    if t is not None and t.dtype != want:
+        raise TypeError(f"{name} must be {want}, got {t.dtype}")
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise PagedKVError(rc, what)
+
+
+# ---------------------------------------------------------------------------
+def paged_kv_append(k_pool, v_pool, k_new, v_new, block_tables, context_lens, slot_out=None):
+    """Write each sequence's new K/V row to position context_lens[s]-1."""
+    dev = _dev(k_pool, v_pool, k_new, v_new, block_tables, context_lens, slot_out)
+    _int(block_tables, "i32", "block_tables")
+    _int(context_lens, "i32", "context_lens")
+    _int(slot_out, "i64", "slot_out")
+    NB, Hkv, B, D = k_pool.shape
+    S = k_new.shape[0]
+    rc = load().paged_kv_append(_p(k_pool), _p(v_pool), _p(k_new), _p(v_new), _p(block_tables),
+                                _p(context_lens), _p(slot_out), S, Hkv, D, B,
+                                block_tables.shape[1], NB, _dtype_code(k_pool), _stream(dev))
+    _check(rc, "paged_kv_append")
+
+
+def paged_kv_append_tokens(k_pool, v_pool, k_src, v_src, src_cu, start_pos, block_tables):
+    """Write runs of tokens: run r puts rows src_cu[r]..src_cu[r+1]-1 at positions
+    start_pos[r].. of table row r."""
+    dev = _dev(k_pool, v_pool, k_src, v_src, src_cu, start_pos, block_tables)
+    _int(src_cu, "i64", "src_cu")
+    _int(start_pos, "i32", "start_pos")
+    _int(block_tables, "i32", "block_tables")
+    NB, Hkv, B, D = k_pool.shape
+    rc = load().paged_kv_append_tokens(_p(k_pool), _p(v_pool), _p(k_src), _p(v_src), _p(src_cu),
+                                       _p(start_pos), _p(block_tables), block_tables.shape[0],
+                                       k_src.shape[0], Hkv, D, B, block_tables.shape[1], NB,
+                                       _dtype_code(k_pool), _stream(dev))
+    _check(rc, "paged_kv_append_tokens")
+
+
+def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens,
+                           scale: Optional[float] = None, partition_size: int = 0,
+                           part_o=None, part_lse=None):
+    """Decode attention; single pass (partition_size 0) writes `out`, split mode
+    writes part_o/part_lse (then call paged_attention_reduce)."""
+    dev = _dev(out, q, k_pool, v_pool, block_tables, context_lens, part_o, part_lse)
+    _int(block_tables, "i32", "block_tables")
+    _int(context_lens, "i32", "context_lens")
+    NB, Hkv, B, D = k_pool.shape
+    S, Hq, _ = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    mp = part_o.shape[2] if part_o is not None else 0
+    rc = load().paged_attention_decode(_p(out), _p(q), _p(k_pool), _p(v_pool), _p(block_tables),
+                                       _p(context_lens), S, Hq, Hkv, D, B, block_tables.shape[1],
+                                       NB, float(scale), int(partition_size), mp, _p(part_o),
+                                       _p(part_lse), _dtype_code(q), _stream(dev))
+    _check(rc, "paged_attention_decode")
+
+
+def paged_attention_reduce(out, part_o, part_lse, context_lens, partition_size: int):
+    """Log-sum-exp merge of split-context partitions into `out`."""
+    dev = _dev(out, part_o, part_lse, context_lens)
+    _int(context_lens, "i32", "context_lens")
+    S, Hq, MP, D = part_o.shape
+    rc = load().paged_attention_reduce(_p(out), _p(part_o), _p(part_lse), _p(context_lens), S, Hq,
+                                       D, int(partition_size), MP, _dtype_code(out), _stream(dev))
+    _check(rc, "paged_attention_reduce")

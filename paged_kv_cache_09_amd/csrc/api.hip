@@ -1,0 +1,341 @@
+// api.hip -- the C ABI of libpagedkv (declared in include/paged_kv.h): argument
+// validation, kernel selection and launch on the caller's stream.
+//
+// Validation happens entirely on the host before any HIP call, so a bad argument
+// returns a status without touching the device.  With PKV_DEBUG_CHECK=1 in the
+// environment, each call additionally checks the device-resident caller contract
+// (context lengths and block-table entries) with a small kernel, synchronises the
+// stream and returns PKV_EDEVICE on a violation.
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/paged_kv.h"
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+namespace {
+
+__device__ int g_debug_flag;  // set by the debug-check kernels, never by the hot path
+
+__global__ void debug_clear_kernel() { g_debug_flag = 0; }
+
+__global__ void debug_tables_kernel(const int32_t *tables, const int32_t *lens, int num_seqs,
+                                    int width, int block_size, int64_t num_blocks)
+{
+    const int s = blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= num_seqs)
+        return;
+    const int n = lens[s];
+    if (n < 0 || (int64_t)n > (int64_t)width * block_size) {
+        atomicOr(&g_debug_flag, 1);
+        return;
+    }
+    const int nb = (n + block_size - 1) / block_size;
+    for (int b = 0; b < nb; ++b) {
+        const int32_t p = tables[(int64_t)s * width + b];
+        if (p < 0 || p >= num_blocks)
+            atomicOr(&g_debug_flag, 2);
+    }
+}
+
+__global__ void debug_runs_kernel(const int64_t *cu, const int32_t *start_pos,
+                                  const int32_t *tables, int num_runs, int64_t total_tokens,
+                                  int width, int block_size, int64_t num_blocks)
+{
+    const int r = blockIdx.x * blockDim.x + threadIdx.x;
+    if (r > num_runs)
+        return;
+    if (r == 0 && cu[0] != 0)
+        atomicOr(&g_debug_flag, 4);
+    if (r == num_runs) {
+        if (cu[num_runs] != total_tokens)
+            atomicOr(&g_debug_flag, 4);
+        return;
+    }
+    const int64_t cnt = cu[r + 1] - cu[r];
+    const int64_t st = start_pos[r];
+    if (cnt < 0 || st < 0 || st + cnt > (int64_t)width * block_size) {
+        atomicOr(&g_debug_flag, 8);
+        return;
+    }
+    if (cnt == 0)
+        return;
+    for (int64_t b = st / block_size; b <= (st + cnt - 1) / block_size; ++b) {
+        const int32_t p = tables[(int64_t)r * width + b];
+        if (p < 0 || p >= num_blocks)
+            atomicOr(&g_debug_flag, 2);
+    }
+}
+
+int read_debug_flag(hipStream_t stream)
+{
+    int flag = 0;
+    if (hipMemcpyFromSymbolAsync(&flag, HIP_SYMBOL(g_debug_flag), sizeof(int), 0,
+                                 hipMemcpyDeviceToHost, stream) != hipSuccess)
+        return PKV_ELAUNCH;
+    if (hipStreamSynchronize(stream) != hipSuccess)
+        return PKV_ELAUNCH;
+    return flag ? PKV_EDEVICE : PKV_OK;
+}
+
+}  // namespace
+
+int debug_check_tables(const int32_t *tables, const int32_t *lens, int num_seqs, int width,
+                       int block_size, int64_t num_blocks, hipStream_t stream)
+{
+    hipLaunchKernelGGL(debug_clear_kernel, dim3(1), dim3(1), 0, stream);
+    hipLaunchKernelGGL(debug_tables_kernel, dim3((num_seqs + 255) / 256), dim3(256), 0, stream,
+                       tables, lens, num_seqs, width, block_size, num_blocks);
+    if (hipGetLastError() != hipSuccess)
+        return PKV_ELAUNCH;
+    return read_debug_flag(stream);
+}
+
+int debug_check_runs(const int64_t *cu, const int32_t *start_pos, const int32_t *tables,
+                     int num_runs, int64_t total_tokens, int width, int block_size,
+                     int64_t num_blocks, hipStream_t stream)
+{
+    hipLaunchKernelGGL(debug_clear_kernel, dim3(1), dim3(1), 0, stream);
+    hipLaunchKernelGGL(debug_runs_kernel, dim3((num_runs + 1 + 255) / 256), dim3(256), 0, stream,
+                       cu, start_pos, tables, num_runs, total_tokens, width, block_size,
+                       num_blocks);
+    if (hipGetLastError() != hipSuccess)
+        return PKV_ELAUNCH;
+    return read_debug_flag(stream);
+}
+
+}  // namespace pkv
+
+namespace {
+
+// Read on every call so that a process can switch the check on and off.
+bool debug_enabled()
+{
+    const char *e = getenv("PKV_DEBUG_CHECK");
+    return e && e[0] && strcmp(e, "0") != 0;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool supported_block(int b) { return b == 16 || b == 32 || b == 64 || b == 128 || b == 256; }
+
+// Checks shared by the pool-facing entry points.
+int check_pool_shape(int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                     int64_t num_blocks, int dtype)
+{
+    if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 ||
+        num_blocks <= 0)
+        return PKV_EINVAL;
+    if (dtype != PKV_FP16 && dtype != PKV_BF16)
+        return PKV_ENOTSUP;
+    if (head_dim != pkv::kHeadDim || !supported_block(block_size))
+        return PKV_ENOTSUP;
+    // the largest element offset must fit the 64-bit address arithmetic
+    if (num_blocks > (int64_t)1 << 40)
+        return PKV_EINVAL;
+    return PKV_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ELAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char *pkv_status_string(int status)
+{
+    switch (status) {
+    case PKV_OK:
+        return "ok";
+    case PKV_EINVAL:
+        return "invalid argument";
+    case PKV_ENOTSUP:
+        return "unsupported shape or dtype";
+    case PKV_EWORKSPACE:
+        return "partition workspace missing or too small";
+    case PKV_ELAUNCH:
+        return "kernel launch failed";
+    case PKV_EDEVICE:
+        return "device-side check failed (context length or block-table entry out of range)";
+    default:
+        return "unknown status";
+    }
+}
+
+int pkv_max_partitions(int max_blocks_per_seq, int block_size, int partition_size)
+{
+    if (max_blocks_per_seq <= 0 || block_size <= 0 || partition_size <= 0)
+        return 0;
+    const int64_t ctx = (int64_t)max_blocks_per_seq * block_size;
+    const int64_t mp = (ctx + partition_size - 1) / partition_size;
+    return mp > INT32_MAX ? 0 : (int)mp;
+}
+
+int paged_kv_append(void *k_pool, void *v_pool, const void *k_new, const void *v_new,
+                    const int32_t *block_tables, const int32_t *context_lens, int64_t *slot_out,
+                    int num_seqs, int num_kv_heads, int head_dim, int block_size,
+                    int max_blocks_per_seq, int64_t num_blocks, int dtype, void *stream)
+{
+    if (!k_pool || !v_pool || !k_new || !v_new || !block_tables || !context_lens)
+        return PKV_EINVAL;
+    if (num_seqs < 0)
+        return PKV_EINVAL;
+    int rc = check_pool_shape(num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                              dtype);
+    if (rc)
+        return rc;
+    if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new) ||
+        ((uintptr_t)slot_out & 7u))
+        return PKV_EINVAL;
+    if ((int64_t)num_seqs * num_kv_heads * 2 * (pkv::kHeadDim / 8) > ((int64_t)1 << 31) * 255)
+        return PKV_EINVAL;
+    if (num_seqs == 0)
+        return PKV_OK;
+    hipStream_t st = (hipStream_t)stream;
+    if (debug_enabled()) {
+        rc = pkv::debug_check_tables(block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                                     block_size, num_blocks, st);
+        if (rc)
+            return rc;
+    }
+    return launch_status(pkv::launch_append(k_pool, v_pool, k_new, v_new, block_tables,
+                                            context_lens, slot_out, num_seqs, num_kv_heads,
+                                            block_size, max_blocks_per_seq, st));
+}
+
+int paged_kv_append_tokens(void *k_pool, void *v_pool, const void *k_src, const void *v_src,
+                           const int64_t *src_cu, const int32_t *start_pos,
+                           const int32_t *block_tables, int num_runs, int64_t total_tokens,
+                           int num_kv_heads, int head_dim, int block_size,
+                           int max_blocks_per_seq, int64_t num_blocks, int dtype, void *stream)
+{
+    if (!k_pool || !v_pool || !src_cu || !start_pos || !block_tables)
+        return PKV_EINVAL;
+    if (num_runs < 0 || total_tokens < 0)
+        return PKV_EINVAL;
+    if (total_tokens > 0 && (!k_src || !v_src))
+        return PKV_EINVAL;
+    int rc = check_pool_shape(num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                              dtype);
+    if (rc)
+        return rc;
+    if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_src) || !aligned16(v_src))
+        return PKV_EINVAL;
+    if (total_tokens * num_kv_heads * 2 * (pkv::kHeadDim / 8) > ((int64_t)1 << 31) * 255)
+        return PKV_EINVAL;
+    if (num_runs == 0 || total_tokens == 0)
+        return PKV_OK;
+    hipStream_t st = (hipStream_t)stream;
+    if (debug_enabled()) {
+        rc = pkv::debug_check_runs(src_cu, start_pos, block_tables, num_runs, total_tokens,
+                                   max_blocks_per_seq, block_size, num_blocks, st);
+        if (rc)
+            return rc;
+    }
+    return launch_status(pkv::launch_append_tokens(k_pool, v_pool, k_src, v_src, src_cu,
+                                                   start_pos, block_tables, num_runs,
+                                                   total_tokens, num_kv_heads, block_size,
+                                                   max_blocks_per_seq, st));
+}
+
+int paged_attention_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
+                           const int32_t *block_tables, const int32_t *context_lens,
+                           int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                           int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                           float scale, int partition_size, int max_partitions, float *part_o,
+                           float *part_lse, int dtype, void *stream)
+{
+    if (!q || !k_pool || !v_pool || !block_tables || !context_lens)
+        return PKV_EINVAL;
+    if (num_seqs < 0 || num_q_heads <= 0 || partition_size < 0)
+        return PKV_EINVAL;
+    int rc = check_pool_shape(num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                              dtype);
+    if (rc)
+        return rc;
+    if (num_q_heads % num_kv_heads != 0)
+        return PKV_EINVAL;
+    const int group = num_q_heads / num_kv_heads;
+    if (group > 16)
+        return PKV_ENOTSUP;
+    if (!(scale == scale) || __builtin_isinf(scale))
+        return PKV_EINVAL;
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+        return PKV_EINVAL;
+    int parts = 1;
+    if (partition_size > 0) {
+        if (partition_size % block_size != 0 || partition_size % 32 != 0)
+            return PKV_EINVAL;
+        const int need = pkv_max_partitions(max_blocks_per_seq, block_size, partition_size);
+        if (!part_o || !part_lse || max_partitions < need || need <= 0)
+            return PKV_EWORKSPACE;
+        if (!aligned16(part_o) || ((uintptr_t)part_lse & 3u))
+            return PKV_EINVAL;
+        parts = need;
+    } else {
+        if (!out || ((uintptr_t)out & 1u))
+            return PKV_EINVAL;
+    }
+    const int64_t items = (int64_t)num_seqs * num_kv_heads * parts;
+    if (items > INT32_MAX)
+        return PKV_EINVAL;
+    if (items == 0)
+        return PKV_OK;
+    hipStream_t st = (hipStream_t)stream;
+    if (debug_enabled()) {
+        rc = pkv::debug_check_tables(block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                                     block_size, num_blocks, st);
+        if (rc)
+            return rc;
+    }
+    pkv::DecodeArgs a;
+    a.out = out;
+    a.q = q;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.tables = block_tables;
+    a.lens = context_lens;
+    a.part_o = part_o;
+    a.part_lse = part_lse;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.width = max_blocks_per_seq;
+    a.partition_size = partition_size;
+    a.max_partitions = partition_size > 0 ? max_partitions : 0;
+    a.parts_per_item = parts;
+    a.n_items = (int)items;
+    a.scale_log2 = scale * pkv::kLog2e;
+    const hipError_t e = group == 1 ? pkv::launch_decode_g1(a, dtype, block_size, st)
+                                    : pkv::launch_decode_mfma(a, dtype, block_size, st);
+    return launch_status(e);
+}
+
+int paged_attention_reduce(void *out, const float *part_o, const float *part_lse,
+                           const int32_t *context_lens, int num_seqs, int num_q_heads,
+                           int head_dim, int partition_size, int max_partitions, int dtype,
+                           void *stream)
+{
+    if (!out || !part_o || !part_lse || !context_lens)
+        return PKV_EINVAL;
+    if (num_seqs < 0 || num_q_heads <= 0 || partition_size <= 0 || max_partitions <= 0)
+        return PKV_EINVAL;
+    if (dtype != PKV_FP16 && dtype != PKV_BF16)
+        return PKV_ENOTSUP;
+    if (head_dim != pkv::kHeadDim)
+        return PKV_ENOTSUP;
+    if (((uintptr_t)out & 3u) || ((uintptr_t)part_o & 7u) || ((uintptr_t)part_lse & 3u))
+        return PKV_EINVAL;
+    const int64_t waves = (int64_t)num_seqs * num_q_heads;
+    if (waves > INT32_MAX / 64)
+        return PKV_EINVAL;
+    if (waves == 0)
+        return PKV_OK;
+    return launch_status(pkv::launch_reduce(out, part_o, part_lse, context_lens, num_seqs,
+                                            num_q_heads, partition_size, max_partitions, dtype,
+                                            (hipStream_t)stream));
+}
+
+}  // extern "C"

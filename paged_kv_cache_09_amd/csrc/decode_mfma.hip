@@ -1,0 +1,325 @@
+// decode_mfma.hip -- paged decode attention for grouped-query attention (GQA).
+//
+// What it computes: the G = Hq/Hkv query heads that share KV head g attend over
+// the logical tokens of their sequence, each K/V row fetched through the block
+// table (page "显存虚拟化革命：PagedAttention 内存池管理与显存碎片终结",
+// blog.llmgo.top, §五.1 kernel sketch; GQA compatibility in its FAQ Q3; the
+// 12-query / 2-KV-head edge model of the pwwt.cn page, section "KV Cache 的物理
+// 膨胀账本").
+//
+// gfx950 design.  A GQA group turns Q.K^T and P.V into dense tiles, so both go to
+// the matrix cores (the group of G <= 16 query rows is padded to 16):
+//   * a work-group is 4 wave64s; one work-group per (sequence, KV head[, partition]);
+//     the waves take 16-token sub-tiles round-robin, double-buffered in VGPRs;
+//   * scores: S^T[16 tok x 16 q] = K[16 x 128] . Q^T with four
+//     v_mfma_f32_16x16x32_{f16,bf16}.  K rows are the A operand and are loaded
+//     straight from HBM with 16-byte loads (lane i+16j holds 8 dims of token i);
+//     Q^T is the B operand, loaded once;
+//   * the accumulator layout of S^T (lane j+16k holds tokens 4k..4k+3 of query
+//     row j) is exactly the B-operand layout of v_mfma_f32_16x16x16 for P^T, so
+//     the probabilities feed P.V without any data movement;
+//   * the V tile must enter P.V with tokens along the contraction axis, i.e.
+//     transposed with respect to the pool's row-major [token][dim] layout.  It is
+//     staged through LDS: coalesced 16-byte global loads, 16-byte LDS writes into
+//     a padded row-major tile, then 2-byte transposing reads (row stride of 272
+//     bytes keeps the four lane groups on disjoint banks);
+//   * online softmax per query row in the exp2 domain: the row max is reduced
+//     across the four lane groups holding the row, the running sum is kept per
+//     lane and reduced once at the end; waves are merged through LDS with the
+//     log-sum-exp rule.
+// Masked positions (tokens >= n in the last block, stale data of reused blocks)
+// get score -inf and a zeroed V row, so a NaN there cannot reach the output.
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kSub = 16;           // tokens per sub-tile
+constexpr int kVStride = 136;      // LDS row stride of a staged V tile, in 16-bit elements
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma_qk(const u32x4 &a, const u32x4 &b, f32x4 c)
+{
+    if constexpr (DT == kFp16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma_pv(const u32x2 &a, const u32x2 &b, f32x4 c)
+{
+    if constexpr (DT == kFp16)
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                     __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                         __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+
+struct SubTile {
+    u32x4 k[4];  // A operand of the four score MFMAs
+    u32x4 v[4];  // rows 4j + lane/16, dims 8*(lane%16).. of the V tile
+};
+
+// Loads of the 16-token sub-tile starting at token tb (block tb/BS holds all 16).
+template <int BS>
+__device__ __forceinline__ void load_sub(SubTile &t, const uint16_t *__restrict__ kp,
+                                         const uint16_t *__restrict__ vp,
+                                         const int32_t *__restrict__ trow, int tb,
+                                         int64_t head_off, int64_t blk_elems, int lane)
+{
+    const int64_t phys = trow[tb / BS];
+    const int64_t base = phys * blk_elems + head_off + (int64_t)(tb % BS) * kHeadDim;
+    const uint16_t *kb = kp + base + (lane & 15) * kHeadDim + (lane >> 4) * 8;
+    const uint16_t *vb = vp + base + lane * 8;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        t.k[kk] = *(const u32x4 *)(kb + kk * 32);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        t.v[j] = *(const u32x4 *)(vb + j * 512);
+}
+
+struct GqaState {
+    float m;        // running max of this lane's query row (uniform over the 4 lane groups)
+    float l;        // this lane's share of the running sum
+    f32x4 acc[8];   // O^T rows 16*jj + 4*(lane/16) + r, column = query row lane%16
+};
+
+template <int DT, bool PARTIAL>
+__device__ __forceinline__ void compute_sub(GqaState &st, const SubTile &t, const u32x4 *qop,
+                                            uint16_t *vlds, int tb, int t_end, int lane,
+                                            float scale_log2)
+{
+    const int col = lane & 15, grp = lane >> 4;
+    // stage V (row-major, padded) for the transposing reads below
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        *(u32x4 *)(vlds + (4 * j + grp) * kVStride + col * 8) = t.v[j];
+
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        s = mfma_qk<DT>(t.k[kk], qop[kk], s);
+
+    float sc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        sc[r] = s[r] * scale_log2;
+        if (PARTIAL && tb + 4 * grp + r >= t_end)
+            sc[r] = kNegInf;
+    }
+    float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mt = fmaxf(mt, xor_lane(mt, 16));
+    mt = fmaxf(mt, xor_lane(mt, 32));
+    const float m_new = fmaxf(st.m, mt);
+    const float ref = safe_ref(m_new);
+    const float alpha = fexp2(st.m - ref);
+    float p[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        p[r] = fexp2(sc[r] - ref);
+        psum += p[r];
+    }
+    st.l = st.l * alpha + psum;
+    st.m = m_new;
+    u32x2 pb;
+    pb.x = (uint32_t)to_bits<DT>(p[0]) | ((uint32_t)to_bits<DT>(p[1]) << 16);
+    pb.y = (uint32_t)to_bits<DT>(p[2]) | ((uint32_t)to_bits<DT>(p[3]) << 16);
+
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+        st.acc[jj] *= alpha;
+        const uint16_t *src = vlds + (4 * grp) * kVStride + 16 * jj + col;
+        uint32_t e0 = src[0], e1 = src[kVStride], e2 = src[2 * kVStride], e3 = src[3 * kVStride];
+        if (PARTIAL) {
+            const int tk = tb + 4 * grp;
+            if (tk + 0 >= t_end) e0 = 0;
+            if (tk + 1 >= t_end) e1 = 0;
+            if (tk + 2 >= t_end) e2 = 0;
+            if (tk + 3 >= t_end) e3 = 0;
+        }
+        u32x2 va;
+        va.x = e0 | (e1 << 16);
+        va.y = e2 | (e3 << 16);
+        st.acc[jj] = mfma_pv<DT>(va, pb, st.acc[jj]);
+    }
+    // the next sub-tile's LDS writes must not pass these reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int DT>
+__device__ __forceinline__ void compute_any(GqaState &st, const SubTile &t, const u32x4 *qop,
+                                            uint16_t *vlds, int tb, int t_end, int lane,
+                                            float scale_log2)
+{
+    if (tb + kSub <= t_end)
+        compute_sub<DT, false>(st, t, qop, vlds, tb, t_end, lane, scale_log2);
+    else
+        compute_sub<DT, true>(st, t, qop, vlds, tb, t_end, lane, scale_log2);
+}
+
+template <int DT, int BS>
+__global__ __launch_bounds__(kWaves * 64) void decode_mfma_kernel(DecodeArgs a)
+{
+    // V staging during the token loop; the cross-wave merge afterwards
+    __shared__ union {
+        uint16_t v[kWaves][kSub * kVStride];
+        float o[kWaves][16][kHeadDim];
+    } sm;
+    __shared__ float s_m[kWaves][16], s_l[kWaves][16];
+
+    const int item = xcd_item(blockIdx.x, a.n_items);
+    const int px = item % a.parts_per_item;
+    const int rest = item / a.parts_per_item;
+    const int s = rest % a.num_seqs;
+    const int g = rest / a.num_seqs;  // kv head
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const int n = a.lens[s];
+
+    int t0 = 0, t1 = n;
+    if (a.partition_size > 0) {
+        t0 = px * a.partition_size;
+        if (t0 >= n)
+            return;
+        t1 = min(n, t0 + a.partition_size);
+    }
+
+    const int tid = threadIdx.x;
+    // wave index, made explicitly uniform so that tile indices and table lookups
+    // stay in SGPRs (scalar loads of the table entries)
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int col = lane & 15, grp = lane >> 4;
+
+    const uint16_t *__restrict__ kp = (const uint16_t *)a.k_pool;
+    const uint16_t *__restrict__ vp = (const uint16_t *)a.v_pool;
+    const int32_t *__restrict__ trow = a.tables + (int64_t)s * a.width;
+    const int64_t blk_elems = (int64_t)a.num_kv_heads * BS * kHeadDim;
+    const int64_t head_off = (int64_t)g * BS * kHeadDim;
+
+    // B operand of the score MFMAs: Q^T, query row `col` of the group (zero padding)
+    u32x4 qop[4];
+    {
+        const uint16_t *qrow = (const uint16_t *)a.q +
+                               ((int64_t)s * a.num_q_heads + (int64_t)g * G + col) * kHeadDim +
+                               grp * 8;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            qop[kk] = col < G ? *(const u32x4 *)(qrow + kk * 32) : (u32x4){0u, 0u, 0u, 0u};
+    }
+
+    GqaState st;
+    st.m = kNegInf;
+    st.l = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+        st.acc[jj] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    uint16_t *vlds = sm.v[w];
+    const int nsub = (t1 - t0 + kSub - 1) / kSub;
+    const int T = nsub > w ? (nsub - w + kWaves - 1) / kWaves : 0;
+    if (T > 0) {
+        SubTile A, B;
+        int tb = t0 + w * kSub;
+        const int step = kWaves * kSub;
+        load_sub<BS>(A, kp, vp, trow, tb, head_off, blk_elems, lane);
+        int j = 0;
+        for (; j + 2 < T; j += 2) {
+            load_sub<BS>(B, kp, vp, trow, tb + step, head_off, blk_elems, lane);
+            compute_any<DT>(st, A, qop, vlds, tb, t1, lane, a.scale_log2);
+            load_sub<BS>(A, kp, vp, trow, tb + 2 * step, head_off, blk_elems, lane);
+            compute_any<DT>(st, B, qop, vlds, tb + step, t1, lane, a.scale_log2);
+            tb += 2 * step;
+        }
+        if (j + 1 < T) {
+            load_sub<BS>(B, kp, vp, trow, tb + step, head_off, blk_elems, lane);
+            compute_any<DT>(st, A, qop, vlds, tb, t1, lane, a.scale_log2);
+            compute_any<DT>(st, B, qop, vlds, tb + step, t1, lane, a.scale_log2);
+        } else {
+            compute_any<DT>(st, A, qop, vlds, tb, t1, lane, a.scale_log2);
+        }
+    }
+
+    // sum of the four lane groups' shares of l (m is already uniform across them)
+    st.l += xor_lane(st.l, 16);
+    st.l += xor_lane(st.l, 32);
+
+    __syncthreads();  // all waves are done with their V staging area
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            sm.o[w][col][16 * jj + 4 * grp + r] = st.acc[jj][r];
+    if (grp == 0) {
+        s_m[w][col] = st.m;
+        s_l[w][col] = st.l;
+    }
+    __syncthreads();
+
+    const int64_t row0 = (int64_t)s * a.num_q_heads + (int64_t)g * G;
+    for (int idx = tid; idx < G * kHeadDim; idx += kWaves * 64) {
+        const int qi = idx / kHeadDim, d = idx % kHeadDim;
+        float M = s_m[0][qi];
+#pragma unroll
+        for (int i = 1; i < kWaves; ++i)
+            M = fmaxf(M, s_m[i][qi]);
+        const float ref = safe_ref(M);
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) {
+            const float wgt = fexp2(s_m[i][qi] - ref);
+            L += s_l[i][qi] * wgt;
+            O += sm.o[i][qi][d] * wgt;
+        }
+        const int64_t row = row0 + qi;
+        if (a.partition_size == 0) {
+            const float o = L > 0.f ? O / L : 0.f;
+            ((uint16_t *)a.out)[row * kHeadDim + d] = to_bits<DT>(o);
+        } else {
+            a.part_o[(row * a.max_partitions + px) * kHeadDim + d] = O / L;
+            if (d == 0)
+                a.part_lse[row * a.max_partitions + px] = (ref + flog2(L)) * kLn2;
+        }
+    }
+}
+
+}  // namespace
+
+template <int DT, int BS>
+static hipError_t launch_mfma_t(const DecodeArgs &a, hipStream_t stream)
+{
+    hipLaunchKernelGGL((decode_mfma_kernel<DT, BS>), dim3(a.n_items), dim3(kWaves * 64), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs &a, int dtype, int block_size, hipStream_t stream)
+{
+#define PKV_MF_CASE(BSV)                                                                  \
+    case BSV:                                                                             \
+        return dtype == kFp16 ? launch_mfma_t<kFp16, BSV>(a, stream)                     \
+                              : launch_mfma_t<kBf16, BSV>(a, stream);
+    switch (block_size) {
+        PKV_MF_CASE(16)
+        PKV_MF_CASE(32)
+        PKV_MF_CASE(64)
+        PKV_MF_CASE(128)
+        PKV_MF_CASE(256)
+    default:
+        return hipErrorInvalidValue;
+    }
+#undef PKV_MF_CASE
+}
+
+}  // namespace pkv

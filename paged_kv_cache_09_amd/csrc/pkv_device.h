@@ -1,0 +1,131 @@
+// pkv_device.h -- device-side helpers shared by the gfx950 kernels of libpagedkv.
+//
+// Pool layout used by every kernel (one K pool and one V pool per layer):
+//   [num_blocks][num_kv_heads][block_size][head_dim], head_dim contiguous.
+// Token t of a sequence lives in physical block table[t / block_size] at offset
+// t % block_size (page "端侧 SLM 显存保活术：在 4GB 内存板卡上实现轻量 PagedAttention
+// 与 KV 缓存分块", pwwt.cn, section "注意力寻址").  Element offsets are formed in
+// 64-bit: a 7B-shaped layer pool holds more than 2^31 elements.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kHeadDim = 128;   // the only head size the kernels are built for
+constexpr int kNumXcd = 8;      // MI355X: 8 accelerator complex dies, each with its own L2
+constexpr int kFp16 = 0;
+constexpr int kBf16 = 1;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// ---- 16-bit storage formats -------------------------------------------------
+// Widen the low / high 16-bit half of a dword to fp32.
+template <int DT>
+__device__ __forceinline__ float lo_f32(uint32_t w)
+{
+    if constexpr (DT == kFp16)
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+    else
+        return __uint_as_float(w << 16);
+}
+template <int DT>
+__device__ __forceinline__ float hi_f32(uint32_t w)
+{
+    if constexpr (DT == kFp16)
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+    else
+        return __uint_as_float(w & 0xFFFF0000u);
+}
+
+// fp32 -> 16-bit pattern, round to nearest even.
+template <int DT>
+__device__ __forceinline__ uint16_t to_bits(float x)
+{
+    if constexpr (DT == kFp16)
+        return __builtin_bit_cast(uint16_t, (_Float16)x);
+    else
+        return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// c + a.lo*b.lo + a.hi*b.hi on packed 16-bit pairs, fp32 accumulate.
+template <int DT>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
+{
+    if constexpr (DT == kFp16)
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b),
+                                      c, false);
+    else
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                               __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// ---- cross-lane -------------------------------------------------------------
+// DPP row operations act inside rows of 16 lanes.  The four steps below give
+// every lane of a row the same sum (each step adds a value and its mirror, and
+// fp32 addition is commutative, so all 16 lanes agree bit for bit).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row_sum16(float x)
+{
+    x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp<0x141>(x);  // row_half_mirror
+    x += dpp<0x140>(x);  // row_mirror
+    return x;
+}
+
+__device__ __forceinline__ float xor_lane(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// Reference point for exp2 in the running softmax: the running max, or 0 while no
+// token has been seen (so that exp2(-inf - ref) = 0 instead of NaN).
+__device__ __forceinline__ float safe_ref(float m) { return m == kNegInf ? 0.f : m; }
+
+// Work-group index -> work item, arranged so that each XCD (work-groups are dealt
+// to the 8 XCDs round-robin) receives a contiguous range of items.  Items are
+// ordered KV-head major, so the work-groups sharing an L2 also share KV heads.
+__device__ __forceinline__ int xcd_item(int b, int n_items)
+{
+    const int x = b % kNumXcd, j = b / kNumXcd;
+    const int q = n_items / kNumXcd, r = n_items % kNumXcd;
+    return x * q + (x < r ? x : r) + j;
+}
+
+// Kernel arguments of the decode kernels.
+struct DecodeArgs {
+    void *out;                  // [S][Hq][D] dtype (single pass)
+    const void *q;              // [S][Hq][D] dtype
+    const void *k_pool;         // [NB][Hkv][B][D]
+    const void *v_pool;
+    const int32_t *tables;      // [S][W]
+    const int32_t *lens;        // [S]
+    float *part_o;              // [S][Hq][MP][D] fp32 (partitioned)
+    float *part_lse;            // [S][Hq][MP]
+    int num_seqs, num_q_heads, num_kv_heads, width;
+    int partition_size;         // 0 = single pass
+    int max_partitions;
+    int parts_per_item;         // partitions launched per (sequence, kv head)
+    int n_items;
+    float scale_log2;           // scale * log2(e)
+};
+
+}  // namespace pkv

@@ -1,0 +1,35 @@
+// pkv_launch.h -- launchers of the gfx950 kernels, called by the C-ABI layer
+// (api.hip) after it has validated the arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct DecodeArgs;
+
+hipError_t launch_decode_g1(const DecodeArgs &a, int dtype, int block_size, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeArgs &a, int dtype, int block_size,
+                              hipStream_t stream);
+hipError_t launch_reduce(void *out, const float *part_o, const float *part_lse,
+                         const int32_t *lens, int num_seqs, int num_q_heads, int partition_size,
+                         int max_partitions, int dtype, hipStream_t stream);
+hipError_t launch_append(void *k_pool, void *v_pool, const void *k_new, const void *v_new,
+                         const int32_t *tables, const int32_t *lens, int64_t *slot_out,
+                         int num_seqs, int num_kv_heads, int block_size, int width,
+                         hipStream_t stream);
+hipError_t launch_append_tokens(void *k_pool, void *v_pool, const void *k_src,
+                                const void *v_src, const int64_t *cu, const int32_t *start_pos,
+                                const int32_t *tables, int num_runs, int64_t total_tokens,
+                                int num_kv_heads, int block_size, int width, hipStream_t stream);
+
+// Debug check of the caller contract on device data (PKV_DEBUG_CHECK=1): returns
+// 0 when lens/tables are valid, a negative PKV status otherwise.  Synchronises.
+int debug_check_tables(const int32_t *tables, const int32_t *lens, int num_seqs, int width,
+                       int block_size, int64_t num_blocks, hipStream_t stream);
+int debug_check_runs(const int64_t *cu, const int32_t *start_pos, const int32_t *tables,
+                     int num_runs, int64_t total_tokens, int width, int block_size,
+                     int64_t num_blocks, hipStream_t stream);
+
+}  // namespace pkv
