@@ -31,56 +31,82 @@
 namespace pkv {
 namespace {
 
-constexpr int kWaves = 4;
 constexpr int kTile = 32;  // tokens per tile
 
-template <int DT, int BS>
-struct G1Tile {
-    u32x4 k[8];
-    u32x4 v[8];
+// Physical blocks of the two 16-token halves of the tile starting at token tb.
+// For BS >= 32 the whole tile sits in block tb/BS.  For BS == 16 the second half
+// uses block tb/16+1 only when it holds tokens of the item, else the first block
+// again (its rows are then masked), so every K/V address stays inside a block of
+// the sequence.  Table indices are clamped to the row so that a lookahead for a
+// tile that does not exist reads a valid entry (whose value is then unused).
+struct TilePhys {
+    int32_t p0, p1;
 };
 
-// Issue the 16 loads of tile `tb` (first token of the tile).  Every address is
-// inside a block that holds tokens of the item: for BS >= 32 the whole tile sits
-// in block tb/BS; for BS == 16 the second half uses block tb/16+1 only when it
-// holds tokens, else it re-reads the first block (those rows are masked).
-template <int DT, int BS>
-__device__ __forceinline__ void load_tile(G1Tile<DT, BS> &t, const uint16_t *__restrict__ kp,
-                                          const uint16_t *__restrict__ vp,
-                                          const int32_t *__restrict__ trow, int tb, int t_end,
-                                          int64_t head_off, int64_t blk_elems, int lane_off)
+template <int BS>
+__device__ __forceinline__ TilePhys tile_phys(const int32_t *__restrict__ trow, int width, int tb,
+                                              int t_end)
 {
+    TilePhys p;
     if constexpr (BS >= kTile) {
-        const int64_t phys = trow[tb / BS];
-        const int64_t base = phys * blk_elems + head_off + (int64_t)(tb % BS) * kHeadDim;
-        const uint16_t *kb = kp + base + lane_off;
-        const uint16_t *vb = vp + base + lane_off;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            t.k[i] = *(const u32x4 *)(kb + i * 4 * kHeadDim);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            t.v[i] = *(const u32x4 *)(vb + i * 4 * kHeadDim);
-        }
+        p.p0 = trow[min(tb / BS, width - 1)];
+        p.p1 = p.p0;
     } else {
         static_assert(BS == 16, "block sizes below 32 other than 16 are not built");
-        const int blk = tb / 16;
-        const int64_t p0 = trow[blk];
-        const int64_t p1 = (tb + 16 < t_end) ? (int64_t)trow[blk + 1] : p0;
-        const uint16_t *k0 = kp + p0 * blk_elems + head_off + lane_off;
-        const uint16_t *k1 = kp + p1 * blk_elems + head_off + lane_off;
-        const uint16_t *v0 = vp + p0 * blk_elems + head_off + lane_off;
-        const uint16_t *v1 = vp + p1 * blk_elems + head_off + lane_off;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            t.k[i] = *(const u32x4 *)((i < 4 ? k0 : k1) + (i & 3) * 4 * kHeadDim);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            t.v[i] = *(const u32x4 *)((i < 4 ? v0 : v1) + (i & 3) * 4 * kHeadDim);
-        }
+        p.p0 = trow[min(tb / 16, width - 1)];
+        const int32_t second = trow[min(tb / 16 + 1, width - 1)];
+        p.p1 = (tb + 16 < t_end) ? second : p.p0;
     }
+    return p;
+}
+
+// Buffer resources of the two 16-token halves of a tile in the K and V pools.
+// Each covers only the rows that hold tokens of the item, so loads of rows past
+// the context length return zeros and fetch nothing from HBM.
+struct TileRsrc {
+    __amdgpu_buffer_rsrc_t k0, k1, v0, v1;
+};
+
+template <int BS>
+__device__ __forceinline__ TileRsrc tile_rsrc(const TilePhys &p, const uint16_t *kp,
+                                              const uint16_t *vp, int tb, int t_end,
+                                              int64_t head_off, int64_t blk_elems)
+{
+    int64_t b0, b1;
+    if constexpr (BS >= kTile) {
+        b0 = (int64_t)p.p0 * blk_elems + head_off + (int64_t)(tb % BS) * kHeadDim;
+        b1 = b0 + 16 * kHeadDim;
+    } else {
+        b0 = (int64_t)p.p0 * blk_elems + head_off;
+        b1 = (int64_t)p.p1 * blk_elems + head_off;
+    }
+    const int valid = t_end - tb;  // >= 1 for a tile that exists
+    // readfirstlane keeps the ranges in SGPRs (the clamp would otherwise be
+    // selected as a VALU med3, making the descriptor look divergent)
+    const int n0 = __builtin_amdgcn_readfirstlane(min(max(valid, 0), 16) * kHeadDim * 2);
+    const int n1 = __builtin_amdgcn_readfirstlane(min(max(valid - 16, 0), 16) * kHeadDim * 2);
+    TileRsrc t;
+    t.k0 = make_rsrc(kp + b0, n0);
+    t.k1 = make_rsrc(kp + b1, n1);
+    t.v0 = make_rsrc(vp + b0, n0);
+    t.v1 = make_rsrc(vp + b1, n1);
+    return t;
+}
+
+// Eight 16-byte loads: rows 4i + lane/16 of the tile, dims 8*(lane%16)..+7.
+struct Half {
+    u32x4 x[8];
+};
+
+__device__ __forceinline__ void load_half(Half &h, __amdgpu_buffer_rsrc_t r0,
+                                          __amdgpu_buffer_rsrc_t r1, int lane_byte)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        h.x[i] = ldbuf(r0, lane_byte + i * 4 * kHeadDim * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        h.x[4 + i] = ldbuf(r1, lane_byte + i * 4 * kHeadDim * 2);
 }
 
 template <int DT>
@@ -90,22 +116,28 @@ struct RowState {
     float acc[8];  // running sum of exp2(score - m) * v[dims 8c..8c+7]
 };
 
-template <int DT, int BS, bool PARTIAL>
-__device__ __forceinline__ void compute_tile(RowState<DT> &st, const G1Tile<DT, BS> &t,
-                                             const u32x4 &q, int tb, int t_end, int r,
-                                             float scale_log2)
+// Scores of the row's 8 tokens of a tile (log2 domain); masked tokens get -inf.
+template <int DT, bool PARTIAL>
+__device__ __forceinline__ void scores(float (&sc)[8], const Half &K, const u32x4 &q, int tb,
+                                       int t_end, int r, float scale_log2)
 {
-    float sc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        float d = dot2<DT>(q.x, t.k[i].x, 0.f);
-        d = dot2<DT>(q.y, t.k[i].y, d);
-        d = dot2<DT>(q.z, t.k[i].z, d);
-        d = dot2<DT>(q.w, t.k[i].w, d);
+        float d = dot2<DT>(q.x, K.x[i].x, 0.f);
+        d = dot2<DT>(q.y, K.x[i].y, d);
+        d = dot2<DT>(q.z, K.x[i].z, d);
+        d = dot2<DT>(q.w, K.x[i].w, d);
         sc[i] = row_sum16(d) * scale_log2;
         if (PARTIAL && tb + 4 * i + r >= t_end)
             sc[i] = kNegInf;
     }
+}
+
+// Online-softmax update of the row state with a tile's scores and V rows.
+template <int DT, bool PARTIAL>
+__device__ __forceinline__ void accumulate(RowState<DT> &st, const float (&sc)[8], const Half &V,
+                                           int tb, int t_end, int r)
+{
     float mt = sc[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i)
@@ -120,7 +152,7 @@ __device__ __forceinline__ void compute_tile(RowState<DT> &st, const G1Tile<DT, 
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         float p = fexp2(sc[i] - ref);
-        u32x4 v = t.v[i];
+        u32x4 v = V.x[i];
         if (PARTIAL && tb + 4 * i + r >= t_end) {
             p = 0.f;
             v = (u32x4){0u, 0u, 0u, 0u};
@@ -136,17 +168,6 @@ __device__ __forceinline__ void compute_tile(RowState<DT> &st, const G1Tile<DT, 
         st.acc[7] += p * hi_f32<DT>(v.w);
     }
     st.m = m_new;
-}
-
-template <int DT, int BS>
-__device__ __forceinline__ void compute_any(RowState<DT> &st, const G1Tile<DT, BS> &t,
-                                            const u32x4 &q, int tb, int t_end, int r,
-                                            float scale_log2)
-{
-    if (tb + kTile <= t_end)
-        compute_tile<DT, BS, false>(st, t, q, tb, t_end, r, scale_log2);
-    else
-        compute_tile<DT, BS, true>(st, t, q, tb, t_end, r, scale_log2);
 }
 
 // Merge the running state of the lane `mask` lanes away into this lane's.
@@ -167,26 +188,22 @@ __device__ __forceinline__ void merge_xor(RowState<DT> &st, int mask)
     st.m = M;
 }
 
-template <int DT, int BS>
-__global__ __launch_bounds__(kWaves * 64) void decode_g1_kernel(DecodeArgs a)
+template <int DT, int BS, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void decode_g1_kernel(DecodeArgs a)
 {
-    __shared__ float s_acc[kWaves][kHeadDim];
-    __shared__ float s_m[kWaves], s_l[kWaves];
+    __shared__ float s_acc[WAVES][kHeadDim];
+    __shared__ float s_m[WAVES], s_l[WAVES];
 
-    const int item = xcd_item(blockIdx.x, a.n_items);
+    // Work items are ordered sequence-major: the KV heads of one sequence are
+    // neighbours in dispatch order, so the concurrently running work-groups read
+    // all heads of the same blocks (whole contiguous slabs of the pool) rather
+    // than one head's slice of many blocks.  Measured faster on MI355X than the
+    // KV-head-major order.
+    const int item = blockIdx.x;
     const int px = item % a.parts_per_item;
     const int rest = item / a.parts_per_item;
-    const int s = rest % a.num_seqs;
-    const int h = rest / a.num_seqs;  // query head == kv head
-    const int n = a.lens[s];
-
-    int t0 = 0, t1 = n;
-    if (a.partition_size > 0) {
-        t0 = px * a.partition_size;
-        if (t0 >= n)
-            return;  // partition holds no token: nothing is written
-        t1 = min(n, t0 + a.partition_size);
-    }
+    const int h = rest % a.num_kv_heads;  // query head == kv head
+    const int s = rest / a.num_kv_heads;
 
     const int tid = threadIdx.x;
     // wave index, made explicitly uniform so that tile indices and table lookups
@@ -200,7 +217,16 @@ __global__ __launch_bounds__(kWaves * 64) void decode_g1_kernel(DecodeArgs a)
     const int32_t *__restrict__ trow = a.tables + (int64_t)s * a.width;
     const int64_t blk_elems = (int64_t)a.num_kv_heads * BS * kHeadDim;
     const int64_t head_off = (int64_t)h * BS * kHeadDim;
-    const int lane_off = r * kHeadDim + c * 8;
+    const int lane_byte = (r * kHeadDim + c * 8) * 2;
+
+    const int n = a.lens[s];
+    int t0 = 0, t1 = n;
+    if (a.partition_size > 0) {
+        t0 = px * a.partition_size;
+        if (t0 >= n)
+            return;  // partition holds no token: nothing is written
+        t1 = min(n, t0 + a.partition_size);
+    }
 
     const u32x4 q = *(const u32x4 *)((const uint16_t *)a.q +
                                      ((int64_t)s * a.num_q_heads + h) * kHeadDim + c * 8);
@@ -212,34 +238,75 @@ __global__ __launch_bounds__(kWaves * 64) void decode_g1_kernel(DecodeArgs a)
     for (int j = 0; j < 8; ++j)
         st.acc[j] = 0.f;
 
+    // Tiles w, w+WAVES, ... of the item belong to this wave.  The K and V halves
+    // are pipelined separately: the next tile's K loads are issued as soon as the
+    // current scores are computed, its V loads as soon as the current V rows are
+    // consumed, so one tile stays in flight with a single register buffer per half.
     const int ntiles = (t1 - t0 + kTile - 1) / kTile;
-    const int T = ntiles > w ? (ntiles - w + kWaves - 1) / kWaves : 0;  // tiles of this wave
+    const int T = ntiles > w ? (ntiles - w + WAVES - 1) / WAVES : 0;
     if (T > 0) {
-        G1Tile<DT, BS> A, B;
+        const int step = WAVES * kTile;
         int tb = t0 + w * kTile;
-        const int step = kWaves * kTile;
-        load_tile<DT, BS>(A, kp, vp, trow, tb, t1, head_off, blk_elems, lane_off);
-        int j = 0;
-        for (; j + 2 < T; j += 2) {
-            load_tile<DT, BS>(B, kp, vp, trow, tb + step, t1, head_off, blk_elems, lane_off);
-            compute_any<DT, BS>(st, A, q, tb, t1, r, a.scale_log2);
-            load_tile<DT, BS>(A, kp, vp, trow, tb + 2 * step, t1, head_off, blk_elems,
-                              lane_off);
-            compute_any<DT, BS>(st, B, q, tb + step, t1, r, a.scale_log2);
-            tb += 2 * step;
+        Half K, V;
+        {
+            const TileRsrc rs = tile_rsrc<BS>(tile_phys<BS>(trow, a.width, tb, t1), kp, vp, tb, t1,
+                                              head_off, blk_elems);
+            load_half(K, rs.k0, rs.k1, lane_byte);
+            load_half(V, rs.v0, rs.v1, lane_byte);
         }
-        if (j + 1 < T) {
-            load_tile<DT, BS>(B, kp, vp, trow, tb + step, t1, head_off, blk_elems, lane_off);
-            compute_any<DT, BS>(st, A, q, tb, t1, r, a.scale_log2);
-            compute_any<DT, BS>(st, B, q, tb + step, t1, r, a.scale_log2);
+        // table entries are looked up one tile ahead of the loads that use them
+        TilePhys pn = tile_phys<BS>(trow, a.width, tb + step, t1);
+        float sc[8];
+        for (int j = 0; j + 1 < T; ++j) {  // every tile here is full
+            const TilePhys pn2 = tile_phys<BS>(trow, a.width, tb + 2 * step, t1);
+            const TileRsrc rn = tile_rsrc<BS>(pn, kp, vp, tb + step, t1, head_off, blk_elems);
+            scores<DT, false>(sc, K, q, tb, t1, r, a.scale_log2);
+            // keep the scheduler from sinking the prefetches below the math they
+            // are meant to overlap
+            __builtin_amdgcn_sched_barrier(0);
+            load_half(K, rn.k0, rn.k1, lane_byte);
+            __builtin_amdgcn_sched_barrier(0);
+            accumulate<DT, false>(st, sc, V, tb, t1, r);
+            __builtin_amdgcn_sched_barrier(0);
+            load_half(V, rn.v0, rn.v1, lane_byte);
+            __builtin_amdgcn_sched_barrier(0);
+            pn = pn2;
+            tb += step;
+        }
+        if (tb + kTile <= t1) {
+            scores<DT, false>(sc, K, q, tb, t1, r, a.scale_log2);
+            accumulate<DT, false>(st, sc, V, tb, t1, r);
         } else {
-            compute_any<DT, BS>(st, A, q, tb, t1, r, a.scale_log2);
+            scores<DT, true>(sc, K, q, tb, t1, r, a.scale_log2);
+            accumulate<DT, true>(st, sc, V, tb, t1, r);
         }
     }
 
     // rows of the wave -> one state per wave (identical in every lane)
     merge_xor<DT>(st, 16);
     merge_xor<DT>(st, 32);
+    if (WAVES == 1) {
+        if (r == 0) {
+            const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+            const int64_t row = (int64_t)s * a.num_q_heads + h;
+            if (a.partition_size == 0) {
+                u32x4 o;
+                o.x = (uint32_t)to_bits<DT>(st.acc[0] * inv) | ((uint32_t)to_bits<DT>(st.acc[1] * inv) << 16);
+                o.y = (uint32_t)to_bits<DT>(st.acc[2] * inv) | ((uint32_t)to_bits<DT>(st.acc[3] * inv) << 16);
+                o.z = (uint32_t)to_bits<DT>(st.acc[4] * inv) | ((uint32_t)to_bits<DT>(st.acc[5] * inv) << 16);
+                o.w = (uint32_t)to_bits<DT>(st.acc[6] * inv) | ((uint32_t)to_bits<DT>(st.acc[7] * inv) << 16);
+                *(u32x4 *)((uint16_t *)a.out + row * kHeadDim + c * 8) = o;
+            } else {
+                float *po = a.part_o + (row * a.max_partitions + px) * kHeadDim + c * 8;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    po[j] = st.acc[j] * inv;
+                if (c == 0)
+                    a.part_lse[row * a.max_partitions + px] = (safe_ref(st.m) + flog2(st.l)) * kLn2;
+            }
+        }
+        return;
+    }
     if (r == 0) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
@@ -255,12 +322,12 @@ __global__ __launch_bounds__(kWaves * 64) void decode_g1_kernel(DecodeArgs a)
         const int d = tid;
         float M = s_m[0];
 #pragma unroll
-        for (int i = 1; i < kWaves; ++i)
+        for (int i = 1; i < WAVES; ++i)
             M = fmaxf(M, s_m[i]);
         const float ref = safe_ref(M);
         float L = 0.f, O = 0.f;
 #pragma unroll
-        for (int i = 0; i < kWaves; ++i) {
+        for (int i = 0; i < WAVES; ++i) {
             const float wgt = fexp2(s_m[i] - ref);
             L += s_l[i] * wgt;
             O += s_acc[i][d] * wgt;
@@ -279,11 +346,16 @@ __global__ __launch_bounds__(kWaves * 64) void decode_g1_kernel(DecodeArgs a)
 
 }  // namespace
 
+// Waves per work-group (tuning knob; 8 measured best for the 7B-shaped batch).
+#ifndef PKV_G1_WAVES
+#define PKV_G1_WAVES 8
+#endif
+
 template <int DT, int BS>
 static hipError_t launch_g1_t(const DecodeArgs &a, hipStream_t stream)
 {
-    hipLaunchKernelGGL((decode_g1_kernel<DT, BS>), dim3(a.n_items), dim3(kWaves * 64), 0, stream,
-                       a);
+    constexpr int W = PKV_G1_WAVES;
+    hipLaunchKernelGGL((decode_g1_kernel<DT, BS, W>), dim3(a.n_items), dim3(W * 64), 0, stream, a);
     return hipGetLastError();
 }
 

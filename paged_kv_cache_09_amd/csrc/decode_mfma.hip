@@ -35,9 +35,11 @@
 namespace pkv {
 namespace {
 
-constexpr int kWaves = 4;
 constexpr int kSub = 16;           // tokens per sub-tile
-constexpr int kVStride = 136;      // LDS row stride of a staged V tile, in 16-bit elements
+// LDS row stride of a staged V tile, in 16-bit elements: 288 bytes = 72 dwords,
+// so the 16 rows of a transposing read start 8 banks apart and one pass of 8
+// rows covers all 64 banks exactly once (likewise each 256-byte row write).
+constexpr int kVStride = 144;
 
 template <int DT>
 __device__ __forceinline__ f32x4 mfma_qk(const u32x4 &a, const u32x4 &b, f32x4 c)
@@ -61,28 +63,57 @@ __device__ __forceinline__ f32x4 mfma_pv(const u32x2 &a, const u32x2 &b, f32x4 c
                                                          __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
 }
 
-struct SubTile {
-    u32x4 k[4];  // A operand of the four score MFMAs
-    u32x4 v[4];  // rows 4j + lane/16, dims 8*(lane%16).. of the V tile
+// K rows of a 16-token sub-tile in the A-operand layout of the four score MFMAs
+// (lane i+16j holds dims 8*(4kk+j)..+7 of token i for MFMA kk).
+struct KOp {
+    u32x4 k[4];
+};
+// V rows of a sub-tile as loaded: lane l holds dims 8*(l%16).. of row 4j + l/16.
+struct VRows {
+    u32x4 v[4];
 };
 
-// Loads of the 16-token sub-tile starting at token tb (block tb/BS holds all 16).
+// Buffer resources over the rows of a 16-token sub-tile that hold tokens of the
+// item (block tb/BS holds all 16 rows).  Rows past the context length lie
+// outside the range: their loads return zeros and fetch nothing.
+struct SubRsrc {
+    __amdgpu_buffer_rsrc_t k, v;
+};
+
 template <int BS>
-__device__ __forceinline__ void load_sub(SubTile &t, const uint16_t *__restrict__ kp,
-                                         const uint16_t *__restrict__ vp,
-                                         const int32_t *__restrict__ trow, int tb,
-                                         int64_t head_off, int64_t blk_elems, int lane)
+__device__ __forceinline__ SubRsrc sub_rsrc(int32_t phys, const uint16_t *kp, const uint16_t *vp,
+                                            int tb, int t_end, int64_t head_off,
+                                            int64_t blk_elems)
 {
-    const int64_t phys = trow[tb / BS];
-    const int64_t base = phys * blk_elems + head_off + (int64_t)(tb % BS) * kHeadDim;
-    const uint16_t *kb = kp + base + (lane & 15) * kHeadDim + (lane >> 4) * 8;
-    const uint16_t *vb = vp + base + lane * 8;
+    const int64_t base = (int64_t)phys * blk_elems + head_off + (int64_t)(tb % BS) * kHeadDim;
+    const int bytes = __builtin_amdgcn_readfirstlane(min(max(t_end - tb, 0), kSub) * kHeadDim * 2);
+    SubRsrc r;
+    r.k = make_rsrc(kp + base, bytes);
+    r.v = make_rsrc(vp + base, bytes);
+    return r;
+}
+
+// Table entry of the sub-tile at token tb; the index is clamped to the row so
+// that a lookahead past the last sub-tile reads a valid (unused) entry.
+template <int BS>
+__device__ __forceinline__ int32_t sub_phys(const int32_t *__restrict__ trow, int width, int tb)
+{
+    return trow[min(tb / BS, width - 1)];
+}
+
+__device__ __forceinline__ void load_k(KOp &t, __amdgpu_buffer_rsrc_t r, int lane)
+{
+    const int kb = (lane & 15) * kHeadDim * 2 + (lane >> 4) * 16;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-        t.k[kk] = *(const u32x4 *)(kb + kk * 32);
+        t.k[kk] = ldbuf(r, kb + kk * 64);
+}
+
+__device__ __forceinline__ void load_v(VRows &t, __amdgpu_buffer_rsrc_t r, int lane)
+{
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        t.v[j] = *(const u32x4 *)(vb + j * 512);
+        t.v[j] = ldbuf(r, lane * 16 + j * 1024);
 }
 
 struct GqaState {
@@ -91,22 +122,18 @@ struct GqaState {
     f32x4 acc[8];   // O^T rows 16*jj + 4*(lane/16) + r, column = query row lane%16
 };
 
+// Scores of the sub-tile, online-softmax update of (m, l); returns the
+// probabilities packed as the B operand of P.V and the rescale factor of acc.
 template <int DT, bool PARTIAL>
-__device__ __forceinline__ void compute_sub(GqaState &st, const SubTile &t, const u32x4 *qop,
-                                            uint16_t *vlds, int tb, int t_end, int lane,
-                                            float scale_log2)
+__device__ __forceinline__ void qk_softmax(GqaState &st, const KOp &K, const u32x4 *qop, int tb,
+                                           int t_end, int lane, float scale_log2, u32x2 &pb,
+                                           float &alpha)
 {
-    const int col = lane & 15, grp = lane >> 4;
-    // stage V (row-major, padded) for the transposing reads below
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        *(u32x4 *)(vlds + (4 * j + grp) * kVStride + col * 8) = t.v[j];
-
+    const int grp = lane >> 4;
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-        s = mfma_qk<DT>(t.k[kk], qop[kk], s);
-
+        s = mfma_qk<DT>(K.k[kk], qop[kk], s);
     float sc[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -119,7 +146,7 @@ __device__ __forceinline__ void compute_sub(GqaState &st, const SubTile &t, cons
     mt = fmaxf(mt, xor_lane(mt, 32));
     const float m_new = fmaxf(st.m, mt);
     const float ref = safe_ref(m_new);
-    const float alpha = fexp2(st.m - ref);
+    alpha = fexp2(st.m - ref);
     float p[4];
     float psum = 0.f;
 #pragma unroll
@@ -129,61 +156,64 @@ __device__ __forceinline__ void compute_sub(GqaState &st, const SubTile &t, cons
     }
     st.l = st.l * alpha + psum;
     st.m = m_new;
-    u32x2 pb;
     pb.x = (uint32_t)to_bits<DT>(p[0]) | ((uint32_t)to_bits<DT>(p[1]) << 16);
     pb.y = (uint32_t)to_bits<DT>(p[2]) | ((uint32_t)to_bits<DT>(p[3]) << 16);
+}
 
+// Stage the V rows of the sub-tile, row-major, in this wave's LDS tile.
+__device__ __forceinline__ void stage_v(const VRows &V, uint16_t *vlds, int lane)
+{
+    const int col = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        *(u32x4 *)(vlds + (4 * j + grp) * kVStride + col * 8) = V.v[j];
+}
+
+// acc = alpha * acc + V^T P^T.  The A operand of each 16x16x16 MFMA (lane l: dim
+// 16jj + l%16 of tokens 4(l/16)..+3) comes from one transposing LDS read: lane j
+// of each 16-lane group points at 4 consecutive elements of row 4(l/16) + j/4,
+// column 16jj + 4(j%4), and the read hands lane i of the group element i%4 of the
+// chunk addressed by lane 4e + i/4, for e = 0..3.  Rows past the context length
+// were loaded as zeros (outside the buffer range), so their zero probabilities
+// multiply zeros, never a stale NaN.
+template <int DT>
+__device__ __forceinline__ void pv_mma(GqaState &st, const uint16_t *vlds, const u32x2 &pb,
+                                       float alpha, int lane)
+{
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const int j = lane & 15, grp = lane >> 4;
+    const uint16_t *base = vlds + (4 * grp + (j >> 2)) * kVStride + 4 * (j & 3);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
         st.acc[jj] *= alpha;
-        const uint16_t *src = vlds + (4 * grp) * kVStride + 16 * jj + col;
-        uint32_t e0 = src[0], e1 = src[kVStride], e2 = src[2 * kVStride], e3 = src[3 * kVStride];
-        if (PARTIAL) {
-            const int tk = tb + 4 * grp;
-            if (tk + 0 >= t_end) e0 = 0;
-            if (tk + 1 >= t_end) e1 = 0;
-            if (tk + 2 >= t_end) e2 = 0;
-            if (tk + 3 >= t_end) e3 = 0;
-        }
-        u32x2 va;
-        va.x = e0 | (e1 << 16);
-        va.y = e2 | (e3 << 16);
-        st.acc[jj] = mfma_pv<DT>(va, pb, st.acc[jj]);
+        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4 *)(base + 16 * jj));
+        st.acc[jj] = mfma_pv<DT>(__builtin_bit_cast(u32x2, va), pb, st.acc[jj]);
     }
     // the next sub-tile's LDS writes must not pass these reads
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int DT>
-__device__ __forceinline__ void compute_any(GqaState &st, const SubTile &t, const u32x4 *qop,
-                                            uint16_t *vlds, int tb, int t_end, int lane,
-                                            float scale_log2)
-{
-    if (tb + kSub <= t_end)
-        compute_sub<DT, false>(st, t, qop, vlds, tb, t_end, lane, scale_log2);
-    else
-        compute_sub<DT, true>(st, t, qop, vlds, tb, t_end, lane, scale_log2);
-}
-
-template <int DT, int BS>
-__global__ __launch_bounds__(kWaves * 64) void decode_mfma_kernel(DecodeArgs a)
+template <int DT, int BS, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void decode_mfma_kernel(DecodeArgs a)
 {
     // V staging during the token loop; the cross-wave merge afterwards
     __shared__ union {
-        uint16_t v[kWaves][kSub * kVStride];
-        float o[kWaves][16][kHeadDim];
+        uint16_t v[WAVES][kSub * kVStride];
+        float o[WAVES][16][kHeadDim];
     } sm;
-    __shared__ float s_m[kWaves][16], s_l[kWaves][16];
+    __shared__ float s_m[WAVES][16], s_l[WAVES][16];
 
-    const int item = xcd_item(blockIdx.x, a.n_items);
+    // sequence-major work items (see the MHA kernel): the KV heads of a sequence
+    // are neighbours in dispatch order
+    const int item = blockIdx.x;
     const int px = item % a.parts_per_item;
     const int rest = item / a.parts_per_item;
-    const int s = rest % a.num_seqs;
-    const int g = rest / a.num_seqs;  // kv head
+    const int g = rest % a.num_kv_heads;  // kv head
+    const int s = rest / a.num_kv_heads;
     const int G = a.num_q_heads / a.num_kv_heads;
     const int n = a.lens[s];
 
@@ -228,27 +258,47 @@ __global__ __launch_bounds__(kWaves * 64) void decode_mfma_kernel(DecodeArgs a)
 
     uint16_t *vlds = sm.v[w];
     const int nsub = (t1 - t0 + kSub - 1) / kSub;
-    const int T = nsub > w ? (nsub - w + kWaves - 1) / kWaves : 0;
+    const int T = nsub > w ? (nsub - w + WAVES - 1) / WAVES : 0;
     if (T > 0) {
-        SubTile A, B;
+        // Single register buffer per operand, pipelined: the next sub-tile's K
+        // loads are issued once the scores are done, its V loads once the current
+        // V rows are staged in LDS, so they overlap softmax and P.V.
         int tb = t0 + w * kSub;
-        const int step = kWaves * kSub;
-        load_sub<BS>(A, kp, vp, trow, tb, head_off, blk_elems, lane);
-        int j = 0;
-        for (; j + 2 < T; j += 2) {
-            load_sub<BS>(B, kp, vp, trow, tb + step, head_off, blk_elems, lane);
-            compute_any<DT>(st, A, qop, vlds, tb, t1, lane, a.scale_log2);
-            load_sub<BS>(A, kp, vp, trow, tb + 2 * step, head_off, blk_elems, lane);
-            compute_any<DT>(st, B, qop, vlds, tb + step, t1, lane, a.scale_log2);
-            tb += 2 * step;
+        const int step = WAVES * kSub;
+        KOp K;
+        VRows V;
+        {
+            const SubRsrc r = sub_rsrc<BS>(sub_phys<BS>(trow, a.width, tb), kp, vp, tb, t1,
+                                           head_off, blk_elems);
+            load_k(K, r.k, lane);
+            load_v(V, r.v, lane);
         }
-        if (j + 1 < T) {
-            load_sub<BS>(B, kp, vp, trow, tb + step, head_off, blk_elems, lane);
-            compute_any<DT>(st, A, qop, vlds, tb, t1, lane, a.scale_log2);
-            compute_any<DT>(st, B, qop, vlds, tb + step, t1, lane, a.scale_log2);
-        } else {
-            compute_any<DT>(st, A, qop, vlds, tb, t1, lane, a.scale_log2);
+        // table entries are looked up one sub-tile ahead of the loads that use them
+        int32_t pn = sub_phys<BS>(trow, a.width, tb + step);
+        u32x2 pb;
+        float alpha;
+        for (int j = 0; j + 1 < T; ++j) {  // every sub-tile here is full
+            const int32_t pn2 = sub_phys<BS>(trow, a.width, tb + 2 * step);
+            const SubRsrc rn = sub_rsrc<BS>(pn, kp, vp, tb + step, t1, head_off, blk_elems);
+            qk_softmax<DT, false>(st, K, qop, tb, t1, lane, a.scale_log2, pb, alpha);
+            __builtin_amdgcn_sched_barrier(0);
+            load_k(K, rn.k, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            stage_v(V, vlds, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            load_v(V, rn.v, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            pv_mma<DT>(st, vlds, pb, alpha, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            pn = pn2;
+            tb += step;
         }
+        if (tb + kSub <= t1)
+            qk_softmax<DT, false>(st, K, qop, tb, t1, lane, a.scale_log2, pb, alpha);
+        else
+            qk_softmax<DT, true>(st, K, qop, tb, t1, lane, a.scale_log2, pb, alpha);
+        stage_v(V, vlds, lane);
+        pv_mma<DT>(st, vlds, pb, alpha, lane);
     }
 
     // sum of the four lane groups' shares of l (m is already uniform across them)
@@ -268,16 +318,16 @@ __global__ __launch_bounds__(kWaves * 64) void decode_mfma_kernel(DecodeArgs a)
     __syncthreads();
 
     const int64_t row0 = (int64_t)s * a.num_q_heads + (int64_t)g * G;
-    for (int idx = tid; idx < G * kHeadDim; idx += kWaves * 64) {
+    for (int idx = tid; idx < G * kHeadDim; idx += WAVES * 64) {
         const int qi = idx / kHeadDim, d = idx % kHeadDim;
         float M = s_m[0][qi];
 #pragma unroll
-        for (int i = 1; i < kWaves; ++i)
+        for (int i = 1; i < WAVES; ++i)
             M = fmaxf(M, s_m[i][qi]);
         const float ref = safe_ref(M);
         float L = 0.f, O = 0.f;
 #pragma unroll
-        for (int i = 0; i < kWaves; ++i) {
+        for (int i = 0; i < WAVES; ++i) {
             const float wgt = fexp2(s_m[i][qi] - ref);
             L += s_l[i][qi] * wgt;
             O += sm.o[i][qi][d] * wgt;
@@ -296,11 +346,17 @@ __global__ __launch_bounds__(kWaves * 64) void decode_mfma_kernel(DecodeArgs a)
 
 }  // namespace
 
+// Waves per work-group (tuning knob).
+#ifndef PKV_MFMA_WAVES
+#define PKV_MFMA_WAVES 4
+#endif
+
 template <int DT, int BS>
 static hipError_t launch_mfma_t(const DecodeArgs &a, hipStream_t stream)
 {
-    hipLaunchKernelGGL((decode_mfma_kernel<DT, BS>), dim3(a.n_items), dim3(kWaves * 64), 0,
-                       stream, a);
+    constexpr int W = PKV_MFMA_WAVES;
+    hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, W>), dim3(a.n_items), dim3(W * 64), 0, stream,
+                       a);
     return hipGetLastError();
 }
 

@@ -4,7 +4,7 @@ Append and slot arithmetic: bit-exact.  Attention outputs (fp16/bf16) and
 partition outputs: |gpu - oracle| <= 1e-2 + 1e-2 |oracle| element by element.
 Every workload runs at its full per-layer size, in the launch configuration the
 benchmark times (single pass for the 7B and prefix workloads, split-context
-partitions of 256 tokens for the edge workload and 1024 for the long-context one),
+partitions of 256 tokens for the edge workload and 2048 for the long-context one),
 plus other partition sizes, ragged and empty sequences, every supported block
 size and several GQA group sizes.
 """
@@ -26,7 +26,7 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():  # pragma: no cover - CPU containers
     pytest.skip("no GPU", allow_module_level=True)
 
-BENCH_P = {"c1a": 0, "c1b": 0, "c2": 256, "c3": 0, "c4": 1024, "c5": 0}
+BENCH_P = {"c1a": 0, "c1b": 0, "c2": 256, "c3": 0, "c4": 2048, "c5": 0}
 ALL = ["c1a", "c1b", "c2", "c3", "c4", "c5"]
 
 _cache = {}

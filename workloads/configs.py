@@ -112,7 +112,7 @@ CONFIGS = {
         block_size=128, dtype="bf16", max_blocks_per_seq=128, value_scale=1.0,
         length_kind="fixed", fixed_lengths=(16384,) * 8,
         pool_blocks=math.ceil(8 * 128 * 1.15),
-        bench_distinct_layers=2, bench_partition_size=1024,
+        bench_distinct_layers=2, bench_partition_size=2048,
     ),
     "c5": Config(
         key="c5", cfg_id=5, title="prefix-sharing tables, 512-token shared prefix",
