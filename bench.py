@@ -60,11 +60,66 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (reference for HBM "
+                         "counter scaling and copy bandwidth) and print its rate")
     return ap.parse_args()
+
+
+# Source files whose contents determine the decode kernels' memory traffic.
+TRAFFIC_SOURCES = ["paged_kv_cache_09_amd/csrc/decode_g1.hip",
+                   "paged_kv_cache_09_amd/csrc/decode_mfma.hip",
+                   "paged_kv_cache_09_amd/csrc/pkv_device.h"]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from the committed counter record of this
+    workload (profiles/<kernel>_<workload>_traffic.json), or None when there is
+    none or the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_reference():
+    """Plain device-to-device copy of 1 GiB (read 1 GiB + write 1 GiB)."""
+    import torch
+    n = 1 << 30
+    a = torch.ones(n // 2, dtype=torch.float16, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    print(json.dumps({"copy_reference": True, "bytes_read": n, "bytes_written": n,
+                      "ms": round(ms, 4), "gbps_read_plus_write": round(2 * n / ms / 1e6, 1)}))
 
 
 def main():
     args = parse()
+    if args.copy_reference:
+        copy_reference()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -118,12 +173,10 @@ def main():
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
 
-    def step(events=None):
+    def step():
         for li in range(cfg.num_layers):
             L = layers[li % R]
             pkv.paged_kv_append(L["k"], L["v"], L["kn"], L["vn"], tables, lens)
-            if events is not None:
-                events[li][0].record()
             if P:
                 pkv.paged_attention_decode(None, L["q"], L["k"], L["v"], tables, lens,
                                            scale=scale, partition_size=P, part_o=part_o,
@@ -131,8 +184,6 @@ def main():
             else:
                 pkv.paged_attention_decode(out[li], L["q"], L["k"], L["v"], tables, lens,
                                            scale=scale)
-            if events is not None:
-                events[li][1].record()
             if P:
                 pkv.paged_attention_reduce(out[li], part_o, part_lse, lens, P)
 
@@ -148,15 +199,34 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
 
-    # ---- per-launch duration of the dominant kernel (same launches, HIP events) ---
-    durs = []
-    for _ in range(max(1, min(args.steps, 10))):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(cfg.num_layers)]
-        step(ev)
+    # ---- average duration of the dominant kernel -----------------------------------
+    # The decode launches of the step (same arguments, same layer pools) are queued
+    # back to back between two HIP events on the stream they run on; the elapsed
+    # time over the launch count is the kernel's average duration (the queue keeps
+    # the dispatches back to back, so inter-kernel gaps are small).
+    def decode_only(li):
+        L = layers[li % R]
+        if P:
+            pkv.paged_attention_decode(None, L["q"], L["k"], L["v"], tables, lens, scale=scale,
+                                       partition_size=P, part_o=part_o, part_lse=part_lse)
+        else:
+            pkv.paged_attention_decode(out[li], L["q"], L["k"], L["v"], tables, lens,
+                                       scale=scale)
+
+    reps = max(1, min(args.steps, 10))
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for li in range(cfg.num_layers):
+        decode_only(li)
+    d0.record()
+    for _ in range(reps):
+        for li in range(cfg.num_layers):
+            decode_only(li)
+    d1.record()
+    torch.cuda.synchronize()
+    decode_ms = d0.elapsed_time(d1) / (reps * cfg.num_layers)
+    if P:  # leave `out` holding the merged result of the last timed step
+        step()
         torch.cuda.synchronize()
-        durs += [a.elapsed_time(b) for a, b in ev]
-    decode_ms = float(np.mean(durs))
 
     assert bool(torch.isfinite(out.float()).all()), "non-finite attention output"
 
@@ -203,7 +273,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(cfg.key),
             "bytes_per_launch": ab["decode"],
             "avg_launch_ms": round(decode_ms, 5),
         },
