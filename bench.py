@@ -57,6 +57,10 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=None,
                     help="override the workload's split-context partition size (0 = single pass)")
     ap.add_argument("--distinct", type=int, default=None, help="override distinct layer pools")
+    ap.add_argument("--separate", action="store_true",
+                    help="run the append and the decode as two launches per layer "
+                         "(paged_kv_append + paged_attention_decode) instead of the fused "
+                         "paged_attention_append_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle sample")
@@ -173,17 +177,26 @@ def main():
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
 
+    fused = not args.separate
+
+    def attend(li):
+        """Decode of layer li; in fused mode it also appends the layer's new rows."""
+        L = layers[li % R]
+        o = None if P else out[li]
+        if fused:
+            pkv.paged_attention_append_decode(o, L["q"], L["k"], L["v"], L["kn"], L["vn"],
+                                              tables, lens, scale=scale, partition_size=P,
+                                              part_o=part_o, part_lse=part_lse)
+        else:
+            pkv.paged_attention_decode(o, L["q"], L["k"], L["v"], tables, lens, scale=scale,
+                                       partition_size=P, part_o=part_o, part_lse=part_lse)
+
     def step():
         for li in range(cfg.num_layers):
             L = layers[li % R]
-            pkv.paged_kv_append(L["k"], L["v"], L["kn"], L["vn"], tables, lens)
-            if P:
-                pkv.paged_attention_decode(None, L["q"], L["k"], L["v"], tables, lens,
-                                           scale=scale, partition_size=P, part_o=part_o,
-                                           part_lse=part_lse)
-            else:
-                pkv.paged_attention_decode(out[li], L["q"], L["k"], L["v"], tables, lens,
-                                           scale=scale)
+            if not fused:
+                pkv.paged_kv_append(L["k"], L["v"], L["kn"], L["vn"], tables, lens)
+            attend(li)
             if P:
                 pkv.paged_attention_reduce(out[li], part_o, part_lse, lens, P)
 
@@ -204,23 +217,14 @@ def main():
     # back to back between two HIP events on the stream they run on; the elapsed
     # time over the launch count is the kernel's average duration (the queue keeps
     # the dispatches back to back, so inter-kernel gaps are small).
-    def decode_only(li):
-        L = layers[li % R]
-        if P:
-            pkv.paged_attention_decode(None, L["q"], L["k"], L["v"], tables, lens, scale=scale,
-                                       partition_size=P, part_o=part_o, part_lse=part_lse)
-        else:
-            pkv.paged_attention_decode(out[li], L["q"], L["k"], L["v"], tables, lens,
-                                       scale=scale)
-
     reps = max(1, min(args.steps, 10))
     d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for li in range(cfg.num_layers):
-        decode_only(li)
+        attend(li)
     d0.record()
     for _ in range(reps):
         for li in range(cfg.num_layers):
-            decode_only(li)
+            attend(li)
     d1.record()
     torch.cuda.synchronize()
     decode_ms = d0.elapsed_time(d1) / (reps * cfg.num_layers)
@@ -236,7 +240,8 @@ def main():
     step_bytes = ab["layer"] * cfg.num_layers
     gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     tokens_per_s = S / (ms_per_step * 1e-3)
-    dec_gbps = ab["decode"] / (decode_ms * 1e-3) / 1e9
+    kernel_bytes = ab["decode"] + (ab["append"] if fused else 0)
+    dec_gbps = kernel_bytes / (decode_ms * 1e-3) / 1e9
 
     result = {
         "metric": METRIC,
@@ -261,20 +266,21 @@ def main():
             "pool_blocks_per_layer": int(w0.num_blocks),
             "distinct_layer_pools": R,
             "partition_size": P,
+            "launches_per_layer": (1 if fused else 2) + (1 if P else 0),
             "accumulate": "fp32",
         },
         "hbm_gbps": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "step_algorithmic_bytes": step_bytes,
         "roofline": {
-            "kernel": "paged_attention_decode",
+            "kernel": "paged_attention_append_decode" if fused else "paged_attention_decode",
             "bound": "hbm",
             "achieved": round(dec_gbps, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(cfg.key),
-            "bytes_per_launch": ab["decode"],
+            "bytes_per_launch": kernel_bytes,
             "avg_launch_ms": round(decode_ms, 5),
         },
         "setup_s": round(setup_s, 1),

@@ -146,6 +146,31 @@ int paged_attention_decode(void *out, const void *q, const void *k_pool, const v
                            float *part_lse, int dtype, void *stream);
 
 /*
+ * paged_attention_append_decode -- the step's cache-append scatter and decode
+ * attention in one launch.
+ *
+ * Same result as paged_kv_append(k_pool, v_pool, k_new, v_new, block_tables,
+ * context_lens, slot_out, ...) followed by paged_attention_decode(...) with the
+ * same arguments: the new rows end up in the pools bit for bit, and attention
+ * covers positions 0 .. n-1 with position n-1 being the new token.  The work-group
+ * that handles position n-1 of (sequence, KV head) writes the new rows to their
+ * slot and uses them from registers, so the slot is never read before it is
+ * written.  Fusing removes one launch and its dependent-latency chain per layer.
+ *
+ *   k_new, v_new   [num_seqs][num_kv_heads][head_dim], required (non-NULL)
+ *   slot_out       optional int64 [num_seqs] as for paged_kv_append
+ * Other arguments and the split-context mode are as for paged_attention_decode
+ * (in split mode the append is done by the partition holding position n-1).
+ */
+int paged_attention_append_decode(void *out, const void *q, void *k_pool, void *v_pool,
+                                  const void *k_new, const void *v_new, int64_t *slot_out,
+                                  const int32_t *block_tables, const int32_t *context_lens,
+                                  int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                  int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                                  float scale, int partition_size, int max_partitions,
+                                  float *part_o, float *part_lse, int dtype, void *stream);
+
+/*
  * paged_attention_reduce -- log-sum-exp merge of split-context partitions.
  *
  * For each (s, h) with P = partition_size and np = ceil(n/P) partitions:

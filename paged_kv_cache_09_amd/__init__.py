@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     lib_path,
     load,
     max_partitions,
+    paged_attention_append_decode,
     paged_attention_decode,
     paged_attention_reduce,
     paged_kv_append,

@@ -54,6 +54,9 @@ def load():
     L.paged_attention_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i64, f32,
                                          i32, i32, P, P, i32, P]
     L.paged_attention_decode.restype = i32
+    L.paged_attention_append_decode.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32,
+                                                i32, i32, i64, f32, i32, i32, P, P, i32, P]
+    L.paged_attention_append_decode.restype = i32
     L.paged_attention_reduce.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, P]
     L.paged_attention_reduce.restype = i32
     _lib = L
@@ -183,6 +186,29 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens,
                                        NB, float(scale), int(partition_size), mp, _p(part_o),
                                        _p(part_lse), _dtype_code(q), _stream(dev))
     _check(rc, "paged_attention_decode")
+
+
+def paged_attention_append_decode(out, q, k_pool, v_pool, k_new, v_new, block_tables,
+                                  context_lens, slot_out=None, scale: Optional[float] = None,
+                                  partition_size: int = 0, part_o=None, part_lse=None):
+    """Append each sequence's new K/V row at position context_lens[s]-1 and run
+    decode attention over positions 0..n-1, in one launch."""
+    dev = _dev(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens, slot_out,
+               part_o, part_lse)
+    _int(block_tables, "i32", "block_tables")
+    _int(context_lens, "i32", "context_lens")
+    _int(slot_out, "i64", "slot_out")
+    NB, Hkv, B, D = k_pool.shape
+    S, Hq, _ = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    mp = part_o.shape[2] if part_o is not None else 0
+    rc = load().paged_attention_append_decode(
+        _p(out), _p(q), _p(k_pool), _p(v_pool), _p(k_new), _p(v_new), _p(slot_out),
+        _p(block_tables), _p(context_lens), S, Hq, Hkv, D, B, block_tables.shape[1], NB,
+        float(scale), int(partition_size), mp, _p(part_o), _p(part_lse), _dtype_code(q),
+        _stream(dev))
+    _check(rc, "paged_attention_append_decode")
 
 
 def paged_attention_reduce(out, part_o, part_lse, context_lens, partition_size: int):

@@ -240,12 +240,18 @@ int paged_kv_append_tokens(void *k_pool, void *v_pool, const void *k_src, const 
                                                    max_blocks_per_seq, st));
 }
 
-int paged_attention_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
-                           const int32_t *block_tables, const int32_t *context_lens,
-                           int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                           int block_size, int max_blocks_per_seq, int64_t num_blocks,
-                           float scale, int partition_size, int max_partitions, float *part_o,
-                           float *part_lse, int dtype, void *stream)
+}  // extern "C"
+
+namespace {
+
+// Shared by the decode entry points: validation, then one launch.  With k_new
+// non-null the kernel also performs the step's append (fused mode).
+int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
+                const void *k_new, const void *v_new, int64_t *slot_out,
+                const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
+                int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                int max_blocks_per_seq, int64_t num_blocks, float scale, int partition_size,
+                int max_partitions, float *part_o, float *part_lse, int dtype, void *stream)
 {
     if (!q || !k_pool || !v_pool || !block_tables || !context_lens)
         return PKV_EINVAL;
@@ -263,6 +269,8 @@ int paged_attention_decode(void *out, const void *q, const void *k_pool, const v
     if (!(scale == scale) || __builtin_isinf(scale))
         return PKV_EINVAL;
     if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+        return PKV_EINVAL;
+    if (k_new && (!aligned16(k_new) || !aligned16(v_new) || ((uintptr_t)slot_out & 7u)))
         return PKV_EINVAL;
     int parts = 1;
     if (partition_size > 0) {
@@ -290,7 +298,7 @@ int paged_attention_decode(void *out, const void *q, const void *k_pool, const v
         if (rc)
             return rc;
     }
-    pkv::DecodeArgs a;
+    pkv::DecodeArgs a{};
     a.out = out;
     a.q = q;
     a.k_pool = k_pool;
@@ -308,9 +316,46 @@ int paged_attention_decode(void *out, const void *q, const void *k_pool, const v
     a.parts_per_item = parts;
     a.n_items = (int)items;
     a.scale_log2 = scale * pkv::kLog2e;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.slot_out = slot_out;
+    a.block_size = block_size;
     const hipError_t e = group == 1 ? pkv::launch_decode_g1(a, dtype, block_size, st)
                                     : pkv::launch_decode_mfma(a, dtype, block_size, st);
     return launch_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attention_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
+                           const int32_t *block_tables, const int32_t *context_lens,
+                           int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                           int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                           float scale, int partition_size, int max_partitions, float *part_o,
+                           float *part_lse, int dtype, void *stream)
+{
+    return decode_impl(out, q, k_pool, v_pool, nullptr, nullptr, nullptr, block_tables,
+                       context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                       max_blocks_per_seq, num_blocks, scale, partition_size, max_partitions,
+                       part_o, part_lse, dtype, stream);
+}
+
+int paged_attention_append_decode(void *out, const void *q, void *k_pool, void *v_pool,
+                                  const void *k_new, const void *v_new, int64_t *slot_out,
+                                  const int32_t *block_tables, const int32_t *context_lens,
+                                  int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                  int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                                  float scale, int partition_size, int max_partitions,
+                                  float *part_o, float *part_lse, int dtype, void *stream)
+{
+    if (!k_new || !v_new)
+        return PKV_EINVAL;
+    return decode_impl(out, q, k_pool, v_pool, k_new, v_new, slot_out, block_tables,
+                       context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                       max_blocks_per_seq, num_blocks, scale, partition_size, max_partitions,
+                       part_o, part_lse, dtype, stream);
 }
 
 int paged_attention_reduce(void *out, const float *part_o, const float *part_lse,

@@ -67,9 +67,11 @@ struct TileRsrc {
     __amdgpu_buffer_rsrc_t k0, k1, v0, v1;
 };
 
+// `t_load` is the end of the rows to fetch: the context end, or one less when the
+// last row is the token being appended (it is then taken from the new rows).
 template <int BS>
 __device__ __forceinline__ TileRsrc tile_rsrc(const TilePhys &p, const uint16_t *kp,
-                                              const uint16_t *vp, int tb, int t_end,
+                                              const uint16_t *vp, int tb, int t_load,
                                               int64_t head_off, int64_t blk_elems)
 {
     int64_t b0, b1;
@@ -80,7 +82,7 @@ __device__ __forceinline__ TileRsrc tile_rsrc(const TilePhys &p, const uint16_t 
         b0 = (int64_t)p.p0 * blk_elems + head_off;
         b1 = (int64_t)p.p1 * blk_elems + head_off;
     }
-    const int valid = t_end - tb;  // >= 1 for a tile that exists
+    const int valid = t_load - tb;
     // readfirstlane keeps the ranges in SGPRs (the clamp would otherwise be
     // selected as a VALU med3, making the descriptor look divergent)
     const int n0 = __builtin_amdgcn_readfirstlane(min(max(valid, 0), 16) * kHeadDim * 2);
@@ -220,12 +222,30 @@ __global__ __launch_bounds__(WAVES * 64) void decode_g1_kernel(DecodeArgs a)
     const int lane_byte = (r * kHeadDim + c * 8) * 2;
 
     const int n = a.lens[s];
+    const bool fused = a.k_new != nullptr;
+    if (fused && n <= 0 && px == 0 && h == 0 && tid == 0 && a.slot_out)
+        a.slot_out[s] = -1;  // padding sequence: nothing appended
     int t0 = 0, t1 = n;
     if (a.partition_size > 0) {
         t0 = px * a.partition_size;
         if (t0 >= n)
             return;  // partition holds no token: nothing is written
         t1 = min(n, t0 + a.partition_size);
+    }
+    // With a fused append, position n-1 (in the item's last tile) is not read
+    // from the pool: it holds stale data until this kernel writes the new row.
+    const bool owns_new = fused && t1 == n;
+    const int t_load = owns_new ? n - 1 : t1;
+    const int ntiles = (t1 - t0 + kTile - 1) / kTile;
+    // the wave holding position n-1 (the item's last tile) fetches the new rows
+    // and their block id up front, so that the latency overlaps its loop
+    const bool new_here = owns_new && ntiles > 0 && w == (ntiles - 1) % WAVES;
+    u32x4 kn = {0u, 0u, 0u, 0u}, vn = {0u, 0u, 0u, 0u};
+    const int64_t phys_n = new_here ? (int64_t)trow[(n - 1) / BS] : 0;  // block of n-1
+    if (new_here) {
+        const int64_t off = ((int64_t)s * a.num_kv_heads + h) * kHeadDim + (threadIdx.x & 15) * 8;
+        kn = *(const u32x4 *)((const uint16_t *)a.k_new + off);
+        vn = *(const u32x4 *)((const uint16_t *)a.v_new + off);
     }
 
     const u32x4 q = *(const u32x4 *)((const uint16_t *)a.q +
@@ -242,24 +262,37 @@ __global__ __launch_bounds__(WAVES * 64) void decode_g1_kernel(DecodeArgs a)
     // are pipelined separately: the next tile's K loads are issued as soon as the
     // current scores are computed, its V loads as soon as the current V rows are
     // consumed, so one tile stays in flight with a single register buffer per half.
-    const int ntiles = (t1 - t0 + kTile - 1) / kTile;
     const int T = ntiles > w ? (ntiles - w + WAVES - 1) / WAVES : 0;
     if (T > 0) {
         const int step = WAVES * kTile;
         int tb = t0 + w * kTile;
         Half K, V;
         {
-            const TileRsrc rs = tile_rsrc<BS>(tile_phys<BS>(trow, a.width, tb, t1), kp, vp, tb, t1,
-                                              head_off, blk_elems);
+            const TileRsrc rs = tile_rsrc<BS>(tile_phys<BS>(trow, a.width, tb, t1), kp, vp, tb,
+                                              t_load, head_off, blk_elems);
             load_half(K, rs.k0, rs.k1, lane_byte);
             load_half(V, rs.v0, rs.v1, lane_byte);
+        }
+        if (new_here) {
+            // write the new rows to their slot now: stores share the in-order
+            // vmcnt counter with loads, so issuing them here lets their latency
+            // overlap the loop instead of the end of the work-group
+            const int tn = n - 1;
+            const int64_t dst = phys_n * blk_elems + head_off + (int64_t)(tn % BS) * kHeadDim + c * 8;
+            if (r == 0)
+                *(u32x4 *)((uint16_t *)a.k_pool + dst) = kn;
+            else if (r == 1)
+                *(u32x4 *)((uint16_t *)a.v_pool + dst) = vn;
+            if (h == 0 && lane == 0 && a.slot_out)
+                a.slot_out[s] = phys_n * BS + tn % BS;
         }
         // table entries are looked up one tile ahead of the loads that use them
         TilePhys pn = tile_phys<BS>(trow, a.width, tb + step, t1);
         float sc[8];
         for (int j = 0; j + 1 < T; ++j) {  // every tile here is full
             const TilePhys pn2 = tile_phys<BS>(trow, a.width, tb + 2 * step, t1);
-            const TileRsrc rn = tile_rsrc<BS>(pn, kp, vp, tb + step, t1, head_off, blk_elems);
+            const TileRsrc rn =
+                tile_rsrc<BS>(pn, kp, vp, tb + step, t_load, head_off, blk_elems);
             scores<DT, false>(sc, K, q, tb, t1, r, a.scale_log2);
             // keep the scheduler from sinking the prefetches below the math they
             // are meant to overlap
@@ -272,6 +305,18 @@ __global__ __launch_bounds__(WAVES * 64) void decode_g1_kernel(DecodeArgs a)
             __builtin_amdgcn_sched_barrier(0);
             pn = pn2;
             tb += step;
+        }
+        if (new_here && tb + kTile >= n) {
+            // this tile holds position n-1: put the new rows in place of the
+            // (unfetched) pool row
+            const int row = n - 1 - tb;  // 0..31
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (row == 4 * i + r) {
+                    K.x[i] = kn;
+                    V.x[i] = vn;
+                }
+            }
         }
         if (tb + kTile <= t1) {
             scores<DT, false>(sc, K, q, tb, t1, r, a.scale_log2);

@@ -80,13 +80,15 @@ struct SubRsrc {
     __amdgpu_buffer_rsrc_t k, v;
 };
 
+// `t_load` is the end of the rows to fetch: the context end, or one less when the
+// last row is the token being appended (it is then taken from the new rows).
 template <int BS>
 __device__ __forceinline__ SubRsrc sub_rsrc(int32_t phys, const uint16_t *kp, const uint16_t *vp,
-                                            int tb, int t_end, int64_t head_off,
+                                            int tb, int t_load, int64_t head_off,
                                             int64_t blk_elems)
 {
     const int64_t base = (int64_t)phys * blk_elems + head_off + (int64_t)(tb % BS) * kHeadDim;
-    const int bytes = __builtin_amdgcn_readfirstlane(min(max(t_end - tb, 0), kSub) * kHeadDim * 2);
+    const int bytes = __builtin_amdgcn_readfirstlane(min(max(t_load - tb, 0), kSub) * kHeadDim * 2);
     SubRsrc r;
     r.k = make_rsrc(kp + base, bytes);
     r.v = make_rsrc(vp + base, bytes);
@@ -216,6 +218,10 @@ __global__ __launch_bounds__(WAVES * 64) void decode_mfma_kernel(DecodeArgs a)
     const int s = rest / a.num_kv_heads;
     const int G = a.num_q_heads / a.num_kv_heads;
     const int n = a.lens[s];
+    const int tid0 = threadIdx.x;
+    const bool fused = a.k_new != nullptr;
+    if (fused && n <= 0 && px == 0 && g == 0 && tid0 == 0 && a.slot_out)
+        a.slot_out[s] = -1;  // padding sequence: nothing appended
 
     int t0 = 0, t1 = n;
     if (a.partition_size > 0) {
@@ -224,6 +230,10 @@ __global__ __launch_bounds__(WAVES * 64) void decode_mfma_kernel(DecodeArgs a)
             return;
         t1 = min(n, t0 + a.partition_size);
     }
+    // With a fused append, position n-1 (in the item's last sub-tile) is not read
+    // from the pool: it holds stale data until this kernel writes the new row.
+    const bool owns_new = fused && t1 == n;
+    const int t_load = owns_new ? n - 1 : t1;
 
     const int tid = threadIdx.x;
     // wave index, made explicitly uniform so that tile indices and table lookups
@@ -258,6 +268,22 @@ __global__ __launch_bounds__(WAVES * 64) void decode_mfma_kernel(DecodeArgs a)
 
     uint16_t *vlds = sm.v[w];
     const int nsub = (t1 - t0 + kSub - 1) / kSub;
+    // the wave holding position n-1 (the item's last sub-tile) fetches the new rows
+    // and their block id up front, so that the latency overlaps its loop:
+    // knew[kk] is the A-operand chunk of the new key (dims 8*(4kk + lane/16)..),
+    // vnew the 16-byte chunk lane%16 of the new value row
+    const bool new_here = owns_new && nsub > 0 && w == (nsub - 1) % WAVES;
+    u32x4 knew[4] = {}, vnew = {0u, 0u, 0u, 0u};
+    const int64_t phys_n = new_here ? (int64_t)trow[(n - 1) / BS] : 0;  // block of n-1
+    if (new_here) {
+        const int64_t off = ((int64_t)s * a.num_kv_heads + g) * kHeadDim;
+        const uint16_t *kq = (const uint16_t *)a.k_new + off;
+        const uint16_t *vq = (const uint16_t *)a.v_new + off;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            knew[kk] = *(const u32x4 *)(kq + 32 * kk + 8 * grp);
+        vnew = *(const u32x4 *)(vq + 8 * col);
+    }
     const int T = nsub > w ? (nsub - w + WAVES - 1) / WAVES : 0;
     if (T > 0) {
         // Single register buffer per operand, pipelined: the next sub-tile's K
@@ -268,10 +294,27 @@ __global__ __launch_bounds__(WAVES * 64) void decode_mfma_kernel(DecodeArgs a)
         KOp K;
         VRows V;
         {
-            const SubRsrc r = sub_rsrc<BS>(sub_phys<BS>(trow, a.width, tb), kp, vp, tb, t1,
+            const SubRsrc r = sub_rsrc<BS>(sub_phys<BS>(trow, a.width, tb), kp, vp, tb, t_load,
                                            head_off, blk_elems);
             load_k(K, r.k, lane);
             load_v(V, r.v, lane);
+        }
+        if (new_here) {
+            // write the new rows to their slot now: stores share the in-order
+            // vmcnt counter with loads, so issuing them here lets their latency
+            // overlap the loop instead of the end of the work-group
+            const int tn = n - 1;
+            const int64_t dst = phys_n * blk_elems + head_off + (int64_t)(tn % BS) * kHeadDim;
+            if (col == (tn & 15)) {
+                // the four lanes of the new row's A-operand slot hold the whole key
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    *(u32x4 *)((uint16_t *)a.k_pool + dst + 32 * kk + 8 * grp) = knew[kk];
+            }
+            if (lane < 16)
+                *(u32x4 *)((uint16_t *)a.v_pool + dst + lane * 8) = vnew;
+            if (g == 0 && lane == 0 && a.slot_out)
+                a.slot_out[s] = phys_n * BS + tn % BS;
         }
         // table entries are looked up one sub-tile ahead of the loads that use them
         int32_t pn = sub_phys<BS>(trow, a.width, tb + step);
@@ -279,7 +322,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_mfma_kernel(DecodeArgs a)
         float alpha;
         for (int j = 0; j + 1 < T; ++j) {  // every sub-tile here is full
             const int32_t pn2 = sub_phys<BS>(trow, a.width, tb + 2 * step);
-            const SubRsrc rn = sub_rsrc<BS>(pn, kp, vp, tb + step, t1, head_off, blk_elems);
+            const SubRsrc rn = sub_rsrc<BS>(pn, kp, vp, tb + step, t_load, head_off, blk_elems);
             qk_softmax<DT, false>(st, K, qop, tb, t1, lane, a.scale_log2, pb, alpha);
             __builtin_amdgcn_sched_barrier(0);
             load_k(K, rn.k, lane);
@@ -293,11 +336,23 @@ __global__ __launch_bounds__(WAVES * 64) void decode_mfma_kernel(DecodeArgs a)
             pn = pn2;
             tb += step;
         }
+        // position n-1 in this sub-tile: put the new rows in place of the
+        // (unfetched) pool row
+        const bool here = new_here && tb + kSub >= n;
+        const int row = n - 1 - tb;  // 0..15 when `here`
+        if (here && (lane & 15) == row) {
+            // the four lanes of row `row` take the new key into the A operand
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                K.k[kk] = knew[kk];
+        }
         if (tb + kSub <= t1)
             qk_softmax<DT, false>(st, K, qop, tb, t1, lane, a.scale_log2, pb, alpha);
         else
             qk_softmax<DT, true>(st, K, qop, tb, t1, lane, a.scale_log2, pb, alpha);
         stage_v(V, vlds, lane);
+        if (here && lane < 16)
+            *(u32x4 *)(vlds + row * kVStride + lane * 8) = vnew;
         pv_mma<DT>(st, vlds, pb, alpha, lane);
     }
 

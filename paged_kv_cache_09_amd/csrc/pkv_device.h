@@ -148,6 +148,12 @@ struct DecodeArgs {
     int parts_per_item;         // partitions launched per (sequence, kv head)
     int n_items;
     float scale_log2;           // scale * log2(e)
+    // fused append (null for plain decode): the new token's rows, written to
+    // position n-1 of each sequence and used in registers for that position
+    const void *k_new;          // [S][Hkv][D]
+    const void *v_new;
+    int64_t *slot_out;          // optional [S]
+    int block_size;
 };
 
 }  // namespace pkv

@@ -43,7 +43,8 @@ class GpuStep:
     """Device state of one layer of a workload: pools filled with the NaN
     sentinel, then history runs and the new token written by the library."""
 
-    def __init__(self, w, device="cuda:0", tables=None, k_pool_bits=None, v_pool_bits=None):
+    def __init__(self, w, device="cuda:0", tables=None, k_pool_bits=None, v_pool_bits=None,
+                 append=True):
         c = w.cfg
         self.w, self.c, self.device = w, c, torch.device(device)
         dt = TORCH_DT[c.dtype]
@@ -67,9 +68,11 @@ class GpuStep:
                 to_dev(w.v_src, c.dtype, self.device), i64(w.seg_cu, self.device),
                 i32(w.seg_start, self.device), i32(w.seg_tables, self.device))
         self.slots = torch.full((c.num_seqs,), -7, dtype=torch.int64, device=self.device)
-        pkv.paged_kv_append(self.k_pool, self.v_pool, to_dev(w.k_new, c.dtype, self.device),
-                            to_dev(w.v_new, c.dtype, self.device), self.tables, self.lens,
-                            self.slots)
+        self.k_new = to_dev(w.k_new, c.dtype, self.device)
+        self.v_new = to_dev(w.v_new, c.dtype, self.device)
+        if append:
+            pkv.paged_kv_append(self.k_pool, self.v_pool, self.k_new, self.v_new, self.tables,
+                                self.lens, self.slots)
 
     def decode(self, partition_size: int = 0, scale=None, max_parts=None):
         c = self.c
@@ -91,6 +94,30 @@ class GpuStep:
                                    part_lse=pl)
         pkv.paged_attention_reduce(out, po, pl, self.lens, partition_size)
         return out, po, pl
+
+
+def fused_step(g: GpuStep, partition_size: int = 0, scale=None):
+    """Append + decode in one launch (paged_attention_append_decode) on a GpuStep
+    built with append=False; returns the output (merged in split mode)."""
+    c = g.c
+    scale = scale_for(c.head_dim) if scale is None else scale
+    out = torch.empty((c.num_seqs, c.num_q_heads, c.head_dim), dtype=TORCH_DT[c.dtype],
+                      device=g.device)
+    out.view(torch.int16).fill_(0x5555)
+    if partition_size == 0:
+        pkv.paged_attention_append_decode(out, g.q, g.k_pool, g.v_pool, g.k_new, g.v_new,
+                                          g.tables, g.lens, g.slots, scale=scale)
+        return out
+    mp = pkv.max_partitions(c.max_blocks_per_seq, c.block_size, partition_size)
+    po = torch.full((c.num_seqs, c.num_q_heads, mp, c.head_dim), float("nan"),
+                    dtype=torch.float32, device=g.device)
+    pl = torch.full((c.num_seqs, c.num_q_heads, mp), float("nan"), dtype=torch.float32,
+                    device=g.device)
+    pkv.paged_attention_append_decode(None, g.q, g.k_pool, g.v_pool, g.k_new, g.v_new, g.tables,
+                                      g.lens, g.slots, scale=scale,
+                                      partition_size=partition_size, part_o=po, part_lse=pl)
+    pkv.paged_attention_reduce(out, po, pl, g.lens, partition_size)
+    return out
 
 
 def tol_ok(got: np.ndarray, ref: np.ndarray, atol=1e-2, rtol=1e-2):

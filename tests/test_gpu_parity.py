@@ -18,7 +18,7 @@ torch = pytest.importorskip("torch")
 
 from workloads import get_config, make_workload  # noqa: E402
 from oracle import oracle as O  # noqa: E402
-from gpu_harness import GpuStep, bits_of, scale_for, tol_ok, widen_out  # noqa: E402
+from gpu_harness import GpuStep, bits_of, fused_step, scale_for, tol_ok, widen_out  # noqa: E402
 import paged_kv_cache_09_amd as pkv  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -108,6 +108,29 @@ def test_decode_partitioned(key, P):
 
 
 # ---------------------------------------------------------------------------
+FUSED = [(k, 0) for k in ALL] + [("c1b", 32), ("c2", 256), ("c3", 64), ("c4", 2048),
+                                 ("c5", 128)]
+
+
+@pytest.mark.parametrize("key,P", FUSED)
+def test_fused_append_decode(key, P):
+    """paged_attention_append_decode = paged_kv_append then paged_attention_decode:
+    pools and slots bit-exact, output within tolerance of the oracle."""
+    w, r = oracle_for(key)
+    print(f"[gpu] fused {key} P={P}", flush=True)
+    g = GpuStep(w, append=False)
+    out = fused_step(g, P)
+    torch.cuda.synchronize()
+    assert np.array_equal(g.slots.cpu().numpy(), r["slots"])
+    ref = referenced_blocks(w)
+    idx = torch.from_numpy(ref.astype(np.int64)).to(g.device)
+    assert np.array_equal(bits_of(g.k_pool[idx]), r["k_pool"][ref])
+    assert np.array_equal(bits_of(g.v_pool[idx]), r["v_pool"][ref])
+    ok, err, nbad = tol_ok(widen_out(out), r["out"])
+    assert ok, f"{key} P={P}: max err {err}, {nbad} bad"
+
+
+# ---------------------------------------------------------------------------
 def _relabel(kbits, vbits, tables, seed):
     rng = np.random.default_rng(seed)
     pi = rng.permutation(kbits.shape[0])
@@ -180,6 +203,15 @@ def test_edge_cases(B, hq, hkv, dt, lens, P):
     for s, n in enumerate(lens):
         if n == 0:
             assert (got[s] == 0).all()
+    # the fused append + decode on a fresh copy gives the same pools and output
+    g2 = GpuStep(w, append=False)
+    out2 = fused_step(g2, P)
+    torch.cuda.synchronize()
+    assert np.array_equal(g2.slots.cpu().numpy(), r["slots"])
+    assert np.array_equal(bits_of(g2.k_pool), r["k_pool"])
+    assert np.array_equal(bits_of(g2.v_pool), r["v_pool"])
+    ok, err, nbad = tol_ok(widen_out(out2), r["out"])
+    assert ok, f"fused: max err {err}, {nbad} bad"
 
 
 def test_scale_zero_is_mean_over_exactly_n_tokens():
