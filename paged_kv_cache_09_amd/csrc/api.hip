@@ -281,7 +281,16 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
             return PKV_EWORKSPACE;
         if (!aligned16(part_o) || ((uintptr_t)part_lse & 3u))
             return PKV_EINVAL;
-        parts = need;
+        // Work-groups per (sequence, KV head): enough for about kTargetGroups
+        // work-groups in total, never more than the partitions a full table row
+        // could hold.  Each work-group strides over its item's partitions, so the
+        // result does not depend on this choice -- only the parallelism does
+        // (sizing the grid by the table width would launch mostly empty
+        // work-groups when contexts are much shorter than the row).
+        constexpr int64_t kTargetGroups = 2048;
+        const int64_t base_items = (int64_t)num_seqs * num_kv_heads;
+        int64_t want = base_items > 0 ? (kTargetGroups + base_items - 1) / base_items : 1;
+        parts = (int)(want < need ? want : need);
     } else {
         if (!out || ((uintptr_t)out & 1u))
             return PKV_EINVAL;

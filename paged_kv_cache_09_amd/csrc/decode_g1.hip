@@ -43,9 +43,12 @@ struct TilePhys {
     int32_t p0, p1;
 };
 
+// Raw table entries of the tile at token tb (the second one is only used for
+// BS == 16).  Reading them does not depend on the context length, so they can
+// be requested before it is known.
 template <int BS>
-__device__ __forceinline__ TilePhys tile_phys(const int32_t *__restrict__ trow, int width, int tb,
-                                              int t_end)
+__device__ __forceinline__ TilePhys tile_entries(const int32_t *__restrict__ trow, int width,
+                                                 int tb)
 {
     TilePhys p;
     if constexpr (BS >= kTile) {
@@ -54,10 +57,24 @@ __device__ __forceinline__ TilePhys tile_phys(const int32_t *__restrict__ trow, 
     } else {
         static_assert(BS == 16, "block sizes below 32 other than 16 are not built");
         p.p0 = trow[min(tb / 16, width - 1)];
-        const int32_t second = trow[min(tb / 16 + 1, width - 1)];
-        p.p1 = (tb + 16 < t_end) ? second : p.p0;
+        p.p1 = trow[min(tb / 16 + 1, width - 1)];
     }
     return p;
+}
+
+template <int BS>
+__device__ __forceinline__ TilePhys tile_select(TilePhys p, int tb, int t_end)
+{
+    if constexpr (BS < kTile)
+        p.p1 = (tb + 16 < t_end) ? p.p1 : p.p0;
+    return p;
+}
+
+template <int BS>
+__device__ __forceinline__ TilePhys tile_phys(const int32_t *__restrict__ trow, int width, int tb,
+                                              int t_end)
+{
+    return tile_select<BS>(tile_entries<BS>(trow, width, tb), tb, t_end);
 }
 
 // Buffer resources of the two 16-token halves of a tile in the K and V pools.
@@ -190,8 +207,13 @@ __device__ __forceinline__ void merge_xor(RowState<DT> &st, int mask)
     st.m = M;
 }
 
-template <int DT, int BS, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void decode_g1_kernel(DecodeArgs a)
+// SPLIT: split-context mode (partition loop); otherwise one pass over the
+// whole context, with the loop folded away at compile time.
+// The register budget is capped so that 4 waves fit on each SIMD (the
+// split variant would otherwise be allocated past that occupancy).
+template <int DT, int BS, int WAVES, bool SPLIT>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
+void decode_g1_kernel(DecodeArgs a)
 {
     __shared__ float s_acc[WAVES][kHeadDim];
     __shared__ float s_m[WAVES], s_l[WAVES];
@@ -202,8 +224,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_g1_kernel(DecodeArgs a)
     // than one head's slice of many blocks.  Measured faster on MI355X than the
     // KV-head-major order.
     const int item = blockIdx.x;
-    const int px = item % a.parts_per_item;
-    const int rest = item / a.parts_per_item;
+    const int parts = SPLIT ? a.parts_per_item : 1;
+    const int px0 = item % parts;
+    const int rest = item / parts;
     const int h = rest % a.num_kv_heads;  // query head == kv head
     const int s = rest / a.num_kv_heads;
 
@@ -220,171 +243,192 @@ __global__ __launch_bounds__(WAVES * 64) void decode_g1_kernel(DecodeArgs a)
     const int64_t blk_elems = (int64_t)a.num_kv_heads * BS * kHeadDim;
     const int64_t head_off = (int64_t)h * BS * kHeadDim;
     const int lane_byte = (r * kHeadDim + c * 8) * 2;
+    const int P = SPLIT ? a.partition_size : 0;
 
+    // The first tile's table entries (and the next tile's) do not depend on the
+    // context length: request them together with it, so the two scalar-load
+    // latencies overlap instead of chaining.
+    const int tb_first = (P > 0 ? px0 * P : 0) + w * kTile;
+    const TilePhys e_first = tile_entries<BS>(trow, a.width, tb_first);
+    const TilePhys e_next = tile_entries<BS>(trow, a.width, tb_first + WAVES * kTile);
     const int n = a.lens[s];
     const bool fused = a.k_new != nullptr;
-    if (fused && n <= 0 && px == 0 && h == 0 && tid == 0 && a.slot_out)
+    if (fused && n <= 0 && px0 == 0 && h == 0 && tid == 0 && a.slot_out)
         a.slot_out[s] = -1;  // padding sequence: nothing appended
-    int t0 = 0, t1 = n;
-    if (a.partition_size > 0) {
-        t0 = px * a.partition_size;
-        if (t0 >= n)
-            return;  // partition holds no token: nothing is written
-        t1 = min(n, t0 + a.partition_size);
-    }
-    // With a fused append, position n-1 (in the item's last tile) is not read
-    // from the pool: it holds stale data until this kernel writes the new row.
-    const bool owns_new = fused && t1 == n;
-    const int t_load = owns_new ? n - 1 : t1;
-    const int ntiles = (t1 - t0 + kTile - 1) / kTile;
-    // the wave holding position n-1 (the item's last tile) fetches the new rows
-    // and their block id up front, so that the latency overlaps its loop
-    const bool new_here = owns_new && ntiles > 0 && w == (ntiles - 1) % WAVES;
-    u32x4 kn = {0u, 0u, 0u, 0u}, vn = {0u, 0u, 0u, 0u};
-    const int64_t phys_n = new_here ? (int64_t)trow[(n - 1) / BS] : 0;  // block of n-1
-    if (new_here) {
-        const int64_t off = ((int64_t)s * a.num_kv_heads + h) * kHeadDim + (threadIdx.x & 15) * 8;
-        kn = *(const u32x4 *)((const uint16_t *)a.k_new + off);
-        vn = *(const u32x4 *)((const uint16_t *)a.v_new + off);
-    }
 
     const u32x4 q = *(const u32x4 *)((const uint16_t *)a.q +
                                      ((int64_t)s * a.num_q_heads + h) * kHeadDim + c * 8);
 
-    RowState<DT> st;
-    st.m = kNegInf;
-    st.l = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        st.acc[j] = 0.f;
-
-    // Tiles w, w+WAVES, ... of the item belong to this wave.  The K and V halves
-    // are pipelined separately: the next tile's K loads are issued as soon as the
-    // current scores are computed, its V loads as soon as the current V rows are
-    // consumed, so one tile stays in flight with a single register buffer per half.
-    const int T = ntiles > w ? (ntiles - w + WAVES - 1) / WAVES : 0;
-    if (T > 0) {
-        const int step = WAVES * kTile;
-        int tb = t0 + w * kTile;
-        Half K, V;
-        {
-            const TileRsrc rs = tile_rsrc<BS>(tile_phys<BS>(trow, a.width, tb, t1), kp, vp, tb,
-                                              t_load, head_off, blk_elems);
-            load_half(K, rs.k0, rs.k1, lane_byte);
-            load_half(V, rs.v0, rs.v1, lane_byte);
-        }
+    // Partitions px0, px0 + parts_per_item, ... of the item belong to this
+    // work-group (the grid is sized from the batch, not from the table width, so
+    // short sequences do not launch empty work-groups).  Single pass: px0 = 0,
+    // one iteration over the whole context (which also writes zeros when n = 0).
+    const int np = SPLIT ? (n + P - 1) / P : 1;
+    for (int px = px0; px < np; px += parts) {
+        if (px != px0)
+            __syncthreads();  // the previous partition's merge is done with LDS
+        const int t0 = P > 0 ? px * P : 0;
+        const int t1 = P > 0 ? min(n, t0 + P) : n;
+        // With a fused append, position n-1 (in the item's last tile) is not read
+        // from the pool: it holds stale data until this kernel writes the new row.
+        const bool owns_new = fused && t1 == n;
+        const int t_load = owns_new ? n - 1 : t1;
+        const int ntiles = (t1 - t0 + kTile - 1) / kTile;
+        // the wave holding position n-1 (the item's last tile) fetches the new
+        // rows and their block id up front, so that the latency overlaps its loop
+        const bool new_here = owns_new && ntiles > 0 && w == (ntiles - 1) % WAVES;
+        u32x4 kn = {0u, 0u, 0u, 0u}, vn = {0u, 0u, 0u, 0u};
+        const int64_t phys_n = new_here ? (int64_t)trow[(n - 1) / BS] : 0;  // block of n-1
         if (new_here) {
-            // write the new rows to their slot now: stores share the in-order
-            // vmcnt counter with loads, so issuing them here lets their latency
-            // overlap the loop instead of the end of the work-group
-            const int tn = n - 1;
-            const int64_t dst = phys_n * blk_elems + head_off + (int64_t)(tn % BS) * kHeadDim + c * 8;
-            if (r == 0)
-                *(u32x4 *)((uint16_t *)a.k_pool + dst) = kn;
-            else if (r == 1)
-                *(u32x4 *)((uint16_t *)a.v_pool + dst) = vn;
-            if (h == 0 && lane == 0 && a.slot_out)
-                a.slot_out[s] = phys_n * BS + tn % BS;
+            const int64_t off = ((int64_t)s * a.num_kv_heads + h) * kHeadDim + c * 8;
+            kn = *(const u32x4 *)((const uint16_t *)a.k_new + off);
+            vn = *(const u32x4 *)((const uint16_t *)a.v_new + off);
         }
-        // table entries are looked up one tile ahead of the loads that use them
-        TilePhys pn = tile_phys<BS>(trow, a.width, tb + step, t1);
-        float sc[8];
-        for (int j = 0; j + 1 < T; ++j) {  // every tile here is full
-            const TilePhys pn2 = tile_phys<BS>(trow, a.width, tb + 2 * step, t1);
-            const TileRsrc rn =
-                tile_rsrc<BS>(pn, kp, vp, tb + step, t_load, head_off, blk_elems);
-            scores<DT, false>(sc, K, q, tb, t1, r, a.scale_log2);
-            // keep the scheduler from sinking the prefetches below the math they
-            // are meant to overlap
-            __builtin_amdgcn_sched_barrier(0);
-            load_half(K, rn.k0, rn.k1, lane_byte);
-            __builtin_amdgcn_sched_barrier(0);
-            accumulate<DT, false>(st, sc, V, tb, t1, r);
-            __builtin_amdgcn_sched_barrier(0);
-            load_half(V, rn.v0, rn.v1, lane_byte);
-            __builtin_amdgcn_sched_barrier(0);
-            pn = pn2;
-            tb += step;
-        }
-        if (new_here && tb + kTile >= n) {
-            // this tile holds position n-1: put the new rows in place of the
-            // (unfetched) pool row
-            const int row = n - 1 - tb;  // 0..31
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if (row == 4 * i + r) {
-                    K.x[i] = kn;
-                    V.x[i] = vn;
-                }
-            }
-        }
-        if (tb + kTile <= t1) {
-            scores<DT, false>(sc, K, q, tb, t1, r, a.scale_log2);
-            accumulate<DT, false>(st, sc, V, tb, t1, r);
-        } else {
-            scores<DT, true>(sc, K, q, tb, t1, r, a.scale_log2);
-            accumulate<DT, true>(st, sc, V, tb, t1, r);
-        }
-    }
 
-    // rows of the wave -> one state per wave (identical in every lane)
-    merge_xor<DT>(st, 16);
-    merge_xor<DT>(st, 32);
-    if (WAVES == 1) {
-        if (r == 0) {
-            const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
-            const int64_t row = (int64_t)s * a.num_q_heads + h;
-            if (a.partition_size == 0) {
-                u32x4 o;
-                o.x = (uint32_t)to_bits<DT>(st.acc[0] * inv) | ((uint32_t)to_bits<DT>(st.acc[1] * inv) << 16);
-                o.y = (uint32_t)to_bits<DT>(st.acc[2] * inv) | ((uint32_t)to_bits<DT>(st.acc[3] * inv) << 16);
-                o.z = (uint32_t)to_bits<DT>(st.acc[4] * inv) | ((uint32_t)to_bits<DT>(st.acc[5] * inv) << 16);
-                o.w = (uint32_t)to_bits<DT>(st.acc[6] * inv) | ((uint32_t)to_bits<DT>(st.acc[7] * inv) << 16);
-                *(u32x4 *)((uint16_t *)a.out + row * kHeadDim + c * 8) = o;
-            } else {
-                float *po = a.part_o + (row * a.max_partitions + px) * kHeadDim + c * 8;
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    po[j] = st.acc[j] * inv;
-                if (c == 0)
-                    a.part_lse[row * a.max_partitions + px] = (safe_ref(st.m) + flog2(st.l)) * kLn2;
-            }
-        }
-        return;
-    }
-    if (r == 0) {
+        RowState<DT> st;
+        st.m = kNegInf;
+        st.l = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            s_acc[w][c * 8 + j] = st.acc[j];
-    }
-    if (lane == 0) {
-        s_m[w] = st.m;
-        s_l[w] = st.l;
-    }
-    __syncthreads();
+            st.acc[j] = 0.f;
 
-    if (tid < kHeadDim) {
-        const int d = tid;
-        float M = s_m[0];
+        // Tiles w, w+WAVES, ... of the partition belong to this wave.  The K and V
+        // halves are pipelined separately: the next tile's K loads are issued as
+        // soon as the current scores are computed, its V loads as soon as the
+        // current V rows are consumed, so one tile stays in flight with a single
+        // register buffer per half.
+        const int T = ntiles > w ? (ntiles - w + WAVES - 1) / WAVES : 0;
+        if (T > 0) {
+            const int step = WAVES * kTile;
+            int tb = t0 + w * kTile;
+            const bool first = px == px0;
+            Half K, V;
+            {
+                const TilePhys ef = first ? e_first : tile_entries<BS>(trow, a.width, tb);
+                const TileRsrc rs = tile_rsrc<BS>(tile_select<BS>(ef, tb, t1), kp, vp, tb,
+                                                  t_load, head_off, blk_elems);
+                load_half(K, rs.k0, rs.k1, lane_byte);
+                load_half(V, rs.v0, rs.v1, lane_byte);
+            }
+            if (new_here) {
+                // write the new rows to their slot now: stores share the in-order
+                // vmcnt counter with loads, so issuing them here lets their latency
+                // overlap the loop instead of the end of the work-group
+                const int tn = n - 1;
+                const int64_t dst =
+                    phys_n * blk_elems + head_off + (int64_t)(tn % BS) * kHeadDim + c * 8;
+                if (r == 0)
+                    *(u32x4 *)((uint16_t *)a.k_pool + dst) = kn;
+                else if (r == 1)
+                    *(u32x4 *)((uint16_t *)a.v_pool + dst) = vn;
+                if (h == 0 && lane == 0 && a.slot_out)
+                    a.slot_out[s] = phys_n * BS + tn % BS;
+            }
+            // table entries are looked up one tile ahead of the loads that use them
+            const TilePhys en = first ? e_next : tile_entries<BS>(trow, a.width, tb + step);
+            TilePhys pn = tile_select<BS>(en, tb + step, t1);
+            float sc[8];
+            for (int j = 0; j + 1 < T; ++j) {  // every tile here is full
+                const TilePhys pn2 = tile_phys<BS>(trow, a.width, tb + 2 * step, t1);
+                const TileRsrc rn =
+                    tile_rsrc<BS>(pn, kp, vp, tb + step, t_load, head_off, blk_elems);
+                scores<DT, false>(sc, K, q, tb, t1, r, a.scale_log2);
+                // keep the scheduler from sinking the prefetches below the math they
+                // are meant to overlap
+                __builtin_amdgcn_sched_barrier(0);
+                load_half(K, rn.k0, rn.k1, lane_byte);
+                __builtin_amdgcn_sched_barrier(0);
+                accumulate<DT, false>(st, sc, V, tb, t1, r);
+                __builtin_amdgcn_sched_barrier(0);
+                load_half(V, rn.v0, rn.v1, lane_byte);
+                __builtin_amdgcn_sched_barrier(0);
+                pn = pn2;
+                tb += step;
+            }
+            if (new_here && tb + kTile >= n) {
+                // this tile holds position n-1: put the new rows in place of the
+                // (unfetched) pool row
+                const int row = n - 1 - tb;  // 0..31
 #pragma unroll
-        for (int i = 1; i < WAVES; ++i)
-            M = fmaxf(M, s_m[i]);
-        const float ref = safe_ref(M);
-        float L = 0.f, O = 0.f;
-#pragma unroll
-        for (int i = 0; i < WAVES; ++i) {
-            const float wgt = fexp2(s_m[i] - ref);
-            L += s_l[i] * wgt;
-            O += s_acc[i][d] * wgt;
+                for (int i = 0; i < 8; ++i) {
+                    if (row == 4 * i + r) {
+                        K.x[i] = kn;
+                        V.x[i] = vn;
+                    }
+                }
+            }
+            if (tb + kTile <= t1) {
+                scores<DT, false>(sc, K, q, tb, t1, r, a.scale_log2);
+                accumulate<DT, false>(st, sc, V, tb, t1, r);
+            } else {
+                scores<DT, true>(sc, K, q, tb, t1, r, a.scale_log2);
+                accumulate<DT, true>(st, sc, V, tb, t1, r);
+            }
         }
+
+        // rows of the wave -> one state per wave (identical in every lane)
+        merge_xor<DT>(st, 16);
+        merge_xor<DT>(st, 32);
         const int64_t row = (int64_t)s * a.num_q_heads + h;
-        if (a.partition_size == 0) {
-            const float o = L > 0.f ? O / L : 0.f;
-            ((uint16_t *)a.out)[row * kHeadDim + d] = to_bits<DT>(o);
-        } else {
-            a.part_o[(row * a.max_partitions + px) * kHeadDim + d] = O / L;
-            if (d == 0)
-                a.part_lse[row * a.max_partitions + px] = (ref + flog2(L)) * kLn2;
+        if (WAVES == 1) {
+            if (r == 0) {
+                const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+                if (P == 0) {
+                    u32x4 o;
+                    o.x = (uint32_t)to_bits<DT>(st.acc[0] * inv) |
+                          ((uint32_t)to_bits<DT>(st.acc[1] * inv) << 16);
+                    o.y = (uint32_t)to_bits<DT>(st.acc[2] * inv) |
+                          ((uint32_t)to_bits<DT>(st.acc[3] * inv) << 16);
+                    o.z = (uint32_t)to_bits<DT>(st.acc[4] * inv) |
+                          ((uint32_t)to_bits<DT>(st.acc[5] * inv) << 16);
+                    o.w = (uint32_t)to_bits<DT>(st.acc[6] * inv) |
+                          ((uint32_t)to_bits<DT>(st.acc[7] * inv) << 16);
+                    *(u32x4 *)((uint16_t *)a.out + row * kHeadDim + c * 8) = o;
+                } else {
+                    float *po = a.part_o + (row * a.max_partitions + px) * kHeadDim + c * 8;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        po[j] = st.acc[j] * inv;
+                    if (c == 0)
+                        a.part_lse[row * a.max_partitions + px] =
+                            (safe_ref(st.m) + flog2(st.l)) * kLn2;
+                }
+            }
+            continue;
+        }
+        if (r == 0) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                s_acc[w][c * 8 + j] = st.acc[j];
+        }
+        if (lane == 0) {
+            s_m[w] = st.m;
+            s_l[w] = st.l;
+        }
+        __syncthreads();
+
+        if (tid < kHeadDim) {
+            const int d = tid;
+            float M = s_m[0];
+#pragma unroll
+            for (int i = 1; i < WAVES; ++i)
+                M = fmaxf(M, s_m[i]);
+            const float ref = safe_ref(M);
+            float L = 0.f, O = 0.f;
+#pragma unroll
+            for (int i = 0; i < WAVES; ++i) {
+                const float wgt = fexp2(s_m[i] - ref);
+                L += s_l[i] * wgt;
+                O += s_acc[i][d] * wgt;
+            }
+            if (P == 0) {
+                const float o = L > 0.f ? O / L : 0.f;
+                ((uint16_t *)a.out)[row * kHeadDim + d] = to_bits<DT>(o);
+            } else {
+                a.part_o[(row * a.max_partitions + px) * kHeadDim + d] = O / L;
+                if (d == 0)
+                    a.part_lse[row * a.max_partitions + px] = (ref + flog2(L)) * kLn2;
+            }
         }
     }
 }
@@ -400,7 +444,12 @@ template <int DT, int BS>
 static hipError_t launch_g1_t(const DecodeArgs &a, hipStream_t stream)
 {
     constexpr int W = PKV_G1_WAVES;
-    hipLaunchKernelGGL((decode_g1_kernel<DT, BS, W>), dim3(a.n_items), dim3(W * 64), 0, stream, a);
+    if (a.partition_size > 0)
+        hipLaunchKernelGGL((decode_g1_kernel<DT, BS, W, true>), dim3(a.n_items), dim3(W * 64), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((decode_g1_kernel<DT, BS, W, false>), dim3(a.n_items), dim3(W * 64), 0,
+                           stream, a);
     return hipGetLastError();
 }
 

@@ -199,8 +199,14 @@ __device__ __forceinline__ void pv_mma(GqaState &st, const uint16_t *vlds, const
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int DT, int BS, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void decode_mfma_kernel(DecodeArgs a)
+// SPLIT: split-context mode (partition loop); otherwise one pass over the
+// whole context, with the loop folded away at compile time.
+// The register budget is capped so that 4 waves (single pass) or 3 waves (split
+// mode, which keeps more state live across its partition loop) fit on each SIMD
+// without spilling.
+template <int DT, int BS, int WAVES, bool SPLIT>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SPLIT ? 3 : 4)))
+void decode_mfma_kernel(DecodeArgs a)
 {
     // V staging during the token loop; the cross-wave merge afterwards
     __shared__ union {
@@ -212,29 +218,12 @@ __global__ __launch_bounds__(WAVES * 64) void decode_mfma_kernel(DecodeArgs a)
     // sequence-major work items (see the MHA kernel): the KV heads of a sequence
     // are neighbours in dispatch order
     const int item = blockIdx.x;
-    const int px = item % a.parts_per_item;
-    const int rest = item / a.parts_per_item;
+    const int parts = SPLIT ? a.parts_per_item : 1;
+    const int px0 = item % parts;
+    const int rest = item / parts;
     const int g = rest % a.num_kv_heads;  // kv head
     const int s = rest / a.num_kv_heads;
     const int G = a.num_q_heads / a.num_kv_heads;
-    const int n = a.lens[s];
-    const int tid0 = threadIdx.x;
-    const bool fused = a.k_new != nullptr;
-    if (fused && n <= 0 && px == 0 && g == 0 && tid0 == 0 && a.slot_out)
-        a.slot_out[s] = -1;  // padding sequence: nothing appended
-
-    int t0 = 0, t1 = n;
-    if (a.partition_size > 0) {
-        t0 = px * a.partition_size;
-        if (t0 >= n)
-            return;
-        t1 = min(n, t0 + a.partition_size);
-    }
-    // With a fused append, position n-1 (in the item's last sub-tile) is not read
-    // from the pool: it holds stale data until this kernel writes the new row.
-    const bool owns_new = fused && t1 == n;
-    const int t_load = owns_new ? n - 1 : t1;
-
     const int tid = threadIdx.x;
     // wave index, made explicitly uniform so that tile indices and table lookups
     // stay in SGPRs (scalar loads of the table entries)
@@ -247,6 +236,18 @@ __global__ __launch_bounds__(WAVES * 64) void decode_mfma_kernel(DecodeArgs a)
     const int32_t *__restrict__ trow = a.tables + (int64_t)s * a.width;
     const int64_t blk_elems = (int64_t)a.num_kv_heads * BS * kHeadDim;
     const int64_t head_off = (int64_t)g * BS * kHeadDim;
+    const int P = SPLIT ? a.partition_size : 0;
+
+    // The first sub-tile's table entry (and the next one's) do not depend on the
+    // context length: request them together with it, so the two scalar-load
+    // latencies overlap instead of chaining.
+    const int tb_first = (P > 0 ? px0 * P : 0) + w * kSub;
+    const int32_t e_first = sub_phys<BS>(trow, a.width, tb_first);
+    const int32_t e_next = sub_phys<BS>(trow, a.width, tb_first + WAVES * kSub);
+    const int n = a.lens[s];
+    const bool fused = a.k_new != nullptr;
+    if (fused && n <= 0 && px0 == 0 && g == 0 && tid == 0 && a.slot_out)
+        a.slot_out[s] = -1;  // padding sequence: nothing appended
 
     // B operand of the score MFMAs: Q^T, query row `col` of the group (zero padding)
     u32x4 qop[4];
@@ -258,143 +259,161 @@ __global__ __launch_bounds__(WAVES * 64) void decode_mfma_kernel(DecodeArgs a)
         for (int kk = 0; kk < 4; ++kk)
             qop[kk] = col < G ? *(const u32x4 *)(qrow + kk * 32) : (u32x4){0u, 0u, 0u, 0u};
     }
-
-    GqaState st;
-    st.m = kNegInf;
-    st.l = 0.f;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj)
-        st.acc[jj] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
     uint16_t *vlds = sm.v[w];
-    const int nsub = (t1 - t0 + kSub - 1) / kSub;
-    // the wave holding position n-1 (the item's last sub-tile) fetches the new rows
-    // and their block id up front, so that the latency overlaps its loop:
-    // knew[kk] is the A-operand chunk of the new key (dims 8*(4kk + lane/16)..),
-    // vnew the 16-byte chunk lane%16 of the new value row
-    const bool new_here = owns_new && nsub > 0 && w == (nsub - 1) % WAVES;
-    u32x4 knew[4] = {}, vnew = {0u, 0u, 0u, 0u};
-    const int64_t phys_n = new_here ? (int64_t)trow[(n - 1) / BS] : 0;  // block of n-1
-    if (new_here) {
-        const int64_t off = ((int64_t)s * a.num_kv_heads + g) * kHeadDim;
-        const uint16_t *kq = (const uint16_t *)a.k_new + off;
-        const uint16_t *vq = (const uint16_t *)a.v_new + off;
+    const int64_t row0 = (int64_t)s * a.num_q_heads + (int64_t)g * G;
+
+    // Partitions px0, px0 + parts_per_item, ... of the item belong to this
+    // work-group (the grid is sized from the batch, not from the table width).
+    // Single pass: one iteration over the whole context (zeros when n = 0).
+    const int np = SPLIT ? (n + P - 1) / P : 1;
+    for (int px = px0; px < np; px += parts) {
+        if (px != px0)
+            __syncthreads();  // the previous partition's merge is done with LDS
+        const int t0 = P > 0 ? px * P : 0;
+        const int t1 = P > 0 ? min(n, t0 + P) : n;
+        // With a fused append, position n-1 (in the item's last sub-tile) is not
+        // read from the pool: it holds stale data until this kernel writes it.
+        const bool owns_new = fused && t1 == n;
+        const int t_load = owns_new ? n - 1 : t1;
+
+        GqaState st;
+        st.m = kNegInf;
+        st.l = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            knew[kk] = *(const u32x4 *)(kq + 32 * kk + 8 * grp);
-        vnew = *(const u32x4 *)(vq + 8 * col);
-    }
-    const int T = nsub > w ? (nsub - w + WAVES - 1) / WAVES : 0;
-    if (T > 0) {
-        // Single register buffer per operand, pipelined: the next sub-tile's K
-        // loads are issued once the scores are done, its V loads once the current
-        // V rows are staged in LDS, so they overlap softmax and P.V.
-        int tb = t0 + w * kSub;
-        const int step = WAVES * kSub;
-        KOp K;
-        VRows V;
-        {
-            const SubRsrc r = sub_rsrc<BS>(sub_phys<BS>(trow, a.width, tb), kp, vp, tb, t_load,
-                                           head_off, blk_elems);
-            load_k(K, r.k, lane);
-            load_v(V, r.v, lane);
-        }
+        for (int jj = 0; jj < 8; ++jj)
+            st.acc[jj] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+        const int nsub = (t1 - t0 + kSub - 1) / kSub;
+        // the wave holding position n-1 (the item's last sub-tile) fetches the new
+        // rows and their block id up front, so that the latency overlaps its loop:
+        // knew[kk] is the A-operand chunk of the new key (dims 8*(4kk + lane/16)..),
+        // vnew the 16-byte chunk lane%16 of the new value row
+        const bool new_here = owns_new && nsub > 0 && w == (nsub - 1) % WAVES;
+        u32x4 knew[4] = {}, vnew = {0u, 0u, 0u, 0u};
+        const int64_t phys_n = new_here ? (int64_t)trow[(n - 1) / BS] : 0;  // block of n-1
         if (new_here) {
-            // write the new rows to their slot now: stores share the in-order
-            // vmcnt counter with loads, so issuing them here lets their latency
-            // overlap the loop instead of the end of the work-group
-            const int tn = n - 1;
-            const int64_t dst = phys_n * blk_elems + head_off + (int64_t)(tn % BS) * kHeadDim;
-            if (col == (tn & 15)) {
-                // the four lanes of the new row's A-operand slot hold the whole key
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    *(u32x4 *)((uint16_t *)a.k_pool + dst + 32 * kk + 8 * grp) = knew[kk];
-            }
-            if (lane < 16)
-                *(u32x4 *)((uint16_t *)a.v_pool + dst + lane * 8) = vnew;
-            if (g == 0 && lane == 0 && a.slot_out)
-                a.slot_out[s] = phys_n * BS + tn % BS;
-        }
-        // table entries are looked up one sub-tile ahead of the loads that use them
-        int32_t pn = sub_phys<BS>(trow, a.width, tb + step);
-        u32x2 pb;
-        float alpha;
-        for (int j = 0; j + 1 < T; ++j) {  // every sub-tile here is full
-            const int32_t pn2 = sub_phys<BS>(trow, a.width, tb + 2 * step);
-            const SubRsrc rn = sub_rsrc<BS>(pn, kp, vp, tb + step, t_load, head_off, blk_elems);
-            qk_softmax<DT, false>(st, K, qop, tb, t1, lane, a.scale_log2, pb, alpha);
-            __builtin_amdgcn_sched_barrier(0);
-            load_k(K, rn.k, lane);
-            __builtin_amdgcn_sched_barrier(0);
-            stage_v(V, vlds, lane);
-            __builtin_amdgcn_sched_barrier(0);
-            load_v(V, rn.v, lane);
-            __builtin_amdgcn_sched_barrier(0);
-            pv_mma<DT>(st, vlds, pb, alpha, lane);
-            __builtin_amdgcn_sched_barrier(0);
-            pn = pn2;
-            tb += step;
-        }
-        // position n-1 in this sub-tile: put the new rows in place of the
-        // (unfetched) pool row
-        const bool here = new_here && tb + kSub >= n;
-        const int row = n - 1 - tb;  // 0..15 when `here`
-        if (here && (lane & 15) == row) {
-            // the four lanes of row `row` take the new key into the A operand
+            const int64_t off = ((int64_t)s * a.num_kv_heads + g) * kHeadDim;
+            const uint16_t *kq = (const uint16_t *)a.k_new + off;
+            const uint16_t *vq = (const uint16_t *)a.v_new + off;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                K.k[kk] = knew[kk];
+                knew[kk] = *(const u32x4 *)(kq + 32 * kk + 8 * grp);
+            vnew = *(const u32x4 *)(vq + 8 * col);
         }
-        if (tb + kSub <= t1)
-            qk_softmax<DT, false>(st, K, qop, tb, t1, lane, a.scale_log2, pb, alpha);
-        else
-            qk_softmax<DT, true>(st, K, qop, tb, t1, lane, a.scale_log2, pb, alpha);
-        stage_v(V, vlds, lane);
-        if (here && lane < 16)
-            *(u32x4 *)(vlds + row * kVStride + lane * 8) = vnew;
-        pv_mma<DT>(st, vlds, pb, alpha, lane);
-    }
-
-    // sum of the four lane groups' shares of l (m is already uniform across them)
-    st.l += xor_lane(st.l, 16);
-    st.l += xor_lane(st.l, 32);
-
-    __syncthreads();  // all waves are done with their V staging area
+        const int T = nsub > w ? (nsub - w + WAVES - 1) / WAVES : 0;
+        if (T > 0) {
+            // Single register buffer per operand, pipelined: the next sub-tile's K
+            // loads are issued once the scores are done, its V loads once the
+            // current V rows are staged in LDS, so they overlap softmax and P.V.
+            int tb = t0 + w * kSub;
+            const int step = WAVES * kSub;
+            const bool first = px == px0;
+            KOp K;
+            VRows V;
+            {
+                const int32_t ef = first ? e_first : sub_phys<BS>(trow, a.width, tb);
+                const SubRsrc r = sub_rsrc<BS>(ef, kp, vp, tb, t_load, head_off, blk_elems);
+                load_k(K, r.k, lane);
+                load_v(V, r.v, lane);
+            }
+            if (new_here) {
+                // write the new rows to their slot now: stores share the in-order
+                // vmcnt counter with loads, so issuing them here lets their latency
+                // overlap the loop instead of the end of the work-group
+                const int tn = n - 1;
+                const int64_t dst =
+                    phys_n * blk_elems + head_off + (int64_t)(tn % BS) * kHeadDim;
+                if (col == (tn & 15)) {
+                    // the four lanes of the new row's A-operand slot hold the key
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj)
+                    for (int kk = 0; kk < 4; ++kk)
+                        *(u32x4 *)((uint16_t *)a.k_pool + dst + 32 * kk + 8 * grp) = knew[kk];
+                }
+                if (lane < 16)
+                    *(u32x4 *)((uint16_t *)a.v_pool + dst + lane * 8) = vnew;
+                if (g == 0 && lane == 0 && a.slot_out)
+                    a.slot_out[s] = phys_n * BS + tn % BS;
+            }
+            // table entries are looked up one sub-tile ahead of the loads that use them
+            int32_t pn = first ? e_next : sub_phys<BS>(trow, a.width, tb + step);
+            u32x2 pb;
+            float alpha;
+            for (int j = 0; j + 1 < T; ++j) {  // every sub-tile here is full
+                const int32_t pn2 = sub_phys<BS>(trow, a.width, tb + 2 * step);
+                const SubRsrc rn =
+                    sub_rsrc<BS>(pn, kp, vp, tb + step, t_load, head_off, blk_elems);
+                qk_softmax<DT, false>(st, K, qop, tb, t1, lane, a.scale_log2, pb, alpha);
+                __builtin_amdgcn_sched_barrier(0);
+                load_k(K, rn.k, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                stage_v(V, vlds, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                load_v(V, rn.v, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                pv_mma<DT>(st, vlds, pb, alpha, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                pn = pn2;
+                tb += step;
+            }
+            // position n-1 in this sub-tile: put the new rows in place of the
+            // (unfetched) pool row
+            const bool here = new_here && tb + kSub >= n;
+            const int row = n - 1 - tb;  // 0..15 when `here`
+            if (here && (lane & 15) == row) {
+                // the four lanes of row `row` take the new key into the A operand
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            sm.o[w][col][16 * jj + 4 * grp + r] = st.acc[jj][r];
-    if (grp == 0) {
-        s_m[w][col] = st.m;
-        s_l[w][col] = st.l;
-    }
-    __syncthreads();
-
-    const int64_t row0 = (int64_t)s * a.num_q_heads + (int64_t)g * G;
-    for (int idx = tid; idx < G * kHeadDim; idx += WAVES * 64) {
-        const int qi = idx / kHeadDim, d = idx % kHeadDim;
-        float M = s_m[0][qi];
-#pragma unroll
-        for (int i = 1; i < WAVES; ++i)
-            M = fmaxf(M, s_m[i][qi]);
-        const float ref = safe_ref(M);
-        float L = 0.f, O = 0.f;
-#pragma unroll
-        for (int i = 0; i < WAVES; ++i) {
-            const float wgt = fexp2(s_m[i][qi] - ref);
-            L += s_l[i][qi] * wgt;
-            O += sm.o[i][qi][d] * wgt;
+                for (int kk = 0; kk < 4; ++kk)
+                    K.k[kk] = knew[kk];
+            }
+            if (tb + kSub <= t1)
+                qk_softmax<DT, false>(st, K, qop, tb, t1, lane, a.scale_log2, pb, alpha);
+            else
+                qk_softmax<DT, true>(st, K, qop, tb, t1, lane, a.scale_log2, pb, alpha);
+            stage_v(V, vlds, lane);
+            if (here && lane < 16)
+                *(u32x4 *)(vlds + row * kVStride + lane * 8) = vnew;
+            pv_mma<DT>(st, vlds, pb, alpha, lane);
         }
-        const int64_t row = row0 + qi;
-        if (a.partition_size == 0) {
-            const float o = L > 0.f ? O / L : 0.f;
-            ((uint16_t *)a.out)[row * kHeadDim + d] = to_bits<DT>(o);
-        } else {
-            a.part_o[(row * a.max_partitions + px) * kHeadDim + d] = O / L;
-            if (d == 0)
-                a.part_lse[row * a.max_partitions + px] = (ref + flog2(L)) * kLn2;
+
+        // sum of the four lane groups' shares of l (m is already uniform across them)
+        st.l += xor_lane(st.l, 16);
+        st.l += xor_lane(st.l, 32);
+
+        __syncthreads();  // all waves are done with their V staging area
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sm.o[w][col][16 * jj + 4 * grp + r] = st.acc[jj][r];
+        if (grp == 0) {
+            s_m[w][col] = st.m;
+            s_l[w][col] = st.l;
+        }
+        __syncthreads();
+
+        for (int idx = tid; idx < G * kHeadDim; idx += WAVES * 64) {
+            const int qi = idx / kHeadDim, d = idx % kHeadDim;
+            float M = s_m[0][qi];
+#pragma unroll
+            for (int i = 1; i < WAVES; ++i)
+                M = fmaxf(M, s_m[i][qi]);
+            const float ref = safe_ref(M);
+            float L = 0.f, O = 0.f;
+#pragma unroll
+            for (int i = 0; i < WAVES; ++i) {
+                const float wgt = fexp2(s_m[i][qi] - ref);
+                L += s_l[i][qi] * wgt;
+                O += sm.o[i][qi][d] * wgt;
+            }
+            const int64_t row = row0 + qi;
+            if (P == 0) {
+                const float o = L > 0.f ? O / L : 0.f;
+                ((uint16_t *)a.out)[row * kHeadDim + d] = to_bits<DT>(o);
+            } else {
+                a.part_o[(row * a.max_partitions + px) * kHeadDim + d] = O / L;
+                if (d == 0)
+                    a.part_lse[row * a.max_partitions + px] = (ref + flog2(L)) * kLn2;
+            }
         }
     }
 }
@@ -410,8 +429,12 @@ template <int DT, int BS>
 static hipError_t launch_mfma_t(const DecodeArgs &a, hipStream_t stream)
 {
     constexpr int W = PKV_MFMA_WAVES;
-    hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, W>), dim3(a.n_items), dim3(W * 64), 0, stream,
-                       a);
+    if (a.partition_size > 0)
+        hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, W, true>), dim3(a.n_items), dim3(W * 64), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, W, false>), dim3(a.n_items), dim3(W * 64),
+                           0, stream, a);
     return hipGetLastError();
 }
 

@@ -4,7 +4,7 @@ Append and slot arithmetic: bit-exact.  Attention outputs (fp16/bf16) and
 partition outputs: |gpu - oracle| <= 1e-2 + 1e-2 |oracle| element by element.
 Every workload runs at its full per-layer size, in the launch configuration the
 benchmark times (single pass for the 7B and prefix workloads, split-context
-partitions of 256 tokens for the edge workload and 2048 for the long-context one),
+partitions of 512 tokens for the edge workload and 2048 for the long-context one),
 plus other partition sizes, ragged and empty sequences, every supported block
 size and several GQA group sizes.
 """
@@ -26,7 +26,7 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():  # pragma: no cover - CPU containers
     pytest.skip("no GPU", allow_module_level=True)
 
-BENCH_P = {"c1a": 0, "c1b": 0, "c2": 256, "c3": 0, "c4": 2048, "c5": 0}
+BENCH_P = {"c1a": 0, "c1b": 0, "c2": 512, "c3": 0, "c4": 2048, "c5": 0}
 ALL = ["c1a", "c1b", "c2", "c3", "c4", "c5"]
 
 _cache = {}
@@ -83,7 +83,7 @@ def test_decode_single_pass(key):
     assert ok, f"{key}: max err {err}, {nbad} elements out of tolerance"
 
 
-PARTS = [("c1a", 32), ("c1b", 64), ("c2", 256), ("c2", 512), ("c3", 64), ("c3", 128),
+PARTS = [("c1a", 32), ("c1b", 64), ("c2", 256), ("c2", 512), ("c3", 64), ("c3", 128), ("c3", 4096),
          ("c4", 1024), ("c4", 2048), ("c5", 128), ("c5", 256)]
 
 
@@ -108,7 +108,7 @@ def test_decode_partitioned(key, P):
 
 
 # ---------------------------------------------------------------------------
-FUSED = [(k, 0) for k in ALL] + [("c1b", 32), ("c2", 256), ("c3", 64), ("c4", 2048),
+FUSED = [(k, 0) for k in ALL] + [("c1b", 32), ("c2", 512), ("c3", 64), ("c4", 2048),
                                  ("c5", 128)]
 
 

@@ -93,7 +93,7 @@ CONFIGS = {
         num_seqs=32, num_layers=24, num_q_heads=12, num_kv_heads=2, head_dim=128,
         block_size=16, dtype="fp16", max_blocks_per_seq=128, value_scale=1.0,
         length_kind="uniform", uniform_lo=16, uniform_hi=2048, pool_blocks=4096,
-        bench_distinct_layers=24, bench_partition_size=256,
+        bench_distinct_layers=24, bench_partition_size=512,
     ),
     "c3": Config(
         key="c3", cfg_id=3, title="Llama-2-7B attention shape, 32 layers, MHA",
