@@ -76,6 +76,8 @@ def lib():
         L.oracle_append.restype = C.c_int
         L.oracle_append_tokens.argtypes = [P, P, P, P, P, P, P] + [i64] * 6
         L.oracle_append_tokens.restype = C.c_int
+        L.oracle_copy_blocks.argtypes = [P, P, P, P] + [i64] * 5
+        L.oracle_copy_blocks.restype = C.c_int
         L.oracle_attention.argtypes = [P, P, P, P, P, P] + [i64] * 7 + [C.c_double, C.c_int,
                                                                           C.c_int]
         L.oracle_attention.restype = C.c_int
@@ -154,6 +156,18 @@ def append_tokens(k_pool, v_pool, k_src, v_src, cu, start_pos, seg_tables, block
                                     seg_tables.shape[0], Hkv, D, block_size,
                                     seg_tables.shape[1], num_blocks)
     _check(rc, "append_tokens")
+
+
+def copy_blocks(k_pool, v_pool, src, dst):
+    """Copy-on-write duplication: block dst[i] of both pools becomes a copy of
+    block src[i] (pools [NB][Hkv][B][D] uint16, modified in place)."""
+    assert k_pool.flags.c_contiguous and v_pool.flags.c_contiguous
+    NB, Hkv, B, D = k_pool.shape
+    src, dst = _c(src, np.int32), _c(dst, np.int32)
+    assert src.shape == dst.shape
+    rc = lib().oracle_copy_blocks(_p(k_pool), _p(v_pool), _p(src), _p(dst), src.shape[0], Hkv,
+                                  D, B, NB)
+    _check(rc, "copy_blocks")
 
 
 def attention(q, k_pool, v_pool, tables, lens, num_kv_heads, block_size, num_blocks, scale,

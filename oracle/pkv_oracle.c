@@ -31,6 +31,12 @@
  *    logical order (blog.llmgo.top page, §二.1 "逻辑块" and §五 intro); this oracle
  *    evaluates softmax(scale * q.K^T) V in fp64 token by token through the walk,
  *    with a two-pass softmax (max, then sum of exp).
+ *  - Block copy (copy-on-write): before a branch appends to a partly filled
+ *    block that another branch still references, the whole block is duplicated
+ *    into a fresh physical block and only the appending branch's table entry is
+ *    pointed at the copy (blog.llmgo.top page, §四, steps 1-3 of the
+ *    copy-on-write mechanism).  Every element of every head of the block is
+ *    copied, in K and in V.
  *  - Partials and merge: attention over the token range of one partition, its
  *    log-sum-exp, and the exact log-sum-exp combination of partitions.  The
  *    pages do not describe partitions; the merge is the algebraic identity
@@ -210,6 +216,40 @@ int oracle_append_tokens(uint16_t *k_pool, uint16_t *v_pool, const uint16_t *k_s
     }
     free(map);
     return rc;
+}
+
+/* ---- block copy (copy-on-write) ------------------------------------------ */
+/* For each pair i, block dst[i] of both pools becomes a copy of block src[i] as
+ * it was before the call.  A destination that is also a source, or that appears
+ * twice, would make the result depend on the copy order: OR_EDUP. */
+int oracle_copy_blocks(uint16_t *k_pool, uint16_t *v_pool, const int32_t *src,
+                       const int32_t *dst, int64_t num_pairs, int64_t num_kv_heads,
+                       int64_t head_dim, int64_t block_size, int64_t num_blocks)
+{
+    int rc = check_dims(num_kv_heads, head_dim, block_size, 1, num_blocks);
+    if (rc)
+        return rc;
+    if (num_pairs < 0)
+        return OR_EARG;
+    for (int64_t i = 0; i < num_pairs; ++i)
+        if (src[i] < 0 || src[i] >= num_blocks || dst[i] < 0 || dst[i] >= num_blocks)
+            return OR_ETABLE;
+    for (int64_t i = 0; i < num_pairs; ++i)
+        for (int64_t j = 0; j < num_pairs; ++j)
+            if (dst[i] == src[j] || (j != i && dst[i] == dst[j]))
+                return OR_EDUP;
+    for (int64_t i = 0; i < num_pairs; ++i)
+        for (int64_t h = 0; h < num_kv_heads; ++h)
+            for (int64_t off = 0; off < block_size; ++off)
+                for (int64_t d = 0; d < head_dim; ++d) {
+                    int64_t from = oracle_elem_offset(src[i], h, off, d, num_kv_heads, block_size,
+                                                      head_dim);
+                    int64_t to = oracle_elem_offset(dst[i], h, off, d, num_kv_heads, block_size,
+                                                    head_dim);
+                    k_pool[to] = k_pool[from];
+                    v_pool[to] = v_pool[from];
+                }
+    return OR_OK;
 }
 
 /* ---- attention over tokens [t0, t1) of one (sequence, query head) --------- */

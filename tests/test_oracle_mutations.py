@@ -31,6 +31,10 @@ MUTANTS = {
     "missing_normalisation": ("        o[d] /= l;\n", "        o[d] /= 1.0;\n"),
     "last_token_skipped": ("for (int64_t t = t0; t < t1; ++t) {\n        int64_t phys, off;\n        int rc",
                            "for (int64_t t = t0; t < t1 - 1; ++t) {\n        int64_t phys, off;\n        int rc"),
+    "copy_direction_swapped": ("k_pool[to] = k_pool[from];", "k_pool[from] = k_pool[to];"),
+    "copy_skips_values": ("v_pool[to] = v_pool[from];", ""),
+    "copy_last_row_dropped": ("for (int64_t off = 0; off < block_size; ++off)",
+                              "for (int64_t off = 0; off < block_size - 1; ++off)"),
 }
 
 
@@ -46,7 +50,8 @@ def _build(tmp_path, text, name):
 def _run_pins(lib_path):
     env = dict(os.environ, PKV_ORACLE_LIB=lib_path, OMP_NUM_THREADS="2")
     cmd = [sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-           os.path.join(ROOT, "tests", "test_oracle_pins.py")]
+           os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+           os.path.join(ROOT, "tests", "test_oracle_cow.py")]
     return subprocess.run(cmd, env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
 
 
