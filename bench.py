@@ -17,6 +17,11 @@ Prints ONE JSON line.  `value` is decode tokens/s over the whole step (sequences
 step time); the line also carries the algorithmic HBM rate of the step, the
 roofline of the dominant kernel (decode attention) timed per launch with HIP
 events, and the fp64 CPU oracle timed on a bounded sample on the host cores.
+
+`--op append_tokens` and `--op copy_blocks` instead time the block-level writers
+on the same workload shapes (the prefill scatter of every layer, and a
+copy-on-write fork of every sequence in every layer) and print one line each,
+with GB/s as the value.
 """
 from __future__ import annotations
 
@@ -54,6 +59,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c3", help="workload key (c1a c1b c2 c3 c4 c5)")
+    ap.add_argument("--op", default="step", choices=["step", "append_tokens", "copy_blocks"],
+                    help="step: the decode step (default, the headline line); append_tokens: "
+                         "the prefill scatter of the workload's histories into every layer; "
+                         "copy_blocks: copy-on-write copies of the workload's forks")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="override the workload's split-context partition size (0 = single pass)")
     ap.add_argument("--distinct", type=int, default=None, help="override distinct layer pools")
@@ -70,33 +79,60 @@ def parse():
     return ap.parse_args()
 
 
-# Source files whose contents determine the decode kernels' memory traffic.
-TRAFFIC_SOURCES = ["paged_kv_cache_09_amd/csrc/decode_g1.hip",
-                   "paged_kv_cache_09_amd/csrc/decode_mfma.hip",
-                   "paged_kv_cache_09_amd/csrc/pkv_device.h"]
+# Source files whose contents determine each kernel's memory traffic.
+TRAFFIC_SOURCES = {
+    "decode": ["paged_kv_cache_09_amd/csrc/decode_g1.hip",
+               "paged_kv_cache_09_amd/csrc/decode_mfma.hip",
+               "paged_kv_cache_09_amd/csrc/pkv_device.h"],
+    "append_tokens": ["paged_kv_cache_09_amd/csrc/append.hip"],
+    "copy_blocks": ["paged_kv_cache_09_amd/csrc/copy.hip",
+                    "paged_kv_cache_09_amd/csrc/pkv_device.h"],
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kind: str = "decode") -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES:
+    for f in TRAFFIC_SOURCES[kind]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per decode launch from the committed counter record of this
+def measured_traffic(workload: str, kind: str = "decode"):
+    """HBM bytes per launch from the committed counter record of this kernel and
     workload (profiles/<kernel>_<workload>_traffic.json), or None when there is
     none or the kernel sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{kind}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(kind):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def time_launches(fn, reps: int, warm: int = 2) -> float:
+    """Average duration in ms of fn()'s launches, queued back to back between two
+    events on torch's current stream (the stream the binding launches on)."""
+    import torch
+    for _ in range(warm):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def roofline(kernel: str, nbytes: int, ms: float, traffic):
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": kernel, "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+            "bytes_per_launch": int(nbytes), "avg_launch_ms": round(ms, 5)}
 
 
 def copy_reference():
@@ -128,7 +164,15 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.op == "append_tokens":
+        bench_append_tokens(args)
+    elif args.op == "copy_blocks":
+        bench_copy_blocks(args)
+    else:
+        bench_step(args)
 
+
+def bench_step(args):
     import torch
     import paged_kv_cache_09_amd as pkv
     from workloads import get_config, make_workload
@@ -279,7 +323,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(cfg.key),
+            "traffic": measured_traffic(cfg.key, "decode"),
             "bytes_per_launch": kernel_bytes,
             "avg_launch_ms": round(decode_ms, 5),
         },
@@ -290,6 +334,142 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w0, cfg, scale, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
+
+
+def _side_line(metric, value, unit, args, cfg, dtype, config, roof, extra=None):
+    line = {"metric": metric, "value": round(value, 1), "unit": unit, "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(roof["avg_launch_ms"] *
+                                                                              config["launches"], 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+            "data": "synthetic (seeded)", "config": config, "roofline": roof}
+    line.update(extra or {})
+    return line
+
+
+def bench_append_tokens(args):
+    """Prefill scatter: every layer's K/V of the workload's histories (one run per
+    sequence, positions 0..n-2) written into that layer's pools, one
+    paged_kv_append_tokens launch per layer.  value = algorithmic GB/s."""
+    import torch
+    import paged_kv_cache_09_amd as pkv
+    from workloads import get_config, make_workload
+
+    cfg = get_config(args.config)
+    R = min(cfg.num_layers, args.distinct or cfg.bench_distinct_layers)
+    dev = torch.device("cuda:0")
+    tdt = {"fp16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(tdt)
+
+    w = make_workload(cfg, layer=0)
+    T = int(w.total_history_tokens())
+    layers = []
+    for d in range(R):
+        wd = w if d == 0 else make_workload(cfg, layer=d)
+        kp = torch.zeros(wd.pool_shape(), dtype=tdt, device=dev)
+        layers.append(dict(k=kp, v=torch.zeros_like(kp), ks=up(wd.k_src), vs=up(wd.v_src)))
+    cu = torch.from_numpy(w.seg_cu).to(dev)
+    st = torch.from_numpy(w.seg_start).to(dev)
+    tb = torch.from_numpy(w.seg_tables).to(dev)
+    torch.cuda.synchronize()
+
+    def one(li):
+        L = layers[li % R]
+        pkv.paged_kv_append_tokens(L["k"], L["v"], L["ks"], L["vs"], cu, st, tb)
+
+    it = iter(range(1 << 30))
+    ms = time_launches(lambda: one(next(it)), args.steps * cfg.num_layers,
+                       warm=args.warmup * cfg.num_layers)
+    e = cfg.elem_bytes
+    rows = 2 * T * cfg.num_kv_heads * cfg.head_dim * e           # K and V rows
+    nblk = int(sum(-(-(int(s) + int(n)) // cfg.block_size) - int(s) // cfg.block_size
+                   for s, n in zip(w.seg_start, np.diff(w.seg_cu))))
+    meta = 8 * (len(w.seg_cu)) + 4 * len(w.seg_start) + 4 * nblk
+    nbytes = 2 * rows + meta                                      # read + write
+    roof = roofline("paged_kv_append_tokens", nbytes, ms,
+                    measured_traffic(cfg.key, "append_tokens"))
+    config = {"workload": f"{cfg.key} prefill scatter: {cfg.title}", "runs": int(len(w.seg_start)),
+              "tokens_per_layer": T, "layers": cfg.num_layers, "kv_heads": cfg.num_kv_heads,
+              "head_dim": cfg.head_dim, "block_size": cfg.block_size, "distinct_layer_pools": R,
+              "launches": cfg.num_layers}
+    line = _side_line("prefill KV scatter (paged_kv_append_tokens) GB/s, 1 GPU", roof["achieved"],
+                      "GB/s", args, cfg, cfg.dtype, config, roof,
+                      {"tokens_per_s": round(T / (ms * 1e-3) / cfg.num_layers, 1)})
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        kp, vp = O.new_pools(w.num_blocks, cfg.num_kv_heads, cfg.block_size, cfg.head_dim, 0)
+        reps, spent = 0, 0.0
+        while reps == 0 or (spent < args.cpu_seconds and reps < 20):
+            t = time.perf_counter()
+            O.append_tokens(kp, vp, w.k_src, w.v_src, w.seg_cu, w.seg_start, w.seg_tables,
+                            cfg.block_size, w.num_blocks)
+            spent += time.perf_counter() - t
+            reps += 1
+        line["cpu_baseline"] = {"value": round(nbytes * reps / spent / 1e9, 3), "unit": "GB/s",
+                                "cores": 1, "kind": "oracle",
+                                "sample": f"one layer's scatter ({T} tokens), {reps} repetitions, "
+                                          f"{spent:.1f} s, single-threaded C"}
+    print(json.dumps(line), flush=True)
+
+
+def bench_copy_blocks(args):
+    """Copy-on-write: every sequence of the workload forks once, so its partly
+    filled last block is copied to a fresh block in every layer (one
+    paged_kv_copy_blocks launch covering all layers).  value = algorithmic GB/s."""
+    import torch
+    import paged_kv_cache_09_amd as pkv
+    from workloads import get_config
+
+    cfg = get_config(args.config)
+    dev = torch.device("cuda:0")
+    tdt = {"fp16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
+    S, L = cfg.num_seqs, cfg.num_layers
+    NB = 2 * S                          # the forked blocks and their copies, per layer
+    shape = (NB, cfg.num_kv_heads, cfg.block_size, cfg.head_dim)
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    kps, vps = [], []
+    for _ in range(L):
+        for lst in (kps, vps):
+            lst.append(torch.randint(-32768, 32767, shape, dtype=torch.int16, device=dev,
+                                     generator=g).view(tdt))
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(NB).astype(np.int32)
+    src = torch.from_numpy(perm[:S].copy()).to(dev)
+    dst = torch.from_numpy(perm[S:].copy()).to(dev)
+    torch.cuda.synchronize()
+
+    def one():
+        pkv.paged_kv_copy_blocks(kps, vps, src, dst)
+
+    ms = time_launches(one, args.steps, warm=args.warmup)
+    slab = cfg.num_kv_heads * cfg.block_size * cfg.head_dim * cfg.elem_bytes
+    nbytes = 2 * (S * L * 2 * slab) + 8 * S                        # read + write, pair ids
+    roof = roofline("paged_kv_copy_blocks", nbytes, ms, measured_traffic(cfg.key, "copy_blocks"))
+    config = {"workload": f"{cfg.key} fork: every sequence copies one block in all layers "
+                          f"({cfg.title})", "pairs": S, "layers": L,
+              "block_bytes_per_pool": slab, "pool_blocks_per_layer": NB, "launches": 1}
+    line = _side_line("copy-on-write block copy (paged_kv_copy_blocks) GB/s, 1 GPU",
+                      roof["achieved"], "GB/s", args, cfg, cfg.dtype, config, roof)
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        Ls = min(L, 4)
+        host = [np.random.default_rng(i).integers(0, 1 << 16, size=shape, dtype=np.uint16)
+                for i in range(2 * Ls)]
+        reps, spent = 0, 0.0
+        while reps == 0 or (spent < args.cpu_seconds and reps < 20):
+            t = time.perf_counter()
+            for i in range(Ls):
+                O.copy_blocks(host[2 * i], host[2 * i + 1], perm[:S], perm[S:])
+            spent += time.perf_counter() - t
+            reps += 1
+        sample_bytes = 2 * (S * Ls * 2 * slab)
+        line["cpu_baseline"] = {"value": round(sample_bytes * reps / spent / 1e9, 3),
+                                "unit": "GB/s", "cores": 1, "kind": "oracle",
+                                "sample": f"{S} pairs x {Ls} of {L} layers, {reps} repetitions, "
+                                          f"{spent:.1f} s, single-threaded C"}
+    print(json.dumps(line), flush=True)
 
 
 def cpu_baseline(w, cfg, scale, budget_s):

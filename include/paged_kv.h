@@ -109,6 +109,32 @@ int paged_kv_append_tokens(void *k_pool, void *v_pool, const void *k_src, const 
                            int max_blocks_per_seq, int64_t num_blocks, int dtype, void *stream);
 
 /*
+ * paged_kv_copy_blocks -- copy-on-write duplication of whole blocks.
+ *
+ * For each pair i, physical block dst_blocks[i] of every layer's K pool and V
+ * pool becomes a bit copy of block src_blocks[i] as it was before the call.  This
+ * is the deep copy the block manager orders when a branch is about to append to
+ * a partly filled block that another branch still references: the copy goes to a
+ * fresh block, the appending branch's table entry is then pointed at it, and the
+ * append writes into the copy (blog.llmgo.top page, §四, copy-on-write steps
+ * 1-3).  A block id names the same block in every layer, hence the layer list.
+ * The library changes no table and keeps no reference counts: the caller does.
+ *
+ *   k_pools, v_pools  HOST arrays of num_layers DEVICE pointers, each a pool
+ *                     [num_blocks][num_kv_heads][block_size][head_dim] (16-byte
+ *                     aligned); 1 <= num_layers <= 128, else PKV_EINVAL / ENOTSUP
+ *   src_blocks, dst_blocks  DEVICE int32 [num_pairs]
+ * Caller contract (checked only with PKV_DEBUG_CHECK=1, else undefined): every
+ * id in [0, num_blocks); no destination appears twice or as any pair's source (a
+ * source may be copied to several destinations, e.g. one prompt forked into
+ * several samples).  num_pairs == 0 does nothing.
+ */
+int paged_kv_copy_blocks(void *const *k_pools, void *const *v_pools, int num_layers,
+                         const int32_t *src_blocks, const int32_t *dst_blocks, int num_pairs,
+                         int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                         int dtype, void *stream);
+
+/*
  * paged_attention_decode -- decode attention over the paged pools.
  *
  * For every sequence s and query head h (KV head g = h / (num_q_heads /

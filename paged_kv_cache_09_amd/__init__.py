@@ -19,5 +19,6 @@ from ._lib import (  # noqa: F401
     paged_attention_reduce,
     paged_kv_append,
     paged_kv_append_tokens,
+    paged_kv_copy_blocks,
     status_string,
 )

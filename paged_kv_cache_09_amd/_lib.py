@@ -51,6 +51,8 @@ def load():
     L.paged_kv_append_tokens.argtypes = [P, P, P, P, P, P, P, i32, i64, i32, i32, i32, i32, i64,
                                          i32, P]
     L.paged_kv_append_tokens.restype = i32
+    L.paged_kv_copy_blocks.argtypes = [P, P, i32, P, P, i32, i32, i32, i32, i64, i32, P]
+    L.paged_kv_copy_blocks.restype = i32
     L.paged_attention_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i64, f32,
                                          i32, i32, P, P, i32, P]
     L.paged_attention_decode.restype = i32
@@ -166,6 +168,31 @@ def paged_kv_append_tokens(k_pool, v_pool, k_src, v_src, src_cu, start_pos, bloc
                                        k_src.shape[0], Hkv, D, B, block_tables.shape[1], NB,
                                        _dtype_code(k_pool), _stream(dev))
     _check(rc, "paged_kv_append_tokens")
+
+
+def paged_kv_copy_blocks(k_pools, v_pools, src_blocks, dst_blocks):
+    """Copy-on-write: block dst_blocks[i] of every pool in k_pools / v_pools (one
+    K and one V pool per layer) becomes a copy of block src_blocks[i]."""
+    k_pools, v_pools = list(k_pools), list(v_pools)
+    if len(k_pools) != len(v_pools) or not k_pools:
+        raise ValueError("k_pools and v_pools must be non-empty lists of equal length")
+    dev = _dev(*k_pools, *v_pools, src_blocks, dst_blocks)
+    _int(src_blocks, "i32", "src_blocks")
+    _int(dst_blocks, "i32", "dst_blocks")
+    if src_blocks.shape != dst_blocks.shape or src_blocks.dim() != 1:
+        raise ValueError("src_blocks and dst_blocks must be 1-D and of equal length")
+    shape, dtype = k_pools[0].shape, k_pools[0].dtype
+    for t in k_pools + v_pools:
+        if t.shape != shape or t.dtype != dtype:
+            raise ValueError("every pool must have the same shape and dtype")
+    NB, Hkv, B, D = shape
+    L = len(k_pools)
+    kp = (C.c_void_p * L)(*[t.data_ptr() for t in k_pools])
+    vp = (C.c_void_p * L)(*[t.data_ptr() for t in v_pools])
+    rc = load().paged_kv_copy_blocks(kp, vp, L, _p(src_blocks), _p(dst_blocks),
+                                     src_blocks.shape[0], Hkv, D, B, NB, _dtype_code(k_pools[0]),
+                                     _stream(dev))
+    _check(rc, "paged_kv_copy_blocks")
 
 
 def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens,

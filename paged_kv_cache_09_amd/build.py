@@ -20,7 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
-SOURCES = ["api.hip", "append.hip", "decode_g1.hip", "decode_mfma.hip", "reduce.hip"]
+SOURCES = ["api.hip", "append.hip", "copy.hip", "decode_g1.hip", "decode_mfma.hip",
+           "reduce.hip"]
 ARCH = "gfx950"
 
 COMMON = [

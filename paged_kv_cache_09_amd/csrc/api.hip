@@ -69,6 +69,24 @@ __global__ void debug_runs_kernel(const int64_t *cu, const int32_t *start_pos,
     }
 }
 
+// Copy pairs: ids inside the pool; a destination may be neither another pair's
+// destination nor any pair's source (the result would depend on copy order).
+__global__ void debug_copies_kernel(const int32_t *src, const int32_t *dst, int num_pairs,
+                                    int64_t num_blocks)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= num_pairs)
+        return;
+    const int32_t d = dst[i], s = src[i];
+    if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks) {
+        atomicOr(&g_debug_flag, 2);
+        return;
+    }
+    for (int j = 0; j < num_pairs; ++j)
+        if (src[j] == d || (j != i && dst[j] == d))
+            atomicOr(&g_debug_flag, 16);
+}
+
 int read_debug_flag(hipStream_t stream)
 {
     int flag = 0;
@@ -101,6 +119,17 @@ int debug_check_runs(const int64_t *cu, const int32_t *start_pos, const int32_t 
     hipLaunchKernelGGL(debug_runs_kernel, dim3((num_runs + 1 + 255) / 256), dim3(256), 0, stream,
                        cu, start_pos, tables, num_runs, total_tokens, width, block_size,
                        num_blocks);
+    if (hipGetLastError() != hipSuccess)
+        return PKV_ELAUNCH;
+    return read_debug_flag(stream);
+}
+
+int debug_check_copies(const int32_t *src, const int32_t *dst, int num_pairs,
+                       int64_t num_blocks, hipStream_t stream)
+{
+    hipLaunchKernelGGL(debug_clear_kernel, dim3(1), dim3(1), 0, stream);
+    hipLaunchKernelGGL(debug_copies_kernel, dim3((num_pairs + 255) / 256), dim3(256), 0, stream,
+                       src, dst, num_pairs, num_blocks);
     if (hipGetLastError() != hipSuccess)
         return PKV_ELAUNCH;
     return read_debug_flag(stream);
@@ -158,7 +187,8 @@ const char *pkv_status_string(int status)
     case PKV_ELAUNCH:
         return "kernel launch failed";
     case PKV_EDEVICE:
-        return "device-side check failed (context length or block-table entry out of range)";
+        return "device-side check failed (context length, block-table entry or copy pair "
+               "out of range, or overlapping copy pairs)";
     default:
         return "unknown status";
     }
@@ -223,7 +253,8 @@ int paged_kv_append_tokens(void *k_pool, void *v_pool, const void *k_src, const 
         return rc;
     if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_src) || !aligned16(v_src))
         return PKV_EINVAL;
-    if (total_tokens * num_kv_heads * 2 * (pkv::kHeadDim / 8) > ((int64_t)1 << 31) * 255)
+    // one work-group per few rows; the grid must stay below 2^32 threads
+    if (pkv::append_tokens_groups(total_tokens, num_kv_heads, nullptr) >= ((int64_t)1 << 24))
         return PKV_EINVAL;
     if (num_runs == 0 || total_tokens == 0)
         return PKV_OK;
@@ -238,6 +269,36 @@ int paged_kv_append_tokens(void *k_pool, void *v_pool, const void *k_src, const 
                                                    start_pos, block_tables, num_runs,
                                                    total_tokens, num_kv_heads, block_size,
                                                    max_blocks_per_seq, st));
+}
+
+int paged_kv_copy_blocks(void *const *k_pools, void *const *v_pools, int num_layers,
+                         const int32_t *src_blocks, const int32_t *dst_blocks, int num_pairs,
+                         int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                         int dtype, void *stream)
+{
+    if (!k_pools || !v_pools || num_layers <= 0 || num_pairs < 0)
+        return PKV_EINVAL;
+    if (num_layers > pkv::kMaxCopyLayers)
+        return PKV_ENOTSUP;
+    int rc = check_pool_shape(num_kv_heads, head_dim, block_size, 1, num_blocks, dtype);
+    if (rc)
+        return rc;
+    for (int l = 0; l < num_layers; ++l)
+        if (!k_pools[l] || !v_pools[l] || !aligned16(k_pools[l]) || !aligned16(v_pools[l]))
+            return PKV_EINVAL;
+    if (num_pairs == 0)
+        return PKV_OK;
+    if (!src_blocks || !dst_blocks || ((uintptr_t)src_blocks & 3u) || ((uintptr_t)dst_blocks & 3u))
+        return PKV_EINVAL;
+    hipStream_t st = (hipStream_t)stream;
+    if (debug_enabled()) {
+        rc = pkv::debug_check_copies(src_blocks, dst_blocks, num_pairs, num_blocks, st);
+        if (rc)
+            return rc;
+    }
+    const int64_t slab = (int64_t)num_kv_heads * block_size * head_dim;
+    return launch_status(pkv::launch_copy_blocks(k_pools, v_pools, num_layers, src_blocks,
+                                                 dst_blocks, num_pairs, slab, st));
 }
 
 }  // extern "C"

@@ -1,0 +1,78 @@
+// copy.hip -- copy-on-write block duplication.
+//
+// When a branch is about to append to a partly filled block that another branch
+// still references, the block manager gives the branch a fresh physical block
+// holding a deep copy of the shared one and repoints that branch's table entry
+// (page "显存虚拟化革命：PagedAttention 内存池管理与显存碎片终结", blog.llmgo.top,
+// §四, copy-on-write steps 1-3).  A block id names the same block in every layer,
+// so the copy runs over every layer's K and V pools.
+//
+// gfx950 design: in the [NB][Hkv][B][D] layout one block of one pool is a single
+// contiguous slab of Hkv*B*D elements, so a copy is a set of slab-to-slab moves
+// with no address walk.  Each work-group moves 16 KiB of one slab (256 lanes x
+// four 16-byte loads in flight, then four 16-byte stores), the grid spans
+// (slab chunk, pair, layer x {K, V}); pair ids are read with scalar loads.
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;
+constexpr int kCopyVecPerGroup = kCopyThreads * kCopyUnroll;  // 16-byte vectors per group
+
+struct CopyArgs {
+    const int32_t *src;
+    const int32_t *dst;
+    int64_t slab_vec;  // 16-byte vectors per block slab
+    int num_pairs;
+    u32x4 *pools[2 * kMaxCopyLayers];  // layer l: K at 2l, V at 2l+1
+};
+
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyArgs a)
+{
+    u32x4 *pool = a.pools[blockIdx.z];
+    const int64_t v0 = (int64_t)blockIdx.x * kCopyVecPerGroup + threadIdx.x;
+    for (int p = blockIdx.y; p < a.num_pairs; p += gridDim.y) {
+        const u32x4 *from = pool + (int64_t)a.src[p] * a.slab_vec;
+        u32x4 *to = pool + (int64_t)a.dst[p] * a.slab_vec;
+        u32x4 r[kCopyUnroll];
+#pragma unroll
+        for (int j = 0; j < kCopyUnroll; ++j) {
+            const int64_t v = v0 + j * kCopyThreads;
+            if (v < a.slab_vec)
+                r[j] = ldnt(from + v);
+        }
+#pragma unroll
+        for (int j = 0; j < kCopyUnroll; ++j) {
+            const int64_t v = v0 + j * kCopyThreads;
+            if (v < a.slab_vec)
+                to[v] = r[j];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_copy_blocks(void *const *k_pools, void *const *v_pools, int num_layers,
+                              const int32_t *src, const int32_t *dst, int num_pairs,
+                              int64_t slab_elems, hipStream_t stream)
+{
+    CopyArgs a{};
+    a.src = src;
+    a.dst = dst;
+    a.slab_vec = slab_elems / 8;
+    a.num_pairs = num_pairs;
+    for (int l = 0; l < num_layers; ++l) {
+        a.pools[2 * l] = (u32x4 *)k_pools[l];
+        a.pools[2 * l + 1] = (u32x4 *)v_pools[l];
+    }
+    const int64_t gx = (a.slab_vec + kCopyVecPerGroup - 1) / kCopyVecPerGroup;
+    const int gy = num_pairs < 65535 ? num_pairs : 65535;
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)gx, (unsigned)gy, 2u * num_layers),
+                       dim3(kCopyThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace pkv

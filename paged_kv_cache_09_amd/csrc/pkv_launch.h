@@ -9,6 +9,10 @@ namespace pkv {
 
 struct DecodeArgs;
 
+// Most layers one paged_kv_copy_blocks call takes (their pool pointers travel as
+// kernel arguments: 2 KiB of pointers).
+constexpr int kMaxCopyLayers = 128;
+
 hipError_t launch_decode_g1(const DecodeArgs &a, int dtype, int block_size, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs &a, int dtype, int block_size,
                               hipStream_t stream);
@@ -23,6 +27,12 @@ hipError_t launch_append_tokens(void *k_pool, void *v_pool, const void *k_src,
                                 const void *v_src, const int64_t *cu, const int32_t *start_pos,
                                 const int32_t *tables, int num_runs, int64_t total_tokens,
                                 int num_kv_heads, int block_size, int width, hipStream_t stream);
+// Work-groups launch_append_tokens uses for total_tokens rows (and the rows per
+// group it picks).
+int64_t append_tokens_groups(int64_t total_tokens, int num_kv_heads, int *rows_per_group);
+hipError_t launch_copy_blocks(void *const *k_pools, void *const *v_pools, int num_layers,
+                              const int32_t *src, const int32_t *dst, int num_pairs,
+                              int64_t slab_elems, hipStream_t stream);
 
 // Debug check of the caller contract on device data (PKV_DEBUG_CHECK=1): returns
 // 0 when lens/tables are valid, a negative PKV status otherwise.  Synchronises.
@@ -31,5 +41,7 @@ int debug_check_tables(const int32_t *tables, const int32_t *lens, int num_seqs,
 int debug_check_runs(const int64_t *cu, const int32_t *start_pos, const int32_t *tables,
                      int num_runs, int64_t total_tokens, int width, int block_size,
                      int64_t num_blocks, hipStream_t stream);
+int debug_check_copies(const int32_t *src, const int32_t *dst, int num_pairs,
+                       int64_t num_blocks, hipStream_t stream);
 
 }  // namespace pkv

@@ -37,8 +37,9 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     declared = pkv.header_symbols()
-    assert {"paged_kv_append", "paged_kv_append_tokens", "paged_attention_decode",
-            "paged_attention_reduce", "pkv_status_string", "pkv_max_partitions"} <= set(declared)
+    assert {"paged_kv_append", "paged_kv_append_tokens", "paged_kv_copy_blocks",
+            "paged_attention_decode", "paged_attention_append_decode", "paged_attention_reduce",
+            "pkv_status_string", "pkv_max_partitions"} <= set(declared)
     assert pkv.exported_symbols() == declared
 
 
@@ -119,6 +120,29 @@ def test_append_tokens_argument_errors(lib):
     assert f(A, A, A, A, A, A, A, 2, -1, 2, 128, 16, 5, 64, 0, None) == EINVAL
     assert f(A, A, A, A, A, A, A, 2, 10, 2, 64, 16, 5, 64, 0, None) == ENOTSUP
     assert f(A, A, A, A, A, A, A, 0, 0, 2, 128, 16, 5, 64, 0, None) == 0
+
+
+@host_only
+def test_copy_blocks_argument_errors(lib):
+    f = lib.paged_kv_copy_blocks
+    two = (P * 2)(A, A)
+
+    def call(kp=two, vp=two, L=2, src=A, dst=A, n=3, Hkv=2, D=128, B=16, NB=64, dt=0):
+        return f(kp, vp, L, src, dst, n, Hkv, D, B, NB, dt, None)
+
+    assert call(kp=None) == EINVAL
+    assert call(L=0) == EINVAL
+    assert call(n=-1) == EINVAL
+    assert call(src=None) == EINVAL
+    assert call(dst=P((1 << 20) + 2)) == EINVAL                 # misaligned ids
+    assert call(kp=(P * 2)(A, None)) == EINVAL                  # a null pool
+    assert call(vp=(P * 2)(A, P((1 << 20) + 8))) == EINVAL     # a misaligned pool
+    assert call(D=64) == ENOTSUP
+    assert call(B=8) == ENOTSUP
+    assert call(dt=4) == ENOTSUP
+    many = (P * 129)(*([A] * 129))
+    assert call(kp=many, vp=many, L=129) == ENOTSUP            # more layers than one launch takes
+    assert call(n=0, src=None, dst=None) == 0                   # nothing to copy
 
 
 @host_only

@@ -1,0 +1,266 @@
+"""GPU parity of the block-level writers against the oracle, through the C ABI:
+paged_kv_append_tokens (runs of tokens: prompts, prefill chunks) and
+paged_kv_copy_blocks (copy-on-write).  Both are bit copies, so the bar is
+bit-exact pools."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - collected on CPU, skipped by marker
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import paged_kv_cache_09_amd as pkv  # noqa: E402
+from oracle import oracle as O  # noqa: E402
+from gpu_harness import bits_of, i32, i64, scale_for, tol_ok, to_dev, widen_out  # noqa: E402
+
+DEV = torch.device("cuda:0")
+SENTINEL = {"fp16": 0x7E00, "bf16": 0x7FC0}
+
+
+def _pool(NB, Hkv, B, dtype, rng=None):
+    shape = (NB, Hkv, B, 128)
+    if rng is None:
+        return np.full(shape, SENTINEL[dtype], np.uint16)
+    return rng.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# runs of tokens
+# ---------------------------------------------------------------------------
+def _runs_case(seed, num_runs, Hkv, B, max_len, start_mode, empty_frac=0.2):
+    """Ragged runs with empty ones mixed in; each run's table row is a slice of a
+    shuffled free list, so no two runs share a slot.  start_mode 'zero' writes
+    prompts from position 0, 'chunk' continues a prefix of random length."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1, max_len + 1, size=num_runs)
+    lens[rng.random(num_runs) < empty_frac] = 0
+    starts = (np.zeros(num_runs, np.int64) if start_mode == "zero"
+              else rng.integers(0, 3 * B, size=num_runs))
+    W = int(max(1, max(-(-(s + n) // B) for s, n in zip(starts, lens))))
+    need = sum(-(-(s + n) // B) for s, n in zip(starts, lens))
+    NB = int(need + 5)
+    free = rng.permutation(NB)
+    tables = np.full((num_runs, W), -1, np.int32)
+    k = 0
+    for r in range(num_runs):
+        nb = -(-(starts[r] + lens[r]) // B)
+        tables[r, :nb] = free[k:k + nb]
+        k += nb
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T = int(cu[-1])
+    k_src = rng.integers(0, 0x7C00, size=(T, Hkv, 128), dtype=np.uint16)
+    v_src = rng.integers(0, 0x7C00, size=(T, Hkv, 128), dtype=np.uint16)
+    return dict(tables=tables, cu=cu, starts=starts.astype(np.int32), k=k_src, v=v_src, NB=NB,
+                Hkv=Hkv, B=B)
+
+
+RUN_CASES = [
+    # (seed, runs, Hkv, B, max run length, start mode)
+    (1, 5, 2, 16, 70, "zero"),          # c1-like prompts
+    (2, 37, 2, 16, 300, "chunk"),       # prefill chunks continuing a prefix
+    (3, 64, 32, 32, 200, "zero"),       # 7B shape, exactly one probe round
+    (4, 65, 8, 128, 400, "chunk"),      # one more run than a round covers
+    (5, 700, 1, 64, 40, "zero"),        # two probe rounds, 64 rows per group
+    (6, 5000, 4, 16, 9, "chunk"),       # more than 4096 runs: three rounds
+    (7, 3, 64, 256, 600, "zero"),       # wide heads, the largest block
+]
+
+
+@pytest.mark.parametrize("case", RUN_CASES, ids=[f"runs{c[1]}_h{c[2]}_b{c[3]}_{c[5]}"
+                                                 for c in RUN_CASES])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_append_tokens_bit_exact(case, dtype):
+    seed, R, Hkv, B, L, mode = case
+    c = _runs_case(seed, R, Hkv, B, L, mode)
+    print(f"[append_tokens] seed={seed} runs={R} Hkv={Hkv} B={B} T={c['cu'][-1]} {dtype}",
+          flush=True)
+    kp, vp = _pool(c["NB"], Hkv, B, dtype), _pool(c["NB"], Hkv, B, dtype)
+    O.append_tokens(kp, vp, c["k"], c["v"], c["cu"], c["starts"], c["tables"], B, c["NB"])
+    gk, gv = to_dev(_pool(c["NB"], Hkv, B, dtype), dtype, DEV), to_dev(_pool(c["NB"], Hkv, B, dtype), dtype, DEV)
+    pkv.paged_kv_append_tokens(gk, gv, to_dev(c["k"], dtype, DEV), to_dev(c["v"], dtype, DEV),
+                               i64(c["cu"], DEV), i32(c["starts"], DEV), i32(c["tables"], DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(gk), kp)
+    assert np.array_equal(bits_of(gv), vp)
+
+
+def test_append_tokens_then_decode_matches_oracle():
+    """A prompt written as one run per sequence plus the decode step's token gives
+    the oracle's attention (the prefill -> decode hand-over)."""
+    rng = np.random.default_rng(11)
+    S, Hq, Hkv, B = 6, 12, 2, 16
+    prompt = rng.integers(1, 90, size=S)
+    n = (prompt + 1).astype(np.int32)
+    W = int(max(-(-n // B)))
+    NB = int(sum(-(-n // B)) + 4)
+    free = rng.permutation(NB)
+    tables = np.full((S, W), -1, np.int32)
+    k = 0
+    for s in range(S):
+        nb = -(-int(n[s]) // B)
+        tables[s, :nb] = free[k:k + nb]
+        k += nb
+    cu = np.concatenate([[0], np.cumsum(prompt)]).astype(np.int64)
+    T = int(cu[-1])
+    draw = lambda *sh: (rng.standard_normal(sh) * 0.5).astype(np.float16).view(np.uint16)  # noqa: E731
+    ks, vs, kn, vn, q = draw(T, Hkv, 128), draw(T, Hkv, 128), draw(S, Hkv, 128), draw(S, Hkv, 128), draw(S, Hq, 128)
+    starts = np.zeros(S, np.int32)
+    kp, vp = _pool(NB, Hkv, B, "fp16"), _pool(NB, Hkv, B, "fp16")
+    O.append_tokens(kp, vp, ks, vs, cu, starts, tables, B, NB)
+    O.append(kp, vp, kn, vn, tables, n, B, NB)
+    ref = O.attention(q, kp, vp, tables, n, Hkv, B, NB, scale_for(128), "fp16")
+    gk, gv = to_dev(_pool(NB, Hkv, B, "fp16"), "fp16", DEV), to_dev(_pool(NB, Hkv, B, "fp16"), "fp16", DEV)
+    pkv.paged_kv_append_tokens(gk, gv, to_dev(ks, "fp16", DEV), to_dev(vs, "fp16", DEV),
+                               i64(cu, DEV), i32(starts, DEV), i32(tables, DEV))
+    out = torch.empty((S, Hq, 128), dtype=torch.float16, device=DEV)
+    pkv.paged_attention_append_decode(out, to_dev(q, "fp16", DEV), gk, gv, to_dev(kn, "fp16", DEV),
+                                      to_dev(vn, "fp16", DEV), i32(tables, DEV), i32(n, DEV),
+                                      scale=scale_for(128))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(gk), kp) and np.array_equal(bits_of(gv), vp)
+    ok, err, nbad = tol_ok(widen_out(out), ref)
+    assert ok, (err, nbad)
+
+
+# ---------------------------------------------------------------------------
+# copy-on-write block copies
+# ---------------------------------------------------------------------------
+def _pairs(rng, NB, npairs, fork=3):
+    """Distinct destinations, none of them a source; some sources fork into
+    several destinations (one prompt block copied for several samples)."""
+    ids = rng.permutation(NB)
+    nsrc = max(1, npairs // fork)
+    srcs = ids[:nsrc]
+    dst = ids[nsrc:nsrc + npairs]
+    src = srcs[rng.integers(0, nsrc, size=npairs)]
+    return src.astype(np.int32), dst.astype(np.int32)
+
+
+COPY_CASES = [
+    # (seed, layers, NB, Hkv, B, pairs)
+    (1, 1, 64, 2, 16, 1),
+    (2, 3, 64, 2, 16, 12),        # c1/c2 shape, several layers
+    (3, 2, 96, 32, 32, 20),       # 7B shape: 512 KiB per block per pool
+    (4, 4, 40, 8, 128, 9),        # c4 shape
+    (5, 1, 24, 1, 256, 7),
+    (6, 2, 300, 64, 16, 90),
+]
+
+
+@pytest.mark.parametrize("case", COPY_CASES, ids=[f"L{c[1]}_nb{c[2]}_h{c[3]}_b{c[4]}_p{c[5]}"
+                                                   for c in COPY_CASES])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_copy_blocks_bit_exact(case, dtype):
+    seed, L, NB, Hkv, B, npairs = case
+    print(f"[copy_blocks] seed={seed} layers={L} NB={NB} Hkv={Hkv} B={B} pairs={npairs} {dtype}",
+          flush=True)
+    rng = np.random.default_rng(seed)
+    src, dst = _pairs(rng, NB, npairs)
+    host = [(_pool(NB, Hkv, B, dtype, rng), _pool(NB, Hkv, B, dtype, rng)) for _ in range(L)]
+    dev = [(to_dev(k, dtype, DEV), to_dev(v, dtype, DEV)) for k, v in host]
+    for k, v in host:
+        O.copy_blocks(k, v, src, dst)
+    pkv.paged_kv_copy_blocks([k for k, _ in dev], [v for _, v in dev], i32(src, DEV),
+                             i32(dst, DEV))
+    torch.cuda.synchronize()
+    for (hk, hv), (gk, gv) in zip(host, dev):
+        assert np.array_equal(bits_of(gk), hk)
+        assert np.array_equal(bits_of(gv), hv)
+
+
+def test_copy_blocks_strides_over_more_pairs_than_one_grid_row():
+    """70,000 pairs: more than the 65,535 the grid takes in one dimension, so
+    work-groups loop over pairs.  Expected pools: each destination holds its
+    source's pre-call bits, every other block is unchanged."""
+    NB, Hkv, B, npairs = 140_004, 1, 16, 70_000
+    rng = np.random.default_rng(9)
+    perm = rng.permutation(NB).astype(np.int32)
+    src, dst = perm[:npairs].copy(), perm[npairs:2 * npairs].copy()
+    k0 = rng.integers(0, 1 << 16, size=(NB, Hkv, B, 128), dtype=np.uint16)
+    v0 = rng.integers(0, 1 << 16, size=(NB, Hkv, B, 128), dtype=np.uint16)
+    gk, gv = to_dev(k0, "fp16", DEV), to_dev(v0, "fp16", DEV)
+    k0[dst], v0[dst] = k0[src], v0[src]
+    pkv.paged_kv_copy_blocks([gk], [gv], i32(src, DEV), i32(dst, DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(gk), k0) and np.array_equal(bits_of(gv), v0)
+
+
+def test_copy_blocks_at_7b_shape_full_pools():
+    """32 layers of 7B-shaped pools (Hkv 32, B 32, 256 blocks each), 128 forks:
+    every destination equals its source as it was before the call and no other
+    block changes (checked on the device against copies taken before the call)."""
+    L, NB, Hkv, B, npairs = 32, 256, 32, 32, 128
+    g = torch.Generator(device=DEV)
+    g.manual_seed(1234)
+    pools = []
+    for _ in range(L):
+        k = torch.randint(-32768, 32767, (NB, Hkv, B, 128), dtype=torch.int16, device=DEV,
+                          generator=g)
+        v = torch.randint(-32768, 32767, (NB, Hkv, B, 128), dtype=torch.int16, device=DEV,
+                          generator=g)
+        pools.append((k, v))
+    before = [(k.clone(), v.clone()) for k, v in pools]
+    rng = np.random.default_rng(77)
+    perm = rng.permutation(NB).astype(np.int32)
+    src, dst = perm[:npairs].copy(), perm[npairs:2 * npairs].copy()
+    pkv.paged_kv_copy_blocks([k.view(torch.float16) for k, _ in pools],
+                             [v.view(torch.float16) for _, v in pools], i32(src, DEV),
+                             i32(dst, DEV))
+    torch.cuda.synchronize()
+    keep = torch.from_numpy(np.setdiff1d(np.arange(NB), dst)).to(DEV)
+    s_t, d_t = torch.from_numpy(src).long().to(DEV), torch.from_numpy(dst).long().to(DEV)
+    for (k, v), (k0, v0) in zip(pools, before):
+        assert torch.equal(k[d_t], k0[s_t]) and torch.equal(v[d_t], v0[s_t])
+        assert torch.equal(k[keep], k0[keep]) and torch.equal(v[keep], v0[keep])
+
+
+def test_fork_scenario_on_gpu():
+    """The page's fork example with the copy on the GPU: prompt of 20 tokens in
+    blocks [10, 11], branch A's append copies #11 into #45 and writes there,
+    branch B writes in place; pools bit-exact and both branches' attention within
+    tolerance of the oracle run through the same steps."""
+    B, NB, Hkv, Hq, T = 16, 96, 2, 4, 20
+    rng = np.random.default_rng(0)
+    draw = lambda *sh: (rng.standard_normal(sh) * 0.5).astype(np.float16).view(np.uint16)  # noqa: E731
+    pk, pv = draw(T, Hkv, 128), draw(T, Hkv, 128)
+    new_k, new_v, q = draw(2, Hkv, 128), draw(2, Hkv, 128), draw(2, Hq, 128)
+    tables = np.array([[10, 45], [10, 11]], np.int32)
+    lens = np.array([T + 1, T + 1], np.int32)
+    cu, st, pt = np.array([0, T], np.int64), np.array([0], np.int32), np.array([[10, 11]], np.int32)
+    src, dst = np.array([11], np.int32), np.array([45], np.int32)
+    # oracle
+    kp, vp = _pool(NB, Hkv, B, "fp16"), _pool(NB, Hkv, B, "fp16")
+    O.append_tokens(kp, vp, pk, pv, cu, st, pt, B, NB)
+    O.copy_blocks(kp, vp, src, dst)
+    O.append(kp, vp, new_k, new_v, tables, lens, B, NB)
+    ref = O.attention(q, kp, vp, tables, lens, Hkv, B, NB, scale_for(128), "fp16")
+    # GPU
+    gk, gv = to_dev(_pool(NB, Hkv, B, "fp16"), "fp16", DEV), to_dev(_pool(NB, Hkv, B, "fp16"), "fp16", DEV)
+    pkv.paged_kv_append_tokens(gk, gv, to_dev(pk, "fp16", DEV), to_dev(pv, "fp16", DEV),
+                               i64(cu, DEV), i32(st, DEV), i32(pt, DEV))
+    pkv.paged_kv_copy_blocks([gk], [gv], i32(src, DEV), i32(dst, DEV))
+    out = torch.empty((2, Hq, 128), dtype=torch.float16, device=DEV)
+    pkv.paged_attention_append_decode(out, to_dev(q, "fp16", DEV), gk, gv,
+                                      to_dev(new_k, "fp16", DEV), to_dev(new_v, "fp16", DEV),
+                                      i32(tables, DEV), i32(lens, DEV), scale=scale_for(128))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(gk), kp) and np.array_equal(bits_of(gv), vp)
+    ok, err, nbad = tol_ok(widen_out(out), ref)
+    assert ok, (err, nbad)
+
+
+def test_copy_blocks_empty_and_debug_rejections(monkeypatch):
+    k = torch.zeros((8, 2, 16, 128), dtype=torch.float16, device=DEV)
+    v = torch.zeros_like(k)
+    e = torch.zeros(0, dtype=torch.int32, device=DEV)
+    pkv.paged_kv_copy_blocks([k], [v], e, e)  # nothing to copy
+    monkeypatch.setenv("PKV_DEBUG_CHECK", "1")
+    bad = [([1, 2], [2, 3]), ([1, 2], [3, 3]), ([1], [8])]
+    for s_, d_ in bad:
+        with pytest.raises(pkv.PagedKVError) as ei:
+            pkv.paged_kv_copy_blocks([k], [v], i32(s_, DEV), i32(d_, DEV))
+        assert ei.value.status == -5
+    pkv.paged_kv_copy_blocks([k], [v], i32([1, 1], DEV), i32([2, 3], DEV))  # a fork is fine
+    torch.cuda.synchronize()
