@@ -41,11 +41,13 @@ METRIC = ("decode attention tokens/s and achieved HBM GB/s (% of MI355X peak), 1
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
 
 
-def algorithmic_bytes(cfg, lengths, tables_entries):
-    """Bytes one layer of the step must move at minimum, split per kernel."""
+def algorithmic_bytes(cfg, lengths, tables_entries, shared_tokens=0):
+    """Bytes one layer of the step must move at minimum, split per kernel.
+    shared_tokens: attended positions that are re-reads of a prefix another
+    sequence of the batch already reads (its K/V rows count once)."""
     e = cfg.elem_bytes
     S, Hq, Hkv, D = cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
-    kv = int(np.sum(lengths)) * 2 * Hkv * D * e        # K and V rows attended
+    kv = (int(np.sum(lengths)) - shared_tokens) * 2 * Hkv * D * e   # K and V rows
     qo = 2 * S * Hq * D * e                             # q read + output write
     meta = 4 * int(tables_entries) + 4 * S              # table entries + lengths
     append = 2 * S * 2 * Hkv * D * e                    # new K/V rows read + written
@@ -70,6 +72,11 @@ def parse():
                     help="run the append and the decode as two launches per layer "
                          "(paged_kv_append + paged_attention_decode) instead of the fused "
                          "paged_attention_append_decode")
+    ap.add_argument("--no-prefix", action="store_true",
+                    help="for a shared-prefix workload, run the plain fused decode instead of "
+                         "paged_attention_prefix_decode")
+    ap.add_argument("--prefix-partition", type=int, default=None,
+                    help="prefix partition of paged_attention_prefix_decode (0 = one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle sample")
@@ -222,12 +229,29 @@ def bench_step(args):
     setup_s = time.time() - t_setup
 
     fused = not args.separate
+    prefix = cfg.prefix_tokens > 0 and not args.no_prefix
+    if prefix:
+        # one group: every sequence shares the workload's prefix blocks
+        PP = cfg.bench_prefix_partition if args.prefix_partition is None else args.prefix_partition
+        ctx = cfg.max_blocks_per_seq * cfg.block_size
+        mpp = 1 if PP == 0 else -(-ctx // PP)
+        pre_o = torch.empty((S, Hq, mpp, D), dtype=torch.float32, device=dev)
+        pre_lse = torch.empty((S, Hq, mpp), dtype=torch.float32, device=dev)
+        group_cu = torch.tensor([0, S], dtype=torch.int32, device=dev)
+        prefix_lens = torch.tensor([cfg.prefix_tokens], dtype=torch.int32, device=dev)
+        P = 0
 
     def attend(li):
         """Decode of layer li; in fused mode it also appends the layer's new rows."""
         L = layers[li % R]
         o = None if P else out[li]
-        if fused:
+        if prefix:
+            pkv.paged_attention_prefix_decode(o, L["q"], L["k"], L["v"], tables, lens, group_cu,
+                                              prefix_lens, pre_o, pre_lse,
+                                              k_new=L["kn"] if fused else None,
+                                              v_new=L["vn"] if fused else None, scale=scale,
+                                              prefix_partition=PP)
+        elif fused:
             pkv.paged_attention_append_decode(o, L["q"], L["k"], L["v"], L["kn"], L["vn"],
                                               tables, lens, scale=scale, partition_size=P,
                                               part_o=part_o, part_lse=part_lse)
@@ -280,7 +304,10 @@ def bench_step(args):
 
     # ---- accounting -------------------------------------------------------------------
     nblk = int(np.sum(-(-w0.lengths.astype(np.int64) // cfg.block_size)))
-    ab = algorithmic_bytes(cfg, w0.lengths, nblk)
+    # a shared prefix is one set of K/V rows however many sequences attend to it
+    shared = (S - 1) * cfg.prefix_tokens if cfg.prefix_tokens > 0 else 0
+    ab = algorithmic_bytes(cfg, w0.lengths, nblk, shared)
+    logical = algorithmic_bytes(cfg, w0.lengths, nblk)
     step_bytes = ab["layer"] * cfg.num_layers
     gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     tokens_per_s = S / (ms_per_step * 1e-3)
@@ -310,23 +337,30 @@ def bench_step(args):
             "pool_blocks_per_layer": int(w0.num_blocks),
             "distinct_layer_pools": R,
             "partition_size": P,
-            "launches_per_layer": (1 if fused else 2) + (1 if P else 0),
+            "launches_per_layer": (1 if fused else 2) + (1 if (P or prefix) else 0),
+            "shared_prefix": cfg.prefix_tokens,
+            "path": ("paged_attention_prefix_decode (prefix partition %d)" % PP if prefix
+                     else "paged_attention_append_decode" if fused else
+                     "paged_kv_append + paged_attention_decode"),
             "accumulate": "fp32",
         },
         "hbm_gbps": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "step_algorithmic_bytes": step_bytes,
         "roofline": {
-            "kernel": "paged_attention_append_decode" if fused else "paged_attention_decode",
+            "kernel": ("paged_attention_prefix_decode (prefix + suffix pass)" if prefix
+                       else "paged_attention_append_decode" if fused
+                       else "paged_attention_decode"),
             "bound": "hbm",
             "achieved": round(dec_gbps, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(cfg.key, "decode"),
+            "traffic": None if prefix else measured_traffic(cfg.key, "decode"),
             "bytes_per_launch": kernel_bytes,
             "avg_launch_ms": round(decode_ms, 5),
         },
+        "logical_bytes_per_layer": logical["layer"],
         "setup_s": round(setup_s, 1),
     }
 

@@ -197,6 +197,59 @@ int paged_attention_append_decode(void *out, const void *q, void *k_pool, void *
                                   float *part_o, float *part_lse, int dtype, void *stream);
 
 /*
+ * paged_attention_prefix_decode -- decode attention for batches whose sequences
+ * share a prefix, reading each shared block once per tile of sequences.
+ *
+ * Sequences group_cu[k] .. group_cu[k+1]-1 form group k and share the K/V of
+ * their first prefix_lens[k] positions: their tables point at the same physical
+ * blocks there (a system prompt cached once in blocks every session's table
+ * points at: pwwt.cn page, section "共享前缀块（Prefix Caching）"; forked branches
+ * reading blocks with reference count > 1: blog.llmgo.top page, §四).  The result
+ * is the same as paged_attention_decode (or, with k_new / v_new, as
+ * paged_attention_append_decode) on the same tables; only the reads differ.
+ * Two launches:
+ *   1. prefix pass: for each group, 16-row query tiles made of the query heads of
+ *      floor(16/G) consecutive member sequences (G = num_q_heads / num_kv_heads)
+ *      attend over the group's prefix, read through the table row of sequence
+ *      group_cu[k]; the prefix is split into partitions of prefix_partition tokens
+ *      (0: one partition) and each partition's fp32 partial (normalised o,
+ *      natural-log lse) goes to part_o[s][h][p] / part_lse[s][h][p];
+ *   2. suffix pass: each (sequence, KV head) attends over positions
+ *      prefix_lens[k] .. n-1 (appending the new token as
+ *      paged_attention_append_decode does when k_new is given), merges that with
+ *      the prefix partials by the log-sum-exp rule and writes `out`.
+ *
+ *   group_cu       device int32 [num_groups + 1]: 0 = group_cu[0] <= ... <=
+ *                  group_cu[num_groups] = num_seqs (groups are contiguous)
+ *   prefix_lens    device int32 [num_groups], >= 0 (0: the group shares nothing)
+ *   k_new, v_new   optional (both or neither), as for paged_attention_append_decode;
+ *                  slot_out is used only with them
+ *   prefix_partition  0 or a multiple of 16
+ *   max_partitions    row stride of the workspace, at least
+ *                  ceil(max_blocks_per_seq * block_size / prefix_partition)
+ *                  (at least 1 when prefix_partition is 0), else PKV_EWORKSPACE
+ *   part_o, part_lse  fp32 workspace [num_seqs][num_q_heads][max_partitions][head_dim]
+ *                  and [num_seqs][num_q_heads][max_partitions]
+ *   out            [num_seqs][num_q_heads][head_dim], dtype
+ * Caller contract (checked with PKV_DEBUG_CHECK=1 like the other entry points):
+ * every member's table agrees with the first member's on the blocks holding the
+ * prefix, and n >= prefix_lens[k] for every member (n > prefix_lens[k] when
+ * appending, so the new token never lands in a shared block).  Unlike
+ * paged_attention_decode, positions below a sequence's prefix length that share
+ * a 16-position tile with its own positions are read (and masked), so they must
+ * hold finite values -- they do whenever the table is valid for the prefix.
+ */
+int paged_attention_prefix_decode(void *out, const void *q, void *k_pool, void *v_pool,
+                                  const void *k_new, const void *v_new, int64_t *slot_out,
+                                  const int32_t *block_tables, const int32_t *context_lens,
+                                  const int32_t *group_cu, const int32_t *prefix_lens,
+                                  int num_groups, int num_seqs, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int block_size,
+                                  int max_blocks_per_seq, int64_t num_blocks, float scale,
+                                  int prefix_partition, int max_partitions, float *part_o,
+                                  float *part_lse, int dtype, void *stream);
+
+/*
  * paged_attention_reduce -- log-sum-exp merge of split-context partitions.
  *
  * For each (s, h) with P = partition_size and np = ceil(n/P) partitions:

@@ -59,6 +59,10 @@ def load():
     L.paged_attention_append_decode.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32,
                                                 i32, i32, i64, f32, i32, i32, P, P, i32, P]
     L.paged_attention_append_decode.restype = i32
+    L.paged_attention_prefix_decode.argtypes = [P, P, P, P, P, P, P, P, P, P, P, i32, i32, i32,
+                                                i32, i32, i32, i32, i64, f32, i32, i32, P, P,
+                                                i32, P]
+    L.paged_attention_prefix_decode.restype = i32
     L.paged_attention_reduce.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, P]
     L.paged_attention_reduce.restype = i32
     _lib = L
@@ -236,6 +240,32 @@ def paged_attention_append_decode(out, q, k_pool, v_pool, k_new, v_new, block_ta
         float(scale), int(partition_size), mp, _p(part_o), _p(part_lse), _dtype_code(q),
         _stream(dev))
     _check(rc, "paged_attention_append_decode")
+
+
+def paged_attention_prefix_decode(out, q, k_pool, v_pool, block_tables, context_lens, group_cu,
+                                  prefix_lens, part_o, part_lse, k_new=None, v_new=None,
+                                  slot_out=None, scale: Optional[float] = None,
+                                  prefix_partition: int = 0):
+    """Decode attention for sequences grouped by a shared prefix (group k =
+    sequences group_cu[k]..group_cu[k+1]-1, sharing their first prefix_lens[k]
+    positions); appends the new rows first when k_new / v_new are given."""
+    dev = _dev(out, q, k_pool, v_pool, block_tables, context_lens, group_cu, prefix_lens,
+               part_o, part_lse, k_new, v_new, slot_out)
+    for t, n in ((block_tables, "block_tables"), (context_lens, "context_lens"),
+                 (group_cu, "group_cu"), (prefix_lens, "prefix_lens")):
+        _int(t, "i32", n)
+    _int(slot_out, "i64", "slot_out")
+    NB, Hkv, B, D = k_pool.shape
+    S, Hq, _ = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    rc = load().paged_attention_prefix_decode(
+        _p(out), _p(q), _p(k_pool), _p(v_pool), _p(k_new), _p(v_new), _p(slot_out),
+        _p(block_tables), _p(context_lens), _p(group_cu), _p(prefix_lens),
+        prefix_lens.shape[0], S, Hq, Hkv, D, B, block_tables.shape[1], NB, float(scale),
+        int(prefix_partition), part_o.shape[2], _p(part_o), _p(part_lse), _dtype_code(q),
+        _stream(dev))
+    _check(rc, "paged_attention_prefix_decode")
 
 
 def paged_attention_reduce(out, part_o, part_lse, context_lens, partition_size: int):

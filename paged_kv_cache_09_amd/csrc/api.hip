@@ -69,6 +69,26 @@ __global__ void debug_runs_kernel(const int64_t *cu, const int32_t *start_pos,
     }
 }
 
+// Shared-prefix groups: group_cu runs from 0 to num_seqs without decreasing,
+// prefix lengths are >= 0, and every member attends to at least its group's
+// prefix (plus the appended token when the call appends).
+__global__ void debug_groups_kernel(const int32_t *cu, const int32_t *prefix_lens,
+                                    const int32_t *lens, int num_groups, int num_seqs,
+                                    int extra)
+{
+    const int k = blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= num_groups)
+        return;
+    if ((k == 0 && cu[0] != 0) || (k == num_groups - 1 && cu[num_groups] != num_seqs) ||
+        cu[k + 1] < cu[k] || prefix_lens[k] < 0) {
+        atomicOr(&g_debug_flag, 32);
+        return;
+    }
+    for (int s = cu[k]; s < cu[k + 1]; ++s)
+        if (s < 0 || s >= num_seqs || lens[s] < prefix_lens[k] + extra)
+            atomicOr(&g_debug_flag, 32);
+}
+
 // Copy pairs: ids inside the pool; a destination may be neither another pair's
 // destination nor any pair's source (the result would depend on copy order).
 __global__ void debug_copies_kernel(const int32_t *src, const int32_t *dst, int num_pairs,
@@ -119,6 +139,18 @@ int debug_check_runs(const int64_t *cu, const int32_t *start_pos, const int32_t 
     hipLaunchKernelGGL(debug_runs_kernel, dim3((num_runs + 1 + 255) / 256), dim3(256), 0, stream,
                        cu, start_pos, tables, num_runs, total_tokens, width, block_size,
                        num_blocks);
+    if (hipGetLastError() != hipSuccess)
+        return PKV_ELAUNCH;
+    return read_debug_flag(stream);
+}
+
+int debug_check_groups(const int32_t *group_cu, const int32_t *prefix_lens,
+                       const int32_t *lens, int num_groups, int num_seqs, int extra,
+                       hipStream_t stream)
+{
+    hipLaunchKernelGGL(debug_clear_kernel, dim3(1), dim3(1), 0, stream);
+    hipLaunchKernelGGL(debug_groups_kernel, dim3((num_groups + 255) / 256), dim3(256), 0, stream,
+                       group_cu, prefix_lens, lens, num_groups, num_seqs, extra);
     if (hipGetLastError() != hipSuccess)
         return PKV_ELAUNCH;
     return read_debug_flag(stream);
@@ -187,8 +219,8 @@ const char *pkv_status_string(int status)
     case PKV_ELAUNCH:
         return "kernel launch failed";
     case PKV_EDEVICE:
-        return "device-side check failed (context length, block-table entry or copy pair "
-               "out of range, or overlapping copy pairs)";
+        return "device-side check failed (context length, block-table entry, copy pair or "
+               "prefix group out of range, or overlapping copy pairs)";
     default:
         return "unknown status";
     }
@@ -307,13 +339,23 @@ namespace {
 
 // Shared by the decode entry points: validation, then one launch.  With k_new
 // non-null the kernel also performs the step's append (fused mode).
+// Shared-prefix arguments of paged_attention_prefix_decode (null group_cu for the
+// other entry points).
+struct PrefixGroups {
+    const int32_t *group_cu = nullptr;
+    const int32_t *prefix_lens = nullptr;
+    int num_groups = 0;
+};
+
 int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
                 const void *k_new, const void *v_new, int64_t *slot_out,
                 const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
                 int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                 int max_blocks_per_seq, int64_t num_blocks, float scale, int partition_size,
-                int max_partitions, float *part_o, float *part_lse, int dtype, void *stream)
+                int max_partitions, float *part_o, float *part_lse, int dtype, void *stream,
+                const PrefixGroups &pg = PrefixGroups())
 {
+    const bool prefix = pg.group_cu != nullptr;
     if (!q || !k_pool || !v_pool || !block_tables || !context_lens)
         return PKV_EINVAL;
     if (num_seqs < 0 || num_q_heads <= 0 || partition_size < 0)
@@ -334,7 +376,29 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
     if (k_new && (!aligned16(k_new) || !aligned16(v_new) || ((uintptr_t)slot_out & 7u)))
         return PKV_EINVAL;
     int parts = 1;
-    if (partition_size > 0) {
+    int prefix_part = 0, prefix_parts = 0;
+    if (prefix) {
+        // partition_size splits each group's prefix (0: one partition); the
+        // suffix is a single pass that writes `out`
+        if (!pg.prefix_lens || pg.num_groups <= 0 || (num_seqs > 0 && pg.num_groups > num_seqs))
+            return PKV_EINVAL;
+        if (((uintptr_t)pg.group_cu & 3u) || ((uintptr_t)pg.prefix_lens & 3u))
+            return PKV_EINVAL;
+        if (partition_size % 16 != 0)
+            return PKV_EINVAL;
+        const int64_t ctx = (int64_t)max_blocks_per_seq * block_size;
+        if (ctx > ((int64_t)1 << 29))
+            return PKV_EINVAL;
+        prefix_part = partition_size > 0 ? partition_size : (int)((ctx + 15) / 16 * 16);
+        const int64_t need = (ctx + prefix_part - 1) / prefix_part;
+        if (!part_o || !part_lse || max_partitions < need || need <= 0)
+            return PKV_EWORKSPACE;
+        if (!aligned16(part_o) || ((uintptr_t)part_lse & 3u))
+            return PKV_EINVAL;
+        prefix_parts = max_partitions;
+        if (!out || ((uintptr_t)out & 1u))
+            return PKV_EINVAL;
+    } else if (partition_size > 0) {
         if (partition_size % block_size != 0 || partition_size % 32 != 0)
             return PKV_EINVAL;
         const int need = pkv_max_partitions(max_blocks_per_seq, block_size, partition_size);
@@ -365,6 +429,9 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
     if (debug_enabled()) {
         rc = pkv::debug_check_tables(block_tables, context_lens, num_seqs, max_blocks_per_seq,
                                      block_size, num_blocks, st);
+        if (rc == PKV_OK && prefix)
+            rc = pkv::debug_check_groups(pg.group_cu, pg.prefix_lens, context_lens,
+                                         pg.num_groups, num_seqs, k_new ? 1 : 0, st);
         if (rc)
             return rc;
     }
@@ -390,6 +457,25 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
     a.v_new = v_new;
     a.slot_out = slot_out;
     a.block_size = block_size;
+    if (prefix) {
+        // pass 1: each group's prefix, read once per 16-row tile of its query heads;
+        // pass 2: each sequence's own positions, merged with the prefix partials
+        a.partition_size = 0;
+        a.max_partitions = prefix_parts;
+        a.group_cu = pg.group_cu;
+        a.prefix_lens = pg.prefix_lens;
+        a.num_groups = pg.num_groups;
+        a.prefix_part = prefix_part;
+        a.seqs_per_tile = 16 / group;
+        const int64_t tiles = (num_seqs + a.seqs_per_tile - 1) / a.seqs_per_tile;
+        const int64_t pitems = tiles * num_kv_heads * prefix_parts;
+        if (pitems > INT32_MAX)
+            return PKV_EINVAL;
+        hipError_t e = pkv::launch_prefix_mfma(a, (int)pitems, dtype, block_size, st);
+        if (e != hipSuccess)
+            return PKV_ELAUNCH;
+        return launch_status(pkv::launch_decode_mfma(a, dtype, block_size, st));
+    }
     const hipError_t e = group == 1 ? pkv::launch_decode_g1(a, dtype, block_size, st)
                                     : pkv::launch_decode_mfma(a, dtype, block_size, st);
     return launch_status(e);
@@ -426,6 +512,30 @@ int paged_attention_append_decode(void *out, const void *q, void *k_pool, void *
                        context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                        max_blocks_per_seq, num_blocks, scale, partition_size, max_partitions,
                        part_o, part_lse, dtype, stream);
+}
+
+int paged_attention_prefix_decode(void *out, const void *q, void *k_pool, void *v_pool,
+                                  const void *k_new, const void *v_new, int64_t *slot_out,
+                                  const int32_t *block_tables, const int32_t *context_lens,
+                                  const int32_t *group_cu, const int32_t *prefix_lens,
+                                  int num_groups, int num_seqs, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int block_size,
+                                  int max_blocks_per_seq, int64_t num_blocks, float scale,
+                                  int prefix_partition, int max_partitions, float *part_o,
+                                  float *part_lse, int dtype, void *stream)
+{
+    if (!group_cu)
+        return PKV_EINVAL;
+    if ((k_new == nullptr) != (v_new == nullptr))
+        return PKV_EINVAL;
+    PrefixGroups pg;
+    pg.group_cu = group_cu;
+    pg.prefix_lens = prefix_lens;
+    pg.num_groups = num_groups;
+    return decode_impl(out, q, k_pool, v_pool, k_new, v_new, k_new ? slot_out : nullptr,
+                       block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                       block_size, max_blocks_per_seq, num_blocks, scale, prefix_partition,
+                       max_partitions, part_o, part_lse, dtype, stream, pg);
 }
 
 int paged_attention_reduce(void *out, const float *part_o, const float *part_lse,

@@ -40,6 +40,15 @@ constexpr int kSub = 16;           // tokens per sub-tile
 // so the 16 rows of a transposing read start 8 banks apart and one pass of 8
 // rows covers all 64 banks exactly once (likewise each 256-byte row write).
 constexpr int kVStride = 144;
+// LDS row stride, in floats, of the waves' fp32 partial outputs [wave][query row]
+// [dim]: 132 = 4 (mod 64), so the 16 lanes of each phase of a 16-byte write or read
+// start 4 banks apart and cover all 64 banks once.
+constexpr int kOStride = 132;
+// Lazy online softmax: a column's reference max is raised only when a score
+// exceeds it by more than this many log2 units, so most sub-tiles skip the
+// accumulator rescale.  Probabilities then stay below 2^8, which fp16 and bf16
+// represent with the same relative precision as values below 1.
+constexpr float kRescaleSlack = 8.f;
 
 template <int DT>
 __device__ __forceinline__ f32x4 mfma_qk(const u32x4 &a, const u32x4 &b, f32x4 c)
@@ -103,33 +112,41 @@ __device__ __forceinline__ int32_t sub_phys(const int32_t *__restrict__ trow, in
     return trow[min(tb / BS, width - 1)];
 }
 
+template <int CPOL = kLoadStream>
 __device__ __forceinline__ void load_k(KOp &t, __amdgpu_buffer_rsrc_t r, int lane)
 {
     const int kb = (lane & 15) * kHeadDim * 2 + (lane >> 4) * 16;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-        t.k[kk] = ldbuf(r, kb + kk * 64);
+        t.k[kk] = ldbuf<CPOL>(r, kb + kk * 64);
 }
 
+template <int CPOL = kLoadStream>
 __device__ __forceinline__ void load_v(VRows &t, __amdgpu_buffer_rsrc_t r, int lane)
 {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        t.v[j] = ldbuf(r, lane * 16 + j * 1024);
+        t.v[j] = ldbuf<CPOL>(r, lane * 16 + j * 1024);
 }
 
 struct GqaState {
-    float m;        // running max of this lane's query row (uniform over the 4 lane groups)
+    float m;        // reference max of this lane's query row (uniform over the 4 lane
+                    // groups; lags the running max by at most kRescaleSlack)
     float l;        // this lane's share of the running sum
     f32x4 acc[8];   // O^T rows 16*jj + 4*(lane/16) + r, column = query row lane%16
 };
 
 // Scores of the sub-tile, online-softmax update of (m, l); returns the
 // probabilities packed as the B operand of P.V and the rescale factor of acc.
+// Scores of the sub-tile and the online-softmax update of (m, l).  PARTIAL:
+// mask tokens outside [t_beg, t_end) (the sub-tile straddles an end).  Returns
+// whether the wave rescales its accumulators (alpha holds each lane's factor,
+// 1 where the column's reference max did not move); pb receives the
+// probabilities packed as the B operand of P.V.
 template <int DT, bool PARTIAL>
-__device__ __forceinline__ void qk_softmax(GqaState &st, const KOp &K, const u32x4 *qop, int tb,
-                                           int t_end, int lane, float scale_log2, u32x2 &pb,
-                                           float &alpha)
+__device__ __forceinline__ bool qk_softmax(GqaState &st, const KOp &K, const u32x4 *qop, int tb,
+                                           int t_beg, int t_end, int lane, float scale_log2,
+                                           u32x2 &pb, float &alpha)
 {
     const int grp = lane >> 4;
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
@@ -140,15 +157,23 @@ __device__ __forceinline__ void qk_softmax(GqaState &st, const KOp &K, const u32
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         sc[r] = s[r] * scale_log2;
-        if (PARTIAL && tb + 4 * grp + r >= t_end)
+        const int t = tb + 4 * grp + r;
+        if (PARTIAL && (t < t_beg || t >= t_end))
             sc[r] = kNegInf;
     }
     float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mt = fmaxf(mt, xor_lane(mt, 16));
     mt = fmaxf(mt, xor_lane(mt, 32));
-    const float m_new = fmaxf(st.m, mt);
-    const float ref = safe_ref(m_new);
-    alpha = fexp2(st.m - ref);
+    const bool grow = mt > st.m + kRescaleSlack;  // always true for the first scores
+    const bool rescale = __ballot(grow) != 0;     // wave-uniform
+    alpha = 1.f;
+    if (rescale) {
+        const float m_new = grow ? mt : st.m;
+        alpha = fexp2(st.m - safe_ref(m_new));
+        st.l *= alpha;
+        st.m = m_new;
+    }
+    const float ref = safe_ref(st.m);
     float p[4];
     float psum = 0.f;
 #pragma unroll
@@ -156,10 +181,10 @@ __device__ __forceinline__ void qk_softmax(GqaState &st, const KOp &K, const u32
         p[r] = fexp2(sc[r] - ref);
         psum += p[r];
     }
-    st.l = st.l * alpha + psum;
-    st.m = m_new;
+    st.l += psum;
     pb.x = (uint32_t)to_bits<DT>(p[0]) | ((uint32_t)to_bits<DT>(p[1]) << 16);
     pb.y = (uint32_t)to_bits<DT>(p[2]) | ((uint32_t)to_bits<DT>(p[3]) << 16);
+    return rescale;
 }
 
 // Stage the V rows of the sub-tile, row-major, in this wave's LDS tile.
@@ -180,16 +205,20 @@ __device__ __forceinline__ void stage_v(const VRows &V, uint16_t *vlds, int lane
 // multiply zeros, never a stale NaN.
 template <int DT>
 __device__ __forceinline__ void pv_mma(GqaState &st, const uint16_t *vlds, const u32x2 &pb,
-                                       float alpha, int lane)
+                                       bool rescale, float alpha, int lane)
 {
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
     const int j = lane & 15, grp = lane >> 4;
     const uint16_t *base = vlds + (4 * grp + (j >> 2)) * kVStride + 4 * (j & 3);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (rescale) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+            st.acc[jj] *= alpha;
+    }
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
-        st.acc[jj] *= alpha;
         const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_i16x4 *)(base + 16 * jj));
         st.acc[jj] = mfma_pv<DT>(__builtin_bit_cast(u32x2, va), pb, st.acc[jj]);
@@ -199,21 +228,32 @@ __device__ __forceinline__ void pv_mma(GqaState &st, const uint16_t *vlds, const
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// SPLIT: split-context mode (partition loop); otherwise one pass over the
-// whole context, with the loop folded away at compile time.
+// Work modes of the decode kernel.
+constexpr int kModeSingle = 0;  // one pass over positions 0 .. n-1, writes `out`
+constexpr int kModeSplit = 1;   // partitions of the context, writes part_o / part_lse
+constexpr int kModeSuffix = 2;  // shared-prefix mode: positions prefix_len .. n-1, then
+                                // merged with the prefix partials, writes `out`
+
+// MODE kModeSplit runs a partition loop; the other modes one pass, with the loop
+// folded away at compile time.
 // The register budget is capped so that 4 waves (single pass) or 3 waves (split
 // mode, which keeps more state live across its partition loop) fit on each SIMD
 // without spilling.
-template <int DT, int BS, int WAVES, bool SPLIT>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SPLIT ? 3 : 4)))
+template <int DT, int BS, int WAVES, int MODE>
+__global__ __launch_bounds__(WAVES * 64)
+__attribute__((amdgpu_waves_per_eu(MODE == kModeSplit ? 3 : 4)))
 void decode_mfma_kernel(DecodeArgs a)
 {
+    constexpr bool SPLIT = MODE == kModeSplit;
     // V staging during the token loop; the cross-wave merge afterwards
     __shared__ union {
         uint16_t v[WAVES][kSub * kVStride];
-        float o[WAVES][16][kHeadDim];
+        float o[WAVES][16][kOStride];
     } sm;
     __shared__ float s_m[WAVES][16], s_l[WAVES][16];
+    // fused append: the new K and V rows, parked by the wave that owns position
+    // n-1 until its last sub-tile (registers would be held across the whole loop)
+    __shared__ u32x4 s_new[2][kHeadDim / 8];
 
     // sequence-major work items (see the MHA kernel): the KV heads of a sequence
     // are neighbours in dispatch order
@@ -237,11 +277,16 @@ void decode_mfma_kernel(DecodeArgs a)
     const int64_t blk_elems = (int64_t)a.num_kv_heads * BS * kHeadDim;
     const int64_t head_off = (int64_t)g * BS * kHeadDim;
     const int P = SPLIT ? a.partition_size : 0;
+    // shared-prefix mode: this pass covers the positions after the group's prefix
+    const int start = MODE == kModeSuffix
+                          ? a.prefix_lens[group_of(a.group_cu, a.num_groups, s)]
+                          : 0;
+    const int start_sub = start & ~(kSub - 1);  // sub-tiles stay aligned to 16 positions
 
     // The first sub-tile's table entry (and the next one's) do not depend on the
     // context length: request them together with it, so the two scalar-load
     // latencies overlap instead of chaining.
-    const int tb_first = (P > 0 ? px0 * P : 0) + w * kSub;
+    const int tb_first = (P > 0 ? px0 * P : start_sub) + w * kSub;
     const int32_t e_first = sub_phys<BS>(trow, a.width, tb_first);
     const int32_t e_next = sub_phys<BS>(trow, a.width, tb_first + WAVES * kSub);
     const int n = a.lens[s];
@@ -262,6 +307,25 @@ void decode_mfma_kernel(DecodeArgs a)
     uint16_t *vlds = sm.v[w];
     const int64_t row0 = (int64_t)s * a.num_q_heads + (int64_t)g * G;
 
+    // Shared-prefix mode: the first prefix partition's partials of the elements
+    // this thread merges at the end (element e = (query row e/32, dims 4(e%32)..))
+    // are requested now, so their latency overlaps the token loop.
+    constexpr int kPre = 2;
+    f32x4 pre_o[kPre];
+    float pre_l[kPre];
+    if (MODE == kModeSuffix) {
+#pragma unroll
+        for (int k = 0; k < kPre; ++k) {
+            const int e = tid + k * WAVES * 64;
+            if (e < G * 32) {
+                const int64_t row = row0 + (e >> 5);
+                pre_l[k] = a.part_lse[row * a.max_partitions];
+                pre_o[k] = *(const f32x4 *)(a.part_o + row * a.max_partitions * kHeadDim +
+                                            (e & 31) * 4);
+            }
+        }
+    }
+
     // Partitions px0, px0 + parts_per_item, ... of the item belong to this
     // work-group (the grid is sized from the batch, not from the table width).
     // Single pass: one iteration over the whole context (zeros when n = 0).
@@ -269,8 +333,9 @@ void decode_mfma_kernel(DecodeArgs a)
     for (int px = px0; px < np; px += parts) {
         if (px != px0)
             __syncthreads();  // the previous partition's merge is done with LDS
-        const int t0 = P > 0 ? px * P : 0;
+        const int t0 = P > 0 ? px * P : start_sub;
         const int t1 = P > 0 ? min(n, t0 + P) : n;
+        const int t_beg = MODE == kModeSuffix ? start : t0;  // positions below are masked
         // With a fused append, position n-1 (in the item's last sub-tile) is not
         // read from the pool: it holds stale data until this kernel writes it.
         const bool owns_new = fused && t1 == n;
@@ -283,7 +348,7 @@ void decode_mfma_kernel(DecodeArgs a)
         for (int jj = 0; jj < 8; ++jj)
             st.acc[jj] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-        const int nsub = (t1 - t0 + kSub - 1) / kSub;
+        const int nsub = t1 > t0 ? (t1 - t0 + kSub - 1) / kSub : 0;
         // the wave holding position n-1 (the item's last sub-tile) fetches the new
         // rows and their block id up front, so that the latency overlaps its loop:
         // knew[kk] is the A-operand chunk of the new key (dims 8*(4kk + lane/16)..),
@@ -329,8 +394,15 @@ void decode_mfma_kernel(DecodeArgs a)
                     for (int kk = 0; kk < 4; ++kk)
                         *(u32x4 *)((uint16_t *)a.k_pool + dst + 32 * kk + 8 * grp) = knew[kk];
                 }
-                if (lane < 16)
+                if (col == 0) {
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        s_new[0][4 * kk + grp] = knew[kk];
+                }
+                if (lane < 16) {
                     *(u32x4 *)((uint16_t *)a.v_pool + dst + lane * 8) = vnew;
+                    s_new[1][lane] = vnew;
+                }
                 if (g == 0 && lane == 0 && a.slot_out)
                     a.slot_out[s] = phys_n * BS + tn % BS;
             }
@@ -338,11 +410,13 @@ void decode_mfma_kernel(DecodeArgs a)
             int32_t pn = first ? e_next : sub_phys<BS>(trow, a.width, tb + step);
             u32x2 pb;
             float alpha;
+            bool rs;
             for (int j = 0; j + 1 < T; ++j) {  // every sub-tile here is full
                 const int32_t pn2 = sub_phys<BS>(trow, a.width, tb + 2 * step);
                 const SubRsrc rn =
                     sub_rsrc<BS>(pn, kp, vp, tb + step, t_load, head_off, blk_elems);
-                qk_softmax<DT, false>(st, K, qop, tb, t1, lane, a.scale_log2, pb, alpha);
+                rs = qk_softmax<DT, MODE == kModeSuffix>(st, K, qop, tb, t_beg, t1, lane,
+                                                         a.scale_log2, pb, alpha);
                 __builtin_amdgcn_sched_barrier(0);
                 load_k(K, rn.k, lane);
                 __builtin_amdgcn_sched_barrier(0);
@@ -350,7 +424,7 @@ void decode_mfma_kernel(DecodeArgs a)
                 __builtin_amdgcn_sched_barrier(0);
                 load_v(V, rn.v, lane);
                 __builtin_amdgcn_sched_barrier(0);
-                pv_mma<DT>(st, vlds, pb, alpha, lane);
+                pv_mma<DT>(st, vlds, pb, rs, alpha, lane);
                 __builtin_amdgcn_sched_barrier(0);
                 pn = pn2;
                 tb += step;
@@ -363,16 +437,18 @@ void decode_mfma_kernel(DecodeArgs a)
                 // the four lanes of row `row` take the new key into the A operand
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
-                    K.k[kk] = knew[kk];
+                    K.k[kk] = s_new[0][4 * kk + grp];
             }
             if (tb + kSub <= t1)
-                qk_softmax<DT, false>(st, K, qop, tb, t1, lane, a.scale_log2, pb, alpha);
+                rs = qk_softmax<DT, MODE == kModeSuffix>(st, K, qop, tb, t_beg, t1, lane,
+                                                         a.scale_log2, pb, alpha);
             else
-                qk_softmax<DT, true>(st, K, qop, tb, t1, lane, a.scale_log2, pb, alpha);
+                rs = qk_softmax<DT, true>(st, K, qop, tb, t_beg, t1, lane, a.scale_log2, pb,
+                                          alpha);
             stage_v(V, vlds, lane);
             if (here && lane < 16)
-                *(u32x4 *)(vlds + row * kVStride + lane * 8) = vnew;
-            pv_mma<DT>(st, vlds, pb, alpha, lane);
+                *(u32x4 *)(vlds + row * kVStride + lane * 8) = s_new[1][lane];
+            pv_mma<DT>(st, vlds, pb, rs, alpha, lane);
         }
 
         // sum of the four lane groups' shares of l (m is already uniform across them)
@@ -382,60 +458,296 @@ void decode_mfma_kernel(DecodeArgs a)
         __syncthreads();  // all waves are done with their V staging area
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sm.o[w][col][16 * jj + 4 * grp + r] = st.acc[jj][r];
+            *(f32x4 *)&sm.o[w][col][16 * jj + 4 * grp] = st.acc[jj];
         if (grp == 0) {
             s_m[w][col] = st.m;
             s_l[w][col] = st.l;
         }
         __syncthreads();
 
-        for (int idx = tid; idx < G * kHeadDim; idx += WAVES * 64) {
-            const int qi = idx / kHeadDim, d = idx % kHeadDim;
+        // element e: query row qi = e/32 of the group, dims d0 .. d0+3
+        for (int e = tid, k = 0; e < G * 32; e += WAVES * 64, ++k) {
+            const int qi = e >> 5, d0 = (e & 31) * 4;
             float M = s_m[0][qi];
 #pragma unroll
             for (int i = 1; i < WAVES; ++i)
                 M = fmaxf(M, s_m[i][qi]);
             const float ref = safe_ref(M);
-            float L = 0.f, O = 0.f;
+            float L = 0.f;
+            f32x4 O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int i = 0; i < WAVES; ++i) {
                 const float wgt = fexp2(s_m[i][qi] - ref);
                 L += s_l[i][qi] * wgt;
-                O += sm.o[i][qi][d] * wgt;
+                O += *(const f32x4 *)&sm.o[i][qi][d0] * wgt;
             }
             const int64_t row = row0 + qi;
-            if (P == 0) {
-                const float o = L > 0.f ? O / L : 0.f;
-                ((uint16_t *)a.out)[row * kHeadDim + d] = to_bits<DT>(o);
+            if (MODE == kModeSuffix || P == 0) {
+                f32x4 o = {0.f, 0.f, 0.f, 0.f};
+                if (MODE == kModeSuffix) {
+                    // merge with the prefix partitions (normalised o, natural-log lse)
+                    const int np_pre =
+                        min((start + a.prefix_part - 1) / a.prefix_part, a.max_partitions);
+                    const float *lse = a.part_lse + row * a.max_partitions;
+                    const float *po = a.part_o + row * a.max_partitions * kHeadDim + d0;
+                    float X = L > 0.f ? ref : kNegInf;
+                    for (int p = 0; p < np_pre; ++p)
+                        X = fmaxf(X, (p == 0 && k < kPre ? pre_l[k] : lse[p]) * kLog2e);
+                    float den = 0.f;
+                    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+                    if (X != kNegInf) {
+                        if (L > 0.f) {
+                            const float ws = fexp2(ref - X);
+                            num = O * ws;
+                            den = L * ws;
+                        }
+                        for (int p = 0; p < np_pre; ++p) {
+                            const bool pf = p == 0 && k < kPre;
+                            const float lp = (pf ? pre_l[k] : lse[p]) * kLog2e;
+                            if (lp != kNegInf) {
+                                const float wp = fexp2(lp - X);
+                                num += (pf ? pre_o[k] : *(const f32x4 *)(po + p * kHeadDim)) * wp;
+                                den += wp;
+                            }
+                        }
+                    }
+                    if (den > 0.f)
+                        o = num / den;
+                } else if (L > 0.f) {
+                    o = O / L;
+                }
+                u32x2 packed;
+                packed.x = (uint32_t)to_bits<DT>(o[0]) | ((uint32_t)to_bits<DT>(o[1]) << 16);
+                packed.y = (uint32_t)to_bits<DT>(o[2]) | ((uint32_t)to_bits<DT>(o[3]) << 16);
+                *(u32x2 *)((uint16_t *)a.out + row * kHeadDim + d0) = packed;
             } else {
-                a.part_o[(row * a.max_partitions + px) * kHeadDim + d] = O / L;
-                if (d == 0)
+                *(f32x4 *)(a.part_o + (row * a.max_partitions + px) * kHeadDim + d0) = O / L;
+                if (d0 == 0)
                     a.part_lse[row * a.max_partitions + px] = (ref + flog2(L)) * kLn2;
             }
         }
     }
 }
 
+// Cache policy of the prefix pass's K/V loads: each shared block is re-read by
+// every query tile of its group, so the loads keep the default policy (L2 hits).
+#ifndef PKV_PREFIX_CPOL
+#define PKV_PREFIX_CPOL kLoadReuse
+#endif
+
+// Shared-prefix pass.  The sequences of a group share the K/V of their first
+// prefix_len positions (the same physical blocks: page "端侧 SLM 显存保活术：在 4GB
+// 内存板卡上实现轻量 PagedAttention 与 KV 缓存分块", pwwt.cn, section "共享前缀块
+// （Prefix Caching）"; blog.llmgo.top page, §四, concurrent reads of blocks whose
+// reference count exceeds 1).  One work-group takes a 16-row query tile made of
+// the G query heads of floor(16/G) consecutive sequences, one KV head and one
+// prefix partition, so each K/V sub-tile it fetches feeds the score and P.V
+// matrix-core tiles of all those sequences at once (the decode kernel pads a
+// single sequence's G rows to 16 instead).  It writes each row's fp32 partial
+// (normalised o and natural-log lse) of prefix partition pp to
+// part_o / part_lse[row][pp]; partitions past the prefix are not written.  A
+// tile whose sequences span several groups handles each group in turn.
+template <int DT, int BS, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
+void prefix_mfma_kernel(DecodeArgs a)
+{
+    __shared__ union {
+        uint16_t v[WAVES][kSub * kVStride];
+        float o[WAVES][16][kOStride];
+    } sm;
+    __shared__ float s_m[WAVES][16], s_l[WAVES][16];
+    __shared__ int64_t s_row[16];  // output row of each query column, -1 if inactive
+
+    // items: (tile, KV head, partition), partition fastest, then KV head
+    const int item = blockIdx.x;
+    const int npp = a.max_partitions;
+    const int pp = item % npp;
+    const int g = (item / npp) % a.num_kv_heads;
+    const int tile = item / (npp * a.num_kv_heads);
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const int spt = a.seqs_per_tile;
+    const int s0 = tile * spt;
+    const int s_end = min(a.num_seqs, s0 + spt);
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int col = lane & 15, grp = lane >> 4;
+    const int PP = a.prefix_part;
+
+    const uint16_t *__restrict__ kp = (const uint16_t *)a.k_pool;
+    const uint16_t *__restrict__ vp = (const uint16_t *)a.v_pool;
+    const int64_t blk_elems = (int64_t)a.num_kv_heads * BS * kHeadDim;
+    const int64_t head_off = (int64_t)g * BS * kHeadDim;
+    uint16_t *vlds = sm.v[w];
+    // query column -> (sequence, query head) of the tile
+    const int cs = s0 + col / G;
+    const int ch = g * G + col % G;
+
+    int k = group_of(a.group_cu, a.num_groups, s0);
+    for (bool more = true; more; ++k) {
+        const int ga = a.group_cu[k], gb = a.group_cu[k + 1];
+        more = gb < s_end;
+        const int plen = a.prefix_lens[k];
+        const int t0 = pp * PP;
+        if (ga == gb || t0 >= plen)
+            continue;  // uniform: an empty group, or no prefix in this partition
+        const int t1 = min(plen, t0 + PP);
+        const int32_t *__restrict__ trow = a.tables + (int64_t)ga * a.width;
+        const bool active = col < spt * G && cs < s_end && cs >= ga && cs < gb;
+
+        u32x4 qop[4];
+        {
+            const uint16_t *qrow = (const uint16_t *)a.q +
+                                   ((int64_t)cs * a.num_q_heads + ch) * kHeadDim + grp * 8;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                qop[kk] = active ? *(const u32x4 *)(qrow + kk * 32) : (u32x4){0u, 0u, 0u, 0u};
+        }
+        GqaState st;
+        st.m = kNegInf;
+        st.l = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+            st.acc[jj] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+        const int nsub = (t1 - t0 + kSub - 1) / kSub;
+        const int T = nsub > w ? (nsub - w + WAVES - 1) / WAVES : 0;
+        if (T > 0) {
+            int tb = t0 + w * kSub;
+            const int step = WAVES * kSub;
+            KOp K;
+            VRows V;
+            {
+                const SubRsrc r = sub_rsrc<BS>(sub_phys<BS>(trow, a.width, tb), kp, vp, tb, t1,
+                                               head_off, blk_elems);
+                load_k<PKV_PREFIX_CPOL>(K, r.k, lane);
+                load_v<PKV_PREFIX_CPOL>(V, r.v, lane);
+            }
+            int32_t pn = sub_phys<BS>(trow, a.width, tb + step);
+            u32x2 pb;
+            float alpha;
+            bool rs;
+            for (int j = 0; j + 1 < T; ++j) {
+                const int32_t pn2 = sub_phys<BS>(trow, a.width, tb + 2 * step);
+                const SubRsrc rn = sub_rsrc<BS>(pn, kp, vp, tb + step, t1, head_off, blk_elems);
+                rs = qk_softmax<DT, false>(st, K, qop, tb, t0, t1, lane, a.scale_log2, pb, alpha);
+                __builtin_amdgcn_sched_barrier(0);
+                load_k<PKV_PREFIX_CPOL>(K, rn.k, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                stage_v(V, vlds, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                load_v<PKV_PREFIX_CPOL>(V, rn.v, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                pv_mma<DT>(st, vlds, pb, rs, alpha, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                pn = pn2;
+                tb += step;
+            }
+            if (tb + kSub <= t1)
+                rs = qk_softmax<DT, false>(st, K, qop, tb, t0, t1, lane, a.scale_log2, pb, alpha);
+            else
+                rs = qk_softmax<DT, true>(st, K, qop, tb, t0, t1, lane, a.scale_log2, pb, alpha);
+            stage_v(V, vlds, lane);
+            pv_mma<DT>(st, vlds, pb, rs, alpha, lane);
+        }
+        st.l += xor_lane(st.l, 16);
+        st.l += xor_lane(st.l, 32);
+
+        __syncthreads();  // all waves are done with their V staging area
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+            *(f32x4 *)&sm.o[w][col][16 * jj + 4 * grp] = st.acc[jj];
+        if (grp == 0) {
+            s_m[w][col] = st.m;
+            s_l[w][col] = st.l;
+        }
+        if (tid < 16)
+            s_row[tid] = active ? (int64_t)cs * a.num_q_heads + ch : -1;
+        __syncthreads();
+        // element e: query column qi = e/32, dims d0 .. d0+3
+        for (int e = tid; e < 16 * 32; e += WAVES * 64) {
+            const int qi = e >> 5, d0 = (e & 31) * 4;
+            const int64_t row = s_row[qi];
+            if (row < 0)
+                continue;
+            float M = s_m[0][qi];
+#pragma unroll
+            for (int i = 1; i < WAVES; ++i)
+                M = fmaxf(M, s_m[i][qi]);
+            const float ref = safe_ref(M);
+            float L = 0.f;
+            f32x4 O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < WAVES; ++i) {
+                const float wgt = fexp2(s_m[i][qi] - ref);
+                L += s_l[i][qi] * wgt;
+                O += *(const f32x4 *)&sm.o[i][qi][d0] * wgt;
+            }
+            *(f32x4 *)(a.part_o + (row * a.max_partitions + pp) * kHeadDim + d0) = O / L;
+            if (d0 == 0)
+                a.part_lse[row * a.max_partitions + pp] = (ref + flog2(L)) * kLn2;
+        }
+        __syncthreads();  // LDS is reused by the next group of the tile
+    }
+}
+
 }  // namespace
 
-// Waves per work-group (tuning knob).
+// Waves per work-group (tuning knobs): the decode kernel, its suffix pass in
+// shared-prefix mode, and the prefix pass.
 #ifndef PKV_MFMA_WAVES
 #define PKV_MFMA_WAVES 4
+#endif
+#ifndef PKV_SUFFIX_WAVES
+#define PKV_SUFFIX_WAVES 4
+#endif
+#ifndef PKV_PREFIX_WAVES
+#define PKV_PREFIX_WAVES 4
 #endif
 
 template <int DT, int BS>
 static hipError_t launch_mfma_t(const DecodeArgs &a, hipStream_t stream)
 {
     constexpr int W = PKV_MFMA_WAVES;
-    if (a.partition_size > 0)
-        hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, W, true>), dim3(a.n_items), dim3(W * 64), 0,
-                           stream, a);
+    constexpr int WS = PKV_SUFFIX_WAVES;
+    if (a.group_cu)
+        hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, WS, kModeSuffix>), dim3(a.n_items),
+                           dim3(WS * 64), 0, stream, a);
+    else if (a.partition_size > 0)
+        hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, W, kModeSplit>), dim3(a.n_items),
+                           dim3(W * 64), 0, stream, a);
     else
-        hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, W, false>), dim3(a.n_items), dim3(W * 64),
-                           0, stream, a);
+        hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, W, kModeSingle>), dim3(a.n_items),
+                           dim3(W * 64), 0, stream, a);
     return hipGetLastError();
+}
+
+template <int DT, int BS>
+static hipError_t launch_prefix_t(const DecodeArgs &a, int n_items, hipStream_t stream)
+{
+    constexpr int W = PKV_PREFIX_WAVES;
+    hipLaunchKernelGGL((prefix_mfma_kernel<DT, BS, W>), dim3(n_items), dim3(W * 64), 0, stream,
+                       a);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefix_mfma(const DecodeArgs &a, int n_items, int dtype, int block_size,
+                              hipStream_t stream)
+{
+#define PKV_PF_CASE(BSV)                                                                  \
+    case BSV:                                                                             \
+        return dtype == kFp16 ? launch_prefix_t<kFp16, BSV>(a, n_items, stream)          \
+                              : launch_prefix_t<kBf16, BSV>(a, n_items, stream);
+    switch (block_size) {
+        PKV_PF_CASE(16)
+        PKV_PF_CASE(32)
+        PKV_PF_CASE(64)
+        PKV_PF_CASE(128)
+        PKV_PF_CASE(256)
+    default:
+        return hipErrorInvalidValue;
+    }
+#undef PKV_PF_CASE
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, int dtype, int block_size, hipStream_t stream)

@@ -85,10 +85,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
                                              0x00020000);
 }
 
-// 16-byte nontemporal buffer load at byte offset `off` (0 beyond the range).
+// Cache policies of the buffer loads: data read once per step streams past the
+// caches (nontemporal); data many work-groups re-read (a shared prefix) keeps the
+// default policy so that the re-reads hit L2.
+constexpr int kLoadStream = 2;  // nt
+constexpr int kLoadReuse = 0;   // default
+
+// 16-byte buffer load at byte offset `off` (0 beyond the range).
+template <int CPOL = kLoadStream>
 __device__ __forceinline__ u32x4 ldbuf(__amdgpu_buffer_rsrc_t r, int off)
 {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2 /* nt */);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL);
 }
 
 // ---- cross-lane -------------------------------------------------------------
@@ -154,6 +161,31 @@ struct DecodeArgs {
     const void *v_new;
     int64_t *slot_out;          // optional [S]
     int block_size;
+    // shared-prefix mode (null group_cu otherwise): sequences group_cu[k] ..
+    // group_cu[k+1]-1 share their first prefix_lens[k] positions, read through
+    // the table row of sequence group_cu[k]; the prefix pass leaves fp32 partials
+    // of prefix partitions of prefix_part tokens in part_o / part_lse, and the
+    // suffix pass attends over positions prefix_lens[k] .. n-1 and merges them
+    const int32_t *group_cu;    // [num_groups + 1]
+    const int32_t *prefix_lens; // [num_groups]
+    int num_groups;
+    int prefix_part;            // tokens per prefix partition (multiple of 16)
+    int seqs_per_tile;          // prefix pass: sequences per 16-row query tile
 };
+
+// Group of sequence s in shared-prefix mode: the largest k with group_cu[k] <= s.
+// `s` is uniform, so the search runs on scalar loads.
+__device__ __forceinline__ int group_of(const int32_t *__restrict__ cu, int num_groups, int s)
+{
+    int lo = 0, hi = num_groups;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cu[mid] <= s)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    return lo;
+}
 
 }  // namespace pkv

@@ -38,7 +38,8 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     declared = pkv.header_symbols()
     assert {"paged_kv_append", "paged_kv_append_tokens", "paged_kv_copy_blocks",
-            "paged_attention_decode", "paged_attention_append_decode", "paged_attention_reduce",
+            "paged_attention_decode", "paged_attention_append_decode",
+            "paged_attention_prefix_decode", "paged_attention_reduce",
             "pkv_status_string", "pkv_max_partitions"} <= set(declared)
     assert pkv.exported_symbols() == declared
 
@@ -143,6 +144,31 @@ def test_copy_blocks_argument_errors(lib):
     many = (P * 129)(*([A] * 129))
     assert call(kp=many, vp=many, L=129) == ENOTSUP            # more layers than one launch takes
     assert call(n=0, src=None, dst=None) == 0                   # nothing to copy
+
+
+@host_only
+def test_prefix_decode_argument_errors(lib):
+    f = lib.paged_attention_prefix_decode
+
+    def call(out=A, kn=None, vn=None, cu=A, pl=A, G=1, S=2, Hq=12, Hkv=2, B=16, W=5, PP=0,
+             MP=1, po=A, plse=A, dt=0):
+        return f(out, A, A, A, kn, vn, None, A, A, cu, pl, G, S, Hq, Hkv, 128, B, W, 64, 0.088,
+                 PP, MP, po, plse, dt, None)
+
+    assert call(cu=None) == EINVAL
+    assert call(pl=None) == EINVAL
+    assert call(G=0) == EINVAL
+    assert call(G=3) == EINVAL                  # more groups than sequences
+    assert call(kn=A) == EINVAL                 # k_new without v_new
+    assert call(out=None) == EINVAL
+    assert call(PP=24, MP=4) == EINVAL          # prefix partition not a multiple of 16
+    assert call(PP=16, MP=4) == EWORKSPACE      # 80 positions need 5 partitions of 16
+    assert call(MP=0) == EWORKSPACE
+    assert call(po=None) == EWORKSPACE
+    assert call(Hq=34) == ENOTSUP               # group of 17 query heads
+    assert call(B=8) == ENOTSUP
+    assert call(cu=P((1 << 20) + 2)) == EINVAL  # misaligned group offsets
+    assert call(S=0, G=1) == 0                  # nothing to do
 
 
 @host_only

@@ -57,6 +57,7 @@ class Config:
     # cycled working set is well above the 256 MB last-level cache
     bench_distinct_layers: int = 1
     bench_partition_size: int = 0
+    bench_prefix_partition: int = 0  # prefix partition of the shared-prefix path
     notes: str = field(default="", compare=False)
 
     @property
