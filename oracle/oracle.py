@@ -76,6 +76,11 @@ def lib():
         L.oracle_append.restype = C.c_int
         L.oracle_append_tokens.argtypes = [P, P, P, P, P, P, P] + [i64] * 6
         L.oracle_append_tokens.restype = C.c_int
+        L.oracle_locate_slotted.argtypes = [P, i64, i64, i64, i64, P, P]
+        L.oracle_locate_slotted.restype = C.c_int
+        L.oracle_attention_slotted.argtypes = [P, P, P, P, P, P] + [i64] * 7 + [C.c_double,
+                                                                                C.c_int, C.c_int]
+        L.oracle_attention_slotted.restype = C.c_int
         L.oracle_copy_blocks.argtypes = [P, P, P, P] + [i64] * 5
         L.oracle_copy_blocks.restype = C.c_int
         L.oracle_attention.argtypes = [P, P, P, P, P, P] + [i64] * 7 + [C.c_double, C.c_int,
@@ -180,6 +185,32 @@ def attention(q, k_pool, v_pool, tables, lens, num_kv_heads, block_size, num_blo
                                 block_size, tables.shape[1], num_blocks, float(scale),
                                 DTYPES[dtype], nthreads)
     _check(rc, "attention")
+    return out
+
+
+def locate_slotted(segs, block_size: int, num_blocks: int, t: int):
+    """(physical block, in-block offset) of logical token t of a sequence given as
+    (block id, slot offset, length) segments."""
+    segs = _c(segs, np.int32).reshape(-1, 3)
+    phys, off = C.c_int64(), C.c_int64()
+    rc = lib().oracle_locate_slotted(_p(segs), segs.shape[0], block_size, num_blocks, t,
+                                     C.byref(phys), C.byref(off))
+    _check(rc, "locate_slotted")
+    return phys.value, off.value
+
+
+def attention_slotted(q, k_pool, v_pool, segs, num_segs, num_kv_heads, block_size, num_blocks,
+                      scale, dtype: str, nthreads: int = 0) -> np.ndarray:
+    """Decode attention of sequences given as segment lists: segs [S][max_segs][3]
+    (block id, slot offset, length), num_segs [S]."""
+    S, Hq, D = q.shape
+    segs = _c(segs, np.int32)
+    out = np.empty((S, Hq, D), dtype=np.float64)
+    rc = lib().oracle_attention_slotted(_p(out), _p(_c(q, np.uint16)), _p(k_pool), _p(v_pool),
+                                        _p(segs), _p(_c(num_segs, np.int32)), S, Hq,
+                                        num_kv_heads, D, block_size, segs.shape[1], num_blocks,
+                                        float(scale), DTYPES[dtype], nthreads)
+    _check(rc, "attention_slotted")
     return out
 
 

@@ -37,6 +37,12 @@
  *    pointed at the copy (blog.llmgo.top page, §四, steps 1-3 of the
  *    copy-on-write mechanism).  Every element of every head of the block is
  *    copied, in K and in V.
+ *  - Slotted blocks: a short radix-tree node is packed as a slot inside a shared
+ *    block and addressed by a (block id, slot offset, length) triple (mhpq.cn
+ *    page on Radix-Tree fragmentation, sections "Slotted Block 分槽与微块共享架构"
+ *    and "核心设计原则").  A sequence's KV is the concatenation of its segments in
+ *    order; logical token t lies in the segment whose running start s satisfies
+ *    s <= t < s + length, at in-block offset slot_offset + (t - s).
  *  - Partials and merge: attention over the token range of one partition, its
  *    log-sum-exp, and the exact log-sum-exp combination of partitions.  The
  *    pages do not describe partitions; the merge is the algebraic identity
@@ -455,4 +461,110 @@ int oracle_merge(double *out, const double *part_o, const double *part_lse,
             o[d] /= wsum;
     }
     return OR_OK;
+}
+
+/* ---- slotted segments ------------------------------------------------------ */
+/* Physical block and in-block offset of logical token t of a sequence whose KV is
+ * the segments segs[0..num_segs) = (block id, slot offset, length) triples. */
+int oracle_locate_slotted(const int32_t *segs, int64_t num_segs, int64_t block_size,
+                          int64_t num_blocks, int64_t t, int64_t *phys, int64_t *off)
+{
+    if (t < 0 || block_size <= 0 || num_segs < 0)
+        return OR_EARG;
+    int64_t start = 0;
+    for (int64_t i = 0; i < num_segs; ++i) {
+        int64_t blk = segs[3 * i], so = segs[3 * i + 1], len = segs[3 * i + 2];
+        if (so < 0 || len < 0 || so + len > block_size)
+            return OR_EOFFSET;
+        if (t < start + len) {
+            if (blk < 0 || blk >= num_blocks)
+                return OR_ETABLE;
+            *phys = blk;
+            *off = so + (t - start);
+            return OR_OK;
+        }
+        start += len;
+    }
+    return OR_ETABLE;  /* t is past the sequence */
+}
+
+/* Decode attention over slotted segments: out[s][h] = softmax(scale q.K^T) V over
+ * the n = sum of lengths tokens of sequence s, in logical order, two-pass fp64
+ * softmax as in oracle_attention.  segs: [num_seqs][max_segs][3]. */
+int oracle_attention_slotted(double *out, const uint16_t *q, const uint16_t *k_pool,
+                             const uint16_t *v_pool, const int32_t *segs,
+                             const int32_t *num_segs, int64_t num_seqs, int64_t num_q_heads,
+                             int64_t num_kv_heads, int64_t head_dim, int64_t block_size,
+                             int64_t max_segs, int64_t num_blocks, double scale, int dtype,
+                             int nthreads)
+{
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads || head_dim <= 0 ||
+        max_segs < 0)
+        return OR_EARG;
+    const int64_t group = num_q_heads / num_kv_heads;
+    int err = OR_OK;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t sh = 0; sh < num_seqs * num_q_heads; ++sh) {
+        const int64_t s = sh / num_q_heads, h = sh % num_q_heads, g = h / group;
+        const int32_t *row = segs + s * max_segs * 3;
+        const int64_t ns = num_segs[s];
+        double *o = out + sh * head_dim;
+        const uint16_t *qr = q + sh * head_dim;
+        if (ns < 0 || ns > max_segs) {
+#pragma omp atomic write
+            err = OR_EARG;
+            continue;
+        }
+        int64_t n = 0;
+        for (int64_t i = 0; i < ns; ++i)
+            n += row[3 * i + 2];
+        double *z = malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        if (!z) {
+#pragma omp atomic write
+            err = OR_ENOMEM;
+            continue;
+        }
+        double m = -INFINITY;
+        int bad = 0;
+        for (int64_t t = 0; t < n && !bad; ++t) {
+            int64_t phys, off;
+            if (oracle_locate_slotted(row, ns, block_size, num_blocks, t, &phys, &off)) {
+                bad = 1;
+                break;
+            }
+            const uint16_t *k = k_pool + oracle_elem_offset(phys, g, off, 0, num_kv_heads,
+                                                            block_size, head_dim);
+            double acc = 0.0;
+            for (int64_t d = 0; d < head_dim; ++d)
+                acc += widen(qr[d], dtype) * widen(k[d], dtype);
+            z[t] = scale * acc;
+            if (z[t] > m)
+                m = z[t];
+        }
+        for (int64_t d = 0; d < head_dim; ++d)
+            o[d] = 0.0;
+        if (bad) {
+#pragma omp atomic write
+            err = OR_ETABLE;
+            free(z);
+            continue;
+        }
+        double l = 0.0;
+        for (int64_t t = 0; t < n; ++t) {
+            int64_t phys, off;
+            oracle_locate_slotted(row, ns, block_size, num_blocks, t, &phys, &off);
+            const uint16_t *v = v_pool + oracle_elem_offset(phys, g, off, 0, num_kv_heads,
+                                                            block_size, head_dim);
+            const double w = exp(z[t] - m);
+            l += w;
+            for (int64_t d = 0; d < head_dim; ++d)
+                o[d] += w * widen(v[d], dtype);
+        }
+        if (n > 0)
+            for (int64_t d = 0; d < head_dim; ++d)
+                o[d] /= l;
+        free(z);
+    }
+    return err;
 }

@@ -26,15 +26,31 @@ MUTANTS = {
     "merge_weight_sign": ("double w = exp(lse[p] - M);", "double w = exp(M - lse[p]);"),
     "lse_missing_log_sum": ("*lse = m + log(l);", "*lse = m;"),
     "fp16_exponent_bias": ("e - 25);", "e - 24);"),
-    "value_head_zero": ("const uint16_t *v = v_pool + oracle_elem_offset(phys, g, off,",
-                        "const uint16_t *v = v_pool + oracle_elem_offset(phys, 0, off,"),
-    "missing_normalisation": ("        o[d] /= l;\n", "        o[d] /= 1.0;\n"),
+    "value_head_zero": ("const uint16_t *v = v_pool + oracle_elem_offset(phys, g, off, 0, "
+                        "num_kv_heads,\n                                                        "
+                        "block_size, head_dim);\n        double w = exp(z[t - t0] - m);",
+                        "const uint16_t *v = v_pool + oracle_elem_offset(phys, 0, off, 0, "
+                        "num_kv_heads,\n                                                        "
+                        "block_size, head_dim);\n        double w = exp(z[t - t0] - m);"),
+    "missing_normalisation": ("        o[d] /= l;\n    *lse = m + log(l);",
+                              "        o[d] /= 1.0;\n    *lse = m + log(l);"),
+    "slotted_value_head_zero": ("block_size, head_dim);\n            const double w = exp(z[t] - m);",
+                                "block_size, head_dim) - g * block_size * head_dim;\n"
+                                "            const double w = exp(z[t] - m);"),
+    "slotted_missing_normalisation": ("            for (int64_t d = 0; d < head_dim; ++d)\n"
+                                      "                o[d] /= l;",
+                                      "            for (int64_t d = 0; d < head_dim; ++d)\n"
+                                      "                o[d] /= 1.0;"),
     "last_token_skipped": ("for (int64_t t = t0; t < t1; ++t) {\n        int64_t phys, off;\n        int rc",
                            "for (int64_t t = t0; t < t1 - 1; ++t) {\n        int64_t phys, off;\n        int rc"),
     "copy_direction_swapped": ("k_pool[to] = k_pool[from];", "k_pool[from] = k_pool[to];"),
     "copy_skips_values": ("v_pool[to] = v_pool[from];", ""),
     "copy_last_row_dropped": ("for (int64_t off = 0; off < block_size; ++off)",
                               "for (int64_t off = 0; off < block_size - 1; ++off)"),
+    "slot_offset_dropped": ("*off = so + (t - start);", "*off = (t - start);"),
+    "segment_end_inclusive": ("if (t < start + len) {", "if (t <= start + len) {"),
+    "segment_start_not_advanced": ("        start += len;\n    }\n    return OR_ETABLE;",
+                                   "    }\n    return OR_ETABLE;"),
 }
 
 
@@ -51,7 +67,8 @@ def _run_pins(lib_path):
     env = dict(os.environ, PKV_ORACLE_LIB=lib_path, OMP_NUM_THREADS="2")
     cmd = [sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
            os.path.join(ROOT, "tests", "test_oracle_pins.py"),
-           os.path.join(ROOT, "tests", "test_oracle_cow.py")]
+           os.path.join(ROOT, "tests", "test_oracle_cow.py"),
+           os.path.join(ROOT, "tests", "test_oracle_slotted.py")]
     return subprocess.run(cmd, env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
 
 
