@@ -21,7 +21,8 @@ events, and the fp64 CPU oracle timed on a bounded sample on the host cores.
 `--op append_tokens` and `--op copy_blocks` instead time the block-level writers
 on the same workload shapes (the prefill scatter of every layer, and a
 copy-on-write fork of every sequence in every layer) and print one line each,
-with GB/s as the value.
+with GB/s as the value; `--op slotted` times decode over a radix-tree batch
+addressed by slotted (block, offset, length) segments.
 """
 from __future__ import annotations
 
@@ -61,10 +62,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c3", help="workload key (c1a c1b c2 c3 c4 c5)")
-    ap.add_argument("--op", default="step", choices=["step", "append_tokens", "copy_blocks"],
+    ap.add_argument("--op", default="step",
+                    choices=["step", "append_tokens", "copy_blocks", "slotted"],
                     help="step: the decode step (default, the headline line); append_tokens: "
                          "the prefill scatter of the workload's histories into every layer; "
-                         "copy_blocks: copy-on-write copies of the workload's forks")
+                         "copy_blocks: copy-on-write copies of the workload's forks; slotted: "
+                         "decode of a radix-tree batch addressed by slotted segments")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="override the workload's split-context partition size (0 = single pass)")
     ap.add_argument("--distinct", type=int, default=None, help="override distinct layer pools")
@@ -88,16 +91,21 @@ def parse():
 
 # Source files whose contents determine each kernel's memory traffic.
 TRAFFIC_SOURCES = {
-    "decode": ["paged_kv_cache_09_amd/csrc/decode_g1.hip",
-               "paged_kv_cache_09_amd/csrc/decode_mfma.hip",
+    "decode_g1": ["paged_kv_cache_09_amd/csrc/decode_g1.hip",
+                  "paged_kv_cache_09_amd/csrc/pkv_device.h"],
+    "decode_mfma": ["paged_kv_cache_09_amd/csrc/decode_mfma.hip",
+                    "paged_kv_cache_09_amd/csrc/pkv_device.h"],
+    "prefix": ["paged_kv_cache_09_amd/csrc/decode_mfma.hip",
                "paged_kv_cache_09_amd/csrc/pkv_device.h"],
+    "slotted": ["paged_kv_cache_09_amd/csrc/decode_mfma.hip",
+                "paged_kv_cache_09_amd/csrc/pkv_device.h"],
     "append_tokens": ["paged_kv_cache_09_amd/csrc/append.hip"],
     "copy_blocks": ["paged_kv_cache_09_amd/csrc/copy.hip",
                     "paged_kv_cache_09_amd/csrc/pkv_device.h"],
 }
 
 
-def kernel_source_hash(kind: str = "decode") -> str:
+def kernel_source_hash(kind: str) -> str:
     import hashlib
     h = hashlib.sha256()
     for f in TRAFFIC_SOURCES[kind]:
@@ -106,11 +114,11 @@ def kernel_source_hash(kind: str = "decode") -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, kind: str = "decode"):
-    """HBM bytes per launch from the committed counter record of this kernel and
-    workload (profiles/<kernel>_<workload>_traffic.json), or None when there is
-    none or the kernel sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"{kind}_{workload}_traffic.json")
+def measured_traffic(stem: str, kind: str):
+    """HBM bytes per launch from the committed counter record
+    profiles/<stem>_traffic.json, or None when there is none or the sources of
+    that kernel (kind) changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{stem}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -175,6 +183,8 @@ def main():
         bench_append_tokens(args)
     elif args.op == "copy_blocks":
         bench_copy_blocks(args)
+    elif args.op == "slotted":
+        bench_slotted(args)
     else:
         bench_step(args)
 
@@ -356,7 +366,9 @@ def bench_step(args):
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None if prefix else measured_traffic(cfg.key, "decode"),
+            "traffic": (measured_traffic(f"prefix_{cfg.key}", "prefix") if prefix else
+                        measured_traffic(f"decode_{cfg.key}",
+                                         "decode_g1" if Hq == cfg.num_kv_heads else "decode_mfma")),
             "bytes_per_launch": kernel_bytes,
             "avg_launch_ms": round(decode_ms, 5),
         },
@@ -422,7 +434,7 @@ def bench_append_tokens(args):
     meta = 8 * (len(w.seg_cu)) + 4 * len(w.seg_start) + 4 * nblk
     nbytes = 2 * rows + meta                                      # read + write
     roof = roofline("paged_kv_append_tokens", nbytes, ms,
-                    measured_traffic(cfg.key, "append_tokens"))
+                    measured_traffic(f"append_tokens_{cfg.key}", "append_tokens"))
     config = {"workload": f"{cfg.key} prefill scatter: {cfg.title}", "runs": int(len(w.seg_start)),
               "tokens_per_layer": T, "layers": cfg.num_layers, "kv_heads": cfg.num_kv_heads,
               "head_dim": cfg.head_dim, "block_size": cfg.block_size, "distinct_layer_pools": R,
@@ -480,7 +492,8 @@ def bench_copy_blocks(args):
     ms = time_launches(one, args.steps, warm=args.warmup)
     slab = cfg.num_kv_heads * cfg.block_size * cfg.head_dim * cfg.elem_bytes
     nbytes = 2 * (S * L * 2 * slab) + 8 * S                        # read + write, pair ids
-    roof = roofline("paged_kv_copy_blocks", nbytes, ms, measured_traffic(cfg.key, "copy_blocks"))
+    roof = roofline("paged_kv_copy_blocks", nbytes, ms,
+                    measured_traffic(f"copy_blocks_{cfg.key}", "copy_blocks"))
     config = {"workload": f"{cfg.key} fork: every sequence copies one block in all layers "
                           f"({cfg.title})", "pairs": S, "layers": L,
               "block_bytes_per_pool": slab, "pool_blocks_per_layer": NB, "launches": 1}
@@ -503,6 +516,85 @@ def bench_copy_blocks(args):
                                 "unit": "GB/s", "cores": 1, "kind": "oracle",
                                 "sample": f"{S} pairs x {Ls} of {L} layers, {reps} repetitions, "
                                           f"{spent:.1f} s, single-threaded C"}
+    print(json.dumps(line), flush=True)
+
+
+def bench_slotted(args):
+    """Decode of a radix-tree batch at the workload's shapes (a shared 512-token
+    root, shared short nodes packed as slots, a private leaf per sequence), each
+    sequence given as (block, slot offset, length) segments; one
+    paged_attention_decode_slotted launch per step, cycling through R distinct
+    batches.  value = sequences / step time; the roofline counts each node's
+    K/V rows once (unique bytes)."""
+    import torch
+    import paged_kv_cache_09_amd as pkv
+    from workloads import get_config
+    from workloads.slotted import make_slotted_workload
+
+    cfg = get_config(args.config)
+    R = args.distinct or 4
+    dev = torch.device("cuda:0")
+    tdt = {"fp16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(tdt)
+
+    batches = []
+    for d in range(R):
+        w = make_slotted_workload(cfg, seed_id=1000 * cfg.cfg_id + d)
+        kr, vr, cu, st, tb = w.runs()
+        kp = torch.zeros(w.pool_shape(), dtype=tdt, device=dev)
+        vp = torch.zeros_like(kp)
+        pkv.paged_kv_append_tokens(kp, vp, up(kr), up(vr), torch.from_numpy(cu).to(dev),
+                                   torch.from_numpy(st).to(dev), torch.from_numpy(tb).to(dev))
+        batches.append(dict(w=w, k=kp, v=vp, q=up(w.q),
+                            segs=torch.from_numpy(w.segments).to(dev),
+                            ns=torch.from_numpy(w.num_segments).to(dev)))
+    torch.cuda.synchronize()
+    w0 = batches[0]["w"]
+    S, Hq, D = len(w0.paths), cfg.num_q_heads, cfg.head_dim
+    out = torch.empty((S, Hq, D), dtype=tdt, device=dev)
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    it = iter(range(1 << 30))
+
+    def one():
+        b = batches[next(it) % R]
+        pkv.paged_attention_decode_slotted(out, b["q"], b["k"], b["v"], b["segs"], b["ns"],
+                                           scale=scale)
+
+    ms = time_launches(one, args.steps * 4, warm=args.warmup * 4)
+    e, Hkv = cfg.elem_bytes, cfg.num_kv_heads
+    row = 2 * Hkv * D * e                                   # K and V of one token, all heads
+    nseg = int(w0.num_segments.sum())
+    unique = w0.unique_tokens() * row + 2 * S * Hq * D * e + 12 * nseg + 4 * S
+    logical = int(w0.lengths().sum()) * row + 2 * S * Hq * D * e + 12 * nseg + 4 * S
+    roof = roofline("paged_attention_decode_slotted", unique, ms,
+                    measured_traffic(f"slotted_{cfg.key}", "slotted"))
+    config = {"workload": f"{cfg.key} radix-tree batch in slotted blocks ({cfg.title})",
+              "num_seqs": S, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
+              "block_size": cfg.block_size, "mean_context": round(float(w0.lengths().mean()), 1),
+              "unique_tokens": w0.unique_tokens(), "nodes": len(w0.node_k),
+              "max_segments": int(w0.segments.shape[1]), "distinct_batches": R, "launches": 1}
+    line = _side_line("slotted-segment decode tokens/s and unique-byte HBM GB/s, 1 GPU",
+                      S / (ms * 1e-3), "tokens/s", args, cfg, cfg.dtype, config, roof,
+                      {"logical_bytes_per_launch": logical})
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        kr, vr, cu, st, tb = w0.runs()
+        kp, vp = O.new_pools(w0.num_blocks, Hkv, cfg.block_size, D, 0)
+        O.append_tokens(kp, vp, kr, vr, cu, st, tb, cfg.block_size, w0.num_blocks)
+        threads = O.max_threads(0)
+        reps, spent = 0, 0.0
+        while reps == 0 or (spent < args.cpu_seconds and reps < 20):
+            t = time.perf_counter()
+            O.attention_slotted(w0.q, kp, vp, w0.segments, w0.num_segments, Hkv,
+                                cfg.block_size, w0.num_blocks, scale, cfg.dtype, threads)
+            spent += time.perf_counter() - t
+            reps += 1
+        line["cpu_baseline"] = {"value": round(S * reps / spent, 3), "unit": "tokens/s",
+                                "cores": threads, "kind": "oracle",
+                                "sample": f"the whole batch ({S} sequences x {Hq} heads, fp64), "
+                                          f"{reps} repetitions, {spent:.1f} s"}
     print(json.dumps(line), flush=True)
 
 

@@ -250,6 +250,36 @@ int paged_attention_prefix_decode(void *out, const void *q, void *k_pool, void *
                                   float *part_lse, int dtype, void *stream);
 
 /*
+ * paged_attention_decode_slotted -- decode attention over slotted segments.
+ *
+ * Radix-tree prefix caches pack short nodes as slots of shared blocks: a node
+ * of fewer tokens than a block occupies `length` consecutive positions starting
+ * at `slot_offset` of some block, and is addressed by the triple (block_id,
+ * slot_offset, length) (mhpq.cn page on Radix-Tree fragmentation, sections
+ * "Slotted Block 分槽与微块共享架构" and "核心设计原则").  Here each sequence is
+ * the concatenation of its segments; logical token t lies in the segment whose
+ * running start s satisfies s <= t < s + length, at in-block offset
+ * slot_offset + (t - s), of physical block block_id.  A whole block is the
+ * segment (id, 0, block_size), so an ordinary block table is a special case.
+ * out[s][h] = softmax(scale * q.K^T) V over those n = sum(length) tokens; n = 0
+ * gives zeros.  Single pass; all head-group sizes run on the matrix-core path.
+ *
+ *   segments       device int32 [num_seqs][max_segments][3]: (block_id,
+ *                  slot_offset, length); only the first num_segments[s] are read
+ *   num_segments   device int32 [num_seqs], 0 .. max_segments
+ *   out, q         as for paged_attention_decode
+ * Caller contract (checked with PKV_DEBUG_CHECK=1): block_id in [0, num_blocks),
+ * slot_offset >= 0, length >= 0, slot_offset + length <= block_size.  Rows of a
+ * block outside a sequence's segments are never read.
+ */
+int paged_attention_decode_slotted(void *out, const void *q, const void *k_pool,
+                                   const void *v_pool, const int32_t *segments,
+                                   const int32_t *num_segments, int num_seqs, int num_q_heads,
+                                   int num_kv_heads, int head_dim, int block_size,
+                                   int max_segments, int64_t num_blocks, float scale, int dtype,
+                                   void *stream);
+
+/*
  * paged_attention_reduce -- log-sum-exp merge of split-context partitions.
  *
  * For each (s, h) with P = partition_size and np = ceil(n/P) partitions:

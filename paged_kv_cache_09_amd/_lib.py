@@ -63,6 +63,9 @@ def load():
                                                 i32, i32, i32, i32, i64, f32, i32, i32, P, P,
                                                 i32, P]
     L.paged_attention_prefix_decode.restype = i32
+    L.paged_attention_decode_slotted.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32,
+                                                 i64, f32, i32, P]
+    L.paged_attention_decode_slotted.restype = i32
     L.paged_attention_reduce.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, P]
     L.paged_attention_reduce.restype = i32
     _lib = L
@@ -266,6 +269,25 @@ def paged_attention_prefix_decode(out, q, k_pool, v_pool, block_tables, context_
         int(prefix_partition), part_o.shape[2], _p(part_o), _p(part_lse), _dtype_code(q),
         _stream(dev))
     _check(rc, "paged_attention_prefix_decode")
+
+
+def paged_attention_decode_slotted(out, q, k_pool, v_pool, segments, num_segments,
+                                   scale: Optional[float] = None):
+    """Decode attention of sequences given as (block_id, slot_offset, length)
+    segment lists: segments int32 [S][max_segments][3], num_segments int32 [S]."""
+    dev = _dev(out, q, k_pool, v_pool, segments, num_segments)
+    _int(segments, "i32", "segments")
+    _int(num_segments, "i32", "num_segments")
+    if segments.dim() != 3 or segments.shape[2] != 3:
+        raise ValueError("segments must be [num_seqs][max_segments][3]")
+    NB, Hkv, B, D = k_pool.shape
+    S, Hq, _ = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    rc = load().paged_attention_decode_slotted(
+        _p(out), _p(q), _p(k_pool), _p(v_pool), _p(segments), _p(num_segments), S, Hq, Hkv, D,
+        B, segments.shape[1], NB, float(scale), _dtype_code(q), _stream(dev))
+    _check(rc, "paged_attention_decode_slotted")
 
 
 def paged_attention_reduce(out, part_o, part_lse, context_lens, partition_size: int):

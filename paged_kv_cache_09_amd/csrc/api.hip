@@ -89,6 +89,26 @@ __global__ void debug_groups_kernel(const int32_t *cu, const int32_t *prefix_len
             atomicOr(&g_debug_flag, 32);
 }
 
+// Slotted segment lists: counts within [0, max_segments], every segment inside
+// the pool and inside its block.
+__global__ void debug_segments_kernel(const int32_t *segs, const int32_t *nsegs, int num_seqs,
+                                      int max_segs, int block_size, int64_t num_blocks)
+{
+    const int s = blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= num_seqs)
+        return;
+    const int n = nsegs[s];
+    if (n < 0 || n > max_segs) {
+        atomicOr(&g_debug_flag, 64);
+        return;
+    }
+    for (int i = 0; i < n; ++i) {
+        const int32_t *t = segs + ((int64_t)s * max_segs + i) * 3;
+        if (t[0] < 0 || t[0] >= num_blocks || t[1] < 0 || t[2] < 0 || t[1] + t[2] > block_size)
+            atomicOr(&g_debug_flag, 64);
+    }
+}
+
 // Copy pairs: ids inside the pool; a destination may be neither another pair's
 // destination nor any pair's source (the result would depend on copy order).
 __global__ void debug_copies_kernel(const int32_t *src, const int32_t *dst, int num_pairs,
@@ -151,6 +171,17 @@ int debug_check_groups(const int32_t *group_cu, const int32_t *prefix_lens,
     hipLaunchKernelGGL(debug_clear_kernel, dim3(1), dim3(1), 0, stream);
     hipLaunchKernelGGL(debug_groups_kernel, dim3((num_groups + 255) / 256), dim3(256), 0, stream,
                        group_cu, prefix_lens, lens, num_groups, num_seqs, extra);
+    if (hipGetLastError() != hipSuccess)
+        return PKV_ELAUNCH;
+    return read_debug_flag(stream);
+}
+
+int debug_check_segments(const int32_t *segs, const int32_t *nsegs, int num_seqs, int max_segs,
+                         int block_size, int64_t num_blocks, hipStream_t stream)
+{
+    hipLaunchKernelGGL(debug_clear_kernel, dim3(1), dim3(1), 0, stream);
+    hipLaunchKernelGGL(debug_segments_kernel, dim3((num_seqs + 255) / 256), dim3(256), 0, stream,
+                       segs, nsegs, num_seqs, max_segs, block_size, num_blocks);
     if (hipGetLastError() != hipSuccess)
         return PKV_ELAUNCH;
     return read_debug_flag(stream);
@@ -219,8 +250,8 @@ const char *pkv_status_string(int status)
     case PKV_ELAUNCH:
         return "kernel launch failed";
     case PKV_EDEVICE:
-        return "device-side check failed (context length, block-table entry, copy pair or "
-               "prefix group out of range, or overlapping copy pairs)";
+        return "device-side check failed (context length, block-table entry, segment, copy "
+               "pair or prefix group out of range, or overlapping copy pairs)";
     default:
         return "unknown status";
     }
@@ -536,6 +567,60 @@ int paged_attention_prefix_decode(void *out, const void *q, void *k_pool, void *
                        block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                        block_size, max_blocks_per_seq, num_blocks, scale, prefix_partition,
                        max_partitions, part_o, part_lse, dtype, stream, pg);
+}
+
+int paged_attention_decode_slotted(void *out, const void *q, const void *k_pool,
+                                   const void *v_pool, const int32_t *segments,
+                                   const int32_t *num_segments, int num_seqs, int num_q_heads,
+                                   int num_kv_heads, int head_dim, int block_size,
+                                   int max_segments, int64_t num_blocks, float scale, int dtype,
+                                   void *stream)
+{
+    if (!out || !q || !k_pool || !v_pool || !segments || !num_segments)
+        return PKV_EINVAL;
+    if (num_seqs < 0 || num_q_heads <= 0 || max_segments <= 0)
+        return PKV_EINVAL;
+    int rc = check_pool_shape(num_kv_heads, head_dim, block_size, 1, num_blocks, dtype);
+    if (rc)
+        return rc;
+    if (num_q_heads % num_kv_heads != 0)
+        return PKV_EINVAL;
+    if (num_q_heads / num_kv_heads > 16)
+        return PKV_ENOTSUP;
+    if (!(scale == scale) || __builtin_isinf(scale))
+        return PKV_EINVAL;
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || ((uintptr_t)out & 7u) ||
+        ((uintptr_t)segments & 3u) || ((uintptr_t)num_segments & 3u))
+        return PKV_EINVAL;
+    if ((int64_t)max_segments * 3 * num_seqs > ((int64_t)1 << 40))
+        return PKV_EINVAL;
+    const int64_t items = (int64_t)num_seqs * num_kv_heads;
+    if (items > INT32_MAX)
+        return PKV_EINVAL;
+    if (items == 0)
+        return PKV_OK;
+    hipStream_t st = (hipStream_t)stream;
+    if (debug_enabled()) {
+        rc = pkv::debug_check_segments(segments, num_segments, num_seqs, max_segments, block_size,
+                                       num_blocks, st);
+        if (rc)
+            return rc;
+    }
+    pkv::DecodeArgs a{};
+    a.out = out;
+    a.q = q;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.n_items = (int)items;
+    a.scale_log2 = scale * pkv::kLog2e;
+    a.block_size = block_size;
+    a.segments = segments;
+    a.num_segments = num_segments;
+    a.max_segments = max_segments;
+    return launch_status(pkv::launch_slotted_mfma(a, dtype, block_size, st));
 }
 
 int paged_attention_reduce(void *out, const float *part_o, const float *part_lse,

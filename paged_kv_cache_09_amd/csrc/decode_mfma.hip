@@ -691,6 +691,181 @@ void prefix_mfma_kernel(DecodeArgs a)
     }
 }
 
+// Slotted segments.  A short radix-tree node is packed as a slot of a shared
+// block and addressed by a (block id, slot offset, length) triple (mhpq.cn page
+// on Radix-Tree fragmentation, sections "Slotted Block 分槽与微块共享架构" and
+// "核心设计原则"); a sequence is the concatenation of its segments.  One
+// work-group per (sequence, KV head): per round of up to 64 segments, the first
+// wave turns them into sub-tile descriptors (block, first row, row count <= 16;
+// a segment of L rows gives ceil(L/16) of them) with a wave prefix sum and parks
+// them in LDS; then every wave streams its share of the sub-tiles through the
+// same score / softmax / P.V path as the decode kernel.  Each sub-tile's buffer
+// range covers only its segment's rows, so rows of other slots in the block are
+// never fetched (their loads return zeros) and are masked out of the softmax.
+constexpr int kSegRound = 64;
+constexpr int kMaxRoundSubs = kSegRound * 16;  // a 256-row segment gives 16 sub-tiles
+
+// Buffer resources of slotted sub-tile jx: its block, first row and row count
+// come from the LDS descriptors (made uniform for the scalar descriptor).
+__device__ __forceinline__ SubRsrc slot_rsrc(const int32_t *s_phys, const int32_t *s_rows, int jx,
+                                             const uint16_t *kp, const uint16_t *vp,
+                                             int64_t head_off, int64_t blk_elems)
+{
+    const int32_t phys = __builtin_amdgcn_readfirstlane(s_phys[jx]);
+    const int32_t rc = __builtin_amdgcn_readfirstlane(s_rows[jx]);
+    const int64_t b = (int64_t)phys * blk_elems + head_off + (int64_t)(rc >> 8) * kHeadDim;
+    SubRsrc r;
+    r.k = make_rsrc(kp + b, (rc & 0xff) * kHeadDim * 2);
+    r.v = make_rsrc(vp + b, (rc & 0xff) * kHeadDim * 2);
+    return r;
+}
+
+template <int DT, int BS, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(3)))
+void slotted_mfma_kernel(DecodeArgs a)
+{
+    __shared__ union {
+        uint16_t v[WAVES][kSub * kVStride];
+        float o[WAVES][16][kOStride];
+    } sm;
+    __shared__ float s_m[WAVES][16], s_l[WAVES][16];
+    __shared__ int32_t s_phys[kMaxRoundSubs];
+    __shared__ int32_t s_rows[kMaxRoundSubs];  // first row << 8 | row count
+    __shared__ int32_t s_total;
+
+    const int item = blockIdx.x;
+    const int g = item % a.num_kv_heads;
+    const int s = item / a.num_kv_heads;
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int col = lane & 15, grp = lane >> 4;
+
+    const uint16_t *__restrict__ kp = (const uint16_t *)a.k_pool;
+    const uint16_t *__restrict__ vp = (const uint16_t *)a.v_pool;
+    const int64_t blk_elems = (int64_t)a.num_kv_heads * BS * kHeadDim;
+    const int64_t head_off = (int64_t)g * BS * kHeadDim;
+    const int32_t *__restrict__ segs = a.segments + (int64_t)s * a.max_segments * 3;
+    const int nseg = a.num_segments[s];
+    uint16_t *vlds = sm.v[w];
+
+    u32x4 qop[4];
+    {
+        const uint16_t *qrow = (const uint16_t *)a.q +
+                               ((int64_t)s * a.num_q_heads + (int64_t)g * G + col) * kHeadDim +
+                               grp * 8;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            qop[kk] = col < G ? *(const u32x4 *)(qrow + kk * 32) : (u32x4){0u, 0u, 0u, 0u};
+    }
+    GqaState st;
+    st.m = kNegInf;
+    st.l = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+        st.acc[jj] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    for (int base = 0; base < nseg; base += kSegRound) {
+        if (w == 0) {
+            const int i = base + lane;
+            int32_t blk = 0, off = 0, len = 0;
+            if (i < nseg) {
+                blk = segs[3 * i];
+                // a segment never reaches outside its block, whatever the caller passed
+                off = min(max(segs[3 * i + 1], 0), BS);
+                len = min(max(segs[3 * i + 2], 0), BS - off);
+            }
+            const int c = (len + kSub - 1) / kSub;
+            int incl = c;  // inclusive prefix sum over the wave
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int up = __shfl_up(incl, d, 64);
+                if (lane >= d)
+                    incl += up;
+            }
+            for (int k = 0; k < c; ++k) {
+                s_phys[incl - c + k] = blk;
+                s_rows[incl - c + k] = ((off + kSub * k) << 8) | min(kSub, len - kSub * k);
+            }
+            if (lane == 63)
+                s_total = incl;
+        }
+        __syncthreads();
+        const int total = s_total;
+        const int T = total > w ? (total - w + WAVES - 1) / WAVES : 0;
+        if (T > 0) {
+            int j = w;
+            KOp K;
+            VRows V;
+            {
+                const SubRsrc r = slot_rsrc(s_phys, s_rows, j, kp, vp, head_off, blk_elems);
+                load_k(K, r.k, lane);
+                load_v(V, r.v, lane);
+            }
+            u32x2 pb;
+            float alpha;
+            bool rs;
+            for (int it = 0; it + 1 < T; ++it) {
+                const int cnt = __builtin_amdgcn_readfirstlane(s_rows[j]) & 0xff;
+                const SubRsrc rn =
+                    slot_rsrc(s_phys, s_rows, j + WAVES, kp, vp, head_off, blk_elems);
+                rs = qk_softmax<DT, true>(st, K, qop, 0, 0, cnt, lane, a.scale_log2, pb, alpha);
+                __builtin_amdgcn_sched_barrier(0);
+                load_k(K, rn.k, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                stage_v(V, vlds, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                load_v(V, rn.v, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                pv_mma<DT>(st, vlds, pb, rs, alpha, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                j += WAVES;
+            }
+            const int cnt = __builtin_amdgcn_readfirstlane(s_rows[j]) & 0xff;
+            rs = qk_softmax<DT, true>(st, K, qop, 0, 0, cnt, lane, a.scale_log2, pb, alpha);
+            stage_v(V, vlds, lane);
+            pv_mma<DT>(st, vlds, pb, rs, alpha, lane);
+        }
+        __syncthreads();  // the descriptors of this round are no longer read
+    }
+    st.l += xor_lane(st.l, 16);
+    st.l += xor_lane(st.l, 32);
+
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+        *(f32x4 *)&sm.o[w][col][16 * jj + 4 * grp] = st.acc[jj];
+    if (grp == 0) {
+        s_m[w][col] = st.m;
+        s_l[w][col] = st.l;
+    }
+    __syncthreads();
+    const int64_t row0 = (int64_t)s * a.num_q_heads + (int64_t)g * G;
+    for (int e = tid; e < G * 32; e += WAVES * 64) {
+        const int qi = e >> 5, d0 = (e & 31) * 4;
+        float M = s_m[0][qi];
+#pragma unroll
+        for (int i = 1; i < WAVES; ++i)
+            M = fmaxf(M, s_m[i][qi]);
+        const float ref = safe_ref(M);
+        float L = 0.f;
+        f32x4 O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < WAVES; ++i) {
+            const float wgt = fexp2(s_m[i][qi] - ref);
+            L += s_l[i][qi] * wgt;
+            O += *(const f32x4 *)&sm.o[i][qi][d0] * wgt;
+        }
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+        if (L > 0.f)
+            o = O / L;
+        u32x2 packed;
+        packed.x = (uint32_t)to_bits<DT>(o[0]) | ((uint32_t)to_bits<DT>(o[1]) << 16);
+        packed.y = (uint32_t)to_bits<DT>(o[2]) | ((uint32_t)to_bits<DT>(o[3]) << 16);
+        *(u32x2 *)((uint16_t *)a.out + (row0 + qi) * kHeadDim + d0) = packed;
+    }
+}
+
 }  // namespace
 
 // Waves per work-group (tuning knobs): the decode kernel, its suffix pass in
@@ -748,6 +923,33 @@ hipError_t launch_prefix_mfma(const DecodeArgs &a, int n_items, int dtype, int b
         return hipErrorInvalidValue;
     }
 #undef PKV_PF_CASE
+}
+
+template <int DT, int BS>
+static hipError_t launch_slotted_t(const DecodeArgs &a, hipStream_t stream)
+{
+    constexpr int W = PKV_MFMA_WAVES;
+    hipLaunchKernelGGL((slotted_mfma_kernel<DT, BS, W>), dim3(a.n_items), dim3(W * 64), 0, stream,
+                       a);
+    return hipGetLastError();
+}
+
+hipError_t launch_slotted_mfma(const DecodeArgs &a, int dtype, int block_size, hipStream_t stream)
+{
+#define PKV_SL_CASE(BSV)                                                                  \
+    case BSV:                                                                             \
+        return dtype == kFp16 ? launch_slotted_t<kFp16, BSV>(a, stream)                  \
+                              : launch_slotted_t<kBf16, BSV>(a, stream);
+    switch (block_size) {
+        PKV_SL_CASE(16)
+        PKV_SL_CASE(32)
+        PKV_SL_CASE(64)
+        PKV_SL_CASE(128)
+        PKV_SL_CASE(256)
+    default:
+        return hipErrorInvalidValue;
+    }
+#undef PKV_SL_CASE
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, int dtype, int block_size, hipStream_t stream)

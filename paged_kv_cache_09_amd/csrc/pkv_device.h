@@ -171,6 +171,11 @@ struct DecodeArgs {
     int num_groups;
     int prefix_part;            // tokens per prefix partition (multiple of 16)
     int seqs_per_tile;          // prefix pass: sequences per 16-row query tile
+    // slotted mode: each sequence is a list of (block id, slot offset, length)
+    // segments, [num_seqs][max_segments][3], with num_segments[s] in use
+    const int32_t *segments;
+    const int32_t *num_segments;
+    int max_segments;
 };
 
 // Group of sequence s in shared-prefix mode: the largest k with group_cu[k] <= s.

@@ -19,6 +19,9 @@ hipError_t launch_decode_mfma(const DecodeArgs &a, int dtype, int block_size,
 // Shared-prefix pass over n_items (query tile, KV head, prefix partition) items.
 hipError_t launch_prefix_mfma(const DecodeArgs &a, int n_items, int dtype, int block_size,
                               hipStream_t stream);
+// Decode over slotted segment lists (one work-group per (sequence, KV head)).
+hipError_t launch_slotted_mfma(const DecodeArgs &a, int dtype, int block_size,
+                               hipStream_t stream);
 hipError_t launch_reduce(void *out, const float *part_o, const float *part_lse,
                          const int32_t *lens, int num_seqs, int num_q_heads, int partition_size,
                          int max_partitions, int dtype, hipStream_t stream);
@@ -47,6 +50,8 @@ int debug_check_runs(const int64_t *cu, const int32_t *start_pos, const int32_t 
 int debug_check_groups(const int32_t *group_cu, const int32_t *prefix_lens,
                        const int32_t *lens, int num_groups, int num_seqs, int extra,
                        hipStream_t stream);
+int debug_check_segments(const int32_t *segs, const int32_t *nsegs, int num_seqs, int max_segs,
+                         int block_size, int64_t num_blocks, hipStream_t stream);
 int debug_check_copies(const int32_t *src, const int32_t *dst, int num_pairs,
                        int64_t num_blocks, hipStream_t stream);
 

@@ -39,7 +39,8 @@ def test_every_declared_symbol_is_exported(lib):
     declared = pkv.header_symbols()
     assert {"paged_kv_append", "paged_kv_append_tokens", "paged_kv_copy_blocks",
             "paged_attention_decode", "paged_attention_append_decode",
-            "paged_attention_prefix_decode", "paged_attention_reduce",
+            "paged_attention_prefix_decode", "paged_attention_decode_slotted",
+            "paged_attention_reduce",
             "pkv_status_string", "pkv_max_partitions"} <= set(declared)
     assert pkv.exported_symbols() == declared
 
@@ -169,6 +170,26 @@ def test_prefix_decode_argument_errors(lib):
     assert call(B=8) == ENOTSUP
     assert call(cu=P((1 << 20) + 2)) == EINVAL  # misaligned group offsets
     assert call(S=0, G=1) == 0                  # nothing to do
+
+
+@host_only
+def test_slotted_argument_errors(lib):
+    f = lib.paged_attention_decode_slotted
+
+    def call(out=A, sg=A, ns=A, S=2, Hq=12, Hkv=2, B=16, MS=4, NB=64, scale=0.088, dt=0):
+        return f(out, A, A, A, sg, ns, S, Hq, Hkv, 128, B, MS, NB, scale, dt, None)
+
+    assert call(sg=None) == EINVAL
+    assert call(ns=None) == EINVAL
+    assert call(out=None) == EINVAL
+    assert call(MS=0) == EINVAL
+    assert call(Hq=12, Hkv=5) == EINVAL
+    assert call(Hq=34) == ENOTSUP
+    assert call(B=24) == ENOTSUP
+    assert call(dt=2) == ENOTSUP
+    assert call(scale=float("inf")) == EINVAL
+    assert call(sg=P((1 << 20) + 2)) == EINVAL
+    assert call(S=0) == 0
 
 
 @host_only

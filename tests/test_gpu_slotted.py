@@ -1,0 +1,172 @@
+"""GPU parity of paged_attention_decode_slotted (slotted segment lists) with the
+fp64 oracle, through the C ABI: |gpu - oracle| <= 1e-2 + 1e-2 |oracle|.  Pools
+are built on each side by its own code from the same runs; positions no segment
+covers hold the NaN sentinel, so a read outside a sequence's slots would show."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from workloads import get_config, make_workload  # noqa: E402
+from workloads.gen import NAN_BITS  # noqa: E402
+from workloads.slotted import make_slotted_workload, pack  # noqa: E402
+from oracle import oracle as O  # noqa: E402
+from gpu_harness import i32, i64, scale_for, to_dev, tol_ok, widen_out  # noqa: E402
+import paged_kv_cache_09_amd as pkv  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU containers
+    pytest.skip("no GPU", allow_module_level=True)
+
+DEV = torch.device("cuda:0")
+TDT = {"fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _pools_both(runs, NB, Hkv, B, dtype):
+    kr, vr, cu, st, tb = runs
+    kp, vp = O.new_pools(NB, Hkv, B, 128, NAN_BITS[dtype])
+    O.append_tokens(kp, vp, kr, vr, cu, st, tb, B, NB)
+    gk = torch.empty((NB, Hkv, B, 128), dtype=TDT[dtype], device=DEV)
+    sentinel = int(np.array([NAN_BITS[dtype]], np.uint16).view(np.int16)[0])
+    gk.view(torch.int16).fill_(sentinel)
+    gv = gk.clone()
+    pkv.paged_kv_append_tokens(gk, gv, to_dev(kr, dtype, DEV), to_dev(vr, dtype, DEV),
+                               i64(cu, DEV), i32(st, DEV), i32(tb, DEV))
+    return kp, vp, gk, gv
+
+
+def _gpu(q, gk, gv, segs, nsegs, dtype, scale):
+    S, Hq, _ = q.shape
+    out = torch.empty((S, Hq, 128), dtype=TDT[dtype], device=DEV)
+    out.view(torch.int16).fill_(0x5555)
+    pkv.paged_attention_decode_slotted(out, to_dev(q, dtype, DEV), gk, gv, i32(segs, DEV),
+                                       i32(nsegs, DEV), scale=scale)
+    torch.cuda.synchronize()
+    return widen_out(out)
+
+
+def test_radix_batch_matches_oracle():
+    cfg = get_config("c5")
+    w = make_slotted_workload(cfg)
+    print(f"[gpu] slotted radix batch S={len(w.paths)} NB={w.num_blocks} "
+          f"max_segments={w.segments.shape[1]}", flush=True)
+    kp, vp, gk, gv = _pools_both(w.runs(), w.num_blocks, cfg.num_kv_heads, cfg.block_size,
+                                 cfg.dtype)
+    scale = scale_for(128)
+    ref = O.attention_slotted(w.q, kp, vp, w.segments, w.num_segments, cfg.num_kv_heads,
+                              cfg.block_size, w.num_blocks, scale, cfg.dtype)
+    got = _gpu(w.q, gk, gv, w.segments, w.num_segments, cfg.dtype, scale)
+    ok, err, nbad = tol_ok(got, ref)
+    assert ok, (err, nbad)
+
+
+def _node_case(seed, S, Hq, Hkv, B, dtype, node_len_hi, nodes_per_path):
+    """Random tree-less node sets: every sequence walks its own random list of
+    nodes (shared ones included), some paths empty, some nodes of length 0."""
+    rng = np.random.default_rng(seed)
+    nn = max(3 * S + 8, 2 * nodes_per_path)
+    lens = [int(x) for x in rng.integers(0, node_len_hi + 1, size=nn)]
+    free = [int(x) for x in rng.permutation(10 * nn + 16)]
+    node_segs = pack([max(n, 1) for n in lens], B, free)
+    # zero-length nodes keep a (block, offset, 0) segment
+    node_segs = [[(segs[0][0], segs[0][1], 0)] if lens[i] == 0 else segs
+                 for i, segs in enumerate(node_segs)]
+    NB = max(x[0] for segs in node_segs for x in segs) + 1
+
+    def draw(*sh):
+        x = rng.standard_normal(sh).astype(np.float32)
+        if dtype == "fp16":
+            return x.astype(np.float16).view(np.uint16)
+        return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+    node_k = [draw(n, Hkv, 128) for n in lens]
+    node_v = [draw(n, Hkv, 128) for n in lens]
+    paths = [[int(x) for x in rng.choice(nn, size=rng.integers(0, nodes_per_path + 1),
+                                         replace=False)] for _ in range(S)]
+    paths[0] = []
+    MS = max(1, max(sum(len(node_segs[i]) for i in p) for p in paths))
+    segs = np.zeros((S, MS, 3), np.int32)
+    nsegs = np.zeros(S, np.int32)
+    for s, p in enumerate(paths):
+        flat = [x for i in p for x in node_segs[i]]
+        if flat:
+            segs[s, :len(flat)] = flat
+        nsegs[s] = len(flat)
+    rk, rv, st, tb, cu = [], [], [], [], [0]
+    for segs_i, k, v in zip(node_segs, node_k, node_v):
+        r = 0
+        for blk, off, ln in segs_i:
+            rk.append(k[r:r + ln]); rv.append(v[r:r + ln])
+            st.append(off); tb.append([blk]); cu.append(cu[-1] + ln)
+            r += ln
+    runs = (np.concatenate(rk), np.concatenate(rv), np.array(cu, np.int64),
+            np.array(st, np.int32), np.array(tb, np.int32))
+    return dict(NB=NB, segs=segs, nsegs=nsegs, runs=runs, q=draw(S, Hq, 128))
+
+
+NODE_CASES = [
+    # (seed, S, Hq, Hkv, B, dtype, max node length, max nodes per path)
+    (1, 6, 12, 2, 16, "fp16", 20, 6),        # G 6
+    (2, 5, 32, 8, 16, "bf16", 40, 8),        # G 4
+    (3, 4, 16, 16, 32, "fp16", 70, 5),       # G 1 on the matrix-core path
+    (4, 3, 32, 2, 64, "bf16", 150, 4),       # G 16
+    (5, 4, 12, 4, 128, "fp16", 300, 3),      # G 3
+    (6, 3, 16, 8, 256, "bf16", 600, 3),      # G 2, the largest block
+    (7, 3, 12, 2, 16, "fp16", 3, 150),       # ~150 short segments: three rounds of 64
+]
+
+
+@pytest.mark.parametrize("case", NODE_CASES, ids=[f"seed{c[0]}" for c in NODE_CASES])
+def test_random_node_lists(case):
+    seed, S, Hq, Hkv, B, dtype, hi, per = case
+    c = _node_case(seed, S, Hq, Hkv, B, dtype, hi, per)
+    print(f"[gpu] slotted seed={seed} S={S} Hq={Hq} Hkv={Hkv} B={B} {dtype} "
+          f"max_segments={c['segs'].shape[1]}", flush=True)
+    kp, vp, gk, gv = _pools_both(c["runs"], c["NB"], Hkv, B, dtype)
+    scale = scale_for(128)
+    ref = O.attention_slotted(c["q"], kp, vp, c["segs"], c["nsegs"], Hkv, B, c["NB"], scale,
+                              dtype)
+    got = _gpu(c["q"], gk, gv, c["segs"], c["nsegs"], dtype, scale)
+    ok, err, nbad = tol_ok(got, ref)
+    assert ok, (err, nbad)
+    assert (got[0] == 0).all()  # the empty sequence
+
+
+@pytest.mark.parametrize("key", ["c1a", "c2", "c4"])
+def test_block_tables_as_segments(key):
+    """A block table as whole-block segments (plus the partly filled last block)
+    gives the oracle's ordinary attention."""
+    w = make_workload(get_config(key))
+    c = w.cfg
+    print(f"[gpu] slotted from tables {key}", flush=True)
+    r = O.run_step(w, scale_for(c.head_dim))
+    B = c.block_size
+    nb = -(-w.lengths.astype(np.int64) // B)
+    segs = np.zeros((c.num_seqs, int(nb.max()), 3), np.int32)
+    for s in range(c.num_seqs):
+        for j in range(nb[s]):
+            segs[s, j] = (w.tables[s, j], 0, min(B, int(w.lengths[s]) - j * B))
+    gk, gv = to_dev(r["k_pool"], c.dtype, DEV), to_dev(r["v_pool"], c.dtype, DEV)
+    got = _gpu(w.q, gk, gv, segs, nb.astype(np.int32), c.dtype, scale_for(c.head_dim))
+    ok, err, nbad = tol_ok(got, r["out"])
+    assert ok, (err, nbad)
+
+
+def test_slotted_debug_check_rejects_bad_segments(monkeypatch):
+    gk = torch.zeros((8, 2, 16, 128), dtype=torch.float16, device=DEV)
+    q = np.zeros((2, 4, 128), np.uint16)
+    monkeypatch.setenv("PKV_DEBUG_CHECK", "1")
+    bad = [
+        [[[0, 12, 5]], [[1, 0, 3]]],    # slot runs past its block
+        [[[9, 0, 5]], [[1, 0, 3]]],     # block outside the pool
+        [[[0, 0, -1]], [[1, 0, 3]]],    # negative length
+    ]
+    for segs in bad:
+        with pytest.raises(pkv.PagedKVError) as ei:
+            _gpu(q, gk, gk, np.array(segs, np.int32), np.array([1, 1], np.int32), "fp16", 0.1)
+        assert ei.value.status == -5
+    with pytest.raises(pkv.PagedKVError) as ei:  # more segments than the row holds
+        _gpu(q, gk, gk, np.array([[[0, 0, 1]], [[1, 0, 3]]], np.int32),
+             np.array([2, 1], np.int32), "fp16", 0.1)
+    assert ei.value.status == -5

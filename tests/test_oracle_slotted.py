@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 from oracle import brute
+from workloads.slotted import make_slotted_workload, pack
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 SCALE = float(np.float32(1.0 / math.sqrt(128)))
@@ -19,30 +20,10 @@ def golden():
         return json.load(f)
 
 
-def pack_nodes(node_lens, B, rng):
-    """The page's allocation policy: a node shorter than a block goes to the first
-    partly filled block with enough free slots (offset B - free), else to the head
-    of the free list; longer nodes take whole blocks.  Returns per-node segment
-    lists and the number of blocks used (ids in free-list order)."""
-    free_ids = list(range(10 ** 6))
-    partial = []          # [block id, free slots]
-    segs = []
-    for n in node_lens:
-        if n >= B:
-            nb = -(-n // B)
-            ids = [free_ids.pop(0) for _ in range(nb)]
-            segs.append([[ids[i], 0, min(B, n - i * B)] for i in range(nb)])
-            continue
-        for p in partial:
-            if p[1] >= n:
-                segs.append([[p[0], B - p[1], n]])
-                p[1] -= n
-                break
-        else:
-            b = free_ids.pop(0)
-            segs.append([[b, 0, n]])
-            partial.append([b, B - n])
-        partial = [p for p in partial if p[1] > 0]
+def pack_nodes(node_lens, B, rng=None):
+    """The page's slotted allocation (workloads.slotted.pack) on the free list
+    [0, 1, 2, ...]; returns per-node segment lists and the blocks used."""
+    segs = [[list(x) for x in node] for node in pack(node_lens, B, list(range(10 ** 5)))]
     used = max(s[0] for node in segs for s in node) + 1
     return segs, used
 
@@ -51,7 +32,7 @@ def test_golden_allocation_follows_the_page_policy():
     g = golden()
     names = ["A", "B", "C", "D", "E"]
     lens = [sum(s[2] for s in g["allocations"][k]) for k in names]
-    segs, _ = pack_nodes(lens, g["block_size"], None)
+    segs, _ = pack_nodes(lens, g["block_size"])
     for k, sg in zip(names, segs):
         assert sg == g["allocations"][k]
 
@@ -156,3 +137,33 @@ def test_empty_sequence_gives_zeros(oracle_lib):
     out = oracle_lib.attention_slotted(q, kp, kp, np.zeros((1, 1, 3), np.int32),
                                        np.zeros(1, np.int32), 1, 16, 2, SCALE, "fp16")
     assert (out == 0).all()
+
+
+def test_radix_batch_layout(oracle_lib):
+    """The seeded radix-tree batch: segments stay inside their blocks, no two
+    nodes share a slot, and the oracle over the pools equals brute force over
+    the logical arrays of a few sequences."""
+    from workloads import get_config
+    cfg = get_config("c5")
+    w = make_slotted_workload(cfg, num_seqs=24)
+    B = cfg.block_size
+    owner = {}
+    for n, segs in enumerate(w.node_segments):
+        assert sum(x[2] for x in segs) == len(w.node_k[n])
+        for blk, off, ln in segs:
+            assert 0 <= blk < w.num_blocks and off >= 0 and off + ln <= B
+            for r in range(off, off + ln):
+                assert owner.setdefault((blk, r), n) == n
+    kr, vr, cu, st, tb = w.runs()
+    kp, vp = oracle_lib.new_pools(w.num_blocks, cfg.num_kv_heads, B, cfg.head_dim, w.nan_bits)
+    oracle_lib.append_tokens(kp, vp, kr, vr, cu, st, tb, B, w.num_blocks)
+    out = oracle_lib.attention_slotted(w.q, kp, vp, w.segments, w.num_segments, cfg.num_kv_heads,
+                                       B, w.num_blocks, SCALE, cfg.dtype)
+    G = cfg.num_q_heads // cfg.num_kv_heads
+    q = brute.widen(w.q, cfg.dtype)
+    for s in (0, 7, 23):
+        Kb, Vb = w.logical_kv(s)
+        K, V = brute.widen(Kb, cfg.dtype), brute.widen(Vb, cfg.dtype)
+        for h in range(0, cfg.num_q_heads, 5):
+            ref = brute.attention_one(q[s, h], K[:, h // G], V[:, h // G], SCALE)
+            assert np.allclose(out[s, h], ref, rtol=0, atol=1e-12)
