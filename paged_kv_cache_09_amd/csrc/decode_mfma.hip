@@ -162,8 +162,7 @@ __device__ __forceinline__ bool qk_softmax(GqaState &st, const KOp &K, const u32
             sc[r] = kNegInf;
     }
     float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mt = fmaxf(mt, xor_lane(mt, 16));
-    mt = fmaxf(mt, xor_lane(mt, 32));
+    mt = pair_max32(pair_max16(mt));
     const bool grow = mt > st.m + kRescaleSlack;  // always true for the first scores
     const bool rescale = __ballot(grow) != 0;     // wave-uniform
     alpha = 1.f;
@@ -246,7 +245,7 @@ void decode_mfma_kernel(DecodeArgs a)
 {
     constexpr bool SPLIT = MODE == kModeSplit;
     // V staging during the token loop; the cross-wave merge afterwards
-    __shared__ union {
+    __shared__ __attribute__((aligned(16))) union {
         uint16_t v[WAVES][kSub * kVStride];
         float o[WAVES][16][kOStride];
     } sm;
@@ -452,8 +451,7 @@ void decode_mfma_kernel(DecodeArgs a)
         }
 
         // sum of the four lane groups' shares of l (m is already uniform across them)
-        st.l += xor_lane(st.l, 16);
-        st.l += xor_lane(st.l, 32);
+        st.l = pair_sum32(pair_sum16(st.l));
 
         __syncthreads();  // all waves are done with their V staging area
 #pragma unroll
@@ -551,7 +549,7 @@ template <int DT, int BS, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
 void prefix_mfma_kernel(DecodeArgs a)
 {
-    __shared__ union {
+    __shared__ __attribute__((aligned(16))) union {
         uint16_t v[WAVES][kSub * kVStride];
         float o[WAVES][16][kOStride];
     } sm;
@@ -650,8 +648,7 @@ void prefix_mfma_kernel(DecodeArgs a)
             stage_v(V, vlds, lane);
             pv_mma<DT>(st, vlds, pb, rs, alpha, lane);
         }
-        st.l += xor_lane(st.l, 16);
-        st.l += xor_lane(st.l, 32);
+        st.l = pair_sum32(pair_sum16(st.l));
 
         __syncthreads();  // all waves are done with their V staging area
 #pragma unroll
@@ -724,7 +721,7 @@ template <int DT, int BS, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(3)))
 void slotted_mfma_kernel(DecodeArgs a)
 {
-    __shared__ union {
+    __shared__ __attribute__((aligned(16))) union {
         uint16_t v[WAVES][kSub * kVStride];
         float o[WAVES][16][kOStride];
     } sm;
@@ -829,8 +826,7 @@ void slotted_mfma_kernel(DecodeArgs a)
         }
         __syncthreads();  // the descriptors of this round are no longer read
     }
-    st.l += xor_lane(st.l, 16);
-    st.l += xor_lane(st.l, 32);
+    st.l = pair_sum32(pair_sum16(st.l));
 
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj)

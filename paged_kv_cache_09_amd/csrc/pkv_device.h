@@ -118,6 +118,36 @@ __device__ __forceinline__ float row_sum16(float x)
 
 __device__ __forceinline__ float xor_lane(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
+// Max / sum over lanes l and l^16 (or l^32), the same bits in both lanes of the
+// pair.  The gfx950 lane-swap instructions hand every lane both values of its
+// pair in one VALU operation (lane layout checked on the GPU with an in-bounds
+// probe: swap16(x, x) gives {x[l & ~16], x[l | 16]}, swap32 likewise with 32),
+// where a shuffle would round-trip through the LDS crossbar.
+__device__ __forceinline__ float pair_max16(float x)
+{
+    const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float pair_max32(float x)
+{
+    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float pair_sum16(float x)
+{
+    const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+__device__ __forceinline__ float pair_sum32(float x)
+{
+    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
 
