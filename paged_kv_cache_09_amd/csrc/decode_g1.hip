@@ -189,20 +189,37 @@ __device__ __forceinline__ void accumulate(RowState<DT> &st, const float (&sc)[8
     st.m = m_new;
 }
 
-// Merge the running state of the lane `mask` lanes away into this lane's.
-template <int DT>
-__device__ __forceinline__ void merge_xor(RowState<DT> &st, int mask)
+// Swap helpers for the row merges: both values of the lane pair (l, l^16) or
+// (l, l^32), the even-row / lower-half lane's first (gfx950 lane-swap
+// instructions; lane layout checked on the GPU with an in-bounds probe).
+template <int SPAN>
+__device__ __forceinline__ void swap_pair(float x, float &lo, float &hi)
 {
-    const float mo = xor_lane(st.m, mask);
-    const float lo = xor_lane(st.l, mask);
-    const float M = fmaxf(st.m, mo);
+    const unsigned u = __float_as_uint(x);
+    const auto t = SPAN == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                              : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    lo = __uint_as_float(t[0]);
+    hi = __uint_as_float(t[1]);
+}
+
+// Merge the running states of lanes l and l^SPAN; both lanes end with the same
+// state (the lower lane's terms first, as a shuffle-based merge computes it in
+// the lanes that write the result).
+template <int DT, int SPAN>
+__device__ __forceinline__ void merge_pair(RowState<DT> &st)
+{
+    float m0, m1, l0, l1;
+    swap_pair<SPAN>(st.m, m0, m1);
+    swap_pair<SPAN>(st.l, l0, l1);
+    const float M = fmaxf(m0, m1);
     const float ref = safe_ref(M);
-    const float a = fexp2(st.m - ref), b = fexp2(mo - ref);
-    st.l = st.l * a + lo * b;
+    const float a = fexp2(m0 - ref), b = fexp2(m1 - ref);
+    st.l = l0 * a + l1 * b;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const float ao = xor_lane(st.acc[j], mask);
-        st.acc[j] = st.acc[j] * a + ao * b;
+        float x0, x1;
+        swap_pair<SPAN>(st.acc[j], x0, x1);
+        st.acc[j] = x0 * a + x1 * b;
     }
     st.m = M;
 }
@@ -367,8 +384,8 @@ void decode_g1_kernel(DecodeArgs a)
         }
 
         // rows of the wave -> one state per wave (identical in every lane)
-        merge_xor<DT>(st, 16);
-        merge_xor<DT>(st, 32);
+        merge_pair<DT, 16>(st);
+        merge_pair<DT, 32>(st);
         const int64_t row = (int64_t)s * a.num_q_heads + h;
         if (WAVES == 1) {
             if (r == 0) {
