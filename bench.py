@@ -80,6 +80,9 @@ def parse():
                          "paged_attention_prefix_decode")
     ap.add_argument("--prefix-partition", type=int, default=None,
                     help="prefix partition of paged_attention_prefix_decode (0 = one)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one whole step (every layer's launches) in a HIP graph and "
+                         "time graph replays instead of eager launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle sample")
@@ -282,10 +285,24 @@ def bench_step(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    run = step
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        run = graph.replay
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
     for _ in range(args.steps):
-        step()
+        run()
     t1.record()
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
@@ -348,6 +365,7 @@ def bench_step(args):
             "distinct_layer_pools": R,
             "partition_size": P,
             "launches_per_layer": (1 if fused else 2) + (1 if (P or prefix) else 0),
+            "launch": "hip graph replay" if args.graph else "eager",
             "shared_prefix": cfg.prefix_tokens,
             "path": ("paged_attention_prefix_decode (prefix partition %d)" % PP if prefix
                      else "paged_attention_append_decode" if fused else

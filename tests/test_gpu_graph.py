@@ -1,0 +1,77 @@
+"""The library's calls inside a HIP graph (torch.cuda.CUDAGraph capture on the
+current stream): every replay must reproduce the eager result bit for bit, with
+eager work and synchronisation between replays.  The calls enqueue kernels only
+(no memset nodes, no allocation, no synchronisation), so they are capturable."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from workloads import get_config, make_workload  # noqa: E402
+from gpu_harness import GpuStep, scale_for  # noqa: E402
+import paged_kv_cache_09_amd as pkv  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU containers
+    pytest.skip("no GPU", allow_module_level=True)
+
+
+@pytest.mark.parametrize("key,P", [("c1a", 0), ("c2", 512), ("c5", 0)])
+def test_graph_replays_match_eager(key, P):
+    w = make_workload(get_config(key))
+    c = w.cfg
+    print(f"[gpu] graph {key} P={P}", flush=True)
+    g = GpuStep(w, append=False)
+    S, Hq, D = c.num_seqs, c.num_q_heads, c.head_dim
+    dt = g.q.dtype
+    mp = pkv.max_partitions(c.max_blocks_per_seq, c.block_size, P) if P else 1
+    po = torch.zeros((S, Hq, mp, D), dtype=torch.float32, device=g.device)
+    pl = torch.zeros((S, Hq, mp), dtype=torch.float32, device=g.device)
+    out = torch.zeros((S, Hq, D), dtype=dt, device=g.device)
+    scale = scale_for(D)
+    prefix = key == "c5"
+    if prefix:
+        cu = torch.tensor([0, S], dtype=torch.int32, device=g.device)
+        plen = torch.tensor([c.prefix_tokens], dtype=torch.int32, device=g.device)
+
+    def step():
+        if prefix:
+            pkv.paged_attention_prefix_decode(out, g.q, g.k_pool, g.v_pool, g.tables, g.lens, cu,
+                                              plen, po, pl, k_new=g.k_new, v_new=g.v_new,
+                                              slot_out=g.slots, scale=scale)
+        elif P:
+            pkv.paged_attention_append_decode(None, g.q, g.k_pool, g.v_pool, g.k_new, g.v_new,
+                                              g.tables, g.lens, g.slots, scale=scale,
+                                              partition_size=P, part_o=po, part_lse=pl)
+            pkv.paged_attention_reduce(out, po, pl, g.lens, P)
+        else:
+            pkv.paged_attention_append_decode(out, g.q, g.k_pool, g.v_pool, g.k_new, g.v_new,
+                                              g.tables, g.lens, g.slots, scale=scale)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    eager_k = g.k_pool.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), \
+            f"replay {rep} differs from the eager result"
+        # pools hold NaN sentinels in unused slots: compare bit patterns
+        assert torch.equal(g.k_pool.view(torch.int16), eager_k.view(torch.int16))
+        scratch = (g.q.float() * 2).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        del scratch
+    assert np.isfinite(out.float().cpu().numpy()).all()
