@@ -207,17 +207,22 @@ int paged_attention_append_decode(void *out, const void *q, void *k_pool, void *
  * reading blocks with reference count > 1: blog.llmgo.top page, §四).  The result
  * is the same as paged_attention_decode (or, with k_new / v_new, as
  * paged_attention_append_decode) on the same tables; only the reads differ.
- * Two launches:
- *   1. prefix pass: for each group, 16-row query tiles made of the query heads of
- *      floor(16/G) consecutive member sequences (G = num_q_heads / num_kv_heads)
- *      attend over the group's prefix, read through the table row of sequence
- *      group_cu[k]; the prefix is split into partitions of prefix_partition tokens
- *      (0: one partition) and each partition's fp32 partial (normalised o,
- *      natural-log lse) goes to part_o[s][h][p] / part_lse[s][h][p];
+ *
+ * prefix_partition == 0: one launch.  A work-group takes a 16-row query tile
+ *   made of the query heads of floor(16/G) consecutive member sequences (G =
+ *   num_q_heads / num_kv_heads) and one KV head; it streams the group's prefix
+ *   (read through the table row of sequence group_cu[k]) with every member's
+ *   rows active, then each member's own positions prefix_lens[k] .. n-1 with
+ *   only that member's rows active, appends the new tokens when k_new is given,
+ *   and writes `out`.  The workspace is not used (part_o / part_lse may be NULL).
+ * prefix_partition > 0: two launches, for prefixes long enough to need more
+ *   parallelism than tiles x KV heads:
+ *   1. prefix pass: the same tiles over partitions of prefix_partition tokens of
+ *      the prefix; each partition's fp32 partial (normalised o, natural-log lse)
+ *      goes to part_o[s][h][p] / part_lse[s][h][p];
  *   2. suffix pass: each (sequence, KV head) attends over positions
- *      prefix_lens[k] .. n-1 (appending the new token as
- *      paged_attention_append_decode does when k_new is given), merges that with
- *      the prefix partials by the log-sum-exp rule and writes `out`.
+ *      prefix_lens[k] .. n-1 (with the optional append), merges that with the
+ *      prefix partials by the log-sum-exp rule and writes `out`.
  *
  *   group_cu       device int32 [num_groups + 1]: 0 = group_cu[0] <= ... <=
  *                  group_cu[num_groups] = num_seqs (groups are contiguous)
@@ -225,11 +230,12 @@ int paged_attention_append_decode(void *out, const void *q, void *k_pool, void *
  *   k_new, v_new   optional (both or neither), as for paged_attention_append_decode;
  *                  slot_out is used only with them
  *   prefix_partition  0 or a multiple of 16
- *   max_partitions    row stride of the workspace, at least
- *                  ceil(max_blocks_per_seq * block_size / prefix_partition)
- *                  (at least 1 when prefix_partition is 0), else PKV_EWORKSPACE
- *   part_o, part_lse  fp32 workspace [num_seqs][num_q_heads][max_partitions][head_dim]
- *                  and [num_seqs][num_q_heads][max_partitions]
+ *   max_partitions    (prefix_partition > 0) row stride of the workspace, at least
+ *                  ceil(max_blocks_per_seq * block_size / prefix_partition),
+ *                  else PKV_EWORKSPACE
+ *   part_o, part_lse  (prefix_partition > 0) fp32 workspace
+ *                  [num_seqs][num_q_heads][max_partitions][head_dim] and
+ *                  [num_seqs][num_q_heads][max_partitions]
  *   out            [num_seqs][num_q_heads][head_dim], dtype
  * Caller contract (checked with PKV_DEBUG_CHECK=1 like the other entry points):
  * every member's table agrees with the first member's on the blocks holding the

@@ -246,12 +246,13 @@ def paged_attention_append_decode(out, q, k_pool, v_pool, k_new, v_new, block_ta
 
 
 def paged_attention_prefix_decode(out, q, k_pool, v_pool, block_tables, context_lens, group_cu,
-                                  prefix_lens, part_o, part_lse, k_new=None, v_new=None,
-                                  slot_out=None, scale: Optional[float] = None,
+                                  prefix_lens, part_o=None, part_lse=None, k_new=None,
+                                  v_new=None, slot_out=None, scale: Optional[float] = None,
                                   prefix_partition: int = 0):
     """Decode attention for sequences grouped by a shared prefix (group k =
     sequences group_cu[k]..group_cu[k+1]-1, sharing their first prefix_lens[k]
-    positions); appends the new rows first when k_new / v_new are given."""
+    positions); appends the new rows first when k_new / v_new are given.  The
+    workspace part_o / part_lse is needed only with prefix_partition > 0."""
     dev = _dev(out, q, k_pool, v_pool, block_tables, context_lens, group_cu, prefix_lens,
                part_o, part_lse, k_new, v_new, slot_out)
     for t, n in ((block_tables, "block_tables"), (context_lens, "context_lens"),
@@ -266,8 +267,8 @@ def paged_attention_prefix_decode(out, q, k_pool, v_pool, block_tables, context_
         _p(out), _p(q), _p(k_pool), _p(v_pool), _p(k_new), _p(v_new), _p(slot_out),
         _p(block_tables), _p(context_lens), _p(group_cu), _p(prefix_lens),
         prefix_lens.shape[0], S, Hq, Hkv, D, B, block_tables.shape[1], NB, float(scale),
-        int(prefix_partition), part_o.shape[2], _p(part_o), _p(part_lse), _dtype_code(q),
-        _stream(dev))
+        int(prefix_partition), part_o.shape[2] if part_o is not None else 0, _p(part_o),
+        _p(part_lse), _dtype_code(q), _stream(dev))
     _check(rc, "paged_attention_prefix_decode")
 
 

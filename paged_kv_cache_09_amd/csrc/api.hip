@@ -420,14 +420,17 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
         const int64_t ctx = (int64_t)max_blocks_per_seq * block_size;
         if (ctx > ((int64_t)1 << 29))
             return PKV_EINVAL;
-        prefix_part = partition_size > 0 ? partition_size : (int)((ctx + 15) / 16 * 16);
-        const int64_t need = (ctx + prefix_part - 1) / prefix_part;
-        if (!part_o || !part_lse || max_partitions < need || need <= 0)
-            return PKV_EWORKSPACE;
-        if (!aligned16(part_o) || ((uintptr_t)part_lse & 3u))
-            return PKV_EINVAL;
-        prefix_parts = max_partitions;
-        if (!out || ((uintptr_t)out & 1u))
+        if (partition_size > 0) {
+            // two passes: prefix partitions into the workspace, then the suffixes
+            prefix_part = partition_size;
+            const int64_t need = (ctx + prefix_part - 1) / prefix_part;
+            if (!part_o || !part_lse || max_partitions < need || need <= 0)
+                return PKV_EWORKSPACE;
+            if (!aligned16(part_o) || ((uintptr_t)part_lse & 3u))
+                return PKV_EINVAL;
+            prefix_parts = max_partitions;
+        }
+        if (!out || ((uintptr_t)out & 7u))
             return PKV_EINVAL;
     } else if (partition_size > 0) {
         if (partition_size % block_size != 0 || partition_size % 32 != 0)
@@ -488,9 +491,25 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
     a.v_new = v_new;
     a.slot_out = slot_out;
     a.block_size = block_size;
+    if (prefix && partition_size == 0) {
+        // one pass: each work-group streams its tile's prefix, then each member's
+        // own positions, and writes `out`
+        a.partition_size = 0;
+        a.group_cu = pg.group_cu;
+        a.prefix_lens = pg.prefix_lens;
+        a.num_groups = pg.num_groups;
+        a.seqs_per_tile = 16 / group;
+        const int64_t tiles = (num_seqs + a.seqs_per_tile - 1) / a.seqs_per_tile;
+        const int64_t fitems = tiles * num_kv_heads;
+        if (fitems > INT32_MAX)
+            return PKV_EINVAL;
+        return launch_status(
+            pkv::launch_prefix_fused_mfma(a, (int)fitems, dtype, block_size, st));
+    }
     if (prefix) {
-        // pass 1: each group's prefix, read once per 16-row tile of its query heads;
-        // pass 2: each sequence's own positions, merged with the prefix partials
+        // pass 1: each group's prefix partitions, read once per 16-row tile of its
+        // query heads; pass 2: each sequence's own positions, merged with the
+        // prefix partials
         a.partition_size = 0;
         a.max_partitions = prefix_parts;
         a.group_cu = pg.group_cu;

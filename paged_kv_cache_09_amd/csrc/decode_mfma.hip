@@ -139,14 +139,16 @@ struct GqaState {
 // Scores of the sub-tile, online-softmax update of (m, l); returns the
 // probabilities packed as the B operand of P.V and the rescale factor of acc.
 // Scores of the sub-tile and the online-softmax update of (m, l).  PARTIAL:
-// mask tokens outside [t_beg, t_end) (the sub-tile straddles an end).  Returns
+// mask tokens outside [t_beg, t_end) (the sub-tile straddles an end), and the
+// whole column of a lane whose col_on is false (a query row the sub-tile does
+// not belong to).  Returns
 // whether the wave rescales its accumulators (alpha holds each lane's factor,
 // 1 where the column's reference max did not move); pb receives the
 // probabilities packed as the B operand of P.V.
 template <int DT, bool PARTIAL>
 __device__ __forceinline__ bool qk_softmax(GqaState &st, const KOp &K, const u32x4 *qop, int tb,
                                            int t_beg, int t_end, int lane, float scale_log2,
-                                           u32x2 &pb, float &alpha)
+                                           u32x2 &pb, float &alpha, bool col_on = true)
 {
     const int grp = lane >> 4;
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
@@ -158,7 +160,7 @@ __device__ __forceinline__ bool qk_softmax(GqaState &st, const KOp &K, const u32
     for (int r = 0; r < 4; ++r) {
         sc[r] = s[r] * scale_log2;
         const int t = tb + 4 * grp + r;
-        if (PARTIAL && (t < t_beg || t >= t_end))
+        if (PARTIAL && (t < t_beg || t >= t_end || !col_on))
             sc[r] = kNegInf;
     }
     float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
@@ -862,6 +864,259 @@ void slotted_mfma_kernel(DecodeArgs a)
     }
 }
 
+// Shared-prefix decode in one pass.  One work-group per (16-row query tile, KV
+// head), the tile holding the G query heads of floor(16/G) consecutive member
+// sequences of a group.  The work-group's sub-tiles are the group's prefix
+// (positions 0 .. prefix_len-1, read once through the first member's table with
+// every member's columns active) followed by each member's own positions
+// (prefix_len .. n-1, read through its own table with only its G columns
+// active: the other columns score -inf and keep their state).  The waves take
+// the concatenated list round-robin with the decode kernel's score / softmax /
+// P.V code, so every column ends with attention over exactly its sequence's n
+// positions; the optional append is done by the wave owning each member's last
+// sub-tile.  No partials leave the work-group.
+template <int DT, int BS, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void prefix_fused_mfma_kernel(DecodeArgs a)
+{
+    __shared__ __attribute__((aligned(16))) union {
+        uint16_t v[WAVES][kSub * kVStride];
+        float o[WAVES][16][kOStride];
+    } sm;
+    __shared__ float s_m[WAVES][16], s_l[WAVES][16];
+    __shared__ int64_t s_row[16];       // output row of each query column, -1 if inactive
+    __shared__ int32_t s_cum[17];       // sub-tiles before member i's own ones (s_cum[0]: prefix)
+    __shared__ int32_t s_len[16];       // context length of member i (0 outside the group)
+    __shared__ u32x4 s_new[16][2][16];  // parked new K / V rows of member i (fused append)
+
+    const int item = blockIdx.x;
+    const int g = item % a.num_kv_heads;
+    const int tile = item / a.num_kv_heads;
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const int spt = a.seqs_per_tile;
+    const int s0 = tile * spt;
+    const int s_end = min(a.num_seqs, s0 + spt);
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int col = lane & 15, grp = lane >> 4;
+    const bool fused = a.k_new != nullptr;
+
+    const uint16_t *__restrict__ kp = (const uint16_t *)a.k_pool;
+    const uint16_t *__restrict__ vp = (const uint16_t *)a.v_pool;
+    const int64_t blk_elems = (int64_t)a.num_kv_heads * BS * kHeadDim;
+    const int64_t head_off = (int64_t)g * BS * kHeadDim;
+    uint16_t *vlds = sm.v[w];
+    const int cm = col / G;              // member of this lane's query column
+    const int cs = s0 + cm;
+    const int ch = g * G + col % G;
+
+    int k = group_of(a.group_cu, a.num_groups, s0);
+    for (bool more = true; more; ++k) {
+        const int ga = a.group_cu[k], gb = a.group_cu[k + 1];
+        more = gb < s_end;
+        if (ga == gb)
+            continue;  // an empty group (uniform)
+        const int plen = a.prefix_lens[k];
+        const int start_sub = plen & ~(kSub - 1);
+        const int32_t *__restrict__ lead = a.tables + (int64_t)ga * a.width;
+        const bool active = col < spt * G && cs < s_end && cs >= ga && cs < gb;
+
+        // per-member lengths and the cumulative sub-tile counts
+        if (tid < 16) {
+            const int s = s0 + tid;
+            const bool in = tid < spt && s < s_end && s >= ga && s < gb;
+            s_len[tid] = in ? a.lens[s] : 0;
+            if (in && fused && g == 0 && a.lens[s] <= 0 && a.slot_out)
+                a.slot_out[s] = -1;  // padding sequence: nothing appended
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int c = (plen + kSub - 1) / kSub;
+            s_cum[0] = c;
+            for (int i = 0; i < 16; ++i) {
+                const int n = s_len[i];
+                c += n > start_sub ? (n - start_sub + kSub - 1) / kSub : 0;
+                s_cum[i + 1] = c;
+            }
+        }
+        __syncthreads();
+        const int total = __builtin_amdgcn_readfirstlane(s_cum[16]);
+
+        // fused append: the wave that owns member i's last sub-tile writes its new
+        // rows now and parks them in LDS for that sub-tile
+        if (fused) {
+            for (int i = 0; i < spt; ++i) {
+                const int n = __builtin_amdgcn_readfirstlane(s_len[i]);
+                const int last = __builtin_amdgcn_readfirstlane(s_cum[i + 1]) - 1;
+                if (n <= plen || last < 0 || last % WAVES != w)
+                    continue;
+                const int s = s0 + i;
+                const int tn = n - 1;
+                const int64_t phys_n = a.tables[(int64_t)s * a.width + tn / BS];
+                const int64_t off = ((int64_t)s * a.num_kv_heads + g) * kHeadDim;
+                const uint16_t *kq = (const uint16_t *)a.k_new + off;
+                const uint16_t *vq = (const uint16_t *)a.v_new + off;
+                u32x4 knew[4];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    knew[kk] = *(const u32x4 *)(kq + 32 * kk + 8 * grp);
+                const u32x4 vnew = *(const u32x4 *)(vq + 8 * col);
+                const int64_t dst = phys_n * blk_elems + head_off + (int64_t)(tn % BS) * kHeadDim;
+                if (col == (tn & 15)) {
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        *(u32x4 *)((uint16_t *)a.k_pool + dst + 32 * kk + 8 * grp) = knew[kk];
+                }
+                if (col == 0) {
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        s_new[i][0][4 * kk + grp] = knew[kk];
+                }
+                if (lane < 16) {
+                    *(u32x4 *)((uint16_t *)a.v_pool + dst + lane * 8) = vnew;
+                    s_new[i][1][lane] = vnew;
+                }
+                if (g == 0 && lane == 0 && a.slot_out)
+                    a.slot_out[s] = phys_n * BS + tn % BS;
+            }
+        }
+
+        u32x4 qop[4];
+        {
+            const uint16_t *qrow = (const uint16_t *)a.q +
+                                   ((int64_t)cs * a.num_q_heads + ch) * kHeadDim + grp * 8;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                qop[kk] = active ? *(const u32x4 *)(qrow + kk * 32) : (u32x4){0u, 0u, 0u, 0u};
+        }
+        GqaState st;
+        st.m = kNegInf;
+        st.l = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+            st.acc[jj] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+        // sub-tile j: the prefix's (seg -1) or member seg's; the member cursor only
+        // moves forward, so the lookup is one or two LDS reads per sub-tile
+        struct Sub {
+            int seg, tb, t_beg, t_end, t_load;
+            int32_t phys;
+        };
+        auto describe = [&](int j, int &seg) {
+            while (seg < 15 && j >= __builtin_amdgcn_readfirstlane(s_cum[seg + 1]))
+                ++seg;
+            Sub d;
+            d.seg = seg;
+            if (seg < 0) {
+                d.tb = j * kSub;
+                d.t_beg = 0;
+                d.t_end = plen;
+                d.t_load = plen;
+                d.phys = sub_phys<BS>(lead, a.width, d.tb);
+            } else {
+                const int n = __builtin_amdgcn_readfirstlane(s_len[seg]);
+                d.tb = start_sub + (j - __builtin_amdgcn_readfirstlane(s_cum[seg])) * kSub;
+                d.t_beg = plen;
+                d.t_end = n;
+                d.t_load = fused ? n - 1 : n;
+                d.phys = sub_phys<BS>(a.tables + (int64_t)(s0 + seg) * a.width, a.width, d.tb);
+            }
+            return d;
+        };
+        auto load_sub = [&](KOp &K, VRows &V, const Sub &d) {
+            const SubRsrc r = sub_rsrc<BS>(d.phys, kp, vp, d.tb, d.t_load, head_off, blk_elems);
+            if (d.seg < 0) {
+                load_k<kLoadReuse>(K, r.k, lane);
+                load_v<kLoadReuse>(V, r.v, lane);
+            } else {
+                load_k<kLoadStream>(K, r.k, lane);
+                load_v<kLoadStream>(V, r.v, lane);
+            }
+        };
+        if (w < total) {
+            int seg_cur = -1;
+            Sub cur = describe(w, seg_cur);
+            int seg_nxt = seg_cur;
+            KOp K;
+            VRows V;
+            load_sub(K, V, cur);
+            for (int j = w; j < total; j += WAVES) {
+                const bool more_sub = j + WAVES < total;
+                Sub nxt = cur;
+                if (more_sub)
+                    nxt = describe(j + WAVES, seg_nxt);
+                const bool on = cur.seg < 0 ? active : (active && cm == cur.seg);
+                // the member's last sub-tile holds its new token: the parked rows
+                // stand in for the (unfetched) pool row
+                const bool here = fused && cur.seg >= 0 && cur.tb + kSub >= cur.t_end &&
+                                  cur.t_end > plen;
+                const int row = cur.t_end - 1 - cur.tb;
+                if (here && (lane & 15) == row) {
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        K.k[kk] = s_new[cur.seg][0][4 * kk + grp];
+                }
+                u32x2 pb;
+                float alpha;
+                const bool rs = qk_softmax<DT, true>(st, K, qop, cur.tb, cur.t_beg, cur.t_end,
+                                                     lane, a.scale_log2, pb, alpha, on);
+                __builtin_amdgcn_sched_barrier(0);
+                stage_v(V, vlds, lane);
+                if (here && lane < 16)
+                    *(u32x4 *)(vlds + row * kVStride + lane * 8) = s_new[cur.seg][1][lane];
+                __builtin_amdgcn_sched_barrier(0);
+                if (more_sub)
+                    load_sub(K, V, nxt);
+                __builtin_amdgcn_sched_barrier(0);
+                pv_mma<DT>(st, vlds, pb, rs, alpha, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                cur = nxt;
+            }
+        }
+        st.l = pair_sum32(pair_sum16(st.l));
+
+        __syncthreads();  // all waves are done with their V staging area
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+            *(f32x4 *)&sm.o[w][col][16 * jj + 4 * grp] = st.acc[jj];
+        if (grp == 0) {
+            s_m[w][col] = st.m;
+            s_l[w][col] = st.l;
+        }
+        if (tid < 16)
+            s_row[tid] = active ? (int64_t)cs * a.num_q_heads + ch : -1;
+        __syncthreads();
+        for (int e = tid; e < 16 * 32; e += WAVES * 64) {
+            const int qi = e >> 5, d0 = (e & 31) * 4;
+            const int64_t row = s_row[qi];
+            if (row < 0)
+                continue;
+            float M = s_m[0][qi];
+#pragma unroll
+            for (int i = 1; i < WAVES; ++i)
+                M = fmaxf(M, s_m[i][qi]);
+            const float ref = safe_ref(M);
+            float L = 0.f;
+            f32x4 O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < WAVES; ++i) {
+                const float wgt = fexp2(s_m[i][qi] - ref);
+                L += s_l[i][qi] * wgt;
+                O += *(const f32x4 *)&sm.o[i][qi][d0] * wgt;
+            }
+            f32x4 o = {0.f, 0.f, 0.f, 0.f};
+            if (L > 0.f)
+                o = O / L;
+            u32x2 packed;
+            packed.x = (uint32_t)to_bits<DT>(o[0]) | ((uint32_t)to_bits<DT>(o[1]) << 16);
+            packed.y = (uint32_t)to_bits<DT>(o[2]) | ((uint32_t)to_bits<DT>(o[3]) << 16);
+            *(u32x2 *)((uint16_t *)a.out + row * kHeadDim + d0) = packed;
+        }
+        __syncthreads();  // LDS is reused by the next group of the tile
+    }
+}
+
 }  // namespace
 
 // Waves per work-group (tuning knobs): the decode kernel, its suffix pass in
@@ -900,6 +1155,34 @@ static hipError_t launch_prefix_t(const DecodeArgs &a, int n_items, hipStream_t 
     hipLaunchKernelGGL((prefix_mfma_kernel<DT, BS, W>), dim3(n_items), dim3(W * 64), 0, stream,
                        a);
     return hipGetLastError();
+}
+
+template <int DT, int BS>
+static hipError_t launch_prefix_fused_t(const DecodeArgs &a, int n_items, hipStream_t stream)
+{
+    constexpr int W = PKV_PREFIX_WAVES;
+    hipLaunchKernelGGL((prefix_fused_mfma_kernel<DT, BS, W>), dim3(n_items), dim3(W * 64), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefix_fused_mfma(const DecodeArgs &a, int n_items, int dtype, int block_size,
+                                    hipStream_t stream)
+{
+#define PKV_PX_CASE(BSV)                                                                  \
+    case BSV:                                                                             \
+        return dtype == kFp16 ? launch_prefix_fused_t<kFp16, BSV>(a, n_items, stream)    \
+                              : launch_prefix_fused_t<kBf16, BSV>(a, n_items, stream);
+    switch (block_size) {
+        PKV_PX_CASE(16)
+        PKV_PX_CASE(32)
+        PKV_PX_CASE(64)
+        PKV_PX_CASE(128)
+        PKV_PX_CASE(256)
+    default:
+        return hipErrorInvalidValue;
+    }
+#undef PKV_PX_CASE
 }
 
 hipError_t launch_prefix_mfma(const DecodeArgs &a, int n_items, int dtype, int block_size,

@@ -22,6 +22,9 @@ hipError_t launch_prefix_mfma(const DecodeArgs &a, int n_items, int dtype, int b
 // Decode over slotted segment lists (one work-group per (sequence, KV head)).
 hipError_t launch_slotted_mfma(const DecodeArgs &a, int dtype, int block_size,
                                hipStream_t stream);
+// Shared-prefix decode in one pass over n_items (query tile, KV head) items.
+hipError_t launch_prefix_fused_mfma(const DecodeArgs &a, int n_items, int dtype, int block_size,
+                                    hipStream_t stream);
 hipError_t launch_reduce(void *out, const float *part_o, const float *part_lse,
                          const int32_t *lens, int num_seqs, int num_q_heads, int partition_size,
                          int max_partitions, int dtype, hipStream_t stream);

@@ -164,8 +164,7 @@ def test_prefix_decode_argument_errors(lib):
     assert call(out=None) == EINVAL
     assert call(PP=24, MP=4) == EINVAL          # prefix partition not a multiple of 16
     assert call(PP=16, MP=4) == EWORKSPACE      # 80 positions need 5 partitions of 16
-    assert call(MP=0) == EWORKSPACE
-    assert call(po=None) == EWORKSPACE
+    assert call(PP=16, MP=5, po=None) == EWORKSPACE
     assert call(Hq=34) == ENOTSUP               # group of 17 query heads
     assert call(B=8) == ENOTSUP
     assert call(cu=P((1 << 20) + 2)) == EINVAL  # misaligned group offsets
