@@ -47,7 +47,7 @@ struct TilePhys {
 // BS == 16).  Reading them does not depend on the context length, so they can
 // be requested before it is known.
 template <int BS>
-__device__ __forceinline__ TilePhys tile_entries(const int32_t *__restrict__ trow, int width,
+__device__ __forceinline__ TilePhys tile_entries(meta_ptr trow, int width,
                                                  int tb)
 {
     TilePhys p;
@@ -71,7 +71,7 @@ __device__ __forceinline__ TilePhys tile_select(TilePhys p, int tb, int t_end)
 }
 
 template <int BS>
-__device__ __forceinline__ TilePhys tile_phys(const int32_t *__restrict__ trow, int width, int tb,
+__device__ __forceinline__ TilePhys tile_phys(meta_ptr trow, int width, int tb,
                                               int t_end)
 {
     return tile_select<BS>(tile_entries<BS>(trow, width, tb), tb, t_end);
@@ -228,8 +228,11 @@ __device__ __forceinline__ void merge_pair(RowState<DT> &st)
 // whole context, with the loop folded away at compile time.
 // The register budget is capped so that 4 waves fit on each SIMD (the
 // split variant would otherwise be allocated past that occupancy).
+#ifndef PKV_G1_OCCUPANCY
+#define PKV_G1_OCCUPANCY 4  // waves per SIMD the register budget is capped for
+#endif
 template <int DT, int BS, int WAVES, bool SPLIT>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(PKV_G1_OCCUPANCY)))
 void decode_g1_kernel(DecodeArgs a)
 {
     __shared__ float s_acc[WAVES][kHeadDim];
@@ -256,7 +259,7 @@ void decode_g1_kernel(DecodeArgs a)
 
     const uint16_t *__restrict__ kp = (const uint16_t *)a.k_pool;
     const uint16_t *__restrict__ vp = (const uint16_t *)a.v_pool;
-    const int32_t *__restrict__ trow = a.tables + (int64_t)s * a.width;
+    const meta_ptr trow = as_meta(a.tables) + (int64_t)s * a.width;
     const int64_t blk_elems = (int64_t)a.num_kv_heads * BS * kHeadDim;
     const int64_t head_off = (int64_t)h * BS * kHeadDim;
     const int lane_byte = (r * kHeadDim + c * 8) * 2;
@@ -268,7 +271,7 @@ void decode_g1_kernel(DecodeArgs a)
     const int tb_first = (P > 0 ? px0 * P : 0) + w * kTile;
     const TilePhys e_first = tile_entries<BS>(trow, a.width, tb_first);
     const TilePhys e_next = tile_entries<BS>(trow, a.width, tb_first + WAVES * kTile);
-    const int n = a.lens[s];
+    const int n = as_meta(a.lens)[s];
     const bool fused = a.k_new != nullptr;
     if (fused && n <= 0 && px0 == 0 && h == 0 && tid == 0 && a.slot_out)
         a.slot_out[s] = -1;  // padding sequence: nothing appended

@@ -107,7 +107,7 @@ __device__ __forceinline__ SubRsrc sub_rsrc(int32_t phys, const uint16_t *kp, co
 // Table entry of the sub-tile at token tb; the index is clamped to the row so
 // that a lookahead past the last sub-tile reads a valid (unused) entry.
 template <int BS>
-__device__ __forceinline__ int32_t sub_phys(const int32_t *__restrict__ trow, int width, int tb)
+__device__ __forceinline__ int32_t sub_phys(meta_ptr trow, int width, int tb)
 {
     return trow[min(tb / BS, width - 1)];
 }
@@ -274,13 +274,13 @@ void decode_mfma_kernel(DecodeArgs a)
 
     const uint16_t *__restrict__ kp = (const uint16_t *)a.k_pool;
     const uint16_t *__restrict__ vp = (const uint16_t *)a.v_pool;
-    const int32_t *__restrict__ trow = a.tables + (int64_t)s * a.width;
+    const meta_ptr trow = as_meta(a.tables) + (int64_t)s * a.width;
     const int64_t blk_elems = (int64_t)a.num_kv_heads * BS * kHeadDim;
     const int64_t head_off = (int64_t)g * BS * kHeadDim;
     const int P = SPLIT ? a.partition_size : 0;
     // shared-prefix mode: this pass covers the positions after the group's prefix
     const int start = MODE == kModeSuffix
-                          ? a.prefix_lens[group_of(a.group_cu, a.num_groups, s)]
+                          ? as_meta(a.prefix_lens)[group_of(as_meta(a.group_cu), a.num_groups, s)]
                           : 0;
     const int start_sub = start & ~(kSub - 1);  // sub-tiles stay aligned to 16 positions
 
@@ -290,7 +290,7 @@ void decode_mfma_kernel(DecodeArgs a)
     const int tb_first = (P > 0 ? px0 * P : start_sub) + w * kSub;
     const int32_t e_first = sub_phys<BS>(trow, a.width, tb_first);
     const int32_t e_next = sub_phys<BS>(trow, a.width, tb_first + WAVES * kSub);
-    const int n = a.lens[s];
+    const int n = as_meta(a.lens)[s];
     const bool fused = a.k_new != nullptr;
     if (fused && n <= 0 && px0 == 0 && g == 0 && tid == 0 && a.slot_out)
         a.slot_out[s] = -1;  // padding sequence: nothing appended
@@ -583,16 +583,16 @@ void prefix_mfma_kernel(DecodeArgs a)
     const int cs = s0 + col / G;
     const int ch = g * G + col % G;
 
-    int k = group_of(a.group_cu, a.num_groups, s0);
+    int k = group_of(as_meta(a.group_cu), a.num_groups, s0);
     for (bool more = true; more; ++k) {
-        const int ga = a.group_cu[k], gb = a.group_cu[k + 1];
+        const int ga = as_meta(a.group_cu)[k], gb = as_meta(a.group_cu)[k + 1];
         more = gb < s_end;
-        const int plen = a.prefix_lens[k];
+        const int plen = as_meta(a.prefix_lens)[k];
         const int t0 = pp * PP;
         if (ga == gb || t0 >= plen)
             continue;  // uniform: an empty group, or no prefix in this partition
         const int t1 = min(plen, t0 + PP);
-        const int32_t *__restrict__ trow = a.tables + (int64_t)ga * a.width;
+        const meta_ptr trow = as_meta(a.tables) + (int64_t)ga * a.width;
         const bool active = col < spt * G && cs < s_end && cs >= ga && cs < gb;
 
         u32x4 qop[4];
@@ -904,6 +904,7 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
 
     const uint16_t *__restrict__ kp = (const uint16_t *)a.k_pool;
     const uint16_t *__restrict__ vp = (const uint16_t *)a.v_pool;
+    const meta_ptr tabs = as_meta(a.tables);
     const int64_t blk_elems = (int64_t)a.num_kv_heads * BS * kHeadDim;
     const int64_t head_off = (int64_t)g * BS * kHeadDim;
     uint16_t *vlds = sm.v[w];
@@ -911,15 +912,14 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
     const int cs = s0 + cm;
     const int ch = g * G + col % G;
 
-    int k = group_of(a.group_cu, a.num_groups, s0);
+    int k = group_of(as_meta(a.group_cu), a.num_groups, s0);
     for (bool more = true; more; ++k) {
-        const int ga = a.group_cu[k], gb = a.group_cu[k + 1];
+        const int ga = as_meta(a.group_cu)[k], gb = as_meta(a.group_cu)[k + 1];
         more = gb < s_end;
         if (ga == gb)
             continue;  // an empty group (uniform)
-        const int plen = a.prefix_lens[k];
+        const int plen = as_meta(a.prefix_lens)[k];
         const int start_sub = plen & ~(kSub - 1);
-        const int32_t *__restrict__ lead = a.tables + (int64_t)ga * a.width;
         const bool active = col < spt * G && cs < s_end && cs >= ga && cs < gb;
 
         // per-member lengths and the cumulative sub-tile counts
@@ -953,7 +953,7 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
                     continue;
                 const int s = s0 + i;
                 const int tn = n - 1;
-                const int64_t phys_n = a.tables[(int64_t)s * a.width + tn / BS];
+                const int64_t phys_n = tabs[(int64_t)s * a.width + tn / BS];
                 const int64_t off = ((int64_t)s * a.num_kv_heads + g) * kHeadDim;
                 const uint16_t *kq = (const uint16_t *)a.k_new + off;
                 const uint16_t *vq = (const uint16_t *)a.v_new + off;
@@ -1008,20 +1008,26 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
                 ++seg;
             Sub d;
             d.seg = seg;
+            int row;
             if (seg < 0) {
                 d.tb = j * kSub;
                 d.t_beg = 0;
                 d.t_end = plen;
                 d.t_load = plen;
-                d.phys = sub_phys<BS>(lead, a.width, d.tb);
+                row = ga;
             } else {
                 const int n = __builtin_amdgcn_readfirstlane(s_len[seg]);
                 d.tb = start_sub + (j - __builtin_amdgcn_readfirstlane(s_cum[seg])) * kSub;
                 d.t_beg = plen;
                 d.t_end = n;
                 d.t_load = fused ? n - 1 : n;
-                d.phys = sub_phys<BS>(a.tables + (int64_t)(s0 + seg) * a.width, a.width, d.tb);
+                row = s0 + seg;
             }
+            // a uniform index keeps the table lookup a scalar load: as a vector load
+            // it would wait (in-order vmcnt) for every K/V load in flight
+            const int64_t idx = (int64_t)__builtin_amdgcn_readfirstlane(row) * a.width +
+                                __builtin_amdgcn_readfirstlane(min(d.tb / BS, a.width - 1));
+            d.phys = tabs[idx];
             return d;
         };
         auto load_sub = [&](KOp &K, VRows &V, const Sub &d) {
@@ -1034,44 +1040,61 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
                 load_v<kLoadStream>(V, r.v, lane);
             }
         };
-        if (w < total) {
-            int seg_cur = -1;
-            Sub cur = describe(w, seg_cur);
-            int seg_nxt = seg_cur;
-            KOp K;
-            VRows V;
-            load_sub(K, V, cur);
-            for (int j = w; j < total; j += WAVES) {
-                const bool more_sub = j + WAVES < total;
-                Sub nxt = cur;
-                if (more_sub)
-                    nxt = describe(j + WAVES, seg_nxt);
-                const bool on = cur.seg < 0 ? active : (active && cm == cur.seg);
-                // the member's last sub-tile holds its new token: the parked rows
-                // stand in for the (unfetched) pool row
-                const bool here = fused && cur.seg >= 0 && cur.tb + kSub >= cur.t_end &&
-                                  cur.t_end > plen;
-                const int row = cur.t_end - 1 - cur.tb;
-                if (here && (lane & 15) == row) {
+        // Sub-tile i of this wave (j = w + i * WAVES) uses register buffer i % 2, so
+        // two sub-tiles are in flight per wave: the work-groups of this kernel are
+        // few (one per tile and KV head) and each streams a long list, so the
+        // per-wave bytes in flight set the rate.
+        auto step = [&](KOp &K, VRows &V, Sub &cur, int j, int &seg) {
+            const int jn = j + 2 * WAVES;  // the sub-tile this buffer takes next
+            const bool more_sub = jn < total;
+            Sub nxt = cur;
+            if (more_sub)
+                nxt = describe(jn, seg);
+            const bool on = cur.seg < 0 ? active : (active && cm == cur.seg);
+            // the member's last sub-tile holds its new token: the parked rows stand
+            // in for the (unfetched) pool row
+            const bool here =
+                fused && cur.seg >= 0 && cur.tb + kSub >= cur.t_end && cur.t_end > plen;
+            const int row = cur.t_end - 1 - cur.tb;
+            if (here && (lane & 15) == row) {
 #pragma unroll
-                    for (int kk = 0; kk < 4; ++kk)
-                        K.k[kk] = s_new[cur.seg][0][4 * kk + grp];
-                }
-                u32x2 pb;
-                float alpha;
-                const bool rs = qk_softmax<DT, true>(st, K, qop, cur.tb, cur.t_beg, cur.t_end,
-                                                     lane, a.scale_log2, pb, alpha, on);
-                __builtin_amdgcn_sched_barrier(0);
-                stage_v(V, vlds, lane);
-                if (here && lane < 16)
-                    *(u32x4 *)(vlds + row * kVStride + lane * 8) = s_new[cur.seg][1][lane];
-                __builtin_amdgcn_sched_barrier(0);
-                if (more_sub)
-                    load_sub(K, V, nxt);
-                __builtin_amdgcn_sched_barrier(0);
-                pv_mma<DT>(st, vlds, pb, rs, alpha, lane);
-                __builtin_amdgcn_sched_barrier(0);
-                cur = nxt;
+                for (int kk = 0; kk < 4; ++kk)
+                    K.k[kk] = s_new[cur.seg][0][4 * kk + grp];
+            }
+            u32x2 pb;
+            float alpha;
+            const bool rs = qk_softmax<DT, true>(st, K, qop, cur.tb, cur.t_beg, cur.t_end, lane,
+                                                 a.scale_log2, pb, alpha, on);
+            __builtin_amdgcn_sched_barrier(0);
+            stage_v(V, vlds, lane);
+            if (here && lane < 16)
+                *(u32x4 *)(vlds + row * kVStride + lane * 8) = s_new[cur.seg][1][lane];
+            __builtin_amdgcn_sched_barrier(0);
+            if (more_sub)
+                load_sub(K, V, nxt);
+            __builtin_amdgcn_sched_barrier(0);
+            pv_mma<DT>(st, vlds, pb, rs, alpha, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            cur = nxt;
+        };
+        if (w < total) {
+            // two cursors over the member list, one per buffer
+            int seg_a = -1, seg_b = -1;
+            Sub ca = describe(w, seg_a);
+            KOp KA, KB;
+            VRows VA, VB;
+            load_sub(KA, VA, ca);
+            const bool has_b = w + WAVES < total;
+            Sub cb = ca;
+            if (has_b) {
+                seg_b = seg_a;
+                cb = describe(w + WAVES, seg_b);
+                load_sub(KB, VB, cb);
+            }
+            for (int j = w; j < total; j += 2 * WAVES) {
+                step(KA, VA, ca, j, seg_a);
+                if (j + WAVES < total)
+                    step(KB, VB, cb, j + WAVES, seg_b);
             }
         }
         st.l = pair_sum32(pair_sum16(st.l));

@@ -169,6 +169,15 @@ __device__ __forceinline__ int xcd_item(int b, int n_items)
     return x * q + (x < r ? x : r) + j;
 }
 
+// Read-only metadata (block tables, lengths, group bounds, segment lists) does
+// not change while a kernel runs.  Read through the constant address space, a
+// wave-uniform entry compiles to a scalar load, whose wait (lgkmcnt) is separate
+// from the vector-memory counter.  Read through a generic pointer it becomes a
+// vector load, and since vmcnt retires in order, waiting for it also waits for
+// every K/V load the wave has in flight, draining the pipeline once per tile.
+typedef const __attribute__((address_space(4))) int32_t *meta_ptr;
+__device__ __forceinline__ meta_ptr as_meta(const int32_t *p) { return (meta_ptr)p; }
+
 // Kernel arguments of the decode kernels.
 struct DecodeArgs {
     void *out;                  // [S][Hq][D] dtype (single pass)
@@ -210,7 +219,7 @@ struct DecodeArgs {
 
 // Group of sequence s in shared-prefix mode: the largest k with group_cu[k] <= s.
 // `s` is uniform, so the search runs on scalar loads.
-__device__ __forceinline__ int group_of(const int32_t *__restrict__ cu, int num_groups, int s)
+__device__ __forceinline__ int group_of(meta_ptr cu, int num_groups, int s)
 {
     int lo = 0, hi = num_groups;
     while (hi - lo > 1) {
