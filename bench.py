@@ -364,7 +364,7 @@ def bench_step(args):
             "pool_blocks_per_layer": int(w0.num_blocks),
             "distinct_layer_pools": R,
             "partition_size": P,
-            "launches_per_layer": (1 if fused else 2) + (1 if (P or prefix) else 0),
+            "launches_per_layer": (1 if fused else 2) + (1 if P or (prefix and PP) else 0),
             "launch": "hip graph replay" if args.graph else "eager",
             "shared_prefix": cfg.prefix_tokens,
             "path": ("paged_attention_prefix_decode (prefix partition %d)" % PP if prefix
@@ -376,7 +376,8 @@ def bench_step(args):
         "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "step_algorithmic_bytes": step_bytes,
         "roofline": {
-            "kernel": ("paged_attention_prefix_decode (prefix + suffix pass)" if prefix
+            "kernel": (("paged_attention_prefix_decode (prefix + suffix pass)" if PP else
+                        "paged_attention_prefix_decode (one pass)") if prefix
                        else "paged_attention_append_decode" if fused
                        else "paged_attention_decode"),
             "bound": "hbm",

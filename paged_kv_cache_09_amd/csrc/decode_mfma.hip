@@ -873,10 +873,16 @@ void slotted_mfma_kernel(DecodeArgs a)
 // active: the other columns score -inf and keep their state).  The waves take
 // the concatenated list round-robin with the decode kernel's score / softmax /
 // P.V code, so every column ends with attention over exactly its sequence's n
-// positions; the optional append is done by the wave owning each member's last
-// sub-tile.  No partials leave the work-group.
+// positions.  The optional append is written to the pool in the prologue, before
+// a barrier, so the new rows are then read like any other.  No partials leave
+// the work-group.
+//
+// The prefix is re-read from L2 by every tile of the group: with 16-column tiles
+// the L2-to-CU traffic (prefix re-reads plus each member's own rows), not HBM,
+// bounds this kernel; more waves per work-group make each step slower by as much
+// as they add steps in flight.
 template <int DT, int BS, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
 void prefix_fused_mfma_kernel(DecodeArgs a)
 {
     __shared__ __attribute__((aligned(16))) union {
@@ -887,7 +893,6 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
     __shared__ int64_t s_row[16];       // output row of each query column, -1 if inactive
     __shared__ int32_t s_cum[17];       // sub-tiles before member i's own ones (s_cum[0]: prefix)
     __shared__ int32_t s_len[16];       // context length of member i (0 outside the group)
-    __shared__ u32x4 s_new[16][2][16];  // parked new K / V rows of member i (fused append)
 
     const int item = blockIdx.x;
     const int g = item % a.num_kv_heads;
@@ -940,55 +945,45 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
                 s_cum[i + 1] = c;
             }
         }
-        __syncthreads();
-        const int total = __builtin_amdgcn_readfirstlane(s_cum[16]);
-
-        // fused append: the wave that owns member i's last sub-tile writes its new
-        // rows now and parks them in LDS for that sub-tile
+        // Fused append, spread over the work-group: each thread moves one 16-byte
+        // chunk of a member's new K or V row to its slot.  The barrier below makes
+        // the rows visible to the whole work-group, so the member's last sub-tile
+        // then reads position n-1 from the pool like any other row (substituting
+        // the rows in registers instead cost about 50 registers per lane).
         if (fused) {
-            for (int i = 0; i < spt; ++i) {
-                const int n = __builtin_amdgcn_readfirstlane(s_len[i]);
-                const int last = __builtin_amdgcn_readfirstlane(s_cum[i + 1]) - 1;
-                if (n <= plen || last < 0 || last % WAVES != w)
-                    continue;
+            for (int e = tid; e < spt * 32; e += WAVES * 64) {
+                const int i = e >> 5, kv = (e >> 4) & 1, c = e & 15;
+                const int n = s_len[i];
+                if (n <= plen)
+                    continue;  // not in the group, or nothing to append past the prefix
                 const int s = s0 + i;
                 const int tn = n - 1;
                 const int64_t phys_n = tabs[(int64_t)s * a.width + tn / BS];
-                const int64_t off = ((int64_t)s * a.num_kv_heads + g) * kHeadDim;
-                const uint16_t *kq = (const uint16_t *)a.k_new + off;
-                const uint16_t *vq = (const uint16_t *)a.v_new + off;
-                u32x4 knew[4];
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    knew[kk] = *(const u32x4 *)(kq + 32 * kk + 8 * grp);
-                const u32x4 vnew = *(const u32x4 *)(vq + 8 * col);
-                const int64_t dst = phys_n * blk_elems + head_off + (int64_t)(tn % BS) * kHeadDim;
-                if (col == (tn & 15)) {
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk)
-                        *(u32x4 *)((uint16_t *)a.k_pool + dst + 32 * kk + 8 * grp) = knew[kk];
-                }
-                if (col == 0) {
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk)
-                        s_new[i][0][4 * kk + grp] = knew[kk];
-                }
-                if (lane < 16) {
-                    *(u32x4 *)((uint16_t *)a.v_pool + dst + lane * 8) = vnew;
-                    s_new[i][1][lane] = vnew;
-                }
-                if (g == 0 && lane == 0 && a.slot_out)
+                const int64_t src = ((int64_t)s * a.num_kv_heads + g) * kHeadDim + 8 * c;
+                const u32x4 val =
+                    *(const u32x4 *)((const uint16_t *)(kv ? a.v_new : a.k_new) + src);
+                const int64_t dst =
+                    phys_n * blk_elems + head_off + (int64_t)(tn % BS) * kHeadDim + 8 * c;
+                *(u32x4 *)((uint16_t *)(kv ? a.v_pool : a.k_pool) + dst) = val;
+                if (g == 0 && kv == 0 && c == 0 && a.slot_out)
                     a.slot_out[s] = phys_n * BS + tn % BS;
             }
         }
+        __syncthreads();
+        const int total = __builtin_amdgcn_readfirstlane(s_cum[16]);
 
+        // every lane loads a valid query row (inactive columns read a neighbour's
+        // and zero it): no load sits under a lane-dependent branch
         u32x4 qop[4];
         {
             const uint16_t *qrow = (const uint16_t *)a.q +
-                                   ((int64_t)cs * a.num_q_heads + ch) * kHeadDim + grp * 8;
+                                   ((int64_t)min(cs, s_end - 1) * a.num_q_heads + ch) * kHeadDim +
+                                   grp * 8;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                qop[kk] = active ? *(const u32x4 *)(qrow + kk * 32) : (u32x4){0u, 0u, 0u, 0u};
+            for (int kk = 0; kk < 4; ++kk) {
+                const u32x4 v = *(const u32x4 *)(qrow + kk * 32);
+                qop[kk] = active ? v : (u32x4){0u, 0u, 0u, 0u};
+            }
         }
         GqaState st;
         st.m = kNegInf;
@@ -997,105 +992,79 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
         for (int jj = 0; jj < 8; ++jj)
             st.acc[jj] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-        // sub-tile j: the prefix's (seg -1) or member seg's; the member cursor only
-        // moves forward, so the lookup is one or two LDS reads per sub-tile
+        // Sub-tile j: the prefix's (seg -1) or member seg's; the member cursor only
+        // moves forward, so the lookup is one or two LDS reads per sub-tile.  A j
+        // past the list describes an empty sub-tile (a zero-byte buffer range), so
+        // that every step issues its loads unconditionally: the compiler's count of
+        // loads in flight then agrees on every path, and each wait covers only the
+        // sub-tile it needs instead of draining both buffers.
         struct Sub {
             int seg, tb, t_beg, t_end, t_load;
             int32_t phys;
         };
         auto describe = [&](int j, int &seg) {
-            while (seg < 15 && j >= __builtin_amdgcn_readfirstlane(s_cum[seg + 1]))
+            const int jc = min(j, total - 1);
+            while (seg < 15 && jc >= __builtin_amdgcn_readfirstlane(s_cum[seg + 1]))
                 ++seg;
             Sub d;
             d.seg = seg;
             int row;
             if (seg < 0) {
-                d.tb = j * kSub;
+                d.tb = jc * kSub;
                 d.t_beg = 0;
                 d.t_end = plen;
                 d.t_load = plen;
                 row = ga;
             } else {
                 const int n = __builtin_amdgcn_readfirstlane(s_len[seg]);
-                d.tb = start_sub + (j - __builtin_amdgcn_readfirstlane(s_cum[seg])) * kSub;
+                d.tb = start_sub + (jc - __builtin_amdgcn_readfirstlane(s_cum[seg])) * kSub;
                 d.t_beg = plen;
                 d.t_end = n;
-                d.t_load = fused ? n - 1 : n;
+                d.t_load = n;
                 row = s0 + seg;
             }
-            // a uniform index keeps the table lookup a scalar load: as a vector load
-            // it would wait (in-order vmcnt) for every K/V load in flight
+            if (j != jc)
+                d.t_load = d.tb;
             const int64_t idx = (int64_t)__builtin_amdgcn_readfirstlane(row) * a.width +
                                 __builtin_amdgcn_readfirstlane(min(d.tb / BS, a.width - 1));
             d.phys = tabs[idx];
             return d;
         };
+        // One cache policy for the whole list (the default one, which keeps the
+        // prefix in L2 for the group's other tiles): a policy chosen per sub-tile
+        // would split the loads over two code paths.
         auto load_sub = [&](KOp &K, VRows &V, const Sub &d) {
             const SubRsrc r = sub_rsrc<BS>(d.phys, kp, vp, d.tb, d.t_load, head_off, blk_elems);
-            if (d.seg < 0) {
-                load_k<kLoadReuse>(K, r.k, lane);
-                load_v<kLoadReuse>(V, r.v, lane);
-            } else {
-                load_k<kLoadStream>(K, r.k, lane);
-                load_v<kLoadStream>(V, r.v, lane);
-            }
+            load_k<kLoadReuse>(K, r.k, lane);
+            load_v<kLoadReuse>(V, r.v, lane);
         };
-        // Sub-tile i of this wave (j = w + i * WAVES) uses register buffer i % 2, so
-        // two sub-tiles are in flight per wave: the work-groups of this kernel are
-        // few (one per tile and KV head) and each streams a long list, so the
-        // per-wave bytes in flight set the rate.
-        auto step = [&](KOp &K, VRows &V, Sub &cur, int j, int &seg) {
-            const int jn = j + 2 * WAVES;  // the sub-tile this buffer takes next
-            const bool more_sub = jn < total;
-            Sub nxt = cur;
-            if (more_sub)
-                nxt = describe(jn, seg);
+        // Sub-tiles w, w + WAVES, ... belong to this wave: the scores of the current
+        // one are computed, then the next one's loads are issued into the same
+        // registers, overlapping the softmax and P.V of the current sub-tile.
+        auto step = [&](KOp &K, VRows &V, Sub &cur, int jn, int &seg) {
+            const Sub nxt = describe(jn, seg);
             const bool on = cur.seg < 0 ? active : (active && cm == cur.seg);
-            // the member's last sub-tile holds its new token: the parked rows stand
-            // in for the (unfetched) pool row
-            const bool here =
-                fused && cur.seg >= 0 && cur.tb + kSub >= cur.t_end && cur.t_end > plen;
-            const int row = cur.t_end - 1 - cur.tb;
-            if (here && (lane & 15) == row) {
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    K.k[kk] = s_new[cur.seg][0][4 * kk + grp];
-            }
             u32x2 pb;
             float alpha;
             const bool rs = qk_softmax<DT, true>(st, K, qop, cur.tb, cur.t_beg, cur.t_end, lane,
                                                  a.scale_log2, pb, alpha, on);
             __builtin_amdgcn_sched_barrier(0);
             stage_v(V, vlds, lane);
-            if (here && lane < 16)
-                *(u32x4 *)(vlds + row * kVStride + lane * 8) = s_new[cur.seg][1][lane];
             __builtin_amdgcn_sched_barrier(0);
-            if (more_sub)
-                load_sub(K, V, nxt);
+            load_sub(K, V, nxt);
             __builtin_amdgcn_sched_barrier(0);
             pv_mma<DT>(st, vlds, pb, rs, alpha, lane);
             __builtin_amdgcn_sched_barrier(0);
             cur = nxt;
         };
         if (w < total) {
-            // two cursors over the member list, one per buffer
-            int seg_a = -1, seg_b = -1;
-            Sub ca = describe(w, seg_a);
-            KOp KA, KB;
-            VRows VA, VB;
-            load_sub(KA, VA, ca);
-            const bool has_b = w + WAVES < total;
-            Sub cb = ca;
-            if (has_b) {
-                seg_b = seg_a;
-                cb = describe(w + WAVES, seg_b);
-                load_sub(KB, VB, cb);
-            }
-            for (int j = w; j < total; j += 2 * WAVES) {
-                step(KA, VA, ca, j, seg_a);
-                if (j + WAVES < total)
-                    step(KB, VB, cb, j + WAVES, seg_b);
-            }
+            int seg = -1;
+            Sub cur = describe(w, seg);
+            KOp K;
+            VRows V;
+            load_sub(K, V, cur);
+            for (int j = w; j < total; j += WAVES)
+                step(K, V, cur, j + WAVES, seg);
         }
         st.l = pair_sum32(pair_sum16(st.l));
 
