@@ -146,6 +146,38 @@ def time_launches(fn, reps: int, warm: int = 2) -> float:
     return e0.elapsed_time(e1) / reps
 
 
+def time_launches_graph(fn, reps: int) -> tuple:
+    """Average duration in ms of fn()'s launches with no host time between them:
+    `reps` calls are captured in one HIP graph and a replay of it is timed between
+    two events on the stream it runs on.  Eager launches of short kernels leave the
+    GPU idle while Python marshals the next call, which would count as kernel time.
+    Falls back to eager back-to-back launches if capture fails.  Returns (ms, how)."""
+    import torch
+    try:
+        fn()
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(reps):
+                fn()
+        graph.replay()
+        torch.cuda.synchronize()
+    except RuntimeError:
+        return time_launches(fn, reps), "eager back-to-back launches"
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps, "hip graph replay of back-to-back launches"
+
+
 def roofline(kernel: str, nbytes: int, ms: float, traffic):
     gbps = nbytes / (ms * 1e-3) / 1e9
     return {"kernel": kernel, "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
@@ -308,21 +340,16 @@ def bench_step(args):
     ms_per_step = t0.elapsed_time(t1) / args.steps
 
     # ---- average duration of the dominant kernel -----------------------------------
-    # The decode launches of the step (same arguments, same layer pools) are queued
-    # back to back between two HIP events on the stream they run on; the elapsed
-    # time over the launch count is the kernel's average duration (the queue keeps
-    # the dispatches back to back, so inter-kernel gaps are small).
+    # The decode launches of the step (same arguments, same layer pools) run back
+    # to back from a HIP graph, timed by two events on the stream they run on; the
+    # elapsed time over the launch count is the kernel's average duration.
     reps = max(1, min(args.steps, 10))
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for li in range(cfg.num_layers):
-        attend(li)
-    d0.record()
-    for _ in range(reps):
+
+    def attend_all():
         for li in range(cfg.num_layers):
             attend(li)
-    d1.record()
-    torch.cuda.synchronize()
-    decode_ms = d0.elapsed_time(d1) / (reps * cfg.num_layers)
+    decode_ms, kernel_timing = time_launches_graph(attend_all, reps)
+    decode_ms /= cfg.num_layers
     if P:  # leave `out` holding the merged result of the last timed step
         step()
         torch.cuda.synchronize()
@@ -390,6 +417,7 @@ def bench_step(args):
                                          "decode_g1" if Hq == cfg.num_kv_heads else "decode_mfma")),
             "bytes_per_launch": kernel_bytes,
             "avg_launch_ms": round(decode_ms, 5),
+            "timing": kernel_timing,
         },
         "logical_bytes_per_layer": logical["layer"],
         "setup_s": round(setup_s, 1),
