@@ -211,7 +211,7 @@ def main():
         copy_reference()
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "bench.py drives one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     if args.op == "append_tokens":
