@@ -331,13 +331,16 @@ def bench_step(args):
         graph.replay()
         torch.cuda.synchronize()
         run = graph.replay
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(args.steps):
+    # one event between consecutive steps: the first and last bracket the K steps
+    # (ms_per_step), the ones between give each step's own time (percentiles)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record()
+    for i in range(args.steps):
         run()
-    t1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
+    ms_per_step = ev[0].elapsed_time(ev[-1]) / args.steps
+    step_ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
 
     # ---- average duration of the dominant kernel -----------------------------------
     # The decode launches of the step (same arguments, same layer pools) run back
@@ -376,6 +379,7 @@ def bench_step(args):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "step_ms_p10_p50_p90": [round(float(x), 4) for x in np.percentile(step_ms, [10, 50, 90])],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -665,6 +669,14 @@ def cpu_baseline(w, cfg, scale, budget_s):
         reps += 1
     per_layer = spent / reps
     step_s = per_layer * c.num_layers
+    # the same layer once more on one thread (the append is idempotent: same rows,
+    # same slots)
+    t = time.perf_counter()
+    O.append(kp, vp, w.k_new, w.v_new, w.tables, w.lengths, c.block_size, w.num_blocks)
+    O.attention(w.q, kp, vp, w.tables, w.lengths, c.num_kv_heads, c.block_size, w.num_blocks,
+                scale, c.dtype, 1)
+    one_s = (time.perf_counter() - t) * c.num_layers
+    O.max_threads(threads)  # the thread count set for the run above persists
     return {
         "value": round(c.num_seqs / step_s, 3),
         "unit": "tokens/s",
@@ -673,7 +685,20 @@ def cpu_baseline(w, cfg, scale, budget_s):
         "sample": (f"layer 0 of {c.num_layers} ({c.num_seqs} sequences x {c.num_q_heads} heads, "
                    f"append + fp64 attention), {reps} repetitions, {spent:.1f} s; "
                    f"step time = per-layer time x {c.num_layers}"),
+        "single_thread_value": round(c.num_seqs / one_s, 3),
+        "cpu_model": _cpu_model(),
     }
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 if __name__ == "__main__":
