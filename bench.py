@@ -428,7 +428,18 @@ def bench_step(args):
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w0, cfg, scale, args.cpu_seconds)
+        result["cpu_baseline"], ref = cpu_baseline(w0, cfg, scale, args.cpu_seconds)
+        # the oracle's layer-0 output (computed by that baseline run) against the
+        # GPU's layer-0 output of the last timed step
+        got = out[0].float().cpu().numpy().astype(np.float64)
+        err = np.abs(got - ref)
+        result["parity_vs_oracle"] = {
+            "layer": 0,
+            "max_abs_err": float(err.max()),
+            "within_tolerance": bool(np.all(err <= 1e-2 + 1e-2 * np.abs(ref))),
+            "tolerance": "|gpu - oracle| <= 1e-2 + 1e-2 |oracle|, elementwise",
+        }
+    result["rocm"] = torch.version.hip
 
     print(json.dumps(result), flush=True)
 
@@ -652,7 +663,8 @@ def bench_slotted(args):
 def cpu_baseline(w, cfg, scale, budget_s):
     """Time the fp64 oracle on one layer of the same workload (append + attention of
     every sequence and head), repeated until about `budget_s` seconds of CPU time,
-    and scale to the whole step (all layers)."""
+    and scale to the whole step (all layers).  Returns the baseline record and the
+    oracle's output of that layer."""
     from oracle import oracle as O
     c = cfg
     kp, vp = O.new_pools(w.num_blocks, c.num_kv_heads, c.block_size, c.head_dim, w.nan_bits)
@@ -663,8 +675,8 @@ def cpu_baseline(w, cfg, scale, budget_s):
     while reps == 0 or (spent < budget_s and reps < 50):
         t = time.perf_counter()
         O.append(kp, vp, w.k_new, w.v_new, w.tables, w.lengths, c.block_size, w.num_blocks)
-        O.attention(w.q, kp, vp, w.tables, w.lengths, c.num_kv_heads, c.block_size,
-                    w.num_blocks, scale, c.dtype, threads)
+        ref = O.attention(w.q, kp, vp, w.tables, w.lengths, c.num_kv_heads, c.block_size,
+                          w.num_blocks, scale, c.dtype, threads)
         spent += time.perf_counter() - t
         reps += 1
     per_layer = spent / reps
@@ -687,7 +699,7 @@ def cpu_baseline(w, cfg, scale, budget_s):
                    f"step time = per-layer time x {c.num_layers}"),
         "single_thread_value": round(c.num_seqs / one_s, 3),
         "cpu_model": _cpu_model(),
-    }
+    }, ref
 
 
 def _cpu_model() -> str:
