@@ -498,7 +498,7 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
         a.group_cu = pg.group_cu;
         a.prefix_lens = pg.prefix_lens;
         a.num_groups = pg.num_groups;
-        a.seqs_per_tile = 16 / group;
+        a.seqs_per_tile = pkv::kPrefixHalves * (16 / group);
         const int64_t tiles = (num_seqs + a.seqs_per_tile - 1) / a.seqs_per_tile;
         const int64_t fitems = tiles * num_kv_heads;
         if (fitems > INT32_MAX)

@@ -864,41 +864,78 @@ void slotted_mfma_kernel(DecodeArgs a)
     }
 }
 
-// Shared-prefix decode in one pass.  One work-group per (16-row query tile, KV
-// head), the tile holding the G query heads of floor(16/G) consecutive member
-// sequences of a group.  The work-group's sub-tiles are the group's prefix
-// (positions 0 .. prefix_len-1, read once through the first member's table with
-// every member's columns active) followed by each member's own positions
-// (prefix_len .. n-1, read through its own table with only its G columns
-// active: the other columns score -inf and keep their state).  The waves take
-// the concatenated list round-robin with the decode kernel's score / softmax /
-// P.V code, so every column ends with attention over exactly its sequence's n
-// positions.  The optional append is written to the pool in the prologue, before
-// a barrier, so the new rows are then read like any other.  No partials leave
-// the work-group.
+// P.V of one staged sub-tile for NH column halves: the V^T operand is read from
+// LDS once (eight transposing reads into separate registers) and multiplied with
+// each half's probabilities.
+template <int DT, int NH>
+__device__ __forceinline__ void pv_mma_halves(GqaState (&st)[NH], const uint16_t *vlds,
+                                              const u32x2 (&pb)[NH], const bool (&rescale)[NH],
+                                              const float (&alpha)[NH], int lane)
+{
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const int j = lane & 15, grp = lane >> 4;
+    const uint16_t *base = vlds + (4 * grp + (j >> 2)) * kVStride + 4 * (j & 3);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    i16x4 va[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+        va[jj] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + 16 * jj));
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        if (rescale[h]) {
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj)
+                st[h].acc[jj] *= alpha[h];
+        }
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+            st[h].acc[jj] = mfma_pv<DT>(__builtin_bit_cast(u32x2, va[jj]), pb[h], st[h].acc[jj]);
+    }
+    // the next sub-tile's LDS writes must not pass these reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Shared-prefix decode in one pass.  One work-group per (query tile, KV head).  A
+// tile is NH halves of 16 MFMA columns; each half holds the G query heads of
+// floor(16/G) consecutive member sequences of a group.  The work-group's
+// sub-tiles are the group's prefix (positions 0 .. prefix_len-1, read once
+// through the first member's table with every member's columns active) followed
+// by each member's own positions (prefix_len .. n-1, read through its own table
+// with only its G columns active: the other columns score -inf and keep their
+// state).  The waves take the concatenated list round-robin with the decode
+// kernel's score / softmax / P.V code, so every column ends with attention over
+// exactly its sequence's n positions.  The optional append is written to the pool
+// in the prologue, before a barrier, so the new rows are then read like any
+// other.  No partials leave the work-group.
 //
-// The prefix is re-read from L2 by every tile of the group: with 16-column tiles
-// the L2-to-CU traffic (prefix re-reads plus each member's own rows), not HBM,
-// bounds this kernel; more waves per work-group make each step slower by as much
-// as they add steps in flight.
-template <int DT, int BS, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(4)))
+// The prefix is re-read from L2 by every tile of the group, and L2-to-CU
+// delivery (about 12 TB/s for this access pattern on MI355X, measured with a
+// plain read probe), not HBM, bounds the kernel.  Two halves per tile (NH = 2)
+// halve the prefix re-reads: each K/V sub-tile feeds 32 columns, at the cost of
+// twice the score and P.V work per prefix sub-tile.
+template <int DT, int BS, int WAVES, int NH>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 4 : 2)))
 void prefix_fused_mfma_kernel(DecodeArgs a)
 {
+    constexpr int kCols = 16 * NH;   // query columns of a tile
+    constexpr int kMembers = kCols;  // most member sequences of a tile (G = 1)
     __shared__ __attribute__((aligned(16))) union {
         uint16_t v[WAVES][kSub * kVStride];
-        float o[WAVES][16][kOStride];
+        float o[WAVES][kCols][kOStride];
     } sm;
-    __shared__ float s_m[WAVES][16], s_l[WAVES][16];
-    __shared__ int64_t s_row[16];       // output row of each query column, -1 if inactive
-    __shared__ int32_t s_cum[17];       // sub-tiles before member i's own ones (s_cum[0]: prefix)
-    __shared__ int32_t s_len[16];       // context length of member i (0 outside the group)
+    __shared__ float s_m[WAVES][kCols], s_l[WAVES][kCols];
+    __shared__ int64_t s_row[kCols];         // output row of each query column, -1 if inactive
+    __shared__ int32_t s_cum[kMembers + 1];  // sub-tiles before member i's own ones (s_cum[0]: prefix)
+    __shared__ int32_t s_len[kMembers];      // context length of member i (0 outside the group)
 
     const int item = blockIdx.x;
     const int g = item % a.num_kv_heads;
     const int tile = item / a.num_kv_heads;
     const int G = a.num_q_heads / a.num_kv_heads;
-    const int spt = a.seqs_per_tile;
+    const int spt = a.seqs_per_tile;  // NH * floor(16 / G)
+    const int sph = spt / NH;         // member sequences per half
     const int s0 = tile * spt;
     const int s_end = min(a.num_seqs, s0 + spt);
     const int tid = threadIdx.x;
@@ -913,9 +950,11 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
     const int64_t blk_elems = (int64_t)a.num_kv_heads * BS * kHeadDim;
     const int64_t head_off = (int64_t)g * BS * kHeadDim;
     uint16_t *vlds = sm.v[w];
-    const int cm = col / G;              // member of this lane's query column
-    const int cs = s0 + cm;
-    const int ch = g * G + col % G;
+    const int ch = g * G + col % G;  // query head of this lane's column
+    int cm[NH];                      // member of this lane's column in each half
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+        cm[h] = h * sph + col / G;
 
     int k = group_of(as_meta(a.group_cu), a.num_groups, s0);
     for (bool more = true; more; ++k) {
@@ -925,10 +964,15 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
             continue;  // an empty group (uniform)
         const int plen = as_meta(a.prefix_lens)[k];
         const int start_sub = plen & ~(kSub - 1);
-        const bool active = col < spt * G && cs < s_end && cs >= ga && cs < gb;
+        bool active[NH];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            const int cs = s0 + cm[h];
+            active[h] = col < sph * G && cs < s_end && cs >= ga && cs < gb;
+        }
 
         // per-member lengths and the cumulative sub-tile counts
-        if (tid < 16) {
+        if (tid < kMembers) {
             const int s = s0 + tid;
             const bool in = tid < spt && s < s_end && s >= ga && s < gb;
             s_len[tid] = in ? a.lens[s] : 0;
@@ -939,7 +983,7 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
         if (tid == 0) {
             int c = (plen + kSub - 1) / kSub;
             s_cum[0] = c;
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 0; i < kMembers; ++i) {
                 const int n = s_len[i];
                 c += n > start_sub ? (n - start_sub + kSub - 1) / kSub : 0;
                 s_cum[i + 1] = c;
@@ -970,41 +1014,45 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
             }
         }
         __syncthreads();
-        const int total = __builtin_amdgcn_readfirstlane(s_cum[16]);
+        const int total = __builtin_amdgcn_readfirstlane(s_cum[kMembers]);
 
         // every lane loads a valid query row (inactive columns read a neighbour's
         // and zero it): no load sits under a lane-dependent branch
-        u32x4 qop[4];
-        {
-            const uint16_t *qrow = (const uint16_t *)a.q +
-                                   ((int64_t)min(cs, s_end - 1) * a.num_q_heads + ch) * kHeadDim +
-                                   grp * 8;
+        u32x4 qop[NH][4];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            const uint16_t *qrow =
+                (const uint16_t *)a.q +
+                ((int64_t)min(s0 + cm[h], s_end - 1) * a.num_q_heads + ch) * kHeadDim + grp * 8;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 const u32x4 v = *(const u32x4 *)(qrow + kk * 32);
-                qop[kk] = active ? v : (u32x4){0u, 0u, 0u, 0u};
+                qop[h][kk] = active[h] ? v : (u32x4){0u, 0u, 0u, 0u};
             }
         }
-        GqaState st;
-        st.m = kNegInf;
-        st.l = 0.f;
+        GqaState st[NH];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-            st.acc[jj] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < NH; ++h) {
+            st[h].m = kNegInf;
+            st[h].l = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj)
+                st[h].acc[jj] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
 
         // Sub-tile j: the prefix's (seg -1) or member seg's; the member cursor only
         // moves forward, so the lookup is one or two LDS reads per sub-tile.  A j
         // past the list describes an empty sub-tile (a zero-byte buffer range), so
         // that every step issues its loads unconditionally: the compiler's count of
         // loads in flight then agrees on every path, and each wait covers only the
-        // sub-tile it needs instead of draining both buffers.
+        // sub-tile it needs.
         struct Sub {
             int seg, tb, t_beg, t_end, t_load;
             int32_t phys;
         };
         auto describe = [&](int j, int &seg) {
             const int jc = min(j, total - 1);
-            while (seg < 15 && jc >= __builtin_amdgcn_readfirstlane(s_cum[seg + 1]))
+            while (seg < kMembers - 1 && jc >= __builtin_amdgcn_readfirstlane(s_cum[seg + 1]))
                 ++seg;
             Sub d;
             d.seg = seg;
@@ -1043,17 +1091,21 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
         // registers, overlapping the softmax and P.V of the current sub-tile.
         auto step = [&](KOp &K, VRows &V, Sub &cur, int jn, int &seg) {
             const Sub nxt = describe(jn, seg);
-            const bool on = cur.seg < 0 ? active : (active && cm == cur.seg);
-            u32x2 pb;
-            float alpha;
-            const bool rs = qk_softmax<DT, true>(st, K, qop, cur.tb, cur.t_beg, cur.t_end, lane,
-                                                 a.scale_log2, pb, alpha, on);
+            u32x2 pb[NH];
+            float alpha[NH];
+            bool rs[NH];
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+                const bool on = cur.seg < 0 ? active[h] : (active[h] && cm[h] == cur.seg);
+                rs[h] = qk_softmax<DT, true>(st[h], K, qop[h], cur.tb, cur.t_beg, cur.t_end,
+                                             lane, a.scale_log2, pb[h], alpha[h], on);
+            }
             __builtin_amdgcn_sched_barrier(0);
             stage_v(V, vlds, lane);
             __builtin_amdgcn_sched_barrier(0);
             load_sub(K, V, nxt);
             __builtin_amdgcn_sched_barrier(0);
-            pv_mma<DT>(st, vlds, pb, rs, alpha, lane);
+            pv_mma_halves<DT, NH>(st, vlds, pb, rs, alpha, lane);
             __builtin_amdgcn_sched_barrier(0);
             cur = nxt;
         };
@@ -1066,20 +1118,29 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
             for (int j = w; j < total; j += WAVES)
                 step(K, V, cur, j + WAVES, seg);
         }
-        st.l = pair_sum32(pair_sum16(st.l));
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+            st[h].l = pair_sum32(pair_sum16(st[h].l));
 
         __syncthreads();  // all waves are done with their V staging area
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-            *(f32x4 *)&sm.o[w][col][16 * jj + 4 * grp] = st.acc[jj];
-        if (grp == 0) {
-            s_m[w][col] = st.m;
-            s_l[w][col] = st.l;
+        for (int h = 0; h < NH; ++h) {
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj)
+                *(f32x4 *)&sm.o[w][16 * h + col][16 * jj + 4 * grp] = st[h].acc[jj];
+            if (grp == 0) {
+                s_m[w][16 * h + col] = st[h].m;
+                s_l[w][16 * h + col] = st[h].l;
+            }
         }
-        if (tid < 16)
-            s_row[tid] = active ? (int64_t)cs * a.num_q_heads + ch : -1;
+        if (tid < kCols) {
+            const int h = tid / 16, c = tid % 16;
+            const int mi = h * sph + c / G, cs = s0 + mi;
+            const bool act = c < sph * G && cs < s_end && cs >= ga && cs < gb;
+            s_row[tid] = act ? (int64_t)cs * a.num_q_heads + g * G + c % G : -1;
+        }
         __syncthreads();
-        for (int e = tid; e < 16 * 32; e += WAVES * 64) {
+        for (int e = tid; e < kCols * 32; e += WAVES * 64) {
             const int qi = e >> 5, d0 = (e & 31) * 4;
             const int64_t row = s_row[qi];
             if (row < 0)
@@ -1122,6 +1183,11 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
 #ifndef PKV_PREFIX_WAVES
 #define PKV_PREFIX_WAVES 4
 #endif
+// one-pass shared-prefix kernel (8 waves measured faster than 4 with two halves
+// per tile; its LDS merge area allows at most 8)
+#ifndef PKV_PFX_FUSED_WAVES
+#define PKV_PFX_FUSED_WAVES 8
+#endif
 
 template <int DT, int BS>
 static hipError_t launch_mfma_t(const DecodeArgs &a, hipStream_t stream)
@@ -1152,9 +1218,9 @@ static hipError_t launch_prefix_t(const DecodeArgs &a, int n_items, hipStream_t 
 template <int DT, int BS>
 static hipError_t launch_prefix_fused_t(const DecodeArgs &a, int n_items, hipStream_t stream)
 {
-    constexpr int W = PKV_PREFIX_WAVES;
-    hipLaunchKernelGGL((prefix_fused_mfma_kernel<DT, BS, W>), dim3(n_items), dim3(W * 64), 0,
-                       stream, a);
+    constexpr int W = PKV_PFX_FUSED_WAVES;
+    hipLaunchKernelGGL((prefix_fused_mfma_kernel<DT, BS, W, kPrefixHalves>), dim3(n_items),
+                       dim3(W * 64), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -22,7 +22,13 @@ hipError_t launch_prefix_mfma(const DecodeArgs &a, int n_items, int dtype, int b
 // Decode over slotted segment lists (one work-group per (sequence, KV head)).
 hipError_t launch_slotted_mfma(const DecodeArgs &a, int dtype, int block_size,
                                hipStream_t stream);
-// Shared-prefix decode in one pass over n_items (query tile, KV head) items.
+// Shared-prefix decode in one pass over n_items (query tile, KV head) items.  A
+// tile is kPrefixHalves halves of 16 query columns, each half floor(16 / G)
+// member sequences (tuning knob: 1 or 2).
+#ifndef PKV_PREFIX_HALVES
+#define PKV_PREFIX_HALVES 2
+#endif
+constexpr int kPrefixHalves = PKV_PREFIX_HALVES;
 hipError_t launch_prefix_fused_mfma(const DecodeArgs &a, int n_items, int dtype, int block_size,
                                     hipStream_t stream);
 hipError_t launch_reduce(void *out, const float *part_o, const float *part_lse,
