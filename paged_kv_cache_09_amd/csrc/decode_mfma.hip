@@ -1141,11 +1141,21 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
             float alpha[NH];
             bool rs[NH];
             const KOp KA = k_operand(K, klds, lane);
+            // a prefix sub-tile that the prefix fills needs no mask: its positions
+            // are all in range, and a column outside the tile only updates a state
+            // that is never written out
+            if (cur.seg < 0 && cur.tb + kSub <= cur.t_end) {
 #pragma unroll
-            for (int h = 0; h < NH; ++h) {
-                const bool on = cur.seg < 0 ? active[h] : (active[h] && cm[h] == cur.seg);
-                rs[h] = qk_softmax<DT, true>(st[h], KA, qop[h], cur.tb, cur.t_beg, cur.t_end,
-                                             lane, a.scale_log2, pb[h], alpha[h], on);
+                for (int h = 0; h < NH; ++h)
+                    rs[h] = qk_softmax<DT, false>(st[h], KA, qop[h], cur.tb, 0, cur.t_end, lane,
+                                                  a.scale_log2, pb[h], alpha[h]);
+            } else {
+#pragma unroll
+                for (int h = 0; h < NH; ++h) {
+                    const bool on = cur.seg < 0 ? active[h] : (active[h] && cm[h] == cur.seg);
+                    rs[h] = qk_softmax<DT, true>(st[h], KA, qop[h], cur.tb, cur.t_beg, cur.t_end,
+                                                 lane, a.scale_log2, pb[h], alpha[h], on);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
             stage_v(V, vlds, lane);
