@@ -22,31 +22,68 @@ struct ReduceArgs {
     int num_seqs, num_q_heads, partition_size, max_partitions;
 };
 
+// Max over the 64 lanes of a wave (every lane gets the result).
+__device__ __forceinline__ float wave_max(float x)
+{
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1)
+        x = fmaxf(x, xor_lane(x, m));
+    return x;
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a)
 {
-    const int wave = (blockIdx.x * 256 + threadIdx.x) >> 6;
+    // the wave index is uniform: the length and the partition count come from
+    // scalar loads, and every loop below is wave-uniform
+    const int wave = __builtin_amdgcn_readfirstlane((blockIdx.x * 256 + threadIdx.x) >> 6);
     const int lane = threadIdx.x & 63;
     if (wave >= a.num_seqs * a.num_q_heads)
         return;
     const int s = wave / a.num_q_heads;
-    const int n = a.lens[s];
+    const int n = as_meta(a.lens)[s];
     const int np = n > 0 ? (n + a.partition_size - 1) / a.partition_size : 0;
     const int64_t row = wave;
     const float *lse = a.part_lse + row * a.max_partitions;
     const float *po = a.part_o + row * a.max_partitions * kHeadDim + 2 * lane;
 
+    // partition p's lse is read by lane p % 64 (one load for up to 64 partitions),
+    // instead of a dependent chain of loads
     float M = kNegInf;
-    for (int p = 0; p < np; ++p)
-        M = fmaxf(M, lse[p]);
+    for (int p0 = 0; p0 < np; p0 += 64) {
+        const int p = p0 + lane;
+        M = fmaxf(M, p < np ? lse[p] : kNegInf);
+    }
+    M = wave_max(M);
     const float ref = safe_ref(M);
     float W = 0.f, o0 = 0.f, o1 = 0.f;
-    for (int p = 0; p < np; ++p) {
-        const float wgt = fexp2((lse[p] - ref) * kLog2e);
-        const float2 v = *(const float2 *)(po + (int64_t)p * kHeadDim);
-        W += wgt;
-        o0 += wgt * v.x;
-        o1 += wgt * v.y;
+    for (int p0 = 0; p0 < np; p0 += 64) {
+        const int p = p0 + lane;
+        const float wl = p < np ? fexp2((lse[p] - ref) * kLog2e) : 0.f;
+        const int cnt = min(64, np - p0);
+        // the partition rows are independent loads: four are in flight together
+        int i = 0;
+        for (; i + 4 <= cnt; i += 4) {
+            float2 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                v[u] = *(const float2 *)(po + (int64_t)(p0 + i + u) * kHeadDim);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float wgt =
+                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i + u));
+                W += wgt;
+                o0 += wgt * v[u].x;
+                o1 += wgt * v[u].y;
+            }
+        }
+        for (; i < cnt; ++i) {
+            const float wgt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i));
+            const float2 v = *(const float2 *)(po + (int64_t)(p0 + i) * kHeadDim);
+            W += wgt;
+            o0 += wgt * v.x;
+            o1 += wgt * v.y;
+        }
     }
     const float inv = W > 0.f ? 1.f / W : 0.f;
     const uint32_t packed = (uint32_t)to_bits<DT>(o0 * inv) | ((uint32_t)to_bits<DT>(o1 * inv) << 16);
