@@ -231,7 +231,10 @@ def bench_step(args):
 
     cfg = get_config(args.config)
     P = cfg.bench_partition_size if args.partition_size is None else args.partition_size
-    R = min(cfg.num_layers, args.distinct or cfg.bench_distinct_layers)
+    # R distinct sets of pools (and q, new rows), cycled over the layers of a step
+    # and over consecutive steps, so that the K/V a launch reads is not still in the
+    # 256 MB MALL from an earlier launch
+    R = args.distinct or cfg.bench_distinct_layers
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tdt = {"fp16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
@@ -286,9 +289,14 @@ def bench_step(args):
         prefix_lens = torch.tensor([cfg.prefix_tokens], dtype=torch.int32, device=dev)
         P = 0
 
-    def attend(li):
-        """Decode of layer li; in fused mode it also appends the layer's new rows."""
-        L = layers[li % R]
+    def pool(si, li):
+        """The pool set of layer li in step si."""
+        return layers[(si * cfg.num_layers + li) % R]
+
+    def attend(si, li):
+        """Decode of layer li in step si; in fused mode it also appends the layer's
+        new rows."""
+        L = pool(si, li)
         o = None if P else out[li]
         if prefix:
             pkv.paged_attention_prefix_decode(o, L["q"], L["k"], L["v"], tables, lens, group_cu,
@@ -304,39 +312,41 @@ def bench_step(args):
             pkv.paged_attention_decode(o, L["q"], L["k"], L["v"], tables, lens, scale=scale,
                                        partition_size=P, part_o=part_o, part_lse=part_lse)
 
-    def step():
+    def step(si):
         for li in range(cfg.num_layers):
-            L = layers[li % R]
+            L = pool(si, li)
             if not fused:
                 pkv.paged_kv_append(L["k"], L["v"], L["kn"], L["vn"], tables, lens)
-            attend(li)
+            attend(si, li)
             if P:
                 pkv.paged_attention_reduce(out[li], part_o, part_lse, lens, P)
 
     # ---- timed region ------------------------------------------------------------
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
-    run = step
+    run = lambda i: step(args.warmup + i)
     if args.graph:
+        # a graph replays the launches it captured: one step, with the pools of
+        # step 0 (no cycling across steps)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            step()
+            step(0)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            step()
+            step(0)
         graph.replay()
         torch.cuda.synchronize()
-        run = graph.replay
+        run = lambda i: graph.replay()
     # one event between consecutive steps: the first and last bracket the K steps
     # (ms_per_step), the ones between give each step's own time (percentiles)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     ev[0].record()
     for i in range(args.steps):
-        run()
+        run(i)
         ev[i + 1].record()
     torch.cuda.synchronize()
     ms_per_step = ev[0].elapsed_time(ev[-1]) / args.steps
@@ -346,16 +356,22 @@ def bench_step(args):
     # The decode launches of the step (same arguments, same layer pools) run back
     # to back from a HIP graph, timed by two events on the stream they run on; the
     # elapsed time over the launch count is the kernel's average duration.
-    reps = max(1, min(args.steps, 10))
+    reps = max(R, min(args.steps, 10))
+    rep_ctr = [0]
 
     def attend_all():
+        # each call is one more step's launches, so a capture of `reps` calls
+        # cycles through the pool sets as the timed steps do
+        si = rep_ctr[0]
+        rep_ctr[0] += 1
         for li in range(cfg.num_layers):
-            attend(li)
+            attend(si, li)
     decode_ms, kernel_timing = time_launches_graph(attend_all, reps)
     decode_ms /= cfg.num_layers
-    if P:  # leave `out` holding the merged result of the last timed step
-        step()
-        torch.cuda.synchronize()
+    # leave `out` holding step 0's result: layer 0 from the first pool set, whose
+    # inputs the oracle baseline uses
+    step(0)
+    torch.cuda.synchronize()
 
     assert bool(torch.isfinite(out.float()).all()), "non-finite attention output"
 
@@ -463,7 +479,7 @@ def bench_append_tokens(args):
     from workloads import get_config, make_workload
 
     cfg = get_config(args.config)
-    R = min(cfg.num_layers, args.distinct or cfg.bench_distinct_layers)
+    R = args.distinct or cfg.bench_distinct_layers
     dev = torch.device("cuda:0")
     tdt = {"fp16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
 
