@@ -112,6 +112,8 @@ def _dtype_code(t) -> int:
 
 
 def _dev(*ts):
+    """Index of the one GPU all given tensors live on (None entries are skipped);
+    raises for CPU, non-contiguous or mixed-device tensors."""
     dev = None
     for t in ts:
         if t is None:
@@ -120,19 +122,35 @@ def _dev(*ts):
             raise ValueError("all tensors must be on the GPU (no CPU path exists)")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+        d = t.get_device()
         if dev is None:
-            dev = t.device
-        elif t.device != dev:
+            dev = d
+        elif d != dev:
             raise ValueError("tensors are on different devices")
     return dev
 
 
 def _p(t):
-    return None if t is None else C.c_void_p(t.data_ptr())
+    # ctypes turns the int into the c_void_p argument
+    return None if t is None else t.data_ptr()
+
+
+_raw_stream = None
 
 
 def _stream(dev):
-    return C.c_void_p(_torch().cuda.current_stream(dev).cuda_stream)
+    """Handle of the current HIP stream of device `dev` (torch's current stream):
+    the library enqueues its kernels there."""
+    global _raw_stream
+    torch = _torch()
+    if dev is None:
+        dev = torch.cuda.current_device()
+    if _raw_stream is None:
+        # the raw-handle query skips building a Stream object on every call
+        _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", False)
+    if _raw_stream:
+        return _raw_stream(dev)
+    return torch.cuda.current_stream(dev).cuda_stream
 
 
 def _int(t, dtype, name):
