@@ -54,6 +54,31 @@ def _compile(src: str, asm: bool) -> str:
     return obj
 
 
+# A plain-C program that drives the library through include/paged_kv.h only (no
+# Python, no torch); the GPU tests run it.
+C_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi_check.c")
+C_CHECK_BIN = os.path.join(ROOT, "tests", "c_abi_check")
+
+
+def build_c_check() -> str:
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler for the C-ABI check")
+    tmp = C_CHECK_BIN + ".tmp%d" % os.getpid()
+    cmd = [cc, "-O2", "-std=c11", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+           f"-I{os.path.join(rocm, 'include')}", f"-I{os.path.join(ROOT, 'include')}",
+           C_CHECK_SRC, "-o", tmp, f"-L{PKG}", "-lpagedkv", f"-L{os.path.join(rocm, 'lib')}",
+           "-lamdhip64", "-lm", "-Wl,-rpath,$ORIGIN/../paged_kv_cache_09_amd",
+           f"-Wl,-rpath,{os.path.join(rocm, 'lib')}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("building the C-ABI check failed")
+    os.replace(tmp, C_CHECK_BIN)
+    return C_CHECK_BIN
+
+
 def build(asm: bool = False, jobs: int = 8) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
@@ -62,6 +87,7 @@ def build(asm: bool = False, jobs: int = 8) -> str:
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     subprocess.run(cmd, check=True, capture_output=True, cwd=BUILD)
     os.replace(tmp, LIB)
+    build_c_check()
     return LIB
 
 
