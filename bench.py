@@ -185,8 +185,8 @@ def roofline(kernel: str, nbytes: int, ms: float, traffic):
             "bytes_per_launch": int(nbytes), "avg_launch_ms": round(ms, 5)}
 
 
-def copy_reference():
-    """Plain device-to-device copy of 1 GiB (read 1 GiB + write 1 GiB)."""
+def copy_rate(reps: int = 10) -> dict:
+    """Plain device-to-device copy of 1 GiB (read 1 GiB + write 1 GiB), timed."""
     import torch
     n = 1 << 30
     a = torch.ones(n // 2, dtype=torch.float16, device="cuda:0")
@@ -196,13 +196,19 @@ def copy_reference():
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(10):
+    for _ in range(reps):
         b.copy_(a)
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / 10
-    print(json.dumps({"copy_reference": True, "bytes_read": n, "bytes_written": n,
-                      "ms": round(ms, 4), "gbps_read_plus_write": round(2 * n / ms / 1e6, 1)}))
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return {"bytes_read": n, "bytes_written": n, "ms": round(ms, 4),
+            "gbps_read_plus_write": round(2 * n / ms / 1e6, 1)}
+
+
+def copy_reference():
+    print(json.dumps({"copy_reference": True, **copy_rate()}))
 
 
 def main():
@@ -456,6 +462,8 @@ def bench_step(args):
             "tolerance": "|gpu - oracle| <= 1e-2 + 1e-2 |oracle|, elementwise",
         }
     result["rocm"] = torch.version.hip
+    # context for the roofline: what a plain 1 GiB device copy moves on this GPU
+    result["copy_1gib_gbps_read_plus_write"] = copy_rate(5)["gbps_read_plus_write"]
 
     print(json.dumps(result), flush=True)
 
