@@ -291,7 +291,8 @@ int paged_attention_decode_slotted(void *out, const void *q, const void *k_pool,
  * For each (s, h) with P = partition_size and np = ceil(n/P) partitions:
  *   M = max_p part_lse[s][h][p],  w_p = exp(part_lse[s][h][p] - M),
  *   out[s][h][:] = sum_p w_p part_o[s][h][p][:] / sum_p w_p   (p < np),
- * rounded to dtype; n == 0 gives zeros.  Exact in real arithmetic: softmax over
+ * rounded to dtype; n == 0 gives zeros.  Only partitions p < max_partitions are
+ * read (np > max_partitions is a caller error).  Exact in real arithmetic: softmax over
  * a union of token ranges is the lse-weighted mean of the per-range softmaxes
  * (not on the pages; the pages describe no partitioning).
  */

@@ -31,6 +31,9 @@ __device__ __forceinline__ float wave_max(float x)
     return x;
 }
 
+// Partitions whose rows are requested before the context length is known.
+constexpr int kEarly = 8;
+
 template <int DT>
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a)
 {
@@ -41,16 +44,31 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a)
     if (wave >= a.num_seqs * a.num_q_heads)
         return;
     const int s = wave / a.num_q_heads;
-    const int n = as_meta(a.lens)[s];
-    const int np = n > 0 ? (n + a.partition_size - 1) / a.partition_size : 0;
     const int64_t row = wave;
-    const float *lse = a.part_lse + row * a.max_partitions;
-    const float *po = a.part_o + row * a.max_partitions * kHeadDim + 2 * lane;
+    const int MP = a.max_partitions;
+    const float *lse = a.part_lse + row * MP;
+    const float *po = a.part_o + row * MP * kHeadDim + 2 * lane;
 
-    // partition p's lse is read by lane p % 64 (one load for up to 64 partitions),
-    // instead of a dependent chain of loads
-    float M = kNegInf;
-    for (int p0 = 0; p0 < np; p0 += 64) {
+    // The loads of the first 64 lse values and of the first kEarly partition rows
+    // do not depend on the context length: they are issued together with its load,
+    // so the three latencies overlap instead of chaining.  Entries of partitions
+    // the decode did not write (p >= np) are read but never used: every use below
+    // is guarded by p < np, a wave-uniform condition, so their contents (arbitrary
+    // bits, possibly NaN) cannot reach the result.
+    const float lse0 = lane < MP ? lse[lane] : kNegInf;
+    float2 early[kEarly];
+#pragma unroll
+    for (int i = 0; i < kEarly; ++i)
+        if (i < MP)
+            early[i] = *(const float2 *)(po + (int64_t)i * kHeadDim);
+    const int n = as_meta(a.lens)[s];
+    // a length needing more partitions than the workspace holds is a caller error;
+    // only the partitions the workspace holds are read
+    const int np = n > 0 ? min((n + a.partition_size - 1) / a.partition_size, MP) : 0;
+
+    // partition p's lse is read by lane p % 64 (one load for up to 64 partitions)
+    float M = lane < np ? lse0 : kNegInf;
+    for (int p0 = 64; p0 < np; p0 += 64) {
         const int p = p0 + lane;
         M = fmaxf(M, p < np ? lse[p] : kNegInf);
     }
@@ -59,10 +77,26 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a)
     float W = 0.f, o0 = 0.f, o1 = 0.f;
     for (int p0 = 0; p0 < np; p0 += 64) {
         const int p = p0 + lane;
-        const float wl = p < np ? fexp2((lse[p] - ref) * kLog2e) : 0.f;
+        const float lp = p0 == 0 ? lse0 : (p < np ? lse[p] : kNegInf);
+        const float wl = p < np ? fexp2((lp - ref) * kLog2e) : 0.f;
         const int cnt = min(64, np - p0);
-        // the partition rows are independent loads: four are in flight together
         int i = 0;
+        if (p0 == 0) {
+            // the rows requested up front
+#pragma unroll
+            for (int u = 0; u < kEarly; ++u) {
+                if (u < cnt) {
+                    const float wgt =
+                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u));
+                    W += wgt;
+                    o0 += wgt * early[u].x;
+                    o1 += wgt * early[u].y;
+                }
+            }
+            i = min(cnt, kEarly);
+        }
+        // the remaining partition rows are independent loads: four are in flight
+        // together
         for (; i + 4 <= cnt; i += 4) {
             float2 v[4];
 #pragma unroll
