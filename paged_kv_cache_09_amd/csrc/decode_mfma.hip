@@ -1017,24 +1017,29 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
             active[h] = col < sph * G && cs < s_end && cs >= ga && cs < gb;
         }
 
-        // per-member lengths and the cumulative sub-tile counts
-        if (tid < kMembers) {
-            const int s = s0 + tid;
-            const bool in = tid < spt && s < s_end && s >= ga && s < gb;
-            s_len[tid] = in ? a.lens[s] : 0;
-            if (in && fused && g == 0 && a.lens[s] <= 0 && a.slot_out)
+        // per-member lengths and the cumulative sub-tile counts: lane i of wave 0
+        // takes member i, and a wave prefix sum gives the running counts
+        if (w == 0) {
+            const int s = s0 + lane;
+            const bool in = lane < kMembers && lane < spt && s < s_end && s >= ga && s < gb;
+            const int n = in ? a.lens[s] : 0;
+            if (in && fused && g == 0 && n <= 0 && a.slot_out)
                 a.slot_out[s] = -1;  // padding sequence: nothing appended
+            int incl = n > start_sub ? (n - start_sub + kSub - 1) / kSub : 0;
+#pragma unroll
+            for (int d = 1; d < kMembers; d <<= 1) {
+                const int up = __shfl_up(incl, d, 64);
+                incl += lane >= d ? up : 0;
+            }
+            const int base = (plen + kSub - 1) / kSub;
+            if (lane < kMembers) {
+                s_len[lane] = n;
+                s_cum[lane + 1] = base + incl;
+            }
+            if (lane == 0)
+                s_cum[0] = base;
         }
         __syncthreads();
-        if (tid == 0) {
-            int c = (plen + kSub - 1) / kSub;
-            s_cum[0] = c;
-            for (int i = 0; i < kMembers; ++i) {
-                const int n = s_len[i];
-                c += n > start_sub ? (n - start_sub + kSub - 1) / kSub : 0;
-                s_cum[i + 1] = c;
-            }
-        }
         // Fused append, spread over the work-group: each thread moves one 16-byte
         // chunk of a member's new K or V row to its slot.  The barrier below makes
         // the rows visible to the whole work-group, so the member's last sub-tile
@@ -1086,32 +1091,50 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
                 st[h].acc[jj] = (f32x4){0.f, 0.f, 0.f, 0.f};
         }
 
-        // Sub-tile j: the prefix's (seg -1) or member seg's; the member cursor only
-        // moves forward, so the lookup is one or two LDS reads per sub-tile.  A j
-        // past the list describes an empty sub-tile (a zero-byte buffer range), so
-        // that every step issues its loads unconditionally: the compiler's count of
-        // loads in flight then agrees on every path, and each wait covers only the
-        // sub-tile it needs.
+        // Sub-tile j of the work-group's list: the list interleaves the prefix
+        // sub-tiles (seg -1, read from L2 after their first use) evenly with the
+        // members' own ones (seg >= 0, mostly HBM reads), so that HBM is busy
+        // through the whole loop instead of only once the prefix is done.  With P
+        // prefix sub-tiles among T, position j is prefix sub-tile pi = floor(j P / T)
+        // when floor((j+1) P / T) exceeds pi, else the members' sub-tile j - pi,
+        // counted member after member.  The member cursor only moves forward, so the
+        // lookup is one or two LDS reads per sub-tile.  A j past the list describes
+        // an empty sub-tile (a zero-byte buffer range), so that every step issues
+        // its loads unconditionally: the compiler's count of loads in flight then
+        // agrees on every path, and each wait covers only the sub-tile it needs.
+        const int n_pre = __builtin_amdgcn_readfirstlane(s_cum[0]);
         struct Sub {
             int seg, tb, t_beg, t_end, t_load;
             int32_t phys;
         };
         auto describe = [&](int j, int &seg) {
             const int jc = min(j, total - 1);
-            while (seg < kMembers - 1 && jc >= __builtin_amdgcn_readfirstlane(s_cum[seg + 1]))
-                ++seg;
+            int pi, pi1;  // prefix sub-tiles before positions jc and jc + 1
+            if (total <= 46340) {  // the products fit 32 bits
+                pi = jc * n_pre / total;
+                pi1 = (jc + 1) * n_pre / total;
+            } else {
+                pi = (int)((int64_t)jc * n_pre / total);
+                pi1 = (int)((int64_t)(jc + 1) * n_pre / total);
+            }
+            const bool pre = pi1 > pi;
+            const int jm = n_pre + jc - pi;  // s_cum coordinate of a member sub-tile
+            if (!pre) {
+                while (seg < kMembers - 1 && jm >= __builtin_amdgcn_readfirstlane(s_cum[seg + 1]))
+                    ++seg;
+            }
             Sub d;
-            d.seg = seg;
+            d.seg = pre ? -1 : seg;
             int row;
-            if (seg < 0) {
-                d.tb = jc * kSub;
+            if (pre) {
+                d.tb = pi * kSub;
                 d.t_beg = 0;
                 d.t_end = plen;
                 d.t_load = plen;
                 row = ga;
             } else {
                 const int n = __builtin_amdgcn_readfirstlane(s_len[seg]);
-                d.tb = start_sub + (jc - __builtin_amdgcn_readfirstlane(s_cum[seg])) * kSub;
+                d.tb = start_sub + (jm - __builtin_amdgcn_readfirstlane(s_cum[seg])) * kSub;
                 d.t_beg = plen;
                 d.t_end = n;
                 d.t_load = n;
@@ -1119,24 +1142,29 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
             }
             if (j != jc)
                 d.t_load = d.tb;
-            const int64_t idx = (int64_t)__builtin_amdgcn_readfirstlane(row) * a.width +
-                                __builtin_amdgcn_readfirstlane(min(d.tb / BS, a.width - 1));
-            d.phys = tabs[idx];
+            // requested here, made uniform (and waited for) only when the sub-tile's
+            // loads are issued, one step later
+            d.phys = table_entry_v(a.tables + (int64_t)__builtin_amdgcn_readfirstlane(row) * a.width,
+                                   a.width, __builtin_amdgcn_readfirstlane(min(d.tb / BS, a.width - 1)));
             return d;
         };
         // One cache policy for the whole list (the default one, which keeps the
         // prefix in L2 for the group's other tiles): a policy chosen per sub-tile
         // would split the loads over two code paths.
         auto load_sub = [&](KOp &K, VRows &V, const Sub &d) {
-            const SubRsrc r = sub_rsrc<BS>(d.phys, kp, vp, d.tb, d.t_load, head_off, blk_elems);
+            const SubRsrc r = sub_rsrc<BS>(__builtin_amdgcn_readfirstlane(d.phys), kp, vp, d.tb,
+                                           d.t_load, head_off, blk_elems);
             load_k<kLoadReuse>(K, r.k, lane);
             load_v<kLoadReuse>(V, r.v, lane);
         };
         // Sub-tiles w, w + WAVES, ... belong to this wave: the scores of the current
         // one are computed, then the next one's loads are issued into the same
-        // registers, overlapping the softmax and P.V of the current sub-tile.
-        auto step = [&](KOp &K, VRows &V, Sub &cur, int jn, int &seg) {
-            const Sub nxt = describe(jn, seg);
+        // registers, overlapping the softmax and P.V of the current sub-tile.  The
+        // table entry of the sub-tile after next is requested at the same time, so
+        // that its latency (a member's own blocks miss the caches) never sits
+        // between a sub-tile's description and its loads.
+        auto step = [&](KOp &K, VRows &V, Sub &cur, Sub &nxt, int jn2, int &seg) {
+            const Sub nxt2 = describe(jn2, seg);
             u32x2 pb[NH];
             float alpha[NH];
             bool rs[NH];
@@ -1165,15 +1193,17 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
             pv_mma_halves<DT, NH>(st, vlds, pb, rs, alpha, lane);
             __builtin_amdgcn_sched_barrier(0);
             cur = nxt;
+            nxt = nxt2;
         };
         if (w < total) {
             int seg = -1;
             Sub cur = describe(w, seg);
+            Sub nxt = describe(w + WAVES, seg);
             KOp K;
             VRows V;
             load_sub(K, V, cur);
             for (int j = w; j < total; j += WAVES)
-                step(K, V, cur, j + WAVES, seg);
+                step(K, V, cur, nxt, j + 2 * WAVES, seg);
         }
 #pragma unroll
         for (int h = 0; h < NH; ++h)
