@@ -361,8 +361,10 @@ def bench_step(args):
     # ---- average duration of the dominant kernel -----------------------------------
     # The decode launches of the step (same arguments, same layer pools) run back
     # to back from a HIP graph, timed by two events on the stream they run on; the
-    # elapsed time over the launch count is the kernel's average duration.
-    reps = max(R, min(args.steps, 10))
+    # elapsed time over the launch count is the kernel's average duration.  At least
+    # 64 launches are captured, so that the replay's own start-up latency (a few
+    # microseconds) is spread thin over short one-layer launches.
+    reps = max(R, min(args.steps, 10), -(-64 // cfg.num_layers))
     rep_ctr = [0]
 
     def attend_all():
