@@ -36,7 +36,9 @@
  *   blocks 0 .. ceil(n/block_size)-1 lie in [0, num_blocks); no two sequences
  *   append to the same slot in one call.  With PKV_DEBUG_CHECK=1 each call first
  *   runs a device-side check of these, synchronises `stream`, and returns
- *   PKV_EDEVICE if one fails.
+ *   PKV_EDEVICE if one fails.  The check keeps its verdict in one flag per device:
+ *   checked calls that run at the same time on one device (from several threads)
+ *   may report each other's violations.
  * Supported shapes: head_dim = 128; block_size in {16, 32, 64, 128, 256};
  *   num_q_heads a multiple of num_kv_heads with a group of at most 16 query
  *   heads per KV head.  Others give PKV_ENOTSUP.

@@ -165,15 +165,85 @@ def _check(rc: int, what: str):
         raise PagedKVError(rc, what)
 
 
+# The C ABI receives bare pointers and trusts the sizes it is given; a tensor
+# smaller than they imply would be read or written past its end.  The binding
+# therefore checks every tensor's shape and dtype against the sizes it passes,
+# before it touches the device.
+def _expect(t, shape, name: str):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _dims(t, n: int, name: str):
+    if t.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions, got shape {tuple(t.shape)}")
+    return tuple(t.shape)
+
+
+def _same_dtype(ref, *pairs):
+    for t, name in pairs:
+        if t is not None and t.dtype != ref.dtype:
+            raise TypeError(f"{name} is {t.dtype}, expected {ref.dtype} like the pools")
+
+
+def _pools(k_pool, v_pool):
+    """(NB, Hkv, B, D) of a K/V pool pair, checked to match."""
+    shape = _dims(k_pool, 4, "k_pool")
+    _expect(v_pool, shape, "v_pool")
+    _same_dtype(k_pool, (v_pool, "v_pool"))
+    return shape
+
+
+def _workspace(part_o, part_lse, S: int, Hq: int, D: int) -> int:
+    """Partitions the split-mode workspace holds (0 without one)."""
+    torch = _torch()
+    if part_o is None:
+        return 0
+    mp = _dims(part_o, 4, "part_o")[2]
+    _expect(part_o, (S, Hq, mp, D), "part_o")
+    _expect(part_lse, (S, Hq, mp), "part_lse")
+    for t, name in ((part_o, "part_o"), (part_lse, "part_lse")):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32, got {t.dtype}")
+    return mp
+
+
+def _queries(out, q, k_pool, v_pool, block_tables, context_lens):
+    """Shapes of a decode call, checked: (NB, Hkv, B, D, S, Hq, W)."""
+    NB, Hkv, B, D = _pools(k_pool, v_pool)
+    S, Hq, Dq = _dims(q, 3, "q")
+    if Dq != D:
+        raise ValueError(f"q has head_dim {Dq}, the pools {D}")
+    _same_dtype(k_pool, (q, "q"), (out, "out"))
+    _expect(out, (S, Hq, D), "out")
+    W = _tables(block_tables, S)
+    _expect(context_lens, (S,), "context_lens")
+    return NB, Hkv, B, D, S, Hq, W
+
+
+def _tables(block_tables, S: int):
+    """Table width of int32 [S][W] block tables."""
+    rows, width = _dims(block_tables, 2, "block_tables")
+    if rows != S:
+        raise ValueError(f"block_tables has {rows} rows for {S} sequences")
+    return width
+
+
 # ---------------------------------------------------------------------------
 def paged_kv_append(k_pool, v_pool, k_new, v_new, block_tables, context_lens, slot_out=None):
     """Write each sequence's new K/V row to position context_lens[s]-1."""
+    NB, Hkv, B, D = _pools(k_pool, v_pool)
+    S = _dims(k_new, 3, "k_new")[0]
+    _expect(k_new, (S, Hkv, D), "k_new")
+    _expect(v_new, (S, Hkv, D), "v_new")
+    _same_dtype(k_pool, (k_new, "k_new"), (v_new, "v_new"))
+    _tables(block_tables, S)
+    _expect(context_lens, (S,), "context_lens")
+    _expect(slot_out, (S,), "slot_out")
     dev = _dev(k_pool, v_pool, k_new, v_new, block_tables, context_lens, slot_out)
     _int(block_tables, "i32", "block_tables")
     _int(context_lens, "i32", "context_lens")
     _int(slot_out, "i64", "slot_out")
-    NB, Hkv, B, D = k_pool.shape
-    S = k_new.shape[0]
     rc = load().paged_kv_append(_p(k_pool), _p(v_pool), _p(k_new), _p(v_new), _p(block_tables),
                                 _p(context_lens), _p(slot_out), S, Hkv, D, B,
                                 block_tables.shape[1], NB, _dtype_code(k_pool), _stream(dev))
@@ -183,11 +253,18 @@ def paged_kv_append(k_pool, v_pool, k_new, v_new, block_tables, context_lens, sl
 def paged_kv_append_tokens(k_pool, v_pool, k_src, v_src, src_cu, start_pos, block_tables):
     """Write runs of tokens: run r puts rows src_cu[r]..src_cu[r+1]-1 at positions
     start_pos[r].. of table row r."""
+    NB, Hkv, B, D = _pools(k_pool, v_pool)
+    T = _dims(k_src, 3, "k_src")[0]
+    _expect(k_src, (T, Hkv, D), "k_src")
+    _expect(v_src, (T, Hkv, D), "v_src")
+    _same_dtype(k_pool, (k_src, "k_src"), (v_src, "v_src"))
+    R = _dims(block_tables, 2, "block_tables")[0]
+    _expect(src_cu, (R + 1,), "src_cu")
+    _expect(start_pos, (R,), "start_pos")
     dev = _dev(k_pool, v_pool, k_src, v_src, src_cu, start_pos, block_tables)
     _int(src_cu, "i64", "src_cu")
     _int(start_pos, "i32", "start_pos")
     _int(block_tables, "i32", "block_tables")
-    NB, Hkv, B, D = k_pool.shape
     rc = load().paged_kv_append_tokens(_p(k_pool), _p(v_pool), _p(k_src), _p(v_src), _p(src_cu),
                                        _p(start_pos), _p(block_tables), block_tables.shape[0],
                                        k_src.shape[0], Hkv, D, B, block_tables.shape[1], NB,
@@ -201,15 +278,16 @@ def paged_kv_copy_blocks(k_pools, v_pools, src_blocks, dst_blocks):
     k_pools, v_pools = list(k_pools), list(v_pools)
     if len(k_pools) != len(v_pools) or not k_pools:
         raise ValueError("k_pools and v_pools must be non-empty lists of equal length")
-    dev = _dev(*k_pools, *v_pools, src_blocks, dst_blocks)
-    _int(src_blocks, "i32", "src_blocks")
-    _int(dst_blocks, "i32", "dst_blocks")
     if src_blocks.shape != dst_blocks.shape or src_blocks.dim() != 1:
         raise ValueError("src_blocks and dst_blocks must be 1-D and of equal length")
-    shape, dtype = k_pools[0].shape, k_pools[0].dtype
+    shape = _dims(k_pools[0], 4, "k_pools[0]")
+    dtype = k_pools[0].dtype
     for t in k_pools + v_pools:
         if t.shape != shape or t.dtype != dtype:
             raise ValueError("every pool must have the same shape and dtype")
+    dev = _dev(*k_pools, *v_pools, src_blocks, dst_blocks)
+    _int(src_blocks, "i32", "src_blocks")
+    _int(dst_blocks, "i32", "dst_blocks")
     NB, Hkv, B, D = shape
     L = len(k_pools)
     kp = (C.c_void_p * L)(*[t.data_ptr() for t in k_pools])
@@ -225,16 +303,15 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens,
                            part_o=None, part_lse=None):
     """Decode attention; single pass (partition_size 0) writes `out`, split mode
     writes part_o/part_lse (then call paged_attention_reduce)."""
+    NB, Hkv, B, D, S, Hq, W = _queries(out, q, k_pool, v_pool, block_tables, context_lens)
+    mp = _workspace(part_o, part_lse, S, Hq, D)
     dev = _dev(out, q, k_pool, v_pool, block_tables, context_lens, part_o, part_lse)
     _int(block_tables, "i32", "block_tables")
     _int(context_lens, "i32", "context_lens")
-    NB, Hkv, B, D = k_pool.shape
-    S, Hq, _ = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    mp = part_o.shape[2] if part_o is not None else 0
     rc = load().paged_attention_decode(_p(out), _p(q), _p(k_pool), _p(v_pool), _p(block_tables),
-                                       _p(context_lens), S, Hq, Hkv, D, B, block_tables.shape[1],
+                                       _p(context_lens), S, Hq, Hkv, D, B, W,
                                        NB, float(scale), int(partition_size), mp, _p(part_o),
                                        _p(part_lse), _dtype_code(q), _stream(dev))
     _check(rc, "paged_attention_decode")
@@ -245,19 +322,22 @@ def paged_attention_append_decode(out, q, k_pool, v_pool, k_new, v_new, block_ta
                                   partition_size: int = 0, part_o=None, part_lse=None):
     """Append each sequence's new K/V row at position context_lens[s]-1 and run
     decode attention over positions 0..n-1, in one launch."""
+    NB, Hkv, B, D, S, Hq, W = _queries(out, q, k_pool, v_pool, block_tables, context_lens)
+    _expect(k_new, (S, Hkv, D), "k_new")
+    _expect(v_new, (S, Hkv, D), "v_new")
+    _same_dtype(k_pool, (k_new, "k_new"), (v_new, "v_new"))
+    _expect(slot_out, (S,), "slot_out")
+    mp = _workspace(part_o, part_lse, S, Hq, D)
     dev = _dev(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens, slot_out,
                part_o, part_lse)
     _int(block_tables, "i32", "block_tables")
     _int(context_lens, "i32", "context_lens")
     _int(slot_out, "i64", "slot_out")
-    NB, Hkv, B, D = k_pool.shape
-    S, Hq, _ = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    mp = part_o.shape[2] if part_o is not None else 0
     rc = load().paged_attention_append_decode(
         _p(out), _p(q), _p(k_pool), _p(v_pool), _p(k_new), _p(v_new), _p(slot_out),
-        _p(block_tables), _p(context_lens), S, Hq, Hkv, D, B, block_tables.shape[1], NB,
+        _p(block_tables), _p(context_lens), S, Hq, Hkv, D, B, W, NB,
         float(scale), int(partition_size), mp, _p(part_o), _p(part_lse), _dtype_code(q),
         _stream(dev))
     _check(rc, "paged_attention_append_decode")
@@ -271,21 +351,26 @@ def paged_attention_prefix_decode(out, q, k_pool, v_pool, block_tables, context_
     sequences group_cu[k]..group_cu[k+1]-1, sharing their first prefix_lens[k]
     positions); appends the new rows first when k_new / v_new are given.  The
     workspace part_o / part_lse is needed only with prefix_partition > 0."""
+    NB, Hkv, B, D, S, Hq, W = _queries(out, q, k_pool, v_pool, block_tables, context_lens)
+    G = _dims(prefix_lens, 1, "prefix_lens")[0]
+    _expect(group_cu, (G + 1,), "group_cu")
+    _expect(k_new, (S, Hkv, D), "k_new")
+    _expect(v_new, (S, Hkv, D), "v_new")
+    _same_dtype(k_pool, (k_new, "k_new"), (v_new, "v_new"))
+    _expect(slot_out, (S,), "slot_out")
+    mp = _workspace(part_o, part_lse, S, Hq, D)
     dev = _dev(out, q, k_pool, v_pool, block_tables, context_lens, group_cu, prefix_lens,
                part_o, part_lse, k_new, v_new, slot_out)
     for t, n in ((block_tables, "block_tables"), (context_lens, "context_lens"),
                  (group_cu, "group_cu"), (prefix_lens, "prefix_lens")):
         _int(t, "i32", n)
     _int(slot_out, "i64", "slot_out")
-    NB, Hkv, B, D = k_pool.shape
-    S, Hq, _ = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     rc = load().paged_attention_prefix_decode(
         _p(out), _p(q), _p(k_pool), _p(v_pool), _p(k_new), _p(v_new), _p(slot_out),
         _p(block_tables), _p(context_lens), _p(group_cu), _p(prefix_lens),
-        prefix_lens.shape[0], S, Hq, Hkv, D, B, block_tables.shape[1], NB, float(scale),
-        int(prefix_partition), part_o.shape[2] if part_o is not None else 0, _p(part_o),
+        G, S, Hq, Hkv, D, B, W, NB, float(scale), int(prefix_partition), mp, _p(part_o),
         _p(part_lse), _dtype_code(q), _stream(dev))
     _check(rc, "paged_attention_prefix_decode")
 
@@ -294,13 +379,18 @@ def paged_attention_decode_slotted(out, q, k_pool, v_pool, segments, num_segment
                                    scale: Optional[float] = None):
     """Decode attention of sequences given as (block_id, slot_offset, length)
     segment lists: segments int32 [S][max_segments][3], num_segments int32 [S]."""
+    NB, Hkv, B, D = _pools(k_pool, v_pool)
+    S, Hq, Dq = _dims(q, 3, "q")
+    if Dq != D:
+        raise ValueError(f"q has head_dim {Dq}, the pools {D}")
+    _same_dtype(k_pool, (q, "q"), (out, "out"))
+    _expect(out, (S, Hq, D), "out")
+    if segments.dim() != 3 or segments.shape[0] != S or segments.shape[2] != 3:
+        raise ValueError(f"segments must be [{S}][max_segments][3], got {tuple(segments.shape)}")
+    _expect(num_segments, (S,), "num_segments")
     dev = _dev(out, q, k_pool, v_pool, segments, num_segments)
     _int(segments, "i32", "segments")
     _int(num_segments, "i32", "num_segments")
-    if segments.dim() != 3 or segments.shape[2] != 3:
-        raise ValueError("segments must be [num_seqs][max_segments][3]")
-    NB, Hkv, B, D = k_pool.shape
-    S, Hq, _ = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     rc = load().paged_attention_decode_slotted(
@@ -311,9 +401,12 @@ def paged_attention_decode_slotted(out, q, k_pool, v_pool, segments, num_segment
 
 def paged_attention_reduce(out, part_o, part_lse, context_lens, partition_size: int):
     """Log-sum-exp merge of split-context partitions into `out`."""
+    S, Hq, MP, D = _dims(part_o, 4, "part_o")
+    _workspace(part_o, part_lse, S, Hq, D)
+    _expect(out, (S, Hq, D), "out")
+    _expect(context_lens, (S,), "context_lens")
     dev = _dev(out, part_o, part_lse, context_lens)
     _int(context_lens, "i32", "context_lens")
-    S, Hq, MP, D = part_o.shape
     rc = load().paged_attention_reduce(_p(out), _p(part_o), _p(part_lse), _p(context_lens), S, Hq,
                                        D, int(partition_size), MP, _dtype_code(out), _stream(dev))
     _check(rc, "paged_attention_reduce")

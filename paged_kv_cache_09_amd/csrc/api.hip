@@ -79,13 +79,16 @@ __global__ void debug_groups_kernel(const int32_t *cu, const int32_t *prefix_len
     const int k = blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= num_groups)
         return;
-    if ((k == 0 && cu[0] != 0) || (k == num_groups - 1 && cu[num_groups] != num_seqs) ||
-        cu[k + 1] < cu[k] || prefix_lens[k] < 0) {
+    const int lo = cu[k], hi = cu[k + 1];
+    // bounds first: each thread sees only its own group, and the loop below must
+    // stay short whatever the contents
+    if ((k == 0 && lo != 0) || (k == num_groups - 1 && hi != num_seqs) || lo < 0 ||
+        hi > num_seqs || hi < lo || prefix_lens[k] < 0) {
         atomicOr(&g_debug_flag, 32);
         return;
     }
-    for (int s = cu[k]; s < cu[k + 1]; ++s)
-        if (s < 0 || s >= num_seqs || lens[s] < prefix_lens[k] + extra)
+    for (int s = lo; s < hi; ++s)
+        if (lens[s] < prefix_lens[k] + extra)
             atomicOr(&g_debug_flag, 32);
 }
 

@@ -209,3 +209,66 @@ def test_binding_refuses_cpu_tensors():
         pkv.paged_attention_decode(x, x, x.view(1, 2, 16, 96)[:, :, :, :],
                                    x.view(1, 2, 16, 96), torch.zeros(2, 5, dtype=torch.int32),
                                    torch.zeros(2, dtype=torch.int32))
+
+
+# ---- binding: tensor shapes are checked before the device is touched -----------------
+# CPU tensors suffice: every shape or dtype mismatch below is reported before the
+# binding's device check, and a consistent call then fails only on that check.
+def _t(*shape, dtype="f16"):
+    import torch
+    dt = {"f16": torch.float16, "f32": torch.float32, "i32": torch.int32,
+          "i64": torch.int64}[dtype]
+    return torch.zeros(shape, dtype=dt)
+
+
+def _decode_args(S=2, Hq=4, Hkv=2, NB=8, B=16, W=3):
+    return dict(out=_t(S, Hq, 128), q=_t(S, Hq, 128), k_pool=_t(NB, Hkv, B, 128),
+                v_pool=_t(NB, Hkv, B, 128), block_tables=_t(S, W, dtype="i32"),
+                context_lens=_t(S, dtype="i32"))
+
+
+def test_binding_rejects_mismatched_decode_tensors():
+    a = _decode_args()
+    with pytest.raises(ValueError, match="GPU"):       # consistent: only the device is wrong
+        pkv.paged_attention_decode(**a)
+    bad = [
+        dict(out=_t(2, 4, 64)),                              # output smaller than q
+        dict(v_pool=_t(8, 2, 16, 64)),                       # V pool of another shape
+        dict(block_tables=_t(1, 3, dtype="i32")),            # fewer table rows than sequences
+        dict(context_lens=_t(3, dtype="i32")),               # one length too many
+        dict(q=_t(2, 4, 64), out=_t(2, 4, 64)),              # head_dim unlike the pools
+    ]
+    for b in bad:
+        with pytest.raises(ValueError):
+            pkv.paged_attention_decode(**{**a, **b})
+    with pytest.raises(TypeError):                       # output dtype unlike the pools
+        pkv.paged_attention_decode(**{**a, "out": _t(2, 4, 128, dtype="f32")})
+
+
+def test_binding_rejects_mismatched_workspace_and_new_rows():
+    a = _decode_args()
+    a["out"] = None
+    with pytest.raises(ValueError):                      # part_lse for fewer partitions
+        pkv.paged_attention_decode(**a, partition_size=32, part_o=_t(2, 4, 3, 128, dtype="f32"),
+                                   part_lse=_t(2, 4, 2, dtype="f32"))
+    with pytest.raises(TypeError):                       # fp16 workspace
+        pkv.paged_attention_decode(**a, partition_size=32, part_o=_t(2, 4, 3, 128),
+                                   part_lse=_t(2, 4, 3, dtype="f32"))
+    a = _decode_args()
+    with pytest.raises(ValueError):                      # new rows for one sequence only
+        pkv.paged_attention_append_decode(**a, k_new=_t(1, 2, 128), v_new=_t(1, 2, 128))
+    with pytest.raises(ValueError):                      # slot output of the wrong length
+        pkv.paged_attention_append_decode(**a, k_new=_t(2, 2, 128), v_new=_t(2, 2, 128),
+                                          slot_out=_t(3, dtype="i64"))
+    with pytest.raises(ValueError):                      # reduce into a smaller output
+        pkv.paged_attention_reduce(_t(2, 4, 64), _t(2, 4, 3, 128, dtype="f32"),
+                                   _t(2, 4, 3, dtype="f32"), _t(2, dtype="i32"), 32)
+    with pytest.raises(ValueError):                      # append: V rows of another shape
+        pkv.paged_kv_append(_t(8, 2, 16, 128), _t(8, 2, 16, 128), _t(2, 2, 128),
+                            _t(2, 1, 128), _t(2, 3, dtype="i32"), _t(2, dtype="i32"))
+    with pytest.raises(ValueError):                      # prefix groups: offsets for 2 groups
+        pkv.paged_attention_prefix_decode(**a, group_cu=_t(2, dtype="i32"),
+                                          prefix_lens=_t(2, dtype="i32"))
+    with pytest.raises(ValueError):                      # slotted: segments for 3 sequences
+        pkv.paged_attention_decode_slotted(a["out"], a["q"], a["k_pool"], a["v_pool"],
+                                           _t(3, 4, 3, dtype="i32"), _t(2, dtype="i32"))
