@@ -1097,63 +1097,92 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
         // through the whole loop instead of only once the prefix is done.  With P
         // prefix sub-tiles among T, position j is prefix sub-tile pi = floor(j P / T)
         // when floor((j+1) P / T) exceeds pi, else the members' sub-tile j - pi,
-        // counted member after member.  The member cursor only moves forward, so the
-        // lookup is one or two LDS reads per sub-tile.  A j past the list describes
-        // an empty sub-tile (a zero-byte buffer range), so that every step issues
-        // its loads unconditionally: the compiler's count of loads in flight then
-        // agrees on every path, and each wait covers only the sub-tile it needs.
+        // counted member after member.  A wave describes positions w, w + WAVES, ...
+        // in order, so both quotients advance by a constant step with a carry (no
+        // division per sub-tile), and the member cursor only moves forward (one or
+        // two LDS reads per sub-tile).  A j past the list describes an empty sub-tile
+        // (a zero-byte buffer range), so that every step issues its loads
+        // unconditionally: the compiler's count of loads in flight then agrees on
+        // every path, and each wait covers only the sub-tile it needs.
         const int n_pre = __builtin_amdgcn_readfirstlane(s_cum[0]);
         struct Sub {
             int seg, tb, t_beg, t_end, t_load;
             int32_t phys;
         };
+        // j P = q0 T + r0 and (j + 1) P = q1 T + r1 for the wave's next position j
+        const int tot = max(total, 1);  // no list (total 0) describes nothing
+        const int64_t wp = (int64_t)WAVES * n_pre;
+        const int dq = (int)(wp / tot), dr = (int)(wp % tot);
+        int q0 = (int)((int64_t)w * n_pre / tot), r0 = (int)((int64_t)w * n_pre % tot);
+        int q1 = (int)((int64_t)(w + 1) * n_pre / tot);
+        int r1 = (int)((int64_t)(w + 1) * n_pre % tot);
         auto describe = [&](int j, int &seg) {
-            const int jc = min(j, total - 1);
-            int pi, pi1;  // prefix sub-tiles before positions jc and jc + 1
-            if (total <= 46340) {  // the products fit 32 bits
-                pi = jc * n_pre / total;
-                pi1 = (jc + 1) * n_pre / total;
-            } else {
-                pi = (int)((int64_t)jc * n_pre / total);
-                pi1 = (int)((int64_t)(jc + 1) * n_pre / total);
-            }
-            const bool pre = pi1 > pi;
-            const int jm = n_pre + jc - pi;  // s_cum coordinate of a member sub-tile
-            if (!pre) {
-                while (seg < kMembers - 1 && jm >= __builtin_amdgcn_readfirstlane(s_cum[seg + 1]))
-                    ++seg;
-            }
             Sub d;
-            d.seg = pre ? -1 : seg;
             int row;
-            if (pre) {
-                d.tb = pi * kSub;
+            if (j >= total) {
+                // past the list: an empty sub-tile.  Its buffer range is empty, so no
+                // byte is fetched whatever the table entry; the entry is still read
+                // below, by the same load as on the other path, so that the compiler's
+                // count of loads in flight agrees on both
+                d.seg = -1;
+                d.tb = 0;
                 d.t_beg = 0;
                 d.t_end = plen;
-                d.t_load = plen;
+                d.t_load = 0;
                 row = ga;
             } else {
-                const int n = __builtin_amdgcn_readfirstlane(s_len[seg]);
-                d.tb = start_sub + (jm - __builtin_amdgcn_readfirstlane(s_cum[seg])) * kSub;
-                d.t_beg = plen;
-                d.t_end = n;
-                d.t_load = n;
-                row = s0 + seg;
+                const int pi = q0, pi1 = q1;  // prefix sub-tiles before positions j and j + 1
+                q0 += dq;
+                r0 += dr;
+                if (r0 >= total) {
+                    r0 -= total;
+                    ++q0;
+                }
+                q1 += dq;
+                r1 += dr;
+                if (r1 >= total) {
+                    r1 -= total;
+                    ++q1;
+                }
+                const bool pre = pi1 > pi;
+                const int jm = n_pre + j - pi;  // s_cum coordinate of a member sub-tile
+                if (!pre) {
+                    while (seg < kMembers - 1 &&
+                           jm >= __builtin_amdgcn_readfirstlane(s_cum[seg + 1]))
+                        ++seg;
+                }
+                d.seg = pre ? -1 : seg;
+                if (pre) {
+                    d.tb = pi * kSub;
+                    d.t_beg = 0;
+                    d.t_end = plen;
+                    d.t_load = plen;
+                    row = ga;
+                } else {
+                    const int n = __builtin_amdgcn_readfirstlane(s_len[seg]);
+                    d.tb = start_sub + (jm - __builtin_amdgcn_readfirstlane(s_cum[seg])) * kSub;
+                    d.t_beg = plen;
+                    d.t_end = n;
+                    d.t_load = n;
+                    row = s0 + seg;
+                }
             }
-            if (j != jc)
-                d.t_load = d.tb;
             // requested here, made uniform (and waited for) only when the sub-tile's
             // loads are issued, one step later
-            d.phys = table_entry_v(a.tables + (int64_t)__builtin_amdgcn_readfirstlane(row) * a.width,
-                                   a.width, __builtin_amdgcn_readfirstlane(min(d.tb / BS, a.width - 1)));
+            const int32_t *trow_v =
+                a.tables + (int64_t)__builtin_amdgcn_readfirstlane(row) * a.width;
+            d.phys = table_entry_v(trow_v, a.width,
+                                   __builtin_amdgcn_readfirstlane(min(d.tb / BS, a.width - 1)));
             return d;
         };
         // One cache policy for the whole list (the default one, which keeps the
         // prefix in L2 for the group's other tiles): a policy chosen per sub-tile
         // would split the loads over two code paths.
         auto load_sub = [&](KOp &K, VRows &V, const Sub &d) {
-            const SubRsrc r = sub_rsrc<BS>(__builtin_amdgcn_readfirstlane(d.phys), kp, vp, d.tb,
-                                           d.t_load, head_off, blk_elems);
+            // an empty sub-tile past the list may carry an unused (negative) table
+            // entry: the clamp keeps its base address inside the pool as well
+            const SubRsrc r = sub_rsrc<BS>(max(__builtin_amdgcn_readfirstlane(d.phys), 0), kp, vp,
+                                           d.tb, d.t_load, head_off, blk_elems);
             load_k<kLoadReuse>(K, r.k, lane);
             load_v<kLoadReuse>(V, r.v, lane);
         };
