@@ -10,10 +10,10 @@
 // exactly one multiply-add, so this path is HBM-bound with no reuse to exploit:
 // MFMA would only pad a vector product to a 16-row tile.  The kernel therefore
 // streams K/V straight into VGPRs with 16-byte loads and reduces on the VALU:
-//   * a work-group is 4 wave64s; one work-group per (sequence, head[, partition]);
+//   * a work-group is 8 wave64s; one work-group per (sequence, head[, partition]);
 //   * tokens are processed in tiles of 32; the waves of a work-group take tiles
-//     round-robin and double-buffer them in registers (the loads of tile k+4 are
-//     in flight while tile k is computed);
+//     round-robin, with the next tile's K and V loads in flight while the current
+//     tile is computed (one register buffer per half, see the loop);
 //   * lane l = 16*r + c owns dims 8c..8c+7 of token 4i+r of the tile (i = 0..7):
 //     every load instruction of the wave covers 4 consecutive token rows = 1 KiB
 //     of contiguous memory, and the same mapping serves K and V;
@@ -31,7 +31,15 @@
 namespace pkv {
 namespace {
 
-constexpr int kTile = 32;  // tokens per tile
+// Tokens per tile (tuning knob).  16-token tiles take 75 registers instead of 113
+// and fit 3 work-groups per CU instead of 2, but each wave then has half the bytes
+// in flight: measured 3.6 % slower on the 7B-shaped batch.
+#ifndef PKV_G1_TILE
+#define PKV_G1_TILE 32
+#endif
+constexpr int kTile = PKV_G1_TILE;  // tokens per tile (16 or 32)
+static_assert(kTile == 16 || kTile == 32, "tiles of 16 or 32 tokens");
+constexpr int kRows = kTile / 4;  // token rows of a tile per lane
 
 // Physical blocks of the two 16-token halves of the tile starting at token tb.
 // For BS >= 32 the whole tile sits in block tb/BS.  For BS == 16 the second half
@@ -103,7 +111,9 @@ __device__ __forceinline__ TileRsrc tile_rsrc(const TilePhys &p, const uint16_t 
     // readfirstlane keeps the ranges in SGPRs (the clamp would otherwise be
     // selected as a VALU med3, making the descriptor look divergent)
     const int n0 = __builtin_amdgcn_readfirstlane(min(max(valid, 0), 16) * kHeadDim * 2);
-    const int n1 = __builtin_amdgcn_readfirstlane(min(max(valid - 16, 0), 16) * kHeadDim * 2);
+    const int n1 = kTile > 16
+                       ? __builtin_amdgcn_readfirstlane(min(max(valid - 16, 0), 16) * kHeadDim * 2)
+                       : 0;
     TileRsrc t;
     t.k0 = make_rsrc(kp + b0, n0);
     t.k1 = make_rsrc(kp + b1, n1);
@@ -112,9 +122,9 @@ __device__ __forceinline__ TileRsrc tile_rsrc(const TilePhys &p, const uint16_t 
     return t;
 }
 
-// Eight 16-byte loads: rows 4i + lane/16 of the tile, dims 8*(lane%16)..+7.
+// kRows 16-byte loads: rows 4i + lane/16 of the tile, dims 8*(lane%16)..+7.
 struct Half {
-    u32x4 x[8];
+    u32x4 x[kRows];
 };
 
 __device__ __forceinline__ void load_half(Half &h, __amdgpu_buffer_rsrc_t r0,
@@ -123,9 +133,11 @@ __device__ __forceinline__ void load_half(Half &h, __amdgpu_buffer_rsrc_t r0,
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         h.x[i] = ldbuf(r0, lane_byte + i * 4 * kHeadDim * 2);
+    if constexpr (kRows > 4) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        h.x[4 + i] = ldbuf(r1, lane_byte + i * 4 * kHeadDim * 2);
+        for (int i = 0; i < 4; ++i)
+            h.x[4 + i] = ldbuf(r1, lane_byte + i * 4 * kHeadDim * 2);
+    }
 }
 
 template <int DT>
@@ -135,13 +147,13 @@ struct RowState {
     float acc[8];  // running sum of exp2(score - m) * v[dims 8c..8c+7]
 };
 
-// Scores of the row's 8 tokens of a tile (log2 domain); masked tokens get -inf.
+// Scores of the row's kRows tokens of a tile (log2 domain); masked tokens get -inf.
 template <int DT, bool PARTIAL>
-__device__ __forceinline__ void scores(float (&sc)[8], const Half &K, const u32x4 &q, int tb,
+__device__ __forceinline__ void scores(float (&sc)[kRows], const Half &K, const u32x4 &q, int tb,
                                        int t_end, int r, float scale_log2)
 {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kRows; ++i) {
         float d = dot2<DT>(q.x, K.x[i].x, 0.f);
         d = dot2<DT>(q.y, K.x[i].y, d);
         d = dot2<DT>(q.z, K.x[i].z, d);
@@ -154,12 +166,12 @@ __device__ __forceinline__ void scores(float (&sc)[8], const Half &K, const u32x
 
 // Online-softmax update of the row state with a tile's scores and V rows.
 template <int DT, bool PARTIAL>
-__device__ __forceinline__ void accumulate(RowState<DT> &st, const float (&sc)[8], const Half &V,
-                                           int tb, int t_end, int r)
+__device__ __forceinline__ void accumulate(RowState<DT> &st, const float (&sc)[kRows],
+                                           const Half &V, int tb, int t_end, int r)
 {
     float mt = sc[0];
 #pragma unroll
-    for (int i = 1; i < 8; ++i)
+    for (int i = 1; i < kRows; ++i)
         mt = fmaxf(mt, sc[i]);
     const float m_new = fmaxf(st.m, mt);
     const float ref = safe_ref(m_new);
@@ -169,7 +181,7 @@ __device__ __forceinline__ void accumulate(RowState<DT> &st, const float (&sc)[8
     for (int j = 0; j < 8; ++j)
         st.acc[j] *= alpha;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kRows; ++i) {
         float p = fexp2(sc[i] - ref);
         u32x4 v = V.x[i];
         if (PARTIAL && tb + 4 * i + r >= t_end) {
@@ -347,7 +359,7 @@ void decode_g1_kernel(DecodeArgs a)
             // table entries are looked up one tile ahead of the loads that use them
             const TilePhys en = first ? e_next : tile_entries<BS>(trow, a.width, tb + step);
             TilePhys pn = tile_select<BS>(en, tb + step, t1);
-            float sc[8];
+            float sc[kRows];
             for (int j = 0; j + 1 < T; ++j) {  // every tile here is full
                 const TilePhys pn2 = tile_phys<BS>(trow, a.width, tb + 2 * step, t1);
                 const TileRsrc rn =
@@ -368,9 +380,9 @@ void decode_g1_kernel(DecodeArgs a)
             if (new_here && tb + kTile >= n) {
                 // this tile holds position n-1: put the new rows in place of the
                 // (unfetched) pool row
-                const int row = n - 1 - tb;  // 0..31
+                const int row = n - 1 - tb;  // 0 .. kTile-1
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
+                for (int i = 0; i < kRows; ++i) {
                     if (row == 4 * i + r) {
                         K.x[i] = kn;
                         V.x[i] = vn;
