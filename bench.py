@@ -59,8 +59,8 @@ def algorithmic_bytes(cfg, lengths, tables_entries, shared_tokens=0):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c3", help="workload key (c1a c1b c2 c3 c4 c5)")
     ap.add_argument("--op", default="step",
                     choices=["step", "append_tokens", "copy_blocks", "slotted"],
