@@ -216,6 +216,27 @@ def test_edge_cases(B, hq, hkv, dt, lens, P):
     assert ok, f"fused: max err {err}, {nbad} bad"
 
 
+@pytest.mark.parametrize("P", [0, 1024])
+def test_longest_context(P):
+    """One sequence of 131,071 tokens (1,024 blocks of 128, the last one short of a
+    token) beside a one-token sequence, at the long-context shapes (32 query / 8 KV
+    heads, bf16): single pass (8,192 sub-tiles through one work-group per KV head)
+    and 128 partitions.  Pools, slots and outputs against the oracle."""
+    lens = (131071, 1)
+    print(f"[gpu] longest context n={lens} P={P}", flush=True)
+    w = _small("c4", lengths=lens, width=1025, pool=1030)
+    c = w.cfg
+    r = O.run_step(w, scale_for(c.head_dim))
+    g = GpuStep(w, append=False)
+    out = fused_step(g, P)
+    torch.cuda.synchronize()
+    assert np.array_equal(g.slots.cpu().numpy(), r["slots"])
+    assert np.array_equal(bits_of(g.k_pool), r["k_pool"])
+    assert np.array_equal(bits_of(g.v_pool), r["v_pool"])
+    ok, err, nbad = tol_ok(widen_out(out), r["out"])
+    assert ok, f"max err {err}, {nbad} bad"
+
+
 def test_scale_zero_is_mean_over_exactly_n_tokens():
     """A zero scale makes attention the plain mean of the n value rows; any
     leakage of masked slots (NaN sentinels) or missing token shows up here."""
