@@ -97,18 +97,32 @@ def max_partitions(max_blocks_per_seq: int, block_size: int, partition_size: int
 
 
 # ---------------------------------------------------------------------------
+# The checks below run on every call, so they read each tensor attribute once and
+# compare dtypes by identity (torch dtypes are singletons): a short decode launch
+# is over in about 10 us, and the host has to keep up with it.
+_T = None  # (torch, float16, bfloat16, float32, int32, int64) once torch is imported
+
+
+def _types():
+    global _T
+    if _T is None:
+        import torch
+        _T = (torch, torch.float16, torch.bfloat16, torch.float32, torch.int32, torch.int64)
+    return _T
+
+
 def _torch():
-    import torch
-    return torch
+    return _types()[0]
 
 
 def _dtype_code(t) -> int:
-    torch = _torch()
-    if t.dtype == torch.float16:
+    _, f16, bf16 = _types()[:3]
+    d = t.dtype
+    if d is f16:
         return PKV_FP16
-    if t.dtype == torch.bfloat16:
+    if d is bf16:
         return PKV_BF16
-    raise TypeError(f"unsupported dtype {t.dtype}; expected float16 or bfloat16")
+    raise TypeError(f"unsupported dtype {d}; expected float16 or bfloat16")
 
 
 def _dev(*ts):
@@ -118,11 +132,11 @@ def _dev(*ts):
     for t in ts:
         if t is None:
             continue
-        if not t.is_cuda:
+        d = t.get_device()  # -1 for a CPU tensor
+        if d < 0:
             raise ValueError("all tensors must be on the GPU (no CPU path exists)")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
-        d = t.get_device()
         if dev is None:
             dev = d
         elif d != dev:
@@ -153,11 +167,14 @@ def _stream(dev):
     return torch.cuda.current_stream(dev).cuda_stream
 
 
-def _int(t, dtype, name):
-    torch = _torch()
-    want = {"i32": torch.int32, "i64": torch.int64}[dtype]
-    if t is not None and t.dtype != want:
-        raise TypeError(f"{name} must be {want}, got {t.dtype}")
+def _ints(*specs):
+    """specs: (tensor or None, "i32" | "i64", name); raises on another dtype."""
+    T = _types()
+    for t, kind, name in specs:
+        if t is not None:
+            want = T[4] if kind == "i32" else T[5]
+            if t.dtype is not want:
+                raise TypeError(f"{name} must be {want}, got {t.dtype}")
 
 
 def _check(rc: int, what: str):
@@ -170,20 +187,24 @@ def _check(rc: int, what: str):
 # therefore checks every tensor's shape and dtype against the sizes it passes,
 # before it touches the device.
 def _expect(t, shape, name: str):
-    if t is not None and tuple(t.shape) != tuple(shape):
-        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t is not None:
+        s = t.shape
+        if s != shape:
+            raise ValueError(f"{name} has shape {tuple(s)}, expected {tuple(shape)}")
 
 
 def _dims(t, n: int, name: str):
-    if t.dim() != n:
-        raise ValueError(f"{name} must have {n} dimensions, got shape {tuple(t.shape)}")
-    return tuple(t.shape)
+    s = t.shape
+    if len(s) != n:
+        raise ValueError(f"{name} must have {n} dimensions, got shape {tuple(s)}")
+    return s
 
 
 def _same_dtype(ref, *pairs):
+    d = ref.dtype
     for t, name in pairs:
-        if t is not None and t.dtype != ref.dtype:
-            raise TypeError(f"{name} is {t.dtype}, expected {ref.dtype} like the pools")
+        if t is not None and t.dtype is not d:
+            raise TypeError(f"{name} is {t.dtype}, expected {d} like the pools")
 
 
 def _pools(k_pool, v_pool):
@@ -196,14 +217,16 @@ def _pools(k_pool, v_pool):
 
 def _workspace(part_o, part_lse, S: int, Hq: int, D: int) -> int:
     """Partitions the split-mode workspace holds (0 without one)."""
-    torch = _torch()
     if part_o is None:
         return 0
-    mp = _dims(part_o, 4, "part_o")[2]
-    _expect(part_o, (S, Hq, mp, D), "part_o")
+    s = _dims(part_o, 4, "part_o")
+    mp = s[2]
+    if s != (S, Hq, mp, D):
+        raise ValueError(f"part_o has shape {tuple(s)}, expected {(S, Hq, mp, D)}")
     _expect(part_lse, (S, Hq, mp), "part_lse")
+    f32 = _types()[3]
     for t, name in ((part_o, "part_o"), (part_lse, "part_lse")):
-        if t is not None and t.dtype != torch.float32:
+        if t is not None and t.dtype is not f32:
             raise TypeError(f"{name} must be float32, got {t.dtype}")
     return mp
 
@@ -237,16 +260,15 @@ def paged_kv_append(k_pool, v_pool, k_new, v_new, block_tables, context_lens, sl
     _expect(k_new, (S, Hkv, D), "k_new")
     _expect(v_new, (S, Hkv, D), "v_new")
     _same_dtype(k_pool, (k_new, "k_new"), (v_new, "v_new"))
-    _tables(block_tables, S)
+    W = _tables(block_tables, S)
     _expect(context_lens, (S,), "context_lens")
     _expect(slot_out, (S,), "slot_out")
     dev = _dev(k_pool, v_pool, k_new, v_new, block_tables, context_lens, slot_out)
-    _int(block_tables, "i32", "block_tables")
-    _int(context_lens, "i32", "context_lens")
-    _int(slot_out, "i64", "slot_out")
+    _ints((block_tables, "i32", "block_tables"), (context_lens, "i32", "context_lens"),
+          (slot_out, "i64", "slot_out"))
     rc = load().paged_kv_append(_p(k_pool), _p(v_pool), _p(k_new), _p(v_new), _p(block_tables),
-                                _p(context_lens), _p(slot_out), S, Hkv, D, B,
-                                block_tables.shape[1], NB, _dtype_code(k_pool), _stream(dev))
+                                _p(context_lens), _p(slot_out), S, Hkv, D, B, W, NB,
+                                _dtype_code(k_pool), _stream(dev))
     _check(rc, "paged_kv_append")
 
 
@@ -258,16 +280,14 @@ def paged_kv_append_tokens(k_pool, v_pool, k_src, v_src, src_cu, start_pos, bloc
     _expect(k_src, (T, Hkv, D), "k_src")
     _expect(v_src, (T, Hkv, D), "v_src")
     _same_dtype(k_pool, (k_src, "k_src"), (v_src, "v_src"))
-    R = _dims(block_tables, 2, "block_tables")[0]
+    R, W = _dims(block_tables, 2, "block_tables")
     _expect(src_cu, (R + 1,), "src_cu")
     _expect(start_pos, (R,), "start_pos")
     dev = _dev(k_pool, v_pool, k_src, v_src, src_cu, start_pos, block_tables)
-    _int(src_cu, "i64", "src_cu")
-    _int(start_pos, "i32", "start_pos")
-    _int(block_tables, "i32", "block_tables")
+    _ints((src_cu, "i64", "src_cu"), (start_pos, "i32", "start_pos"),
+          (block_tables, "i32", "block_tables"))
     rc = load().paged_kv_append_tokens(_p(k_pool), _p(v_pool), _p(k_src), _p(v_src), _p(src_cu),
-                                       _p(start_pos), _p(block_tables), block_tables.shape[0],
-                                       k_src.shape[0], Hkv, D, B, block_tables.shape[1], NB,
+                                       _p(start_pos), _p(block_tables), R, T, Hkv, D, B, W, NB,
                                        _dtype_code(k_pool), _stream(dev))
     _check(rc, "paged_kv_append_tokens")
 
@@ -283,11 +303,10 @@ def paged_kv_copy_blocks(k_pools, v_pools, src_blocks, dst_blocks):
     shape = _dims(k_pools[0], 4, "k_pools[0]")
     dtype = k_pools[0].dtype
     for t in k_pools + v_pools:
-        if t.shape != shape or t.dtype != dtype:
+        if t.shape != shape or t.dtype is not dtype:
             raise ValueError("every pool must have the same shape and dtype")
     dev = _dev(*k_pools, *v_pools, src_blocks, dst_blocks)
-    _int(src_blocks, "i32", "src_blocks")
-    _int(dst_blocks, "i32", "dst_blocks")
+    _ints((src_blocks, "i32", "src_blocks"), (dst_blocks, "i32", "dst_blocks"))
     NB, Hkv, B, D = shape
     L = len(k_pools)
     kp = (C.c_void_p * L)(*[t.data_ptr() for t in k_pools])
@@ -306,8 +325,7 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens,
     NB, Hkv, B, D, S, Hq, W = _queries(out, q, k_pool, v_pool, block_tables, context_lens)
     mp = _workspace(part_o, part_lse, S, Hq, D)
     dev = _dev(out, q, k_pool, v_pool, block_tables, context_lens, part_o, part_lse)
-    _int(block_tables, "i32", "block_tables")
-    _int(context_lens, "i32", "context_lens")
+    _ints((block_tables, "i32", "block_tables"), (context_lens, "i32", "context_lens"))
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     rc = load().paged_attention_decode(_p(out), _p(q), _p(k_pool), _p(v_pool), _p(block_tables),
@@ -330,9 +348,8 @@ def paged_attention_append_decode(out, q, k_pool, v_pool, k_new, v_new, block_ta
     mp = _workspace(part_o, part_lse, S, Hq, D)
     dev = _dev(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens, slot_out,
                part_o, part_lse)
-    _int(block_tables, "i32", "block_tables")
-    _int(context_lens, "i32", "context_lens")
-    _int(slot_out, "i64", "slot_out")
+    _ints((block_tables, "i32", "block_tables"), (context_lens, "i32", "context_lens"),
+          (slot_out, "i64", "slot_out"))
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     rc = load().paged_attention_append_decode(
@@ -361,10 +378,9 @@ def paged_attention_prefix_decode(out, q, k_pool, v_pool, block_tables, context_
     mp = _workspace(part_o, part_lse, S, Hq, D)
     dev = _dev(out, q, k_pool, v_pool, block_tables, context_lens, group_cu, prefix_lens,
                part_o, part_lse, k_new, v_new, slot_out)
-    for t, n in ((block_tables, "block_tables"), (context_lens, "context_lens"),
-                 (group_cu, "group_cu"), (prefix_lens, "prefix_lens")):
-        _int(t, "i32", n)
-    _int(slot_out, "i64", "slot_out")
+    _ints((block_tables, "i32", "block_tables"), (context_lens, "i32", "context_lens"),
+          (group_cu, "i32", "group_cu"), (prefix_lens, "i32", "prefix_lens"),
+          (slot_out, "i64", "slot_out"))
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     rc = load().paged_attention_prefix_decode(
@@ -385,17 +401,17 @@ def paged_attention_decode_slotted(out, q, k_pool, v_pool, segments, num_segment
         raise ValueError(f"q has head_dim {Dq}, the pools {D}")
     _same_dtype(k_pool, (q, "q"), (out, "out"))
     _expect(out, (S, Hq, D), "out")
-    if segments.dim() != 3 or segments.shape[0] != S or segments.shape[2] != 3:
-        raise ValueError(f"segments must be [{S}][max_segments][3], got {tuple(segments.shape)}")
+    ss = segments.shape
+    if len(ss) != 3 or ss[0] != S or ss[2] != 3:
+        raise ValueError(f"segments must be [{S}][max_segments][3], got {tuple(ss)}")
     _expect(num_segments, (S,), "num_segments")
     dev = _dev(out, q, k_pool, v_pool, segments, num_segments)
-    _int(segments, "i32", "segments")
-    _int(num_segments, "i32", "num_segments")
+    _ints((segments, "i32", "segments"), (num_segments, "i32", "num_segments"))
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     rc = load().paged_attention_decode_slotted(
         _p(out), _p(q), _p(k_pool), _p(v_pool), _p(segments), _p(num_segments), S, Hq, Hkv, D,
-        B, segments.shape[1], NB, float(scale), _dtype_code(q), _stream(dev))
+        B, ss[1], NB, float(scale), _dtype_code(q), _stream(dev))
     _check(rc, "paged_attention_decode_slotted")
 
 
@@ -406,7 +422,7 @@ def paged_attention_reduce(out, part_o, part_lse, context_lens, partition_size: 
     _expect(out, (S, Hq, D), "out")
     _expect(context_lens, (S,), "context_lens")
     dev = _dev(out, part_o, part_lse, context_lens)
-    _int(context_lens, "i32", "context_lens")
+    _ints((context_lens, "i32", "context_lens"))
     rc = load().paged_attention_reduce(_p(out), _p(part_o), _p(part_lse), _p(context_lens), S, Hq,
                                        D, int(partition_size), MP, _dtype_code(out), _stream(dev))
     _check(rc, "paged_attention_reduce")

@@ -10,7 +10,9 @@
 // gfx950 design.  A GQA group turns Q.K^T and P.V into dense tiles, so both go to
 // the matrix cores (the group of G <= 16 query rows is padded to 16):
 //   * a work-group is 4 wave64s; one work-group per (sequence, KV head[, partition]);
-//     the waves take 16-token sub-tiles round-robin, double-buffered in VGPRs;
+//     the waves take 16-token sub-tiles round-robin, double-buffered in VGPRs (the
+//     one-pass shared-prefix kernel uses 8 waves and 32 query columns: two 16-column
+//     halves, each holding floor(16/G) member sequences);
 //   * scores: S^T[16 tok x 16 q] = K[16 x 128] . Q^T with four
 //     v_mfma_f32_16x16x32_{f16,bf16}.  K rows are the A operand and are loaded
 //     straight from HBM with 16-byte loads (lane i+16j holds 8 dims of token i);
@@ -21,8 +23,9 @@
 //   * the V tile must enter P.V with tokens along the contraction axis, i.e.
 //     transposed with respect to the pool's row-major [token][dim] layout.  It is
 //     staged through LDS: coalesced 16-byte global loads, 16-byte LDS writes into
-//     a padded row-major tile, then 2-byte transposing reads (row stride of 272
-//     bytes keeps the four lane groups on disjoint banks);
+//     a padded row-major tile, then 2-byte transposing reads (a row stride of 288
+//     bytes keeps the lanes of one read on distinct banks; the K tile uses the same
+//     stride when it is staged);
 //   * online softmax per query row in the exp2 domain: the row max is reduced
 //     across the four lane groups holding the row, the running sum is kept per
 //     lane and reduced once at the end; waves are merged through LDS with the
