@@ -212,6 +212,12 @@ bool debug_enabled()
     return e && e[0] && strcmp(e, "0") != 0;
 }
 
+bool slotted_tiles_enabled()
+{
+    const char *e = getenv("PKV_SLOTTED_TILES");
+    return !(e && strcmp(e, "0") == 0);
+}
+
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool supported_block(int b) { return b == 16 || b == 32 || b == 64 || b == 128 || b == 256; }
@@ -642,6 +648,18 @@ int paged_attention_decode_slotted(void *out, const void *q, const void *k_pool,
     a.segments = segments;
     a.num_segments = num_segments;
     a.max_segments = max_segments;
+    // Tiles of consecutive sequences read their common leading segments once; they
+    // need the whole list of a tile's sub-tiles in LDS, so a batch whose worst-case
+    // tile exceeds it runs one work-group per sequence.  PKV_SLOTTED_TILES=0 forces
+    // the latter.
+    const int spt = pkv::kPrefixHalves * (16 / (num_q_heads / num_kv_heads));
+    const int64_t tile_subs = (int64_t)spt * max_segments * ((block_size + 15) / 16);
+    if (slotted_tiles_enabled() && tile_subs <= pkv::kSlottedTileSubs) {
+        a.seqs_per_tile = spt;
+        const int64_t tiles = (num_seqs + spt - 1) / spt;
+        return launch_status(pkv::launch_slotted_tiled_mfma(a, (int)(tiles * num_kv_heads),
+                                                            dtype, block_size, st));
+    }
     return launch_status(pkv::launch_slotted_mfma(a, dtype, block_size, st));
 }
 

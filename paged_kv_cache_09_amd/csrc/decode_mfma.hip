@@ -1289,6 +1289,357 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
     }
 }
 
+// Slotted decode in tiles of sequences.  One work-group per (query tile, KV head),
+// with the tile of the one-pass shared-prefix kernel: NH halves of 16 MFMA
+// columns, each holding the G query heads of floor(16/G) consecutive sequences.
+// A radix-tree batch lists each sequence as the path of nodes from the root, so
+// consecutive sequences start with the same segments.  The tile's common segments
+// -- the leading triples that every member lists identically, found by comparing
+// the first kCommonScan of them -- become sub-tiles read once for the whole tile
+// with every column active; each member's remaining segments become sub-tiles
+// with only its G columns active (the others score -inf and keep their state).
+// The whole list of descriptors sits in LDS: the host takes this path only when
+// a tile's sub-tiles fit (members x max_segments x ceil(B/16) <= kTileSubs).  The
+// waves take the list round-robin with the common sub-tiles spread evenly among
+// the members' ones, as in the shared-prefix kernel.
+constexpr int kTileSubs = kSlottedTileSubs;  // descriptor capacity of one tile's list
+constexpr int kCommonScan = 64;              // leading segments compared across a tile
+
+__device__ __forceinline__ int wave_sum_i(int x)
+{
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1)
+        x += __shfl_xor(x, d, 64);
+    return x;
+}
+
+// Sub-tile descriptor: physical block, and first row | row count << 8 | owner << 16,
+// where owner is the member index + 1, or 0 for a common sub-tile.
+__device__ __forceinline__ int32_t slot_desc(int first_row, int rows, int owner)
+{
+    return first_row | (rows << 8) | (owner << 16);
+}
+
+template <int DT, int BS, int WAVES, int NH>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void slotted_tiled_mfma_kernel(DecodeArgs a)
+{
+    constexpr int kCols = 16 * NH;   // query columns of a tile
+    constexpr int kMembers = kCols;  // most member sequences of a tile (G = 1)
+    __shared__ __attribute__((aligned(16))) union {
+        uint16_t v[WAVES][kStageElems];
+        float o[WAVES][kCols][kOStride];
+    } sm;
+    __shared__ float s_m[WAVES][kCols], s_l[WAVES][kCols];
+    __shared__ int32_t s_phys[kTileSubs];
+    __shared__ int32_t s_desc[kTileSubs];
+    __shared__ uint64_t s_diff[WAVES];  // per wave: segment indices where a member differs
+    __shared__ int32_t s_cnt[kMembers];  // each member's own sub-tiles
+    __shared__ int32_t s_ncom;          // common sub-tiles
+
+    const int item = blockIdx.x;
+    const int g = item % a.num_kv_heads;
+    const int tile = item / a.num_kv_heads;
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const int spt = a.seqs_per_tile;  // NH * floor(16 / G)
+    const int sph = spt / NH;         // member sequences per half
+    const int s0 = tile * spt;
+    const int m = min(a.num_seqs - s0, spt);  // members of this tile, >= 1
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int col = lane & 15, grp = lane >> 4;
+    const int ms = a.max_segments;
+
+    const uint16_t *__restrict__ kp = (const uint16_t *)a.k_pool;
+    const uint16_t *__restrict__ vp = (const uint16_t *)a.v_pool;
+    const int64_t blk_elems = (int64_t)a.num_kv_heads * BS * kHeadDim;
+    const int64_t head_off = (int64_t)g * BS * kHeadDim;
+    uint16_t *vlds = sm.v[w];
+    uint16_t *klds = vlds + kSub * kVStride;
+    // segments of member i, and how many are in use (clamped to the row)
+    auto seg_row = [&](int i) { return a.segments + (int64_t)(s0 + i) * ms * 3; };
+    auto seg_count = [&](int i) { return min(max(a.num_segments[s0 + i], 0), ms); };
+    // a segment never reaches outside its block, whatever the caller passed
+    auto clamp_seg = [&](int &off, int &len) {
+        off = min(max(off, 0), BS);
+        len = min(max(len, 0), BS - off);
+    };
+
+    // 1. Common segments: lane k compares segment k of every member with member
+    // 0's; each wave takes members 1 + w, 1 + w + WAVES, ...
+    const int n0 = seg_count(0);
+    int b0 = 0, o0 = 0, l0 = 0;
+    if (lane < n0) {
+        const int32_t *r = seg_row(0) + 3 * lane;
+        b0 = r[0];
+        o0 = r[1];
+        l0 = r[2];
+    }
+    {
+        bool diff = lane >= n0;
+        for (int i = 1 + w; i < m; i += WAVES) {
+            const int ni = seg_count(i);
+            if (lane < ni && lane < n0) {
+                const int32_t *r = seg_row(i) + 3 * lane;
+                diff |= r[0] != b0 || r[1] != o0 || r[2] != l0;
+            } else {
+                diff = true;
+            }
+        }
+        const uint64_t d = __ballot(diff);
+        if (lane == 0)
+            s_diff[w] = d;
+    }
+    __syncthreads();
+    int ncom;
+    {
+        uint64_t d = 0;
+#pragma unroll
+        for (int i = 0; i < WAVES; ++i)
+            d |= s_diff[i];
+        ncom = d ? __builtin_ctzll(d) : kCommonScan;
+    }
+
+    // 2. The common sub-tiles (wave 0, from member 0's segments) at the head of
+    // the list, and each member's count of own sub-tiles
+    if (w == 0) {
+        int off = o0, len = l0;
+        clamp_seg(off, len);
+        const int c = lane < ncom ? (len + kSub - 1) / kSub : 0;
+        int incl = c;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int up = __shfl_up(incl, d, 64);
+            incl += lane >= d ? up : 0;
+        }
+        for (int k = 0; k < c; ++k) {
+            s_phys[incl - c + k] = b0;
+            s_desc[incl - c + k] = slot_desc(off + kSub * k, min(kSub, len - kSub * k), 0);
+        }
+        if (lane == 63)
+            s_ncom = incl;
+    }
+    for (int i = w; i < m; i += WAVES) {
+        const int ni = seg_count(i);
+        const int32_t *r = seg_row(i);
+        int cnt = 0;
+        for (int base = ncom; base < ni; base += 64) {
+            int c = 0;
+            if (base + lane < ni) {
+                int off = r[3 * (base + lane) + 1], len = r[3 * (base + lane) + 2];
+                clamp_seg(off, len);
+                c = (len + kSub - 1) / kSub;
+            }
+            cnt += wave_sum_i(c);
+        }
+        if (lane == 0)
+            s_cnt[i] = cnt;
+    }
+    __syncthreads();
+
+    // 3. Each member's own sub-tiles, member after member, after the common ones
+    const int n_pre = __builtin_amdgcn_readfirstlane(s_ncom);
+    int total = n_pre;
+    for (int i = 0; i < m; ++i)
+        total += __builtin_amdgcn_readfirstlane(s_cnt[i]);
+    for (int i = w; i < m; i += WAVES) {
+        int pos = n_pre;
+        for (int k = 0; k < i; ++k)
+            pos += __builtin_amdgcn_readfirstlane(s_cnt[k]);
+        const int ni = seg_count(i);
+        const int32_t *r = seg_row(i);
+        for (int base = ncom; base < ni; base += 64) {
+            int blk = 0, off = 0, len = 0, c = 0;
+            if (base + lane < ni) {
+                blk = r[3 * (base + lane)];
+                off = r[3 * (base + lane) + 1];
+                len = r[3 * (base + lane) + 2];
+                clamp_seg(off, len);
+                c = (len + kSub - 1) / kSub;
+            }
+            int incl = c;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int up = __shfl_up(incl, d, 64);
+                incl += lane >= d ? up : 0;
+            }
+            for (int k = 0; k < c; ++k) {
+                s_phys[pos + incl - c + k] = blk;
+                s_desc[pos + incl - c + k] =
+                    slot_desc(off + kSub * k, min(kSub, len - kSub * k), i + 1);
+            }
+            pos += __builtin_amdgcn_readlane(incl, 63);
+        }
+    }
+    __syncthreads();
+
+    const int ch = g * G + col % G;  // query head of this lane's column
+    int cm[NH];                      // member of this lane's column in each half
+    bool active[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        cm[h] = h * sph + col / G;
+        active[h] = col < sph * G && cm[h] < m;
+    }
+    // every lane loads a valid query row (inactive columns read a neighbour's and
+    // zero it): no load sits under a lane-dependent branch
+    u32x4 qop[NH][4];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        const uint16_t *qrow = (const uint16_t *)a.q +
+                               ((int64_t)(s0 + min(cm[h], m - 1)) * a.num_q_heads + ch) *
+                                   kHeadDim +
+                               grp * 8;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const u32x4 v = *(const u32x4 *)(qrow + kk * 32);
+            qop[h][kk] = active[h] ? v : (u32x4){0u, 0u, 0u, 0u};
+        }
+    }
+    GqaState st[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        st[h].m = kNegInf;
+        st[h].l = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+            st[h].acc[jj] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+
+    // Position j of the list is common sub-tile pi = floor(j P / T) when
+    // floor((j+1) P / T) exceeds pi, else the members' sub-tile j - pi (entry
+    // P + j - pi); the quotients advance by a constant step with a carry.  A j past
+    // the list describes an empty sub-tile (zero rows, so its buffer range is
+    // empty and nothing is fetched), so every step issues its loads the same way.
+    struct Sub {
+        int32_t phys, desc;
+    };
+    const int tot = max(total, 1);
+    const int64_t wp = (int64_t)WAVES * n_pre;
+    const int dq = (int)(wp / tot), dr = (int)(wp % tot);
+    int q0 = (int)((int64_t)w * n_pre / tot), r0 = (int)((int64_t)w * n_pre % tot);
+    int q1 = (int)((int64_t)(w + 1) * n_pre / tot);
+    int r1 = (int)((int64_t)(w + 1) * n_pre % tot);
+    auto describe = [&](int j) {
+        int idx = 0;
+        const bool past = j >= total;
+        if (!past) {
+            const int pi = q0, pi1 = q1;
+            q0 += dq;
+            r0 += dr;
+            if (r0 >= total) {
+                r0 -= total;
+                ++q0;
+            }
+            q1 += dq;
+            r1 += dr;
+            if (r1 >= total) {
+                r1 -= total;
+                ++q1;
+            }
+            idx = pi1 > pi ? pi : n_pre + j - pi;
+        }
+        Sub d;
+        d.phys = __builtin_amdgcn_readfirstlane(s_phys[idx]);
+        d.desc = past ? 0 : __builtin_amdgcn_readfirstlane(s_desc[idx]);
+        return d;
+    };
+    auto load_sub = [&](KOp &K, VRows &V, const Sub &d) {
+        const int64_t b = (int64_t)d.phys * blk_elems + head_off +
+                          (int64_t)(d.desc & 0xff) * kHeadDim;
+        const int bytes = ((d.desc >> 8) & 0xff) * kHeadDim * 2;
+        load_k<kLoadReuse>(K, make_rsrc(kp + b, bytes), lane);
+        load_v<kLoadReuse>(V, make_rsrc(vp + b, bytes), lane);
+    };
+    auto step = [&](KOp &K, VRows &V, Sub &cur, Sub &nxt, int jn) {
+        const Sub nxt2 = describe(jn);
+        u32x2 pb[NH];
+        float alpha[NH];
+        bool rs[NH];
+        const int rows = (cur.desc >> 8) & 0xff;
+        const int owner = (cur.desc >> 16) - 1;  // -1: common
+        const KOp KA = k_operand(K, klds, lane);
+        // a full common sub-tile needs no mask: a column outside the tile only
+        // updates a state that is never written out
+        if (owner < 0 && rows == kSub) {
+#pragma unroll
+            for (int h = 0; h < NH; ++h)
+                rs[h] = qk_softmax<DT, false>(st[h], KA, qop[h], 0, 0, kSub, lane, a.scale_log2,
+                                              pb[h], alpha[h]);
+        } else {
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+                const bool on = owner < 0 ? active[h] : (active[h] && cm[h] == owner);
+                rs[h] = qk_softmax<DT, true>(st[h], KA, qop[h], 0, 0, rows, lane, a.scale_log2,
+                                             pb[h], alpha[h], on);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        stage_v(V, vlds, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        load_sub(K, V, nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        pv_mma_halves<DT, NH>(st, vlds, pb, rs, alpha, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        cur = nxt;
+        nxt = nxt2;
+    };
+    if (w < total) {
+        Sub cur = describe(w);
+        Sub nxt = describe(w + WAVES);
+        KOp K;
+        VRows V;
+        load_sub(K, V, cur);
+        for (int j = w; j < total; j += WAVES)
+            step(K, V, cur, nxt, j + 2 * WAVES);
+    }
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+        st[h].l = pair_sum32(pair_sum16(st[h].l));
+
+    __syncthreads();  // all waves are done with their V staging area
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+            *(f32x4 *)&sm.o[w][16 * h + col][16 * jj + 4 * grp] = st[h].acc[jj];
+        if (grp == 0) {
+            s_m[w][16 * h + col] = st[h].m;
+            s_l[w][16 * h + col] = st[h].l;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < kCols * 32; e += WAVES * 64) {
+        const int qi = e >> 5, d0 = (e & 31) * 4;
+        const int h = qi / 16, c = qi % 16;
+        const int mi = h * sph + c / G;
+        if (c >= sph * G || mi >= m)
+            continue;
+        const int64_t row = (int64_t)(s0 + mi) * a.num_q_heads + g * G + c % G;
+        float M = s_m[0][qi];
+#pragma unroll
+        for (int i = 1; i < WAVES; ++i)
+            M = fmaxf(M, s_m[i][qi]);
+        const float ref = safe_ref(M);
+        float L = 0.f;
+        f32x4 O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < WAVES; ++i) {
+            const float wgt = fexp2(s_m[i][qi] - ref);
+            L += s_l[i][qi] * wgt;
+            O += *(const f32x4 *)&sm.o[i][qi][d0] * wgt;
+        }
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+        if (L > 0.f)
+            o = O / L;
+        u32x2 packed;
+        packed.x = (uint32_t)to_bits<DT>(o[0]) | ((uint32_t)to_bits<DT>(o[1]) << 16);
+        packed.y = (uint32_t)to_bits<DT>(o[2]) | ((uint32_t)to_bits<DT>(o[3]) << 16);
+        *(u32x2 *)((uint16_t *)a.out + row * kHeadDim + d0) = packed;
+    }
+}
+
 }  // namespace
 
 // Waves per work-group (tuning knobs): the decode kernel, its suffix pass in
@@ -1388,6 +1739,34 @@ static hipError_t launch_slotted_t(const DecodeArgs &a, hipStream_t stream)
     hipLaunchKernelGGL((slotted_mfma_kernel<DT, BS, W>), dim3(a.n_items), dim3(W * 64), 0, stream,
                        a);
     return hipGetLastError();
+}
+
+template <int DT, int BS>
+static hipError_t launch_slotted_tiled_t(const DecodeArgs &a, int n_items, hipStream_t stream)
+{
+    constexpr int W = PKV_PFX_FUSED_WAVES;
+    hipLaunchKernelGGL((slotted_tiled_mfma_kernel<DT, BS, W, kPrefixHalves>), dim3(n_items),
+                       dim3(W * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_slotted_tiled_mfma(const DecodeArgs &a, int n_items, int dtype, int block_size,
+                                     hipStream_t stream)
+{
+#define PKV_ST_CASE(BSV)                                                                  \
+    case BSV:                                                                             \
+        return dtype == kFp16 ? launch_slotted_tiled_t<kFp16, BSV>(a, n_items, stream)   \
+                              : launch_slotted_tiled_t<kBf16, BSV>(a, n_items, stream);
+    switch (block_size) {
+        PKV_ST_CASE(16)
+        PKV_ST_CASE(32)
+        PKV_ST_CASE(64)
+        PKV_ST_CASE(128)
+        PKV_ST_CASE(256)
+    default:
+        return hipErrorInvalidValue;
+    }
+#undef PKV_ST_CASE
 }
 
 hipError_t launch_slotted_mfma(const DecodeArgs &a, int dtype, int block_size, hipStream_t stream)

@@ -31,6 +31,12 @@ hipError_t launch_slotted_mfma(const DecodeArgs &a, int dtype, int block_size,
 constexpr int kPrefixHalves = PKV_PREFIX_HALVES;
 hipError_t launch_prefix_fused_mfma(const DecodeArgs &a, int n_items, int dtype, int block_size,
                                     hipStream_t stream);
+// Slotted decode over n_items (query tile, KV head) items, tiles as for the
+// one-pass shared-prefix kernel; a tile's sub-tile list must fit in
+// kSlottedTileSubs descriptors (members x max_segments x ceil(B / 16)).
+constexpr int kSlottedTileSubs = 1024;
+hipError_t launch_slotted_tiled_mfma(const DecodeArgs &a, int n_items, int dtype, int block_size,
+                                     hipStream_t stream);
 hipError_t launch_reduce(void *out, const float *part_o, const float *part_lse,
                          const int32_t *lens, int num_seqs, int num_q_heads, int partition_size,
                          int max_partitions, int dtype, hipStream_t stream);

@@ -36,6 +36,15 @@ def _pools_both(runs, NB, Hkv, B, dtype):
     return kp, vp, gk, gv
 
 
+@pytest.fixture(params=["tiles", "per_sequence"])
+def mode(request, monkeypatch):
+    """Both kernels: tiles of sequences (the default wherever a tile's sub-tile
+    list fits in LDS) and one work-group per sequence (PKV_SLOTTED_TILES=0)."""
+    if request.param == "per_sequence":
+        monkeypatch.setenv("PKV_SLOTTED_TILES", "0")
+    return request.param
+
+
 def _gpu(q, gk, gv, segs, nsegs, dtype, scale):
     S, Hq, _ = q.shape
     out = torch.empty((S, Hq, 128), dtype=TDT[dtype], device=DEV)
@@ -46,10 +55,10 @@ def _gpu(q, gk, gv, segs, nsegs, dtype, scale):
     return widen_out(out)
 
 
-def test_radix_batch_matches_oracle():
+def test_radix_batch_matches_oracle(mode):
     cfg = get_config("c5")
     w = make_slotted_workload(cfg)
-    print(f"[gpu] slotted radix batch S={len(w.paths)} NB={w.num_blocks} "
+    print(f"[gpu] slotted radix batch ({mode}) S={len(w.paths)} NB={w.num_blocks} "
           f"max_segments={w.segments.shape[1]}", flush=True)
     kp, vp, gk, gv = _pools_both(w.runs(), w.num_blocks, cfg.num_kv_heads, cfg.block_size,
                                  cfg.dtype)
@@ -61,9 +70,11 @@ def test_radix_batch_matches_oracle():
     assert ok, (err, nbad)
 
 
-def _node_case(seed, S, Hq, Hkv, B, dtype, node_len_hi, nodes_per_path):
+def _node_case(seed, S, Hq, Hkv, B, dtype, node_len_hi, nodes_per_path, trunks=False):
     """Random tree-less node sets: every sequence walks its own random list of
-    nodes (shared ones included), some paths empty, some nodes of length 0."""
+    nodes (shared ones included), some paths empty, some nodes of length 0.
+    With trunks, runs of consecutive sequences first walk a common random list
+    of nodes (cut short for some), as the paths of a radix tree do."""
     rng = np.random.default_rng(seed)
     nn = max(3 * S + 8, 2 * nodes_per_path)
     lens = [int(x) for x in rng.integers(0, node_len_hi + 1, size=nn)]
@@ -84,7 +95,18 @@ def _node_case(seed, S, Hq, Hkv, B, dtype, node_len_hi, nodes_per_path):
     node_v = [draw(n, Hkv, 128) for n in lens]
     paths = [[int(x) for x in rng.choice(nn, size=rng.integers(0, nodes_per_path + 1),
                                          replace=False)] for _ in range(S)]
-    paths[0] = []
+    if trunks:
+        s = 0
+        while s < S:
+            run = int(rng.integers(8, 80))
+            trunk = [int(x) for x in rng.choice(nn, size=rng.integers(0, nodes_per_path + 1),
+                                                replace=False)]
+            for t in range(s, min(S, s + run)):
+                cut = len(trunk) if rng.random() < 0.97 else int(rng.integers(0, len(trunk) + 1))
+                own = [x for x in paths[t] if x not in trunk[:cut]][:int(rng.integers(0, 4))]
+                paths[t] = trunk[:cut] + own
+            s += run
+    paths[-1 if trunks else 0] = []
     MS = max(1, max(sum(len(node_segs[i]) for i in p) for p in paths))
     segs = np.zeros((S, MS, 3), np.int32)
     nsegs = np.zeros(S, np.int32)
@@ -117,11 +139,24 @@ NODE_CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", NODE_CASES, ids=[f"seed{c[0]}" for c in NODE_CASES])
-def test_random_node_lists(case):
+# runs of sequences sharing leading nodes: the tiles' common sub-tiles
+TRUNK_CASES = [
+    # (seed, S, Hq, Hkv, B, dtype, max node length, max nodes per path)
+    (11, 37, 32, 8, 16, "fp16", 40, 10),     # G 4: 8 per tile, a partial last tile
+    (12, 45, 16, 16, 16, "bf16", 30, 5),     # G 1: 32 per tile, then a partial tile
+    (13, 9, 12, 2, 16, "fp16", 33, 8),       # G 6: 4 per tile (12 of 16 columns per half)
+    (14, 7, 32, 2, 64, "bf16", 150, 4),      # G 16: 2 per tile
+    (15, 19, 24, 8, 16, "fp16", 17, 40),     # G 3, many short segments
+    (22, 70, 8, 8, 16, "fp16", 30, 6),       # G 1: two full tiles of 32 with common nodes
+]
+
+
+@pytest.mark.parametrize("case", NODE_CASES + TRUNK_CASES,
+                         ids=[f"seed{c[0]}" for c in NODE_CASES + TRUNK_CASES])
+def test_random_node_lists(case, mode):
     seed, S, Hq, Hkv, B, dtype, hi, per = case
-    c = _node_case(seed, S, Hq, Hkv, B, dtype, hi, per)
-    print(f"[gpu] slotted seed={seed} S={S} Hq={Hq} Hkv={Hkv} B={B} {dtype} "
+    c = _node_case(seed, S, Hq, Hkv, B, dtype, hi, per, trunks=seed >= 11)
+    print(f"[gpu] slotted ({mode}) seed={seed} S={S} Hq={Hq} Hkv={Hkv} B={B} {dtype} "
           f"max_segments={c['segs'].shape[1]}", flush=True)
     kp, vp, gk, gv = _pools_both(c["runs"], c["NB"], Hkv, B, dtype)
     scale = scale_for(128)
@@ -130,7 +165,7 @@ def test_random_node_lists(case):
     got = _gpu(c["q"], gk, gv, c["segs"], c["nsegs"], dtype, scale)
     ok, err, nbad = tol_ok(got, ref)
     assert ok, (err, nbad)
-    assert (got[0] == 0).all()  # the empty sequence
+    assert (got[-1 if seed >= 11 else 0] == 0).all()  # the empty sequence
 
 
 @pytest.mark.parametrize("key", ["c1a", "c2", "c4"])
