@@ -272,6 +272,13 @@ int paged_attention_prefix_decode(void *out, const void *q, void *k_pool, void *
  * out[s][h] = softmax(scale * q.K^T) V over those n = sum(length) tokens; n = 0
  * gives zeros.  Single pass; all head-group sizes run on the matrix-core path.
  *
+ * Consecutive sequences whose lists begin with the same triples (the shared path
+ * of a radix tree) have those rows read once per tile of 2 * floor(16 / G)
+ * sequences, whenever a tile's sub-tile list fits the kernel's LDS
+ * (2 * floor(16 / G) * max_segments * ceil(block_size / 16) <= 1024); otherwise,
+ * or with the environment variable PKV_SLOTTED_TILES=0, one work-group per
+ * (sequence, KV head).  Both give the same attention up to summation order.
+ *
  *   segments       device int32 [num_seqs][max_segments][3]: (block_id,
  *                  slot_offset, length); only the first num_segments[s] are read
  *   num_segments   device int32 [num_seqs], 0 .. max_segments
