@@ -790,7 +790,7 @@ void slotted_mfma_kernel(DecodeArgs a)
     const int64_t blk_elems = (int64_t)a.num_kv_heads * BS * kHeadDim;
     const int64_t head_off = (int64_t)g * BS * kHeadDim;
     const int32_t *__restrict__ segs = a.segments + (int64_t)s * a.max_segments * 3;
-    const int nseg = a.num_segments[s];
+    const int nseg = min(max(a.num_segments[s], 0), a.max_segments);  // never past the row
     uint16_t *vlds = sm.v[w];
     uint16_t *klds = vlds + kSub * kVStride;
 

@@ -168,6 +168,26 @@ def test_random_node_lists(case, mode):
     assert (got[-1 if seed >= 11 else 0] == 0).all()  # the empty sequence
 
 
+def test_segment_counts_are_clamped_to_the_row(mode):
+    """Without the debug check, a count above max_segments reads no further than
+    the sequence's own row (as if it were max_segments), and a negative count
+    reads nothing."""
+    seed, S, Hq, Hkv, B, dtype, hi, per = TRUNK_CASES[0]
+    c = _node_case(seed, S, Hq, Hkv, B, dtype, hi, per, trunks=True)
+    MS = c["segs"].shape[1]
+    print(f"[gpu] slotted ({mode}) clamped counts S={S} max_segments={MS}", flush=True)
+    kp, vp, gk, gv = _pools_both(c["runs"], c["NB"], Hkv, B, dtype)
+    scale = scale_for(128)
+    over = c["nsegs"].copy()
+    over[1::3] = MS + 1000
+    over[2::5] = -7
+    clamped = np.clip(over, 0, MS).astype(np.int32)
+    got = _gpu(c["q"], gk, gv, c["segs"], over, dtype, scale)
+    ref = _gpu(c["q"], gk, gv, c["segs"], clamped, dtype, scale)
+    assert (got == ref).all()
+    assert (got[2::5] == 0).all()
+
+
 @pytest.mark.parametrize("key", ["c1a", "c2", "c4"])
 def test_block_tables_as_segments(key):
     """A block table as whole-block segments (plus the partly filled last block)
