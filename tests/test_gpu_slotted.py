@@ -148,6 +148,8 @@ TRUNK_CASES = [
     (14, 7, 32, 2, 64, "bf16", 150, 4),      # G 16: 2 per tile
     (15, 19, 24, 8, 16, "fp16", 17, 40),     # G 3, many short segments
     (22, 70, 8, 8, 16, "fp16", 30, 6),       # G 1: two full tiles of 32 with common nodes
+    (23, 40, 16, 8, 16, "bf16", 25, 8),      # G 2: 16 per tile
+    (33, 7, 32, 2, 256, "fp16", 600, 3),     # G 16 at the largest block: 16 sub-tiles a segment
 ]
 
 
