@@ -75,6 +75,10 @@ def parse():
                     help="run the append and the decode as two launches per layer "
                          "(paged_kv_append + paged_attention_decode) instead of the fused "
                          "paged_attention_append_decode")
+    ap.add_argument("--no-merge", action="store_true",
+                    help="for a split workload, run the split decode and the standalone merge "
+                         "(paged_attention_reduce) as two launches per layer instead of "
+                         "paged_attention_split_decode, which merges in the same launch")
     ap.add_argument("--no-prefix", action="store_true",
                     help="for a shared-prefix workload, run the plain fused decode instead of "
                          "paged_attention_prefix_decode")
@@ -284,6 +288,10 @@ def bench_step(args):
 
     fused = not args.separate
     prefix = cfg.prefix_tokens > 0 and not args.no_prefix
+    # split workloads merge their partitions in the decode launch itself, with one
+    # zeroed arrival counter per (sequence, KV head) that every launch leaves zero
+    merged = bool(P) and not args.no_merge and not prefix
+    counters = torch.zeros((S, cfg.num_kv_heads), dtype=torch.int32, device=dev)
     if prefix:
         # one group: every sequence shares the workload's prefix blocks
         PP = cfg.bench_prefix_partition if args.prefix_partition is None else args.prefix_partition
@@ -310,6 +318,11 @@ def bench_step(args):
                                               k_new=L["kn"] if fused else None,
                                               v_new=L["vn"] if fused else None, scale=scale,
                                               prefix_partition=PP)
+        elif merged:
+            pkv.paged_attention_split_decode(out[li], L["q"], L["k"], L["v"], tables, lens, P,
+                                             part_o, part_lse, counters,
+                                             k_new=L["kn"] if fused else None,
+                                             v_new=L["vn"] if fused else None, scale=scale)
         elif fused:
             pkv.paged_attention_append_decode(o, L["q"], L["k"], L["v"], L["kn"], L["vn"],
                                               tables, lens, scale=scale, partition_size=P,
@@ -324,7 +337,7 @@ def bench_step(args):
             if not fused:
                 pkv.paged_kv_append(L["k"], L["v"], L["kn"], L["vn"], tables, lens)
             attend(si, li)
-            if P:
+            if P and not merged:
                 pkv.paged_attention_reduce(out[li], part_o, part_lse, lens, P)
 
     # ---- timed region ------------------------------------------------------------
@@ -419,12 +432,17 @@ def bench_step(args):
             "pool_blocks_per_layer": int(w0.num_blocks),
             "distinct_layer_pools": R,
             "partition_size": P,
-            "launches_per_layer": (1 if fused else 2) + (1 if P or (prefix and PP) else 0),
+            "launches_per_layer": ((1 if fused else 2) +
+                                   (1 if (P and not merged) or (prefix and PP) else 0)),
             "launch": "hip graph replay" if args.graph else "eager",
             "shared_prefix": cfg.prefix_tokens,
             "path": ("paged_attention_prefix_decode (prefix partition %d)" % PP if prefix
-                     else "paged_attention_append_decode" if fused else
-                     "paged_kv_append + paged_attention_decode"),
+                     else ("paged_attention_split_decode (merged in launch)" +
+                           (" with the fused append" if fused else " after paged_kv_append"))
+                     if merged
+                     else ("paged_attention_append_decode" if fused else
+                           "paged_kv_append + paged_attention_decode") +
+                     (" + paged_attention_reduce" if P else "")),
             "accumulate": "fp32",
         },
         "hbm_gbps": round(gbps, 1),
@@ -433,6 +451,8 @@ def bench_step(args):
         "roofline": {
             "kernel": (("paged_attention_prefix_decode (prefix + suffix pass)" if PP else
                         "paged_attention_prefix_decode (one pass)") if prefix
+                       else "paged_attention_split_decode (partitions merged in launch)"
+                       if merged
                        else "paged_attention_append_decode" if fused
                        else "paged_attention_decode"),
             "bound": "hbm",

@@ -42,6 +42,10 @@
  * Supported shapes: head_dim = 128; block_size in {16, 32, 64, 128, 256};
  *   num_q_heads a multiple of num_kv_heads with a group of at most 16 query
  *   heads per KV head.  Others give PKV_ENOTSUP.
+ * Softmax scale. Every attention entry point takes `scale`, the factor applied
+ *   to q.k before the softmax.  A NaN (PKV_DEFAULT_SCALE) selects the usual
+ *   1/sqrt(head_dim); an infinite scale gives PKV_EINVAL.  0 is valid (every
+ *   score is then equal: the output is the mean of the attended V rows).
  */
 #ifndef PAGED_KV_H
 #define PAGED_KV_H
@@ -63,6 +67,9 @@ extern "C" {
 /* storage formats */
 #define PKV_FP16 0
 #define PKV_BF16 1
+
+/* `scale` argument that selects 1/sqrt(head_dim) */
+#define PKV_DEFAULT_SCALE (__builtin_nanf(""))
 
 /* Human-readable text of a status code (static storage). */
 const char *pkv_status_string(int status);
@@ -149,11 +156,11 @@ int paged_kv_copy_blocks(void *const *k_pools, void *const *v_pools, int num_lay
  *
  *   out            [num_seqs][num_q_heads][head_dim], dtype (single-pass mode)
  *   q              [num_seqs][num_q_heads][head_dim], dtype
- *   scale          softmax scale, usually 1/sqrt(head_dim)
+ *   scale          softmax scale (NaN: 1/sqrt(head_dim))
  *   partition_size 0: single pass, each (sequence, KV head) is handled whole and
  *                  `out` is written; part_o/part_lse/max_partitions are ignored.
- *                  > 0: split-context mode; must be a multiple of block_size and
- *                  of 32.  Partition p covers tokens [p*P, min(n, (p+1)*P)) and
+ *                  > 0: split-context mode; must be a multiple of block_size
+ *                  (else PKV_EINVAL).  Partition p covers tokens [p*P, min(n, (p+1)*P)) and
  *                  writes part_o[s][h][p][:] (fp32, that partition's normalised
  *                  attention output) and part_lse[s][h][p] (fp32, natural-log
  *                  log-sum-exp of the partition's scaled scores).  Partitions
@@ -197,6 +204,45 @@ int paged_attention_append_decode(void *out, const void *q, void *k_pool, void *
                                   int block_size, int max_blocks_per_seq, int64_t num_blocks,
                                   float scale, int partition_size, int max_partitions,
                                   float *part_o, float *part_lse, int dtype, void *stream);
+
+/*
+ * paged_attention_split_decode -- split-context decode whose partitions are
+ * merged in the same launch.
+ *
+ * Same result as paged_attention_decode (or, with k_new / v_new, as
+ * paged_attention_append_decode) in split-context mode followed by
+ * paged_attention_reduce, with `out` written by this one launch: partition p of
+ * (sequence s, KV head g) covers tokens [p*P, min(n, (p+1)*P)), each of the
+ * item's work-groups writes its partitions' fp32 partials to the workspace and
+ * counts itself in counters[s][g]; the last one to arrive merges the item's
+ * partials by the log-sum-exp rule of paged_attention_reduce (the same
+ * operations, so the same bits) and puts the counter back to 0.  A context of at
+ * most one partition (n <= P) is written to `out` directly, without partials.
+ * The pages describe no partitioning; the merge is the exact identity of
+ * paged_attention_reduce.
+ *
+ *   out            [num_seqs][num_q_heads][head_dim], dtype, required
+ *   k_new, v_new   optional (both or neither): append the step's new rows as
+ *                  paged_attention_append_decode does; slot_out only with them
+ *   partition_size > 0, a multiple of block_size
+ *   max_partitions, part_o, part_lse   the workspace, as for
+ *                  paged_attention_decode, at most 2^31 - 1 bytes of part_o
+ *                  (else PKV_EWORKSPACE); its contents afterwards are
+ *                  unspecified
+ *   counters       device int32 [num_seqs][num_kv_heads], ALL ZERO when the call
+ *                  starts; every call that completes leaves them zero, so one
+ *                  zero-filled array serves any number of consecutive calls
+ *                  (and graph replays).  Calls that run at the same time must
+ *                  use different counters and workspaces.
+ */
+int paged_attention_split_decode(void *out, const void *q, void *k_pool, void *v_pool,
+                                 const void *k_new, const void *v_new, int64_t *slot_out,
+                                 const int32_t *block_tables, const int32_t *context_lens,
+                                 int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                 int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                                 float scale, int partition_size, int max_partitions,
+                                 float *part_o, float *part_lse, int32_t *counters, int dtype,
+                                 void *stream);
 
 /*
  * paged_attention_prefix_decode -- decode attention for batches whose sequences

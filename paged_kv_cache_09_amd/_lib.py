@@ -59,6 +59,9 @@ def load():
     L.paged_attention_append_decode.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32,
                                                 i32, i32, i64, f32, i32, i32, P, P, i32, P]
     L.paged_attention_append_decode.restype = i32
+    L.paged_attention_split_decode.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32,
+                                               i32, i32, i64, f32, i32, i32, P, P, P, i32, P]
+    L.paged_attention_split_decode.restype = i32
     L.paged_attention_prefix_decode.argtypes = [P, P, P, P, P, P, P, P, P, P, P, i32, i32, i32,
                                                 i32, i32, i32, i32, i64, f32, i32, i32, P, P,
                                                 i32, P]
@@ -175,6 +178,12 @@ def _ints(*specs):
             want = T[4] if kind == "i32" else T[5]
             if t.dtype is not want:
                 raise TypeError(f"{name} must be {want}, got {t.dtype}")
+
+
+def _scale(scale) -> float:
+    """The `scale` argument: None passes NaN, which the library reads as
+    1/sqrt(head_dim)."""
+    return math.nan if scale is None else float(scale)
 
 
 def _check(rc: int, what: str):
@@ -326,11 +335,10 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens,
     mp = _workspace(part_o, part_lse, S, Hq, D)
     dev = _dev(out, q, k_pool, v_pool, block_tables, context_lens, part_o, part_lse)
     _ints((block_tables, "i32", "block_tables"), (context_lens, "i32", "context_lens"))
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
+    scale = _scale(scale)
     rc = load().paged_attention_decode(_p(out), _p(q), _p(k_pool), _p(v_pool), _p(block_tables),
                                        _p(context_lens), S, Hq, Hkv, D, B, W,
-                                       NB, float(scale), int(partition_size), mp, _p(part_o),
+                                       NB, scale, int(partition_size), mp, _p(part_o),
                                        _p(part_lse), _dtype_code(q), _stream(dev))
     _check(rc, "paged_attention_decode")
 
@@ -350,14 +358,39 @@ def paged_attention_append_decode(out, q, k_pool, v_pool, k_new, v_new, block_ta
                part_o, part_lse)
     _ints((block_tables, "i32", "block_tables"), (context_lens, "i32", "context_lens"),
           (slot_out, "i64", "slot_out"))
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
+    scale = _scale(scale)
     rc = load().paged_attention_append_decode(
         _p(out), _p(q), _p(k_pool), _p(v_pool), _p(k_new), _p(v_new), _p(slot_out),
         _p(block_tables), _p(context_lens), S, Hq, Hkv, D, B, W, NB,
-        float(scale), int(partition_size), mp, _p(part_o), _p(part_lse), _dtype_code(q),
+        scale, int(partition_size), mp, _p(part_o), _p(part_lse), _dtype_code(q),
         _stream(dev))
     _check(rc, "paged_attention_append_decode")
+
+
+def paged_attention_split_decode(out, q, k_pool, v_pool, block_tables, context_lens,
+                                 partition_size: int, part_o, part_lse, counters, k_new=None,
+                                 v_new=None, slot_out=None, scale: Optional[float] = None):
+    """Split-context decode whose partitions are merged into `out` by the same
+    launch (the last work-group of each (sequence, KV head) merges); appends the
+    new rows first when k_new / v_new are given.  counters: int32 [S][Hkv], zero
+    on entry and left zero."""
+    NB, Hkv, B, D, S, Hq, W = _queries(out, q, k_pool, v_pool, block_tables, context_lens)
+    _expect(k_new, (S, Hkv, D), "k_new")
+    _expect(v_new, (S, Hkv, D), "v_new")
+    _same_dtype(k_pool, (k_new, "k_new"), (v_new, "v_new"))
+    _expect(slot_out, (S,), "slot_out")
+    _expect(counters, (S, Hkv), "counters")
+    mp = _workspace(part_o, part_lse, S, Hq, D)
+    dev = _dev(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens, slot_out,
+               part_o, part_lse, counters)
+    _ints((block_tables, "i32", "block_tables"), (context_lens, "i32", "context_lens"),
+          (slot_out, "i64", "slot_out"), (counters, "i32", "counters"))
+    rc = load().paged_attention_split_decode(
+        _p(out), _p(q), _p(k_pool), _p(v_pool), _p(k_new), _p(v_new), _p(slot_out),
+        _p(block_tables), _p(context_lens), S, Hq, Hkv, D, B, W, NB, _scale(scale),
+        int(partition_size), mp, _p(part_o), _p(part_lse), _p(counters), _dtype_code(q),
+        _stream(dev))
+    _check(rc, "paged_attention_split_decode")
 
 
 def paged_attention_prefix_decode(out, q, k_pool, v_pool, block_tables, context_lens, group_cu,
@@ -381,12 +414,11 @@ def paged_attention_prefix_decode(out, q, k_pool, v_pool, block_tables, context_
     _ints((block_tables, "i32", "block_tables"), (context_lens, "i32", "context_lens"),
           (group_cu, "i32", "group_cu"), (prefix_lens, "i32", "prefix_lens"),
           (slot_out, "i64", "slot_out"))
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
+    scale = _scale(scale)
     rc = load().paged_attention_prefix_decode(
         _p(out), _p(q), _p(k_pool), _p(v_pool), _p(k_new), _p(v_new), _p(slot_out),
         _p(block_tables), _p(context_lens), _p(group_cu), _p(prefix_lens),
-        G, S, Hq, Hkv, D, B, W, NB, float(scale), int(prefix_partition), mp, _p(part_o),
+        G, S, Hq, Hkv, D, B, W, NB, scale, int(prefix_partition), mp, _p(part_o),
         _p(part_lse), _dtype_code(q), _stream(dev))
     _check(rc, "paged_attention_prefix_decode")
 
@@ -407,11 +439,10 @@ def paged_attention_decode_slotted(out, q, k_pool, v_pool, segments, num_segment
     _expect(num_segments, (S,), "num_segments")
     dev = _dev(out, q, k_pool, v_pool, segments, num_segments)
     _ints((segments, "i32", "segments"), (num_segments, "i32", "num_segments"))
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
+    scale = _scale(scale)
     rc = load().paged_attention_decode_slotted(
         _p(out), _p(q), _p(k_pool), _p(v_pool), _p(segments), _p(num_segments), S, Hq, Hkv, D,
-        B, ss[1], NB, float(scale), _dtype_code(q), _stream(dev))
+        B, ss[1], NB, scale, _dtype_code(q), _stream(dev))
     _check(rc, "paged_attention_decode_slotted")
 
 

@@ -241,6 +241,17 @@ int check_pool_shape(int num_kv_heads, int head_dim, int block_size, int max_blo
 
 int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ELAUNCH; }
 
+// The softmax scale of a call: a NaN selects 1/sqrt(head_dim); an infinite scale
+// is an error (returns false).
+bool resolve_scale(float &scale, int head_dim)
+{
+    if (scale != scale) {
+        scale = 1.0f / __builtin_sqrtf((float)head_dim);
+        return true;
+    }
+    return !__builtin_isinf(scale);
+}
+
 }  // namespace
 
 extern "C" {
@@ -387,13 +398,26 @@ struct PrefixGroups {
     int num_groups = 0;
 };
 
+// Work-groups per (sequence, KV head) in split mode: enough for about
+// kTargetGroups work-groups in total, never more than the partitions a full table
+// row could hold.  Each work-group strides over its item's partitions, so the
+// result does not depend on this choice -- only the parallelism does (sizing the
+// grid by the table width would launch mostly empty work-groups when contexts
+// are much shorter than the row).
+int split_parts(int64_t items, int need)
+{
+    constexpr int64_t kTargetGroups = 2048;
+    const int64_t want = items > 0 ? (kTargetGroups + items - 1) / items : 1;
+    return (int)(want < need ? want : need);
+}
+
 int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
                 const void *k_new, const void *v_new, int64_t *slot_out,
                 const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
                 int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                 int max_blocks_per_seq, int64_t num_blocks, float scale, int partition_size,
                 int max_partitions, float *part_o, float *part_lse, int dtype, void *stream,
-                const PrefixGroups &pg = PrefixGroups())
+                const PrefixGroups &pg = PrefixGroups(), int32_t *counters = nullptr)
 {
     const bool prefix = pg.group_cu != nullptr;
     if (!q || !k_pool || !v_pool || !block_tables || !context_lens)
@@ -409,11 +433,14 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
     const int group = num_q_heads / num_kv_heads;
     if (group > 16)
         return PKV_ENOTSUP;
-    if (!(scale == scale) || __builtin_isinf(scale))
+    if (!resolve_scale(scale, head_dim))
         return PKV_EINVAL;
     if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
         return PKV_EINVAL;
     if (k_new && (!aligned16(k_new) || !aligned16(v_new) || ((uintptr_t)slot_out & 7u)))
+        return PKV_EINVAL;
+    if (counters && (prefix || partition_size <= 0 || !out || ((uintptr_t)out & 7u) ||
+                     ((uintptr_t)counters & 3u)))
         return PKV_EINVAL;
     int parts = 1;
     int prefix_part = 0, prefix_parts = 0;
@@ -442,23 +469,18 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
         if (!out || ((uintptr_t)out & 7u))
             return PKV_EINVAL;
     } else if (partition_size > 0) {
-        if (partition_size % block_size != 0 || partition_size % 32 != 0)
+        if (partition_size % block_size != 0)
             return PKV_EINVAL;
         const int need = pkv_max_partitions(max_blocks_per_seq, block_size, partition_size);
         if (!part_o || !part_lse || max_partitions < need || need <= 0)
             return PKV_EWORKSPACE;
         if (!aligned16(part_o) || ((uintptr_t)part_lse & 3u))
             return PKV_EINVAL;
-        // Work-groups per (sequence, KV head): enough for about kTargetGroups
-        // work-groups in total, never more than the partitions a full table row
-        // could hold.  Each work-group strides over its item's partitions, so the
-        // result does not depend on this choice -- only the parallelism does
-        // (sizing the grid by the table width would launch mostly empty
-        // work-groups when contexts are much shorter than the row).
-        constexpr int64_t kTargetGroups = 2048;
-        const int64_t base_items = (int64_t)num_seqs * num_kv_heads;
-        int64_t want = base_items > 0 ? (kTargetGroups + base_items - 1) / base_items : 1;
-        parts = (int)(want < need ? want : need);
+        parts = split_parts((int64_t)num_seqs * num_kv_heads, need);
+        // the merged mode addresses the workspace with 31-bit byte offsets
+        if (counters && (int64_t)num_seqs * num_q_heads * max_partitions * head_dim * 4 >
+                            (int64_t)INT32_MAX)
+            return PKV_EWORKSPACE;
     } else {
         if (!out || ((uintptr_t)out & 1u))
             return PKV_EINVAL;
@@ -500,6 +522,7 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
     a.v_new = v_new;
     a.slot_out = slot_out;
     a.block_size = block_size;
+    a.counters = counters;
     if (prefix && partition_size == 0) {
         // one pass: each work-group streams its tile's prefix, then each member's
         // own positions, and writes `out`
@@ -573,6 +596,25 @@ int paged_attention_append_decode(void *out, const void *q, void *k_pool, void *
                        part_o, part_lse, dtype, stream);
 }
 
+int paged_attention_split_decode(void *out, const void *q, void *k_pool, void *v_pool,
+                                 const void *k_new, const void *v_new, int64_t *slot_out,
+                                 const int32_t *block_tables, const int32_t *context_lens,
+                                 int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                 int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                                 float scale, int partition_size, int max_partitions,
+                                 float *part_o, float *part_lse, int32_t *counters, int dtype,
+                                 void *stream)
+{
+    if (!counters || !out || partition_size <= 0)
+        return PKV_EINVAL;
+    if ((k_new == nullptr) != (v_new == nullptr))
+        return PKV_EINVAL;
+    return decode_impl(out, q, k_pool, v_pool, k_new, v_new, k_new ? slot_out : nullptr,
+                       block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                       block_size, max_blocks_per_seq, num_blocks, scale, partition_size,
+                       max_partitions, part_o, part_lse, dtype, stream, PrefixGroups(), counters);
+}
+
 int paged_attention_prefix_decode(void *out, const void *q, void *k_pool, void *v_pool,
                                   const void *k_new, const void *v_new, int64_t *slot_out,
                                   const int32_t *block_tables, const int32_t *context_lens,
@@ -615,7 +657,7 @@ int paged_attention_decode_slotted(void *out, const void *q, const void *k_pool,
         return PKV_EINVAL;
     if (num_q_heads / num_kv_heads > 16)
         return PKV_ENOTSUP;
-    if (!(scale == scale) || __builtin_isinf(scale))
+    if (!resolve_scale(scale, head_dim))
         return PKV_EINVAL;
     if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || ((uintptr_t)out & 7u) ||
         ((uintptr_t)segments & 3u) || ((uintptr_t)num_segments & 3u))

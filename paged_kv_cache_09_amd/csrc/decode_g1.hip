@@ -237,18 +237,22 @@ __device__ __forceinline__ void merge_pair(RowState<DT> &st)
 }
 
 // SPLIT: split-context mode (partition loop); otherwise one pass over the
-// whole context, with the loop folded away at compile time.
+// whole context, with the loop folded away at compile time.  MERGE (with SPLIT):
+// the last work-group of an item to finish merges the item's partials into `out`,
+// and a context of one partition is written to `out` directly.
 // The register budget is capped so that 4 waves fit on each SIMD (the
 // split variant would otherwise be allocated past that occupancy).
 #ifndef PKV_G1_OCCUPANCY
 #define PKV_G1_OCCUPANCY 4  // waves per SIMD the register budget is capped for
 #endif
-template <int DT, int BS, int WAVES, bool SPLIT>
+template <int DT, int BS, int WAVES, bool SPLIT, bool MERGE = false>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(PKV_G1_OCCUPANCY)))
 void decode_g1_kernel(DecodeArgs a)
 {
+    static_assert(SPLIT || !MERGE, "the merged mode is a split mode");
     __shared__ float s_acc[WAVES][kHeadDim];
     __shared__ float s_m[WAVES], s_l[WAVES];
+    __shared__ int32_t s_last;
 
     // Work items are ordered sequence-major: the KV heads of one sequence are
     // neighbours in dispatch order, so the concurrently running work-groups read
@@ -296,7 +300,9 @@ void decode_g1_kernel(DecodeArgs a)
     // short sequences do not launch empty work-groups).  Single pass: px0 = 0,
     // one iteration over the whole context (which also writes zeros when n = 0).
     const int np = SPLIT ? (n + P - 1) / P : 1;
-    for (int px = px0; px < np; px += parts) {
+    const bool direct = MERGE && np <= 1;
+    const int np_loop = direct ? (px0 == 0 ? 1 : 0) : np;
+    for (int px = px0; px < np_loop; px += parts) {
         if (px != px0)
             __syncthreads();  // the previous partition's merge is done with LDS
         const int t0 = P > 0 ? px * P : 0;
@@ -405,7 +411,7 @@ void decode_g1_kernel(DecodeArgs a)
         if (WAVES == 1) {
             if (r == 0) {
                 const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
-                if (P == 0) {
+                if (P == 0 || direct) {
                     u32x4 o;
                     o.x = (uint32_t)to_bits<DT>(st.acc[0] * inv) |
                           ((uint32_t)to_bits<DT>(st.acc[1] * inv) << 16);
@@ -453,14 +459,44 @@ void decode_g1_kernel(DecodeArgs a)
                 L += s_l[i] * wgt;
                 O += s_acc[i][d] * wgt;
             }
-            if (P == 0) {
+            if (P == 0 || direct) {
                 const float o = L > 0.f ? O / L : 0.f;
                 ((uint16_t *)a.out)[row * kHeadDim + d] = to_bits<DT>(o);
             } else {
-                a.part_o[(row * a.max_partitions + px) * kHeadDim + d] = O / L;
-                if (d == 0)
-                    a.part_lse[row * a.max_partitions + px] = (ref + flog2(L)) * kLn2;
+                float *po = a.part_o + (row * a.max_partitions + px) * kHeadDim + d;
+                float *pl = a.part_lse + row * a.max_partitions + px;
+                const float lse = (ref + flog2(L)) * kLn2;
+                if constexpr (MERGE) {
+                    // read by another work-group of the item (see arrive_last)
+                    const Workspace ws = workspace_rsrc(a, (int64_t)a.num_seqs * a.num_q_heads);
+                    st_ws1(ws.o, (int)(po - a.part_o) * 4, O / L);
+                    if (d == 0)
+                        st_ws1(ws.lse, (int)(pl - a.part_lse) * 4, lse);
+                } else {
+                    *po = O / L;
+                    if (d == 0)
+                        *pl = lse;
+                }
             }
+        }
+    }
+
+    if constexpr (MERGE) {
+        // the work-groups that wrote partials arrive; the last one merges them
+        if (direct || px0 >= np)
+            return;
+        if (!arrive_last(a.counters + rest, min(np, parts), &s_last))
+            return;
+        if (tid < kHeadDim / 4) {
+            const int64_t row = (int64_t)s * a.num_q_heads + h;
+            const int d0 = tid * 4;
+            const Workspace ws = workspace_rsrc(a, (int64_t)a.num_seqs * a.num_q_heads);
+            const f32x4 o = merge_partials4(ws, (int)(row * a.max_partitions) * 4,
+                                            (int)(row * a.max_partitions * kHeadDim + d0) * 4, np);
+            u32x2 packed;
+            packed.x = (uint32_t)to_bits<DT>(o[0]) | ((uint32_t)to_bits<DT>(o[1]) << 16);
+            packed.y = (uint32_t)to_bits<DT>(o[2]) | ((uint32_t)to_bits<DT>(o[3]) << 16);
+            *(u32x2 *)((uint16_t *)a.out + row * kHeadDim + d0) = packed;
         }
     }
 }
@@ -476,7 +512,10 @@ template <int DT, int BS>
 static hipError_t launch_g1_t(const DecodeArgs &a, hipStream_t stream)
 {
     constexpr int W = PKV_G1_WAVES;
-    if (a.partition_size > 0)
+    if (a.partition_size > 0 && a.counters)
+        hipLaunchKernelGGL((decode_g1_kernel<DT, BS, W, true, true>), dim3(a.n_items),
+                           dim3(W * 64), 0, stream, a);
+    else if (a.partition_size > 0)
         hipLaunchKernelGGL((decode_g1_kernel<DT, BS, W, true>), dim3(a.n_items), dim3(W * 64), 0,
                            stream, a);
     else

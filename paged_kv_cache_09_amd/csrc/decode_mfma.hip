@@ -270,18 +270,22 @@ constexpr int kModeSingle = 0;  // one pass over positions 0 .. n-1, writes `out
 constexpr int kModeSplit = 1;   // partitions of the context, writes part_o / part_lse
 constexpr int kModeSuffix = 2;  // shared-prefix mode: positions prefix_len .. n-1, then
                                 // merged with the prefix partials, writes `out`
+constexpr int kModeMerge = 3;   // split mode whose last work-group per item merges the
+                                // partials into `out` (a context of one partition is
+                                // written to `out` directly)
 
-// MODE kModeSplit runs a partition loop; the other modes one pass, with the loop
-// folded away at compile time.
+// MODE kModeSplit / kModeMerge run a partition loop; the other modes one pass,
+// with the loop folded away at compile time.
 // The register budget is capped so that 4 waves (single pass) or 3 waves (split
-// mode, which keeps more state live across its partition loop) fit on each SIMD
+// modes, which keep more state live across their partition loop) fit on each SIMD
 // without spilling.
 template <int DT, int BS, int WAVES, int MODE>
 __global__ __launch_bounds__(WAVES * 64)
-__attribute__((amdgpu_waves_per_eu(MODE == kModeSplit ? 3 : 4)))
+__attribute__((amdgpu_waves_per_eu(MODE == kModeSplit || MODE == kModeMerge ? 3 : 4)))
 void decode_mfma_kernel(DecodeArgs a)
 {
-    constexpr bool SPLIT = MODE == kModeSplit;
+    constexpr bool MERGE = MODE == kModeMerge;
+    constexpr bool SPLIT = MODE == kModeSplit || MERGE;
     // V staging during the token loop; the cross-wave merge afterwards
     __shared__ __attribute__((aligned(16))) union {
         uint16_t v[WAVES][kStageElems];
@@ -291,6 +295,7 @@ void decode_mfma_kernel(DecodeArgs a)
     // fused append: the new K and V rows, parked by the wave that owns position
     // n-1 until its last sub-tile (registers would be held across the whole loop)
     __shared__ u32x4 s_new[2][kHeadDim / 8];
+    __shared__ int32_t s_last;  // merged split mode: this work-group arrived last
 
     // sequence-major work items (see the MHA kernel): the KV heads of a sequence
     // are neighbours in dispatch order
@@ -367,8 +372,12 @@ void decode_mfma_kernel(DecodeArgs a)
     // Partitions px0, px0 + parts_per_item, ... of the item belong to this
     // work-group (the grid is sized from the batch, not from the table width).
     // Single pass: one iteration over the whole context (zeros when n = 0).
+    // Merged split mode: a context of at most one partition is handled like a
+    // single pass by the item's first work-group, which writes `out` itself.
     const int np = SPLIT ? (n + P - 1) / P : 1;
-    for (int px = px0; px < np; px += parts) {
+    const bool direct = MERGE && np <= 1;
+    const int np_loop = direct ? (px0 == 0 ? 1 : 0) : np;
+    for (int px = px0; px < np_loop; px += parts) {
         if (px != px0)
             __syncthreads();  // the previous partition's merge is done with LDS
         const int t0 = P > 0 ? px * P : start_sub;
@@ -522,7 +531,7 @@ void decode_mfma_kernel(DecodeArgs a)
                 O += *(const f32x4 *)&sm.o[i][qi][d0] * wgt;
             }
             const int64_t row = row0 + qi;
-            if (MODE == kModeSuffix || P == 0) {
+            if (MODE == kModeSuffix || P == 0 || direct) {
                 f32x4 o = {0.f, 0.f, 0.f, 0.f};
                 if (MODE == kModeSuffix) {
                     // merge with the prefix partitions (normalised o, natural-log lse)
@@ -561,10 +570,40 @@ void decode_mfma_kernel(DecodeArgs a)
                 packed.y = (uint32_t)to_bits<DT>(o[2]) | ((uint32_t)to_bits<DT>(o[3]) << 16);
                 *(u32x2 *)((uint16_t *)a.out + row * kHeadDim + d0) = packed;
             } else {
-                *(f32x4 *)(a.part_o + (row * a.max_partitions + px) * kHeadDim + d0) = O / L;
-                if (d0 == 0)
-                    a.part_lse[row * a.max_partitions + px] = (ref + flog2(L)) * kLn2;
+                float *po = a.part_o + (row * a.max_partitions + px) * kHeadDim + d0;
+                const f32x4 ov = O / L;
+                const float lse = (ref + flog2(L)) * kLn2;
+                if constexpr (MERGE) {
+                    // read by another work-group of the item (see arrive_last)
+                    const Workspace ws = workspace_rsrc(a, (int64_t)a.num_seqs * a.num_q_heads);
+                    st_ws4(ws.o, (int)((row * a.max_partitions + px) * kHeadDim + d0) * 4, ov);
+                    if (d0 == 0)
+                        st_ws1(ws.lse, (int)(row * a.max_partitions + px) * 4, lse);
+                } else {
+                    *(f32x4 *)po = ov;
+                    if (d0 == 0)
+                        a.part_lse[row * a.max_partitions + px] = lse;
+                }
             }
+        }
+    }
+
+    if constexpr (MERGE) {
+        // the work-groups that wrote partials arrive; the last one merges them
+        if (direct || px0 >= np)
+            return;
+        if (!arrive_last(a.counters + rest, min(np, parts), &s_last))
+            return;
+        const Workspace ws = workspace_rsrc(a, (int64_t)a.num_seqs * a.num_q_heads);
+        for (int e = tid; e < G * 32; e += WAVES * 64) {
+            const int qi = e >> 5, d0 = (e & 31) * 4;
+            const int64_t row = row0 + qi;
+            const f32x4 o = merge_partials4(ws, (int)(row * a.max_partitions) * 4,
+                                            (int)(row * a.max_partitions * kHeadDim + d0) * 4, np);
+            u32x2 packed;
+            packed.x = (uint32_t)to_bits<DT>(o[0]) | ((uint32_t)to_bits<DT>(o[1]) << 16);
+            packed.y = (uint32_t)to_bits<DT>(o[2]) | ((uint32_t)to_bits<DT>(o[3]) << 16);
+            *(u32x2 *)((uint16_t *)a.out + row * kHeadDim + d0) = packed;
         }
     }
 }
@@ -1667,6 +1706,9 @@ static hipError_t launch_mfma_t(const DecodeArgs &a, hipStream_t stream)
     if (a.group_cu)
         hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, WS, kModeSuffix>), dim3(a.n_items),
                            dim3(WS * 64), 0, stream, a);
+    else if (a.partition_size > 0 && a.counters)
+        hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, W, kModeMerge>), dim3(a.n_items),
+                           dim3(W * 64), 0, stream, a);
     else if (a.partition_size > 0)
         hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, W, kModeSplit>), dim3(a.n_items),
                            dim3(W * 64), 0, stream, a);

@@ -228,7 +228,142 @@ struct DecodeArgs {
     const int32_t *segments;
     const int32_t *num_segments;
     int max_segments;
+    // merged split mode (null otherwise): one arrival counter per (sequence, KV
+    // head); the last work-group of an item to finish merges its partitions into
+    // `out` and puts the counter back to 0
+    int32_t *counters;
 };
+
+// ---- merged split mode --------------------------------------------------------
+// The work-groups of one item exchange their partials through the workspace.
+// The partials are written and read with the agent-coherence cache policy (sc1:
+// the accesses that relaxed atomics at agent scope compile to), which the gfx950
+// memory hierarchy keeps coherent across the XCDs' L2 caches by itself.
+// Release / acquire fences at agent scope would instead write back and
+// invalidate the whole L2 of the XCD in every work-group, which was measured to
+// serialise the work-groups of an XCD (a long-context launch went from 84 to
+// 111 us).  The workspace is addressed through one buffer resource, so its byte
+// offsets must fit in 31 bits (the host checks it).
+constexpr int kAgentCoherent = 16;  // cache policy sc1
+
+struct Workspace {
+    __amdgpu_buffer_rsrc_t o, lse;
+};
+
+__device__ __forceinline__ Workspace workspace_rsrc(const DecodeArgs &a, int64_t rows)
+{
+    Workspace w;
+    w.o = make_rsrc(a.part_o, (int)(rows * a.max_partitions * kHeadDim * 4));
+    w.lse = make_rsrc(a.part_lse, (int)(rows * a.max_partitions * 4));
+    return w;
+}
+
+__device__ __forceinline__ void st_ws4(__amdgpu_buffer_rsrc_t r, int off, f32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0,
+                                           kAgentCoherent);
+}
+__device__ __forceinline__ void st_ws1(__amdgpu_buffer_rsrc_t r, int off, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, kAgentCoherent);
+}
+__device__ __forceinline__ f32x4 ld_ws4(__amdgpu_buffer_rsrc_t r, int off)
+{
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0,
+                                                                           kAgentCoherent));
+}
+__device__ __forceinline__ float ld_ws1(__amdgpu_buffer_rsrc_t r, int off)
+{
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kAgentCoherent));
+}
+
+// Arrival of a work-group that has stored its partitions' partials (st_ws*), in
+// a launch where `expected` work-groups do so for the item counted by *ctr.
+// Returns true, in every thread, in the last one to arrive, which may then read
+// every partial of the item (ld_ws*).  Each wave first waits until its stores
+// are complete (the work-group barrier itself waits only for LDS); then one
+// relaxed increment counts the work-group, and the last arrival puts the counter
+// back to 0, so consecutive launches (and graph replays) need no clearing.
+__device__ __forceinline__ bool arrive_last(int32_t *ctr, int expected, int32_t *s_flag)
+{
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = old == expected - 1;
+        if (last)
+            __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = last;
+    }
+    __syncthreads();
+    return *s_flag != 0;
+}
+
+// Log-sum-exp merge of np >= 1 partials (natural-log lse, normalised fp32 rows) of
+// one query row, for 4 consecutive dims: `lse_off` is the byte offset of the
+// row's lse[0] in the workspace, `o_off` that of dims d0..d0+3 of its partition
+// 0.  The same operations in the same order as the standalone merge kernel (max
+// first, then the weighted sum in partition order), so both give the same bits.
+// Partials are requested kMergeChunk partitions at a time, so a merge of up to
+// kMergeChunk partitions costs one memory round trip.
+constexpr int kMergeChunk = 8;
+
+__device__ __forceinline__ f32x4 merge_partials4(const Workspace &ws, int lse_off, int o_off,
+                                                 int np)
+{
+    float l0[kMergeChunk];
+    f32x4 v0[kMergeChunk];
+#pragma unroll
+    for (int i = 0; i < kMergeChunk; ++i) {
+        const int p = min(i, np - 1);  // never past the row's partitions
+        l0[i] = ld_ws1(ws.lse, lse_off + 4 * p);
+        v0[i] = ld_ws4(ws.o, o_off + p * kHeadDim * 4);
+    }
+    float M = kNegInf;
+#pragma unroll
+    for (int i = 0; i < kMergeChunk; ++i)
+        M = i < np ? fmaxf(M, l0[i]) : M;
+    for (int p0 = kMergeChunk; p0 < np; p0 += kMergeChunk) {
+        float l[kMergeChunk];
+#pragma unroll
+        for (int i = 0; i < kMergeChunk; ++i)
+            l[i] = ld_ws1(ws.lse, lse_off + 4 * min(p0 + i, np - 1));
+#pragma unroll
+        for (int i = 0; i < kMergeChunk; ++i)
+            M = p0 + i < np ? fmaxf(M, l[i]) : M;
+    }
+    const float ref = safe_ref(M);
+    float W = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    auto add = [&](float lp, const f32x4 &v) {
+        const float wgt = fexp2((lp - ref) * kLog2e);
+        W += wgt;
+        o[0] += wgt * v[0];
+        o[1] += wgt * v[1];
+        o[2] += wgt * v[2];
+        o[3] += wgt * v[3];
+    };
+#pragma unroll
+    for (int i = 0; i < kMergeChunk; ++i)
+        if (i < np)
+            add(l0[i], v0[i]);
+    for (int p0 = kMergeChunk; p0 < np; p0 += kMergeChunk) {
+        float l[kMergeChunk];
+        f32x4 v[kMergeChunk];
+#pragma unroll
+        for (int i = 0; i < kMergeChunk; ++i) {
+            const int p = min(p0 + i, np - 1);
+            l[i] = ld_ws1(ws.lse, lse_off + 4 * p);
+            v[i] = ld_ws4(ws.o, o_off + p * kHeadDim * 4);
+        }
+#pragma unroll
+        for (int i = 0; i < kMergeChunk; ++i)
+            if (p0 + i < np)
+                add(l[i], v[i]);
+    }
+    const float inv = W > 0.f ? 1.f / W : 0.f;
+    return o * inv;
+}
 
 // Group of sequence s in shared-prefix mode: the largest k with group_cu[k] <= s.
 // `s` is uniform, so the search runs on scalar loads.

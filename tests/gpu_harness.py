@@ -124,3 +124,26 @@ def tol_ok(got: np.ndarray, ref: np.ndarray, atol=1e-2, rtol=1e-2):
     err = np.abs(got - ref)
     bad = ~(err <= atol + rtol * np.abs(ref))
     return (not bad.any()), float(np.nanmax(err)) if err.size else 0.0, int(bad.sum())
+
+
+def merged_step(g: GpuStep, partition_size: int, append: bool = True, scale=None,
+                counters=None):
+    """paged_attention_split_decode on a GpuStep (built with append=False when
+    `append`): split-context decode merged in the same launch.  Returns the
+    output and the arrival counters (zero after a completed call)."""
+    c = g.c
+    scale = scale_for(c.head_dim) if scale is None else scale
+    out = torch.empty((c.num_seqs, c.num_q_heads, c.head_dim), dtype=TORCH_DT[c.dtype],
+                      device=g.device)
+    out.view(torch.int16).fill_(0x5555)
+    mp = pkv.max_partitions(c.max_blocks_per_seq, c.block_size, partition_size)
+    po = torch.full((c.num_seqs, c.num_q_heads, mp, c.head_dim), float("nan"),
+                    dtype=torch.float32, device=g.device)
+    pl = torch.full((c.num_seqs, c.num_q_heads, mp), float("nan"), dtype=torch.float32,
+                    device=g.device)
+    if counters is None:
+        counters = torch.zeros((c.num_seqs, c.num_kv_heads), dtype=torch.int32, device=g.device)
+    kw = dict(k_new=g.k_new, v_new=g.v_new, slot_out=g.slots) if append else {}
+    pkv.paged_attention_split_decode(out, g.q, g.k_pool, g.v_pool, g.tables, g.lens,
+                                     partition_size, po, pl, counters, scale=scale, **kw)
+    return out, counters

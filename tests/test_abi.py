@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
     assert {"paged_kv_append", "paged_kv_append_tokens", "paged_kv_copy_blocks",
             "paged_attention_decode", "paged_attention_append_decode",
             "paged_attention_prefix_decode", "paged_attention_decode_slotted",
-            "paged_attention_reduce",
+            "paged_attention_reduce", "paged_attention_split_decode",
             "pkv_status_string", "pkv_max_partitions"} <= set(declared)
     assert pkv.exported_symbols() == declared
 
@@ -83,12 +83,13 @@ def decode(lib, **kw):
     (dict(dt=3), ENOTSUP),
     (dict(S=-1), EINVAL),
     (dict(NB=0), EINVAL),
-    (dict(P=48, MP=4, po=A, pl=A), EINVAL),  # partition not a multiple of 32
+    (dict(P=24, MP=4, po=A, pl=A), EINVAL),  # partition not a multiple of the block (16)
     (dict(P=32, B=64, W=2, MP=4, po=A, pl=A), EINVAL),  # not a multiple of the block
     (dict(P=32, MP=1, po=A, pl=A), EWORKSPACE),
     (dict(P=32, MP=3, po=None, pl=A), EWORKSPACE),
     (dict(q=P((1 << 20) + 2)), EINVAL),      # misaligned
-    (dict(scale=float("nan")), EINVAL),
+    (dict(scale=float("inf")), EINVAL),
+    (dict(scale=float("-inf")), EINVAL),
     (dict(S=0), 0),                          # nothing to do
 ])
 def test_decode_argument_errors(lib, kw, code):
@@ -145,6 +146,28 @@ def test_copy_blocks_argument_errors(lib):
     many = (P * 129)(*([A] * 129))
     assert call(kp=many, vp=many, L=129) == ENOTSUP            # more layers than one launch takes
     assert call(n=0, src=None, dst=None) == 0                   # nothing to copy
+
+
+@host_only
+def test_split_decode_argument_errors(lib):
+    f = lib.paged_attention_split_decode
+
+    def call(out=A, kn=None, vn=None, ctr=A, S=2, Hq=12, Hkv=2, B=16, W=5, P_=32, MP=3, po=A,
+             pl=A, scale=0.088, dt=0):
+        return f(out, A, A, A, kn, vn, None, A, A, S, Hq, Hkv, 128, B, W, 64, scale, P_, MP,
+                 po, pl, ctr, dt, None)
+
+    assert call(ctr=None) == EINVAL              # the arrival counters are required
+    assert call(out=None) == EINVAL              # the merge writes `out`
+    assert call(P_=0) == EINVAL                  # a split mode: partitions required
+    assert call(P_=24) == EINVAL                 # not a multiple of the block
+    assert call(kn=A) == EINVAL                  # k_new without v_new
+    assert call(ctr=P((1 << 20) + 2)) == EINVAL  # misaligned counters
+    assert call(MP=2) == EWORKSPACE              # 80 positions need 3 partitions of 32
+    assert call(po=None) == EWORKSPACE
+    assert call(Hq=34) == ENOTSUP
+    assert call(scale=float("inf")) == EINVAL
+    assert call(S=0) == 0
 
 
 @host_only

@@ -17,8 +17,12 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU containers
     pytest.skip("no GPU", allow_module_level=True)
 
 
-@pytest.mark.parametrize("key,P", [("c1a", 0), ("c2", 512), ("c5", 0)])
-def test_graph_replays_match_eager(key, P):
+@pytest.mark.parametrize("key,P,merged", [("c1a", 0, False), ("c2", 512, False),
+                                           ("c5", 0, False), ("c2", 512, True),
+                                           ("c4", 2048, True), ("c3", 64, True)])
+def test_graph_replays_match_eager(key, P, merged):
+    """merged: paged_attention_split_decode, whose arrival counters must be back
+    at zero after every call for the next replay to merge correctly."""
     w = make_workload(get_config(key))
     c = w.cfg
     print(f"[gpu] graph {key} P={P}", flush=True)
@@ -34,12 +38,17 @@ def test_graph_replays_match_eager(key, P):
     if prefix:
         cu = torch.tensor([0, S], dtype=torch.int32, device=g.device)
         plen = torch.tensor([c.prefix_tokens], dtype=torch.int32, device=g.device)
+    ctr = torch.zeros((S, c.num_kv_heads), dtype=torch.int32, device=g.device)
 
     def step():
         if prefix:
             pkv.paged_attention_prefix_decode(out, g.q, g.k_pool, g.v_pool, g.tables, g.lens, cu,
                                               plen, po, pl, k_new=g.k_new, v_new=g.v_new,
                                               slot_out=g.slots, scale=scale)
+        elif merged:
+            pkv.paged_attention_split_decode(out, g.q, g.k_pool, g.v_pool, g.tables, g.lens, P,
+                                             po, pl, ctr, k_new=g.k_new, v_new=g.v_new,
+                                             slot_out=g.slots, scale=scale)
         elif P:
             pkv.paged_attention_append_decode(None, g.q, g.k_pool, g.v_pool, g.k_new, g.v_new,
                                               g.tables, g.lens, g.slots, scale=scale,
@@ -71,6 +80,7 @@ def test_graph_replays_match_eager(key, P):
             f"replay {rep} differs from the eager result"
         # pools hold NaN sentinels in unused slots: compare bit patterns
         assert torch.equal(g.k_pool.view(torch.int16), eager_k.view(torch.int16))
+        assert not bool(ctr.any()), "arrival counters not back at zero"
         scratch = (g.q.float() * 2).sum()  # eager work between replays
         torch.cuda.synchronize()
         del scratch

@@ -18,7 +18,8 @@ torch = pytest.importorskip("torch")
 
 from workloads import get_config, make_workload  # noqa: E402
 from oracle import oracle as O  # noqa: E402
-from gpu_harness import GpuStep, bits_of, fused_step, scale_for, tol_ok, widen_out  # noqa: E402
+from gpu_harness import (GpuStep, bits_of, fused_step, merged_step, scale_for, tol_ok,  # noqa: E402
+                         widen_out)
 import paged_kv_cache_09_amd as pkv  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -133,6 +134,41 @@ def test_fused_append_decode(key, P):
 
 
 # ---------------------------------------------------------------------------
+MERGED = [("c1b", 32), ("c2", 256), ("c2", 512), ("c3", 64), ("c3", 256), ("c4", 128),
+          ("c4", 2048), ("c5", 128)]
+
+
+@pytest.mark.parametrize("key,P", MERGED)
+def test_split_decode_merged_in_launch(key, P):
+    """paged_attention_split_decode: the partitions merged by the last work-group
+    of each item give the oracle's output within tolerance, and the same bits as
+    the split decode followed by the standalone merge; with the fused append, the
+    pools and slots are bit-exact; the arrival counters end at zero, and a second
+    call on the same counters gives the same bits."""
+    w, r = oracle_for(key)
+    print(f"[gpu] merged split {key} P={P}", flush=True)
+    g = GpuStep(w, append=False)
+    out, ctr = merged_step(g, P)
+    torch.cuda.synchronize()
+    assert not bool(ctr.any()), "arrival counters not back at zero"
+    assert np.array_equal(g.slots.cpu().numpy(), r["slots"])
+    ref = referenced_blocks(w)
+    idx = torch.from_numpy(ref.astype(np.int64)).to(g.device)
+    assert np.array_equal(bits_of(g.k_pool[idx]), r["k_pool"][ref])
+    assert np.array_equal(bits_of(g.v_pool[idx]), r["v_pool"][ref])
+    ok, err, nbad = tol_ok(widen_out(out), r["out"])
+    assert ok, f"{key} P={P}: max err {err}, {nbad} bad"
+    # the same pools now hold the appended rows: the plain split + standalone
+    # merge and a second merged call (same counters) must give the same bits
+    out2, _, _ = g.decode(P)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    out3, _ = merged_step(g, P, append=False, counters=ctr)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out3.view(torch.int16))
+    assert not bool(ctr.any())
+
+
+# ---------------------------------------------------------------------------
 def _relabel(kbits, vbits, tables, seed):
     rng = np.random.default_rng(seed)
     pi = rng.permutation(kbits.shape[0])
@@ -180,11 +216,23 @@ EDGE = [
     (128, 32, 8, "bf16", (1, 127, 129, 300)),
     (256, 6, 3, "fp16", (3, 256, 511, 513)),
     (16, 4, 2, "bf16", (16, 32, 48, 64, 80)),
+    # odd group sizes: floor(16 / G) * G < 16 columns of the MFMA tile are used
+    (16, 12, 4, "fp16", (0, 1, 15, 16, 17, 47, 48, 49, 130)),
+    (128, 10, 2, "bf16", (1, 127, 128, 129, 300, 0)),
 ]
 
 
-@pytest.mark.parametrize("B,hq,hkv,dt,lens", EDGE)
-@pytest.mark.parametrize("P", [0, 256])
+def _edge_params():
+    """Each edge case single pass and at P = 256; block size 16 also at P = 16
+    and 48 (partitions that are not a multiple of 32)."""
+    out = []
+    for e in EDGE:
+        for P in [0, 256] + ([16, 48] if e[0] == 16 else []):
+            out.append(e + (P,))
+    return out
+
+
+@pytest.mark.parametrize("B,hq,hkv,dt,lens,P", _edge_params())
 def test_edge_cases(B, hq, hkv, dt, lens, P):
     print(f"[gpu] edge B={B} hq={hq} hkv={hkv} {dt} lens={lens} P={P}", flush=True)
     w = _small(block_size=B, num_q_heads=hq, num_kv_heads=hkv, dtype=dt, lengths=lens,
@@ -214,6 +262,14 @@ def test_edge_cases(B, hq, hkv, dt, lens, P):
     assert np.array_equal(bits_of(g2.v_pool), r["v_pool"])
     ok, err, nbad = tol_ok(widen_out(out2), r["out"])
     assert ok, f"fused: max err {err}, {nbad} bad"
+    if P:
+        # the partitions merged in the launch: same bits as the split + merge
+        g3 = GpuStep(w, append=False)
+        out3, ctr = merged_step(g3, P)
+        torch.cuda.synchronize()
+        assert not bool(ctr.any())
+        assert np.array_equal(bits_of(g3.k_pool), r["k_pool"])
+        assert torch.equal(out3.view(torch.int16), out2.view(torch.int16))
 
 
 @pytest.mark.parametrize("P", [0, 1024])
@@ -273,9 +329,9 @@ def test_argument_errors():
     w = _small(block_size=16, num_q_heads=12, num_kv_heads=2, lengths=(5, 40))
     g = GpuStep(w)
     out = torch.empty_like(g.q)
-    with pytest.raises(pkv.PagedKVError) as e:   # partition not a multiple of 32
+    with pytest.raises(pkv.PagedKVError) as e:   # partition not a multiple of the block
         pkv.paged_attention_decode(None, g.q, g.k_pool, g.v_pool, g.tables, g.lens,
-                                   partition_size=48, part_o=torch.empty(2, 12, 4, 128,
+                                   partition_size=24, part_o=torch.empty(2, 12, 4, 128,
                                                                          device=g.device),
                                    part_lse=torch.empty(2, 12, 4, device=g.device))
     assert e.value.status == -1
