@@ -245,6 +245,35 @@ int paged_attention_split_decode(void *out, const void *q, void *k_pool, void *v
                                  void *stream);
 
 /*
+ * paged_attention_split_decode_noalloc -- paged_attention_split_decode with no
+ * workspace argument and no allocation, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).
+ *
+ * Same arguments and result as paged_attention_split_decode without
+ * max_partitions, part_o, part_lse and counters: the partials and the arrival
+ * counters live in a fixed device array inside the library (16.4 MiB per GPU,
+ * held until the process ends), with max_partitions =
+ * ceil(max_blocks_per_seq * block_size / partition_size).  Limits: num_seqs *
+ * num_kv_heads <= 65536 and num_seqs * num_q_heads * max_partitions <= 32768
+ * (16 MiB of fp32 partial rows); larger calls return PKV_EWORKSPACE.  The call
+ * allocates nothing: the first call on a device resolves that device's copy of
+ * the array (hipGetSymbolAddress, with the device current) and clears its
+ * counters with a kernel on `stream`; later calls only launch the decode.
+ * `stream` must belong to the current device.  Every call on one GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (other streams, other
+ * threads) race and give undefined results.
+ */
+int paged_attention_split_decode_noalloc(void *out, const void *q, void *k_pool, void *v_pool,
+                                         const void *k_new, const void *v_new,
+                                         int64_t *slot_out, const int32_t *block_tables,
+                                         const int32_t *context_lens, int num_seqs,
+                                         int num_q_heads, int num_kv_heads, int head_dim,
+                                         int block_size, int max_blocks_per_seq,
+                                         int64_t num_blocks, float scale, int partition_size,
+                                         int dtype, void *stream);
+
+/*
  * paged_attention_prefix_decode -- decode attention for batches whose sequences
  * share a prefix, reading each shared block once per tile of sequences.
  *

@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     paged_attention_prefix_decode,
     paged_attention_reduce,
     paged_attention_split_decode,
+    paged_attention_split_decode_noalloc,
     paged_kv_append,
     paged_kv_append_tokens,
     paged_kv_copy_blocks,

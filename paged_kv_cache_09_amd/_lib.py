@@ -62,6 +62,9 @@ def load():
     L.paged_attention_split_decode.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32,
                                                i32, i32, i64, f32, i32, i32, P, P, P, i32, P]
     L.paged_attention_split_decode.restype = i32
+    L.paged_attention_split_decode_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32,
+                                                       i32, i32, i32, i64, f32, i32, i32, P]
+    L.paged_attention_split_decode_noalloc.restype = i32
     L.paged_attention_prefix_decode.argtypes = [P, P, P, P, P, P, P, P, P, P, P, i32, i32, i32,
                                                 i32, i32, i32, i32, i64, f32, i32, i32, P, P,
                                                 i32, P]
@@ -391,6 +394,26 @@ def paged_attention_split_decode(out, q, k_pool, v_pool, block_tables, context_l
         int(partition_size), mp, _p(part_o), _p(part_lse), _p(counters), _dtype_code(q),
         _stream(dev))
     _check(rc, "paged_attention_split_decode")
+
+
+def paged_attention_split_decode_noalloc(out, q, k_pool, v_pool, block_tables, context_lens,
+                                         partition_size: int, k_new=None, v_new=None,
+                                         slot_out=None, scale: Optional[float] = None):
+    """paged_attention_split_decode with its partials and arrival counters in the
+    library's own fixed device array: no workspace, no allocation."""
+    NB, Hkv, B, D, S, Hq, W = _queries(out, q, k_pool, v_pool, block_tables, context_lens)
+    _expect(k_new, (S, Hkv, D), "k_new")
+    _expect(v_new, (S, Hkv, D), "v_new")
+    _same_dtype(k_pool, (k_new, "k_new"), (v_new, "v_new"))
+    _expect(slot_out, (S,), "slot_out")
+    dev = _dev(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens, slot_out)
+    _ints((block_tables, "i32", "block_tables"), (context_lens, "i32", "context_lens"),
+          (slot_out, "i64", "slot_out"))
+    rc = load().paged_attention_split_decode_noalloc(
+        _p(out), _p(q), _p(k_pool), _p(v_pool), _p(k_new), _p(v_new), _p(slot_out),
+        _p(block_tables), _p(context_lens), S, Hq, Hkv, D, B, W, NB, _scale(scale),
+        int(partition_size), _dtype_code(q), _stream(dev))
+    _check(rc, "paged_attention_split_decode_noalloc")
 
 
 def paged_attention_prefix_decode(out, q, k_pool, v_pool, block_tables, context_lens, group_cu,

@@ -10,6 +10,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/paged_kv.h"
 #include "pkv_device.h"
 #include "pkv_launch.h"
@@ -417,7 +420,8 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
                 int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                 int max_blocks_per_seq, int64_t num_blocks, float scale, int partition_size,
                 int max_partitions, float *part_o, float *part_lse, int dtype, void *stream,
-                const PrefixGroups &pg = PrefixGroups(), int32_t *counters = nullptr)
+                const PrefixGroups &pg = PrefixGroups(), int32_t *counters = nullptr,
+                bool validate_only = false)
 {
     const bool prefix = pg.group_cu != nullptr;
     if (!q || !k_pool || !v_pool || !block_tables || !context_lens)
@@ -488,7 +492,7 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
     const int64_t items = (int64_t)num_seqs * num_kv_heads * parts;
     if (items > INT32_MAX)
         return PKV_EINVAL;
-    if (items == 0)
+    if (items == 0 || validate_only)
         return PKV_OK;
     hipStream_t st = (hipStream_t)stream;
     if (debug_enabled()) {
@@ -613,6 +617,114 @@ int paged_attention_split_decode(void *out, const void *q, void *k_pool, void *v
                        block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                        block_size, max_blocks_per_seq, num_blocks, scale, partition_size,
                        max_partitions, part_o, part_lse, dtype, stream, PrefixGroups(), counters);
+}
+
+}  // extern "C"
+
+// ---- the entry point that allocates nothing -------------------------------------
+// paged_attention_split_decode_noalloc keeps the partials and the arrival
+// counters of paged_attention_split_decode in this file-scope device array
+// instead of a caller workspace: the arrival counters first, then the partials'
+// lse values, then their rows (byte offsets 256-aligned).  Every GPU the library
+// runs on holds its own copy until the process ends.
+namespace {
+
+constexpr int64_t kNoAllocItems = (int64_t)1 << 16;     // (sequence, KV head) counters
+constexpr int64_t kNoAllocRows = (int64_t)1 << 15;      // (sequence, query head, partition) rows
+constexpr int64_t kNoAllocLseOff = kNoAllocItems * 4;  // 256 KiB
+constexpr int64_t kNoAllocRowOff = kNoAllocLseOff + kNoAllocRows * 4;
+constexpr int64_t kScratchBytes = kNoAllocRowOff + kNoAllocRows * pkv::kHeadDim * 4;  // 16.4 MiB
+static_assert(kNoAllocLseOff % 256 == 0 && kNoAllocRowOff % 256 == 0, "aligned regions");
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of `scratch` per device, resolved once per device (with that
+// device current) by hipGetSymbolAddress.  In host code the array's name is only
+// a host-side stand-in: the address used everywhere is the one resolved here.
+constexpr int kMaxDevices = 64;
+std::atomic<unsigned char *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+__global__ void clear_counters_kernel(int32_t *c, int n)
+{
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+        c[i] = 0;
+}
+
+// The current device's scratch, set up on its first use: the address is resolved
+// and the arrival counters are cleared by a kernel on `stream` (every completed
+// call leaves them zero afterwards).
+int scratch_of_current_device(hipStream_t stream, unsigned char **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return PKV_ELAUNCH;
+    if (dev < 0 || dev >= kMaxDevices)
+        return PKV_ENOTSUP;
+    unsigned char *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p) {
+        *out = p;
+        return PKV_OK;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void *addr = nullptr;
+        if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr)
+            return PKV_ELAUNCH;
+        p = (unsigned char *)addr;
+        hipLaunchKernelGGL(clear_counters_kernel, dim3(64), dim3(256), 0, stream, (int32_t *)p,
+                           (int)kNoAllocItems);
+        if (hipGetLastError() != hipSuccess)
+            return PKV_ELAUNCH;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attention_split_decode_noalloc(void *out, const void *q, void *k_pool, void *v_pool,
+                                         const void *k_new, const void *v_new,
+                                         int64_t *slot_out, const int32_t *block_tables,
+                                         const int32_t *context_lens, int num_seqs,
+                                         int num_q_heads, int num_kv_heads, int head_dim,
+                                         int block_size, int max_blocks_per_seq,
+                                         int64_t num_blocks, float scale, int partition_size,
+                                         int dtype, void *stream)
+{
+    if (!out || partition_size <= 0 || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0)
+        return PKV_EINVAL;
+    if ((k_new == nullptr) != (v_new == nullptr))
+        return PKV_EINVAL;
+    const int mp = pkv_max_partitions(max_blocks_per_seq, block_size, partition_size);
+    if (mp <= 0)
+        return PKV_EINVAL;
+    if ((int64_t)num_seqs * num_kv_heads > kNoAllocItems ||
+        (int64_t)num_seqs * num_q_heads * mp > kNoAllocRows)
+        return PKV_EWORKSPACE;
+    // every argument is checked before the device is touched (placeholder
+    // workspace addresses: validation does not dereference them)
+    float *const ph = (float *)(uintptr_t)256;
+    int rc = decode_impl(out, q, k_pool, v_pool, k_new, v_new, k_new ? slot_out : nullptr,
+                         block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                         head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                         partition_size, mp, ph, ph, dtype, stream, PrefixGroups(),
+                         (int32_t *)ph, true);
+    if (rc != PKV_OK || num_seqs == 0)
+        return rc;
+    unsigned char *base = nullptr;
+    rc = scratch_of_current_device((hipStream_t)stream, &base);
+    if (rc != PKV_OK)
+        return rc;
+    return decode_impl(out, q, k_pool, v_pool, k_new, v_new, k_new ? slot_out : nullptr,
+                       block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                       block_size, max_blocks_per_seq, num_blocks, scale, partition_size, mp,
+                       (float *)(base + kNoAllocRowOff), (float *)(base + kNoAllocLseOff), dtype,
+                       stream, PrefixGroups(), (int32_t *)base);
 }
 
 int paged_attention_prefix_decode(void *out, const void *q, void *k_pool, void *v_pool,

@@ -41,6 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
             "paged_attention_decode", "paged_attention_append_decode",
             "paged_attention_prefix_decode", "paged_attention_decode_slotted",
             "paged_attention_reduce", "paged_attention_split_decode",
+            "paged_attention_split_decode_noalloc",
             "pkv_status_string", "pkv_max_partitions"} <= set(declared)
     assert pkv.exported_symbols() == declared
 
@@ -167,6 +168,27 @@ def test_split_decode_argument_errors(lib):
     assert call(po=None) == EWORKSPACE
     assert call(Hq=34) == ENOTSUP
     assert call(scale=float("inf")) == EINVAL
+    assert call(S=0) == 0
+
+
+@host_only
+def test_split_decode_noalloc_argument_errors(lib):
+    f = lib.paged_attention_split_decode_noalloc
+
+    def call(out=A, kn=None, vn=None, S=2, Hq=12, Hkv=2, B=16, W=5, P_=32, scale=0.088, dt=0):
+        return f(out, A, A, A, kn, vn, None, A, A, S, Hq, Hkv, 128, B, W, 64, scale, P_, dt,
+                 None)
+
+    assert call(out=None) == EINVAL
+    assert call(P_=0) == EINVAL
+    assert call(P_=24) == EINVAL                 # not a multiple of the block
+    assert call(kn=A) == EINVAL                  # k_new without v_new
+    assert call(Hq=34) == ENOTSUP
+    assert call(B=24) == ENOTSUP
+    # beyond the fixed scratch: 65,536 (sequence, KV head) counters, 32,768
+    # (sequence, query head, partition) partial rows
+    assert call(S=32769, Hq=4, Hkv=4, W=1) == EWORKSPACE
+    assert call(S=128, Hq=32, Hkv=32, B=32, W=128, P_=256) == EWORKSPACE  # 65,536 rows
     assert call(S=0) == 0
 
 
