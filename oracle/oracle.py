@@ -83,6 +83,8 @@ def lib():
         L.oracle_attention_slotted.restype = C.c_int
         L.oracle_copy_blocks.argtypes = [P, P, P, P] + [i64] * 5
         L.oracle_copy_blocks.restype = C.c_int
+        L.oracle_copy_slots.argtypes = [P, P, P] + [i64] * 5
+        L.oracle_copy_slots.restype = C.c_int
         L.oracle_attention.argtypes = [P, P, P, P, P, P] + [i64] * 7 + [C.c_double, C.c_int,
                                                                           C.c_int]
         L.oracle_attention.restype = C.c_int
@@ -173,6 +175,18 @@ def copy_blocks(k_pool, v_pool, src, dst):
     rc = lib().oracle_copy_blocks(_p(k_pool), _p(v_pool), _p(src), _p(dst), src.shape[0], Hkv,
                                   D, B, NB)
     _check(rc, "copy_blocks")
+
+
+def copy_slots(k_pool, v_pool, copies):
+    """Copy-on-write split of shared slots: for each row (src block, src offset,
+    dst block, dst offset, length) of `copies` ([n][5] int32), the source rows go
+    to the destination rows of both pools ([NB][Hkv][B][D] uint16, in place)."""
+    assert k_pool.flags.c_contiguous and v_pool.flags.c_contiguous
+    NB, Hkv, B, D = k_pool.shape
+    copies = _c(np.asarray(copies, np.int32).reshape(-1, 5), np.int32)
+    rc = lib().oracle_copy_slots(_p(k_pool), _p(v_pool), _p(copies), copies.shape[0], Hkv, D,
+                                 B, NB)
+    _check(rc, "copy_slots")
 
 
 def attention(q, k_pool, v_pool, tables, lens, num_kv_heads, block_size, num_blocks, scale,

@@ -43,6 +43,13 @@
  *    and "核心设计原则").  A sequence's KV is the concatenation of its segments in
  *    order; logical token t lies in the segment whose running start s satisfies
  *    s <= t < s + length, at in-block offset slot_offset + (t - s).
+ *  - Slot copy (copy-on-write split of a shared slot): when a node that sits in
+ *    a slot of a shared block is appended to, it is split off into a block of
+ *    its own, so the shared slots stay read-only and the write cannot touch them
+ *    (mhpq.cn page, "核心设计原则", copy-on-write on append).  The node's `length`
+ *    rows move from (block, slot offset) to offset 0 of the dedicated block,
+ *    every head, in K and in V; the source rows are left as they are.  Written
+ *    here for any destination offset.
  *  - Partials and merge: attention over the token range of one partition, its
  *    log-sum-exp, and the exact log-sum-exp combination of partitions.  The
  *    pages do not describe partitions; the merge is the algebraic identity
@@ -255,6 +262,59 @@ int oracle_copy_blocks(uint16_t *k_pool, uint16_t *v_pool, const int32_t *src,
                     k_pool[to] = k_pool[from];
                     v_pool[to] = v_pool[from];
                 }
+    return OR_OK;
+}
+
+/* ---- slot copy (copy-on-write split of a shared slot) ---------------------- */
+/* Copy i = copies[5*i .. 5*i+4] = (src block, src offset, dst block, dst offset,
+ * length): rows src offset .. src offset+length-1 of the source block become rows
+ * dst offset .. dst offset+length-1 of the destination block, in every head of
+ * both pools, as they were before the call.  Blocks must lie in the pool and both
+ * row ranges inside their block.  A destination row that is also a source row of
+ * any copy, or a destination row of another copy, would make the result depend
+ * on the copy order: OR_EDUP. */
+static int rows_overlap(int64_t b0, int64_t o0, int64_t n0, int64_t b1, int64_t o1, int64_t n1)
+{
+    return b0 == b1 && o0 < o1 + n1 && o1 < o0 + n0;
+}
+
+int oracle_copy_slots(uint16_t *k_pool, uint16_t *v_pool, const int32_t *copies,
+                      int64_t num_copies, int64_t num_kv_heads, int64_t head_dim,
+                      int64_t block_size, int64_t num_blocks)
+{
+    int rc = check_dims(num_kv_heads, head_dim, block_size, 1, num_blocks);
+    if (rc)
+        return rc;
+    if (num_copies < 0)
+        return OR_EARG;
+    for (int64_t i = 0; i < num_copies; ++i) {
+        const int32_t *c = copies + 5 * i;
+        if (c[0] < 0 || c[0] >= num_blocks || c[2] < 0 || c[2] >= num_blocks)
+            return OR_ETABLE;
+        if (c[1] < 0 || c[3] < 0 || c[4] < 0 || c[1] + c[4] > block_size ||
+            c[3] + c[4] > block_size)
+            return OR_EOFFSET;
+    }
+    for (int64_t i = 0; i < num_copies; ++i)
+        for (int64_t j = 0; j < num_copies; ++j) {
+            const int32_t *a = copies + 5 * i, *b = copies + 5 * j;
+            if (rows_overlap(a[2], a[3], a[4], b[0], b[1], b[4]) ||
+                (j != i && rows_overlap(a[2], a[3], a[4], b[2], b[3], b[4])))
+                return OR_EDUP;
+        }
+    for (int64_t i = 0; i < num_copies; ++i) {
+        const int32_t *c = copies + 5 * i;
+        for (int64_t h = 0; h < num_kv_heads; ++h)
+            for (int64_t r = 0; r < c[4]; ++r)
+                for (int64_t d = 0; d < head_dim; ++d) {
+                    int64_t from = oracle_elem_offset(c[0], h, c[1] + r, d, num_kv_heads,
+                                                      block_size, head_dim);
+                    int64_t to = oracle_elem_offset(c[2], h, c[3] + r, d, num_kv_heads,
+                                                    block_size, head_dim);
+                    k_pool[to] = k_pool[from];
+                    v_pool[to] = v_pool[from];
+                }
+    }
     return OR_OK;
 }
 

@@ -43,10 +43,29 @@ MUTANTS = {
                                       "                o[d] /= 1.0;"),
     "last_token_skipped": ("for (int64_t t = t0; t < t1; ++t) {\n        int64_t phys, off;\n        int rc",
                            "for (int64_t t = t0; t < t1 - 1; ++t) {\n        int64_t phys, off;\n        int rc"),
-    "copy_direction_swapped": ("k_pool[to] = k_pool[from];", "k_pool[from] = k_pool[to];"),
-    "copy_skips_values": ("v_pool[to] = v_pool[from];", ""),
+    # block copy: the anchors end at the slot copy's header, which follows it
+    "copy_direction_swapped": ("head_dim);\n                    k_pool[to] = k_pool[from];\n"
+                               "                    v_pool[to] = v_pool[from];\n                }\n"
+                               "    return OR_OK;\n}\n\n/* ---- slot copy",
+                               "head_dim);\n                    k_pool[from] = k_pool[to];\n"
+                               "                    v_pool[to] = v_pool[from];\n                }\n"
+                               "    return OR_OK;\n}\n\n/* ---- slot copy"),
+    "copy_skips_values": ("head_dim);\n                    k_pool[to] = k_pool[from];\n"
+                          "                    v_pool[to] = v_pool[from];\n                }\n"
+                          "    return OR_OK;\n}\n\n/* ---- slot copy",
+                          "head_dim);\n                    k_pool[to] = k_pool[from];\n"
+                          "                }\n    return OR_OK;\n}\n\n/* ---- slot copy"),
     "copy_last_row_dropped": ("for (int64_t off = 0; off < block_size; ++off)",
                               "for (int64_t off = 0; off < block_size - 1; ++off)"),
+    "slot_copy_ignores_destination_offset": ("int64_t to = oracle_elem_offset(c[2], h, c[3] + r, d,",
+                                             "int64_t to = oracle_elem_offset(c[2], h, r, d,"),
+    "slot_copy_ignores_source_offset": ("int64_t from = oracle_elem_offset(c[0], h, c[1] + r, d,",
+                                        "int64_t from = oracle_elem_offset(c[0], h, r, d,"),
+    "slot_copy_drops_last_row": ("for (int64_t r = 0; r < c[4]; ++r)",
+                                 "for (int64_t r = 0; r < c[4] - 1; ++r)"),
+    "slot_copy_skips_values": ("block_size, head_dim);\n                    k_pool[to] = k_pool[from];\n"
+                               "                    v_pool[to] = v_pool[from];",
+                               "block_size, head_dim);\n                    k_pool[to] = k_pool[from];"),
     "slot_offset_dropped": ("*off = so + (t - start);", "*off = (t - start);"),
     "segment_end_inclusive": ("if (t < start + len) {", "if (t <= start + len) {"),
     "segment_start_not_advanced": ("        start += len;\n    }\n    return OR_ETABLE;",
@@ -68,7 +87,8 @@ def _run_pins(lib_path):
     cmd = [sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
            os.path.join(ROOT, "tests", "test_oracle_pins.py"),
            os.path.join(ROOT, "tests", "test_oracle_cow.py"),
-           os.path.join(ROOT, "tests", "test_oracle_slotted.py")]
+           os.path.join(ROOT, "tests", "test_oracle_slotted.py"),
+           os.path.join(ROOT, "tests", "test_oracle_slot_cow.py")]
     return subprocess.run(cmd, env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
 
 
