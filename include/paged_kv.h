@@ -144,6 +144,34 @@ int paged_kv_copy_blocks(void *const *k_pools, void *const *v_pools, int num_lay
                          int dtype, void *stream);
 
 /*
+ * paged_kv_copy_slots -- copy-on-write split of nodes held in shared slots.
+ *
+ * Radix-tree caches pack short nodes as slots of shared blocks (see
+ * paged_attention_decode_slotted).  When such a node is about to be appended to,
+ * it is split off into a block of its own, so the shared slots stay read-only and
+ * the write cannot touch them (mhpq.cn Radix-Tree page, "核心设计原则",
+ * copy-on-write on append): its rows move to the new block, usually at offset 0,
+ * and the append then continues in place there.  For each copy i, rows
+ * src_offset .. src_offset+length-1 of block src_block become rows dst_offset ..
+ * dst_offset+length-1 of block dst_block, in every KV head of every layer's K and
+ * V pool, as they were before the call; every other row is left as it was.  The
+ * library changes no segment list: the caller repoints the node.
+ *
+ *   k_pools, v_pools  HOST arrays of num_layers DEVICE pool pointers, as for
+ *                     paged_kv_copy_blocks (1 <= num_layers <= 128)
+ *   copies            DEVICE int32 [num_copies][5]: (src_block, src_offset,
+ *                     dst_block, dst_offset, length)
+ * Caller contract (checked only with PKV_DEBUG_CHECK=1): blocks in
+ * [0, num_blocks); offsets and length >= 0 with offset + length <= block_size
+ * (the kernel clamps the rows to the block in any case); no destination row is
+ * a source row of any copy or a destination row of another copy.
+ * num_copies == 0 does nothing.
+ */
+int paged_kv_copy_slots(void *const *k_pools, void *const *v_pools, int num_layers,
+                        const int32_t *copies, int num_copies, int num_kv_heads, int head_dim,
+                        int block_size, int64_t num_blocks, int dtype, void *stream);
+
+/*
  * paged_attention_decode -- decode attention over the paged pools.
  *
  * For every sequence s and query head h (KV head g = h / (num_q_heads /

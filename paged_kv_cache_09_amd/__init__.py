@@ -24,5 +24,6 @@ from ._lib import (  # noqa: F401
     paged_kv_append,
     paged_kv_append_tokens,
     paged_kv_copy_blocks,
+    paged_kv_copy_slots,
     status_string,
 )

@@ -53,6 +53,8 @@ def load():
     L.paged_kv_append_tokens.restype = i32
     L.paged_kv_copy_blocks.argtypes = [P, P, i32, P, P, i32, i32, i32, i32, i64, i32, P]
     L.paged_kv_copy_blocks.restype = i32
+    L.paged_kv_copy_slots.argtypes = [P, P, i32, P, i32, i32, i32, i32, i64, i32, P]
+    L.paged_kv_copy_slots.restype = i32
     L.paged_attention_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i64, f32,
                                          i32, i32, P, P, i32, P]
     L.paged_attention_decode.restype = i32
@@ -327,6 +329,31 @@ def paged_kv_copy_blocks(k_pools, v_pools, src_blocks, dst_blocks):
                                      src_blocks.shape[0], Hkv, D, B, NB, _dtype_code(k_pools[0]),
                                      _stream(dev))
     _check(rc, "paged_kv_copy_blocks")
+
+
+def paged_kv_copy_slots(k_pools, v_pools, copies):
+    """Copy-on-write split of shared slots: for each row (src_block, src_offset,
+    dst_block, dst_offset, length) of `copies` (int32 [n][5] on the GPU), the
+    source rows go to the destination rows of every pool in k_pools / v_pools."""
+    k_pools, v_pools = list(k_pools), list(v_pools)
+    if len(k_pools) != len(v_pools) or not k_pools:
+        raise ValueError("k_pools and v_pools must be non-empty lists of equal length")
+    if copies.dim() != 2 or copies.shape[1] != 5:
+        raise ValueError(f"copies must be [n][5], got {tuple(copies.shape)}")
+    shape = _dims(k_pools[0], 4, "k_pools[0]")
+    dtype = k_pools[0].dtype
+    for t in k_pools + v_pools:
+        if t.shape != shape or t.dtype is not dtype:
+            raise ValueError("every pool must have the same shape and dtype")
+    dev = _dev(*k_pools, *v_pools, copies)
+    _ints((copies, "i32", "copies"))
+    NB, Hkv, B, D = shape
+    L = len(k_pools)
+    kp = (C.c_void_p * L)(*[t.data_ptr() for t in k_pools])
+    vp = (C.c_void_p * L)(*[t.data_ptr() for t in v_pools])
+    rc = load().paged_kv_copy_slots(kp, vp, L, _p(copies), copies.shape[0], Hkv, D, B, NB,
+                                    _dtype_code(k_pools[0]), _stream(dev))
+    _check(rc, "paged_kv_copy_slots")
 
 
 def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens,

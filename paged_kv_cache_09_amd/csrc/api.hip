@@ -133,6 +133,37 @@ __global__ void debug_copies_kernel(const int32_t *src, const int32_t *dst, int 
             atomicOr(&g_debug_flag, 16);
 }
 
+// Slot copies: blocks inside the pool, both row ranges inside their block, and no
+// destination row that is a source row of any copy or a destination row of
+// another (the result would depend on copy order).
+__device__ bool rows_overlap(const int32_t *a, int ab, int ao, const int32_t *b, int bb, int bo)
+{
+    return a[ab] == b[bb] && a[ao] < b[bo] + b[4] && b[bo] < a[ao] + a[4];
+}
+
+__global__ void debug_slot_copies_kernel(const int32_t *copies, int num_copies, int block_size,
+                                         int64_t num_blocks)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= num_copies)
+        return;
+    const int32_t *c = copies + 5 * (int64_t)i;
+    if (c[0] < 0 || c[0] >= num_blocks || c[2] < 0 || c[2] >= num_blocks) {
+        atomicOr(&g_debug_flag, 2);
+        return;
+    }
+    if (c[1] < 0 || c[3] < 0 || c[4] < 0 || c[1] + c[4] > block_size ||
+        c[3] + c[4] > block_size) {
+        atomicOr(&g_debug_flag, 128);
+        return;
+    }
+    for (int j = 0; j < num_copies; ++j) {
+        const int32_t *o = copies + 5 * (int64_t)j;
+        if (rows_overlap(c, 2, 3, o, 0, 1) || (j != i && rows_overlap(c, 2, 3, o, 2, 3)))
+            atomicOr(&g_debug_flag, 16);
+    }
+}
+
 int read_debug_flag(hipStream_t stream)
 {
     int flag = 0;
@@ -199,6 +230,17 @@ int debug_check_copies(const int32_t *src, const int32_t *dst, int num_pairs,
     hipLaunchKernelGGL(debug_clear_kernel, dim3(1), dim3(1), 0, stream);
     hipLaunchKernelGGL(debug_copies_kernel, dim3((num_pairs + 255) / 256), dim3(256), 0, stream,
                        src, dst, num_pairs, num_blocks);
+    if (hipGetLastError() != hipSuccess)
+        return PKV_ELAUNCH;
+    return read_debug_flag(stream);
+}
+
+int debug_check_slot_copies(const int32_t *copies, int num_copies, int block_size,
+                            int64_t num_blocks, hipStream_t stream)
+{
+    hipLaunchKernelGGL(debug_clear_kernel, dim3(1), dim3(1), 0, stream);
+    hipLaunchKernelGGL(debug_slot_copies_kernel, dim3((num_copies + 255) / 256), dim3(256), 0,
+                       stream, copies, num_copies, block_size, num_blocks);
     if (hipGetLastError() != hipSuccess)
         return PKV_ELAUNCH;
     return read_debug_flag(stream);
@@ -274,7 +316,7 @@ const char *pkv_status_string(int status)
         return "kernel launch failed";
     case PKV_EDEVICE:
         return "device-side check failed (context length, block-table entry, segment, copy "
-               "pair or prefix group out of range, or overlapping copy pairs)";
+               "pair, slot copy or prefix group out of range, or overlapping copies)";
     default:
         return "unknown status";
     }
@@ -385,6 +427,36 @@ int paged_kv_copy_blocks(void *const *k_pools, void *const *v_pools, int num_lay
     const int64_t slab = (int64_t)num_kv_heads * block_size * head_dim;
     return launch_status(pkv::launch_copy_blocks(k_pools, v_pools, num_layers, src_blocks,
                                                  dst_blocks, num_pairs, slab, st));
+}
+
+int paged_kv_copy_slots(void *const *k_pools, void *const *v_pools, int num_layers,
+                        const int32_t *copies, int num_copies, int num_kv_heads, int head_dim,
+                        int block_size, int64_t num_blocks, int dtype, void *stream)
+{
+    if (!k_pools || !v_pools || num_layers <= 0 || num_copies < 0)
+        return PKV_EINVAL;
+    if (num_layers > pkv::kMaxCopyLayers)
+        return PKV_ENOTSUP;
+    int rc = check_pool_shape(num_kv_heads, head_dim, block_size, 1, num_blocks, dtype);
+    if (rc)
+        return rc;
+    if (num_kv_heads > (1 << 24))  // the grid's x dimension is heads x chunks
+        return PKV_EINVAL;
+    for (int l = 0; l < num_layers; ++l)
+        if (!k_pools[l] || !v_pools[l] || !aligned16(k_pools[l]) || !aligned16(v_pools[l]))
+            return PKV_EINVAL;
+    if (num_copies == 0)
+        return PKV_OK;
+    if (!copies || ((uintptr_t)copies & 3u))
+        return PKV_EINVAL;
+    hipStream_t st = (hipStream_t)stream;
+    if (debug_enabled()) {
+        rc = pkv::debug_check_slot_copies(copies, num_copies, block_size, num_blocks, st);
+        if (rc)
+            return rc;
+    }
+    return launch_status(pkv::launch_copy_slots(k_pools, v_pools, num_layers, copies, num_copies,
+                                                num_kv_heads, block_size, st));
 }
 
 }  // extern "C"

@@ -1,4 +1,4 @@
-// copy.hip -- copy-on-write block duplication.
+// copy.hip -- copy-on-write block duplication, and the split of a shared slot.
 //
 // When a branch is about to append to a partly filled block that another branch
 // still references, the block manager gives the branch a fresh physical block
@@ -53,7 +53,75 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyArgs a)
     }
 }
 
+// Copy-on-write split of a shared slot: a node held in rows [so, so + len) of a
+// block shared with other nodes is moved to rows [do, do + len) of a block of
+// its own before it is appended to, leaving the shared slots read-only (mhpq.cn
+// Radix-Tree page, "核心设计原则", copy-on-write on append).  In the pool layout
+// the node's rows of one KV head are len * 256 contiguous bytes, so each
+// (copy, head) is one contiguous move: a work-group takes up to 1,024 16-byte
+// vectors of it (four loads in flight per lane, then the stores); the grid spans
+// (head x chunk, copy, layer x {K, V}) and the copy tuple is read with scalar
+// loads.  Offsets and lengths are clamped to the block, so a bad tuple cannot
+// reach another block's rows.
+struct SlotCopyArgs {
+    const int32_t *copies;  // [num_copies][5]: src block, src offset, dst block, dst offset, len
+    int num_copies, num_kv_heads, block_size;
+    int chunks;             // work-groups per (copy, head): ceil(block_size * 16 / 1024)
+    u32x4 *pools[2 * kMaxCopyLayers];
+};
+
+__global__ __launch_bounds__(kCopyThreads) void copy_slots_kernel(SlotCopyArgs a)
+{
+    u32x4 *pool = a.pools[blockIdx.z];
+    const int h = blockIdx.x / a.chunks;
+    const int v0 = (blockIdx.x % a.chunks) * kCopyVecPerGroup + threadIdx.x;
+    constexpr int kVecPerRow = kHeadDim * 2 / 16;
+    for (int i = blockIdx.y; i < a.num_copies; i += gridDim.y) {
+        const meta_ptr c = as_meta(a.copies) + 5 * (int64_t)i;
+        const int B = a.block_size;
+        const int so = min(max(c[1], 0), B), dof = min(max(c[3], 0), B);
+        const int len = min(max(c[4], 0), min(B - so, B - dof));
+        const int64_t from = (((int64_t)c[0] * a.num_kv_heads + h) * B + so) * kVecPerRow;
+        const int64_t to = (((int64_t)c[2] * a.num_kv_heads + h) * B + dof) * kVecPerRow;
+        const int nv = len * kVecPerRow;
+        u32x4 r[kCopyUnroll];
+#pragma unroll
+        for (int j = 0; j < kCopyUnroll; ++j) {
+            const int v = v0 + j * kCopyThreads;
+            if (v < nv)
+                r[j] = ldnt(pool + from + v);
+        }
+#pragma unroll
+        for (int j = 0; j < kCopyUnroll; ++j) {
+            const int v = v0 + j * kCopyThreads;
+            if (v < nv)
+                pool[to + v] = r[j];
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_copy_slots(void *const *k_pools, void *const *v_pools, int num_layers,
+                             const int32_t *copies, int num_copies, int num_kv_heads,
+                             int block_size, hipStream_t stream)
+{
+    SlotCopyArgs a{};
+    a.copies = copies;
+    a.num_copies = num_copies;
+    a.num_kv_heads = num_kv_heads;
+    a.block_size = block_size;
+    a.chunks = (block_size * (kHeadDim * 2 / 16) + kCopyVecPerGroup - 1) / kCopyVecPerGroup;
+    for (int l = 0; l < num_layers; ++l) {
+        a.pools[2 * l] = (u32x4 *)k_pools[l];
+        a.pools[2 * l + 1] = (u32x4 *)v_pools[l];
+    }
+    const int gy = num_copies < 65535 ? num_copies : 65535;
+    hipLaunchKernelGGL(copy_slots_kernel,
+                       dim3((unsigned)(num_kv_heads * a.chunks), (unsigned)gy, 2u * num_layers),
+                       dim3(kCopyThreads), 0, stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_copy_blocks(void *const *k_pools, void *const *v_pools, int num_layers,
                               const int32_t *src, const int32_t *dst, int num_pairs,

@@ -51,6 +51,10 @@ hipError_t launch_append_tokens(void *k_pool, void *v_pool, const void *k_src,
 // Work-groups launch_append_tokens uses for total_tokens rows (and the rows per
 // group it picks).
 int64_t append_tokens_groups(int64_t total_tokens, int num_kv_heads, int *rows_per_group);
+// Slot copies ([num_copies][5] device tuples) over every layer's K and V pools.
+hipError_t launch_copy_slots(void *const *k_pools, void *const *v_pools, int num_layers,
+                             const int32_t *copies, int num_copies, int num_kv_heads,
+                             int block_size, hipStream_t stream);
 hipError_t launch_copy_blocks(void *const *k_pools, void *const *v_pools, int num_layers,
                               const int32_t *src, const int32_t *dst, int num_pairs,
                               int64_t slab_elems, hipStream_t stream);
@@ -69,5 +73,7 @@ int debug_check_segments(const int32_t *segs, const int32_t *nsegs, int num_seqs
                          int block_size, int64_t num_blocks, hipStream_t stream);
 int debug_check_copies(const int32_t *src, const int32_t *dst, int num_pairs,
                        int64_t num_blocks, hipStream_t stream);
+int debug_check_slot_copies(const int32_t *copies, int num_copies, int block_size,
+                            int64_t num_blocks, hipStream_t stream);
 
 }  // namespace pkv

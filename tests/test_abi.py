@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
             "paged_attention_decode", "paged_attention_append_decode",
             "paged_attention_prefix_decode", "paged_attention_decode_slotted",
             "paged_attention_reduce", "paged_attention_split_decode",
-            "paged_attention_split_decode_noalloc",
+            "paged_attention_split_decode_noalloc", "paged_kv_copy_slots",
             "pkv_status_string", "pkv_max_partitions"} <= set(declared)
     assert pkv.exported_symbols() == declared
 
@@ -190,6 +190,28 @@ def test_split_decode_noalloc_argument_errors(lib):
     assert call(S=32769, Hq=4, Hkv=4, W=1) == EWORKSPACE
     assert call(S=128, Hq=32, Hkv=32, B=32, W=128, P_=256) == EWORKSPACE  # 65,536 rows
     assert call(S=0) == 0
+
+
+@host_only
+def test_copy_slots_argument_errors(lib):
+    f = lib.paged_kv_copy_slots
+    two = (P * 2)(A, A)
+
+    def call(kp=two, vp=two, L=2, c=A, n=3, Hkv=2, D=128, B=16, NB=64, dt=0):
+        return f(kp, vp, L, c, n, Hkv, D, B, NB, dt, None)
+
+    assert call(kp=None) == EINVAL
+    assert call(L=0) == EINVAL
+    assert call(n=-1) == EINVAL
+    assert call(c=None) == EINVAL
+    assert call(c=P((1 << 20) + 2)) == EINVAL                   # misaligned tuples
+    assert call(vp=(P * 2)(A, None)) == EINVAL                  # a null pool
+    assert call(D=64) == ENOTSUP
+    assert call(B=24) == ENOTSUP
+    assert call(dt=3) == ENOTSUP
+    many = (P * 129)(*([A] * 129))
+    assert call(kp=many, vp=many, L=129) == ENOTSUP
+    assert call(n=0, c=None) == 0                                # nothing to copy
 
 
 @host_only

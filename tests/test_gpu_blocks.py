@@ -264,3 +264,151 @@ def test_copy_blocks_empty_and_debug_rejections(monkeypatch):
         assert ei.value.status == -5
     pkv.paged_kv_copy_blocks([k], [v], i32([1, 1], DEV), i32([2, 3], DEV))  # a fork is fine
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# slot copies (copy-on-write split of a node held in a shared slot)
+# ---------------------------------------------------------------------------
+def _golden_slot_cow():
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "slot_cow.json")) as f:
+        return json.load(f)
+
+
+def _copy_slots_both(copies, NB, Hkv, B, dtype, layers, seed):
+    """The same random pools and copies on each side; returns (oracle pools per
+    layer, GPU pools per layer)."""
+    rng = np.random.default_rng(seed)
+    host = [(_pool(NB, Hkv, B, dtype, rng), _pool(NB, Hkv, B, dtype, rng)) for _ in range(layers)]
+    gk = [to_dev(k, dtype, DEV) for k, _ in host]
+    gv = [to_dev(v, dtype, DEV) for _, v in host]
+    for k, v in host:
+        O.copy_slots(k, v, copies)
+    pkv.paged_kv_copy_slots(gk, gv, i32(np.asarray(copies, np.int32).reshape(-1, 5), DEV))
+    torch.cuda.synchronize()
+    return host, list(zip(gk, gv))
+
+
+@pytest.mark.parametrize("Hkv,layers", [(1, 1), (8, 3), (32, 2)])
+def test_copy_slots_page_example_bit_exact(Hkv, layers):
+    """Node B's rows (block 0, offset 5, 8 rows) move to offset 0 of block 4 in
+    every head and layer; every other row of both blocks and of the pool keeps its
+    bits."""
+    g = _golden_slot_cow()
+    c = g["copy"]
+    copies = [[c["src_block"], c["src_offset"], c["dst_block"], c["dst_offset"], c["length"]]]
+    host, dev = _copy_slots_both(copies, g["pool_blocks"], Hkv, g["block_size"], "fp16", layers,
+                                 seed=Hkv)
+    for (k, v), (gk, gv) in zip(host, dev):
+        assert np.array_equal(bits_of(gk), k) and np.array_equal(bits_of(gv), v)
+
+
+def _random_copies(rng, NB, B, n):
+    """n copies with random offsets and lengths: sources in the first half of the
+    pool, each destination in a block of its own in the second half (one within
+    its source block's half when both ranges fit apart), so no copy's result
+    depends on the order."""
+    out = []
+    dst_blocks = rng.permutation(np.arange(NB // 2, NB))  # n + 4 blocks, n used below
+    for i in range(n):
+        ln = int(rng.integers(0, B + 1))
+        so = int(rng.integers(0, B - ln + 1))
+        do = int(rng.integers(0, B - ln + 1))
+        out.append([int(rng.integers(0, NB // 2)), so, int(dst_blocks[i]), do, ln])
+    # a move inside one block (no other copy touches it), between disjoint rows
+    sb = int(dst_blocks[n])
+    h = B // 2
+    out.append([sb, 0, sb, h, min(h, 5)])
+    return out
+
+
+@pytest.mark.parametrize("B,Hkv,layers,n", [(16, 2, 1, 7), (32, 8, 2, 20), (64, 4, 3, 9),
+                                            (128, 8, 1, 12), (256, 2, 2, 5), (16, 32, 4, 40)])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_copy_slots_bit_exact(B, Hkv, layers, n, dtype):
+    rng = np.random.default_rng(B * 1000 + Hkv * 10 + n)
+    NB = 2 * n + 8
+    copies = _random_copies(rng, NB, B, n)
+    host, dev = _copy_slots_both(copies, NB, Hkv, B, dtype, layers, seed=n)
+    for (k, v), (gk, gv) in zip(host, dev):
+        assert np.array_equal(bits_of(gk), k) and np.array_equal(bits_of(gv), v)
+
+
+def test_slot_split_then_append_then_decode():
+    """The radix batch at the prefix workload's shapes (32 query / 8 KV heads,
+    blocks of 16): eight paths end at a short level-2 node held in a shared slot.
+    For each, path X keeps reading the node's slot while path Y generates a token:
+    the node is split into a free block of its own (the copy), Y's token is written
+    after it, and both paths attend.  Pools bit-exact and outputs within tolerance
+    of the oracle run through the same steps."""
+    from workloads import get_config
+    from workloads.slotted import make_slotted_workload
+    cfg = get_config("c5")
+    w = make_slotted_workload(cfg)
+    B, Hkv, Hq, NB, dt = cfg.block_size, cfg.num_kv_heads, cfg.num_q_heads, w.num_blocks, cfg.dtype
+    used = {blk for segs in w.node_segments for blk, _, _ in segs}
+    free = [b for b in range(NB) if b not in used]
+    rng = np.random.default_rng(5)
+    draw = lambda *sh: (rng.standard_normal(sh) * 0.5).astype(np.float16).view(np.uint16)  # noqa: E731
+    paths, copies, news = [], [], []
+    for s in range(8):
+        root, l1, l2 = w.paths[s][:3]
+        (blk, off, ln), = w.node_segments[l2]  # a short node: one slot
+        dst = free[s]
+        copies.append([blk, off, dst, 0, ln])
+        base = w.node_segments[root] + w.node_segments[l1]
+        paths.append(base + [(blk, off, ln)])           # X: the shared slot
+        paths.append(base + [(dst, 0, ln + 1)])         # Y: its own block, grown by one
+        news.append((dst, ln))
+    S = len(paths)
+    ms = max(len(p) for p in paths)
+    segs = np.zeros((S, ms, 3), np.int32)
+    nseg = np.array([len(p) for p in paths], np.int32)
+    for i, p in enumerate(paths):
+        segs[i, :len(p)] = p
+    new_k, new_v = draw(8, Hkv, 128), draw(8, Hkv, 128)
+    run_cu = np.arange(9, dtype=np.int64)
+    run_start = np.array([o for _, o in news], np.int32)
+    run_tab = np.array([[b] for b, _ in news], np.int32)
+    q = draw(S, Hq, 128)
+    kr, vr, cu, st, tb = w.runs()
+    # oracle
+    kp, vp = _pool(NB, Hkv, B, dt), _pool(NB, Hkv, B, dt)
+    O.append_tokens(kp, vp, kr, vr, cu, st, tb, B, NB)
+    O.copy_slots(kp, vp, copies)
+    O.append_tokens(kp, vp, new_k, new_v, run_cu, run_start, run_tab, B, NB)
+    ref = O.attention_slotted(q, kp, vp, segs, nseg, Hkv, B, NB, scale_for(128), dt)
+    # GPU
+    gk, gv = to_dev(_pool(NB, Hkv, B, dt), dt, DEV), to_dev(_pool(NB, Hkv, B, dt), dt, DEV)
+    pkv.paged_kv_append_tokens(gk, gv, to_dev(kr, dt, DEV), to_dev(vr, dt, DEV), i64(cu, DEV),
+                               i32(st, DEV), i32(tb, DEV))
+    pkv.paged_kv_copy_slots([gk], [gv], i32(np.array(copies, np.int32), DEV))
+    pkv.paged_kv_append_tokens(gk, gv, to_dev(new_k, dt, DEV), to_dev(new_v, dt, DEV),
+                               i64(run_cu, DEV), i32(run_start, DEV), i32(run_tab, DEV))
+    out = torch.empty((S, Hq, 128), dtype=torch.float16, device=DEV)
+    pkv.paged_attention_decode_slotted(out, to_dev(q, dt, DEV), gk, gv, i32(segs, DEV),
+                                       i32(nseg, DEV), scale=scale_for(128))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(gk), kp) and np.array_equal(bits_of(gv), vp)
+    ok, err, nbad = tol_ok(widen_out(out), ref)
+    assert ok, (err, nbad)
+
+
+def test_copy_slots_empty_and_debug_rejections(monkeypatch):
+    k = torch.zeros((8, 2, 16, 128), dtype=torch.float16, device=DEV)
+    v = torch.zeros_like(k)
+    pkv.paged_kv_copy_slots([k], [v], torch.zeros((0, 5), dtype=torch.int32, device=DEV))
+    monkeypatch.setenv("PKV_DEBUG_CHECK", "1")
+    bad = [[[0, 0, 1, 0, 8], [1, 4, 2, 0, 4]],   # a destination read by another copy
+           [[0, 0, 1, 0, 8], [2, 0, 1, 7, 4]],   # overlapping destinations
+           [[0, 10, 1, 0, 8]],                   # source rows past the block
+           [[0, 0, 8, 0, 4]]]                    # destination outside the pool
+    for c in bad:
+        with pytest.raises(pkv.PagedKVError) as ei:
+            pkv.paged_kv_copy_slots([k], [v], i32(np.array(c, np.int32), DEV))
+        assert ei.value.status == -5
+    # a node split into two blocks (one source, two destinations) is fine
+    pkv.paged_kv_copy_slots([k], [v], i32(np.array([[0, 0, 1, 0, 8], [0, 0, 2, 3, 8]],
+                                                   np.int32), DEV))
+    torch.cuda.synchronize()
