@@ -87,6 +87,14 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="capture one whole step (every layer's launches) in a HIP graph and "
                          "time graph replays instead of eager launches")
+    ap.add_argument("--slotted-batch", default="auto", choices=["auto", "radix", "tables"],
+                    help="--op slotted: the radix-tree batch (radix; the default for the "
+                         "shared-prefix workload) or the workload's block tables written as "
+                         "segments (tables; the default otherwise, in split mode when the "
+                         "workload's partition size is set)")
+    ap.add_argument("--slotted-kernel", default="auto", choices=["auto", "tiles", "per_sequence"],
+                    help="--op slotted, single pass: the library's choice, or force the tiled "
+                         "or the per-sequence kernel (PKV_SLOTTED_TILES)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle sample")
@@ -627,20 +635,43 @@ def bench_copy_blocks(args):
     print(json.dumps(line), flush=True)
 
 
+def _tables_as_segments(w):
+    """A workload's block tables written as slotted segments: whole blocks, then
+    the partly filled last block."""
+    c = w.cfg
+    B = c.block_size
+    nb = -(-w.lengths.astype(np.int64) // B)
+    segs = np.zeros((c.num_seqs, max(1, int(nb.max())), 3), np.int32)
+    for s in range(c.num_seqs):
+        for j in range(nb[s]):
+            segs[s, j] = (w.tables[s, j], 0, min(B, int(w.lengths[s]) - j * B))
+    return segs, nb.astype(np.int32)
+
+
 def bench_slotted(args):
-    """Decode of a radix-tree batch at the workload's shapes (a shared 512-token
-    root, shared short nodes packed as slots, a private leaf per sequence), each
-    sequence given as (block, slot offset, length) segments; one
-    paged_attention_decode_slotted launch per step, cycling through R distinct
-    batches.  value = sequences / step time; the roofline counts each node's
-    K/V rows once (unique bytes)."""
+    """Decode over slotted (block, slot offset, length) segments, one launch per
+    step, cycling through R distinct batches.  The batch is the radix tree at the
+    workload's shapes (a shared 512-token root, shared short nodes packed as
+    slots, a private leaf per sequence; paged_attention_decode_slotted), or the
+    workload's own block tables written as segments (whole blocks; in split mode
+    with the workload's partition size, paged_attention_decode_slotted_split).
+    value = sequences / step time; the roofline counts each node's K/V rows once
+    (unique bytes)."""
     import torch
     import paged_kv_cache_09_amd as pkv
-    from workloads import get_config
+    from workloads import get_config, make_workload
     from workloads.slotted import make_slotted_workload
 
     cfg = get_config(args.config)
-    R = args.distinct or 4
+    kind = args.slotted_batch
+    if kind == "auto":
+        kind = "radix" if cfg.prefix_tokens > 0 else "tables"
+    P = (cfg.bench_partition_size if args.partition_size is None else args.partition_size)
+    if kind == "radix" and args.partition_size is None:
+        P = 0
+    R = args.distinct or (4 if kind == "radix" else cfg.bench_distinct_layers)
+    if args.slotted_kernel != "auto":
+        os.environ["PKV_SLOTTED_TILES"] = "1" if args.slotted_kernel == "tiles" else "0"
     dev = torch.device("cuda:0")
     tdt = {"fp16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
 
@@ -649,54 +680,97 @@ def bench_slotted(args):
 
     batches = []
     for d in range(R):
-        w = make_slotted_workload(cfg, seed_id=1000 * cfg.cfg_id + d)
-        kr, vr, cu, st, tb = w.runs()
-        kp = torch.zeros(w.pool_shape(), dtype=tdt, device=dev)
+        if kind == "radix":
+            w = make_slotted_workload(cfg, seed_id=1000 * cfg.cfg_id + d)
+            kr, vr, cu, st, tb = w.runs()
+            segs, nsegs, NB = w.segments, w.num_segments, w.num_blocks
+            info = dict(unique=w.unique_tokens(), logical=int(w.lengths().sum()),
+                        mean=float(w.lengths().mean()), nodes=len(w.node_k), S=len(w.paths))
+        else:
+            w = make_workload(cfg, layer=d)
+            kr, vr, cu, st, tb = w.k_src, w.v_src, w.seg_cu, w.seg_start, w.seg_tables
+            segs, nsegs = _tables_as_segments(w)
+            NB = w.num_blocks
+            info = dict(unique=int(w.lengths.sum()), logical=int(w.lengths.sum()),
+                        mean=float(w.lengths.mean()), nodes=None, S=cfg.num_seqs)
+        kp = torch.zeros((NB, cfg.num_kv_heads, cfg.block_size, cfg.head_dim), dtype=tdt,
+                         device=dev)
         vp = torch.zeros_like(kp)
         pkv.paged_kv_append_tokens(kp, vp, up(kr), up(vr), torch.from_numpy(cu).to(dev),
                                    torch.from_numpy(st).to(dev), torch.from_numpy(tb).to(dev))
-        batches.append(dict(w=w, k=kp, v=vp, q=up(w.q),
-                            segs=torch.from_numpy(w.segments).to(dev),
-                            ns=torch.from_numpy(w.num_segments).to(dev)))
+        if kind == "tables":
+            # the step's own token, so that every position holds data
+            pkv.paged_kv_append(kp, vp, up(w.k_new), up(w.v_new), torch.from_numpy(w.tables).to(dev),
+                                torch.from_numpy(w.lengths).to(dev))
+        batches.append(dict(w=w, k=kp, v=vp, q=up(w.q), info=info,
+                            segs=torch.from_numpy(segs).to(dev),
+                            ns=torch.from_numpy(nsegs).to(dev)))
     torch.cuda.synchronize()
-    w0 = batches[0]["w"]
-    S, Hq, D = len(w0.paths), cfg.num_q_heads, cfg.head_dim
+    b0 = batches[0]
+    info = b0["info"]
+    S, Hq, D = info["S"], cfg.num_q_heads, cfg.head_dim
+    MS = int(b0["segs"].shape[1])
     out = torch.empty((S, Hq, D), dtype=tdt, device=dev)
     scale = float(np.float32(1.0 / math.sqrt(D)))
+    if P:
+        mp = -(-MS * cfg.block_size // P)
+        po = torch.empty((S, Hq, mp, D), dtype=torch.float32, device=dev)
+        pl = torch.empty((S, Hq, mp), dtype=torch.float32, device=dev)
+        ctr = torch.zeros((S, cfg.num_kv_heads), dtype=torch.int32, device=dev)
     it = iter(range(1 << 30))
 
     def one():
         b = batches[next(it) % R]
-        pkv.paged_attention_decode_slotted(out, b["q"], b["k"], b["v"], b["segs"], b["ns"],
-                                           scale=scale)
+        if P:
+            pkv.paged_attention_decode_slotted_split(out, b["q"], b["k"], b["v"], b["segs"],
+                                                     b["ns"], P, po, pl, ctr, scale=scale)
+        else:
+            pkv.paged_attention_decode_slotted(out, b["q"], b["k"], b["v"], b["segs"], b["ns"],
+                                               scale=scale)
 
-    ms = time_launches(one, args.steps * 4, warm=args.warmup * 4)
+    reps = max(64, R)
+    for _ in range(args.warmup):
+        one()
+    ms, how = time_launches_graph(one, reps)
     e, Hkv = cfg.elem_bytes, cfg.num_kv_heads
     row = 2 * Hkv * D * e                                   # K and V of one token, all heads
-    nseg = int(w0.num_segments.sum())
-    unique = w0.unique_tokens() * row + 2 * S * Hq * D * e + 12 * nseg + 4 * S
-    logical = int(w0.lengths().sum()) * row + 2 * S * Hq * D * e + 12 * nseg + 4 * S
-    roof = roofline("paged_attention_decode_slotted", unique, ms,
-                    measured_traffic(f"slotted_{cfg.key}", "slotted"))
-    config = {"workload": f"{cfg.key} radix-tree batch in slotted blocks ({cfg.title})",
+    nseg = int(b0["ns"].sum())
+    unique = info["unique"] * row + 2 * S * Hq * D * e + 12 * nseg + 4 * S
+    logical = info["logical"] * row + 2 * S * Hq * D * e + 12 * nseg + 4 * S
+    name = "slotted_split" if P else "slotted"
+    roof = roofline("paged_attention_decode_slotted_split" if P else
+                    "paged_attention_decode_slotted", unique, ms,
+                    measured_traffic(f"{name}_{cfg.key}" if kind == "tables" else
+                                     f"slotted_{cfg.key}", "slotted"))
+    roof["timing"] = how
+    what = ("radix-tree batch in slotted blocks" if kind == "radix" else
+            "block tables written as slotted segments")
+    config = {"workload": f"{cfg.key} {what} ({cfg.title})",
               "num_seqs": S, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
-              "block_size": cfg.block_size, "mean_context": round(float(w0.lengths().mean()), 1),
-              "unique_tokens": w0.unique_tokens(), "nodes": len(w0.node_k),
-              "max_segments": int(w0.segments.shape[1]), "distinct_batches": R, "launches": 1}
+              "block_size": cfg.block_size, "mean_context": round(info["mean"], 1),
+              "unique_tokens": info["unique"], "nodes": info["nodes"],
+              "max_segments": MS, "partition_size": P, "distinct_batches": R, "launches": 1,
+              "kernel_choice": args.slotted_kernel}
     line = _side_line("slotted-segment decode tokens/s and unique-byte HBM GB/s, 1 GPU",
                       S / (ms * 1e-3), "tokens/s", args, cfg, cfg.dtype, config, roof,
                       {"logical_bytes_per_launch": logical})
     if not args.no_cpu_baseline:
         from oracle import oracle as O
-        kr, vr, cu, st, tb = w0.runs()
-        kp, vp = O.new_pools(w0.num_blocks, Hkv, cfg.block_size, D, 0)
-        O.append_tokens(kp, vp, kr, vr, cu, st, tb, cfg.block_size, w0.num_blocks)
+        w0 = b0["w"]
+        if kind == "radix":
+            kr, vr, cu, st, tb = w0.runs()
+        else:
+            kr, vr, cu, st, tb = w0.k_src, w0.v_src, w0.seg_cu, w0.seg_start, w0.seg_tables
+        NB = int(b0["k"].shape[0])
+        kp, vp = O.new_pools(NB, Hkv, cfg.block_size, D, 0)
+        O.append_tokens(kp, vp, kr, vr, cu, st, tb, cfg.block_size, NB)
+        segs, nsegs = b0["segs"].cpu().numpy(), b0["ns"].cpu().numpy()
         threads = O.max_threads(0)
         reps, spent = 0, 0.0
         while reps == 0 or (spent < args.cpu_seconds and reps < 20):
             t = time.perf_counter()
-            O.attention_slotted(w0.q, kp, vp, w0.segments, w0.num_segments, Hkv,
-                                cfg.block_size, w0.num_blocks, scale, cfg.dtype, threads)
+            O.attention_slotted(w0.q, kp, vp, segs, nsegs, Hkv, cfg.block_size, NB, scale,
+                                cfg.dtype, threads)
             spent += time.perf_counter() - t
             reps += 1
         line["cpu_baseline"] = {"value": round(S * reps / spent, 3), "unit": "tokens/s",

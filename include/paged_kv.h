@@ -378,9 +378,12 @@ int paged_attention_prefix_decode(void *out, const void *q, void *k_pool, void *
  * Consecutive sequences whose lists begin with the same triples (the shared path
  * of a radix tree) have those rows read once per tile of 2 * floor(16 / G)
  * sequences, whenever a tile's sub-tile list fits the kernel's LDS
- * (2 * floor(16 / G) * max_segments * ceil(block_size / 16) <= 1024); otherwise,
- * or with the environment variable PKV_SLOTTED_TILES=0, one work-group per
- * (sequence, KV head).  Both give the same attention up to summation order.
+ * (2 * floor(16 / G) * max_segments * ceil(block_size / 16) <= 1024) and the
+ * tiles still give at least half of min(num_seqs * num_kv_heads, compute units)
+ * work-groups; otherwise one work-group per (sequence, KV head).  The
+ * environment variable PKV_SLOTTED_TILES=1 takes the tiles whenever the list
+ * fits, PKV_SLOTTED_TILES=0 never.  Both give the same attention up to summation
+ * order.
  *
  *   segments       device int32 [num_seqs][max_segments][3]: (block_id,
  *                  slot_offset, length); only the first num_segments[s] are read
@@ -396,6 +399,40 @@ int paged_attention_decode_slotted(void *out, const void *q, const void *k_pool,
                                    int num_kv_heads, int head_dim, int block_size,
                                    int max_segments, int64_t num_blocks, float scale, int dtype,
                                    void *stream);
+
+/*
+ * paged_attention_decode_slotted_split -- slotted decode in split-context mode,
+ * the partitions merged in the same launch.
+ *
+ * Same result as paged_attention_decode_slotted, for long sequences: each
+ * sequence's positions (the concatenation of its segments, n = sum of lengths)
+ * are cut into partitions of partition_size positions, partition p covering
+ * [p*P, min(n, (p+1)*P)); a segment that straddles a boundary is split between
+ * two partitions.  Partitions are spread over several work-groups per
+ * (sequence, KV head) and merged as in paged_attention_split_decode (arrival
+ * counters, log-sum-exp merge by the last work-group; n <= P is written
+ * directly).  Always one work-group per (sequence, KV head, partition group):
+ * the tiles of paged_attention_decode_slotted are not used.
+ *
+ *   partition_size > 0, a multiple of 16
+ *   max_partitions row stride of the workspace, at least
+ *                  ceil(max_segments * block_size / partition_size), else
+ *                  PKV_EWORKSPACE; at most 2^31 - 1 bytes of part_o
+ *   part_o, part_lse  fp32 workspace [num_seqs][num_q_heads][max_partitions][head_dim]
+ *                  and [num_seqs][num_q_heads][max_partitions]; contents afterwards
+ *                  unspecified
+ *   counters       device int32 [num_seqs][num_kv_heads], all zero when the call
+ *                  starts and left zero, as for paged_attention_split_decode
+ * Other arguments as for paged_attention_decode_slotted.
+ */
+int paged_attention_decode_slotted_split(void *out, const void *q, const void *k_pool,
+                                         const void *v_pool, const int32_t *segments,
+                                         const int32_t *num_segments, int num_seqs,
+                                         int num_q_heads, int num_kv_heads, int head_dim,
+                                         int block_size, int max_segments, int64_t num_blocks,
+                                         float scale, int partition_size, int max_partitions,
+                                         float *part_o, float *part_lse, int32_t *counters,
+                                         int dtype, void *stream);
 
 /*
  * paged_attention_reduce -- log-sum-exp merge of split-context partitions.

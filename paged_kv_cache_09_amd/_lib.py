@@ -74,6 +74,10 @@ def load():
     L.paged_attention_decode_slotted.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32,
                                                  i64, f32, i32, P]
     L.paged_attention_decode_slotted.restype = i32
+    L.paged_attention_decode_slotted_split.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32,
+                                                       i32, i32, i64, f32, i32, i32, P, P, P,
+                                                       i32, P]
+    L.paged_attention_decode_slotted_split.restype = i32
     L.paged_attention_reduce.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, P]
     L.paged_attention_reduce.restype = i32
     _lib = L
@@ -494,6 +498,33 @@ def paged_attention_decode_slotted(out, q, k_pool, v_pool, segments, num_segment
         _p(out), _p(q), _p(k_pool), _p(v_pool), _p(segments), _p(num_segments), S, Hq, Hkv, D,
         B, ss[1], NB, scale, _dtype_code(q), _stream(dev))
     _check(rc, "paged_attention_decode_slotted")
+
+
+def paged_attention_decode_slotted_split(out, q, k_pool, v_pool, segments, num_segments,
+                                         partition_size: int, part_o, part_lse, counters,
+                                         scale: Optional[float] = None):
+    """Slotted-segment decode in split-context mode, the partitions merged in the
+    same launch; counters: int32 [S][Hkv], zero on entry and left zero."""
+    NB, Hkv, B, D = _pools(k_pool, v_pool)
+    S, Hq, Dq = _dims(q, 3, "q")
+    if Dq != D:
+        raise ValueError(f"q has head_dim {Dq}, the pools {D}")
+    _same_dtype(k_pool, (q, "q"), (out, "out"))
+    _expect(out, (S, Hq, D), "out")
+    ss = segments.shape
+    if len(ss) != 3 or ss[0] != S or ss[2] != 3:
+        raise ValueError(f"segments must be [{S}][max_segments][3], got {tuple(ss)}")
+    _expect(num_segments, (S,), "num_segments")
+    _expect(counters, (S, Hkv), "counters")
+    mp = _workspace(part_o, part_lse, S, Hq, D)
+    dev = _dev(out, q, k_pool, v_pool, segments, num_segments, part_o, part_lse, counters)
+    _ints((segments, "i32", "segments"), (num_segments, "i32", "num_segments"),
+          (counters, "i32", "counters"))
+    rc = load().paged_attention_decode_slotted_split(
+        _p(out), _p(q), _p(k_pool), _p(v_pool), _p(segments), _p(num_segments), S, Hq, Hkv, D,
+        B, ss[1], NB, _scale(scale), int(partition_size), mp, _p(part_o), _p(part_lse),
+        _p(counters), _dtype_code(q), _stream(dev))
+    _check(rc, "paged_attention_decode_slotted_split")
 
 
 def paged_attention_reduce(out, part_o, part_lse, context_lens, partition_size: int):

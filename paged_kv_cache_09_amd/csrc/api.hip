@@ -257,10 +257,34 @@ bool debug_enabled()
     return e && e[0] && strcmp(e, "0") != 0;
 }
 
-bool slotted_tiles_enabled()
+// PKV_SLOTTED_TILES: "0" never takes the tiled slotted kernel, "1" takes it
+// whenever a tile's list fits, anything else (the default) also asks for enough
+// work-groups (see slotted_impl).
+int slotted_tiles_mode()
 {
     const char *e = getenv("PKV_SLOTTED_TILES");
-    return !(e && strcmp(e, "0") == 0);
+    if (e && strcmp(e, "0") == 0)
+        return 0;
+    if (e && strcmp(e, "1") == 0)
+        return 1;
+    return 2;
+}
+
+// Compute units of the current device (cached per device; 256 on MI355X).
+int device_cu_count()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -823,16 +847,22 @@ int paged_attention_prefix_decode(void *out, const void *q, void *k_pool, void *
                        max_partitions, part_o, part_lse, dtype, stream, pg);
 }
 
-int paged_attention_decode_slotted(void *out, const void *q, const void *k_pool,
-                                   const void *v_pool, const int32_t *segments,
-                                   const int32_t *num_segments, int num_seqs, int num_q_heads,
-                                   int num_kv_heads, int head_dim, int block_size,
-                                   int max_segments, int64_t num_blocks, float scale, int dtype,
-                                   void *stream)
+}  // extern "C"
+
+namespace {
+
+// Shared by the slotted entry points: validation, then one launch.  With
+// partition_size > 0 the split kernel runs (counters and workspace required).
+int slotted_impl(void *out, const void *q, const void *k_pool, const void *v_pool,
+                 const int32_t *segments, const int32_t *num_segments, int num_seqs,
+                 int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                 int max_segments, int64_t num_blocks, float scale, int partition_size,
+                 int max_partitions, float *part_o, float *part_lse, int32_t *counters, int dtype,
+                 void *stream)
 {
     if (!out || !q || !k_pool || !v_pool || !segments || !num_segments)
         return PKV_EINVAL;
-    if (num_seqs < 0 || num_q_heads <= 0 || max_segments <= 0)
+    if (num_seqs < 0 || num_q_heads <= 0 || max_segments <= 0 || partition_size < 0)
         return PKV_EINVAL;
     int rc = check_pool_shape(num_kv_heads, head_dim, block_size, 1, num_blocks, dtype);
     if (rc)
@@ -848,7 +878,24 @@ int paged_attention_decode_slotted(void *out, const void *q, const void *k_pool,
         return PKV_EINVAL;
     if ((int64_t)max_segments * 3 * num_seqs > ((int64_t)1 << 40))
         return PKV_EINVAL;
-    const int64_t items = (int64_t)num_seqs * num_kv_heads;
+    // a sequence's positions (at most max_segments x block_size) fit in 31 bits
+    if ((int64_t)max_segments * block_size > ((int64_t)1 << 30))
+        return PKV_EINVAL;
+    int parts = 1;
+    if (partition_size > 0) {
+        if (partition_size % 16 != 0 || !counters || ((uintptr_t)counters & 3u))
+            return PKV_EINVAL;
+        const int64_t need64 =
+            ((int64_t)max_segments * block_size + partition_size - 1) / partition_size;
+        if (!part_o || !part_lse || max_partitions < need64)
+            return PKV_EWORKSPACE;
+        if (!aligned16(part_o) || ((uintptr_t)part_lse & 3u))
+            return PKV_EINVAL;
+        if ((int64_t)num_seqs * num_q_heads * max_partitions * head_dim * 4 > (int64_t)INT32_MAX)
+            return PKV_EWORKSPACE;
+        parts = split_parts((int64_t)num_seqs * num_kv_heads, (int)need64);
+    }
+    const int64_t items = (int64_t)num_seqs * num_kv_heads * parts;
     if (items > INT32_MAX)
         return PKV_EINVAL;
     if (items == 0)
@@ -874,19 +921,70 @@ int paged_attention_decode_slotted(void *out, const void *q, const void *k_pool,
     a.segments = segments;
     a.num_segments = num_segments;
     a.max_segments = max_segments;
+    if (partition_size > 0) {
+        a.partition_size = partition_size;
+        a.max_partitions = max_partitions;
+        a.parts_per_item = parts;
+        a.part_o = part_o;
+        a.part_lse = part_lse;
+        a.counters = counters;
+        return launch_status(pkv::launch_slotted_mfma(a, dtype, block_size, st));
+    }
     // Tiles of consecutive sequences read their common leading segments once; they
     // need the whole list of a tile's sub-tiles in LDS, so a batch whose worst-case
-    // tile exceeds it runs one work-group per sequence.  PKV_SLOTTED_TILES=0 forces
-    // the latter.
+    // tile exceeds it runs one work-group per sequence.  Tiles also cut the number
+    // of work-groups by the sequences per tile (up to 32), which only pays when
+    // sequences share segments: the host cannot see the segments, so by default
+    // tiles are taken only while they still give at least half as many
+    // work-groups as min(per-sequence work-groups, compute units).
     const int spt = pkv::kPrefixHalves * (16 / (num_q_heads / num_kv_heads));
     const int64_t tile_subs = (int64_t)spt * max_segments * ((block_size + 15) / 16);
-    if (slotted_tiles_enabled() && tile_subs <= pkv::kSlottedTileSubs) {
+    const int64_t tiles = (num_seqs + spt - 1) / spt;
+    const int mode = slotted_tiles_mode();
+    bool use_tiles = mode != 0 && tile_subs <= pkv::kSlottedTileSubs;
+    if (use_tiles && mode == 2) {
+        const int64_t per_seq = (int64_t)num_seqs * num_kv_heads;
+        const int64_t cap = per_seq < device_cu_count() ? per_seq : device_cu_count();
+        use_tiles = 2 * tiles * num_kv_heads >= cap;
+    }
+    if (use_tiles) {
         a.seqs_per_tile = spt;
-        const int64_t tiles = (num_seqs + spt - 1) / spt;
         return launch_status(pkv::launch_slotted_tiled_mfma(a, (int)(tiles * num_kv_heads),
                                                             dtype, block_size, st));
     }
     return launch_status(pkv::launch_slotted_mfma(a, dtype, block_size, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attention_decode_slotted(void *out, const void *q, const void *k_pool,
+                                   const void *v_pool, const int32_t *segments,
+                                   const int32_t *num_segments, int num_seqs, int num_q_heads,
+                                   int num_kv_heads, int head_dim, int block_size,
+                                   int max_segments, int64_t num_blocks, float scale, int dtype,
+                                   void *stream)
+{
+    return slotted_impl(out, q, k_pool, v_pool, segments, num_segments, num_seqs, num_q_heads,
+                        num_kv_heads, head_dim, block_size, max_segments, num_blocks, scale, 0, 0,
+                        nullptr, nullptr, nullptr, dtype, stream);
+}
+
+int paged_attention_decode_slotted_split(void *out, const void *q, const void *k_pool,
+                                         const void *v_pool, const int32_t *segments,
+                                         const int32_t *num_segments, int num_seqs,
+                                         int num_q_heads, int num_kv_heads, int head_dim,
+                                         int block_size, int max_segments, int64_t num_blocks,
+                                         float scale, int partition_size, int max_partitions,
+                                         float *part_o, float *part_lse, int32_t *counters,
+                                         int dtype, void *stream)
+{
+    if (partition_size <= 0)
+        return PKV_EINVAL;
+    return slotted_impl(out, q, k_pool, v_pool, segments, num_segments, num_seqs, num_q_heads,
+                        num_kv_heads, head_dim, block_size, max_segments, num_blocks, scale,
+                        partition_size, max_partitions, part_o, part_lse, counters, dtype, stream);
 }
 
 int paged_attention_reduce(void *out, const float *part_o, const float *part_lse,

@@ -802,7 +802,15 @@ __device__ __forceinline__ SubRsrc slot_rsrc(const int32_t *s_phys, const int32_
     return r;
 }
 
-template <int DT, int BS, int WAVES>
+// SPLIT: split-context mode with the partitions merged in the launch.  The
+// sequence's logical positions (the concatenation of its segments) are cut into
+// partitions of partition_size tokens; work-group px of an item takes
+// partitions px, px + parts_per_item, ...  Each round's segments are clipped to
+// the partition's positions before they become sub-tiles, so a segment that
+// straddles a partition boundary is split between two partitions.  Partials and
+// the arrival of the work-groups follow the merged split decode (arrive_last); a
+// sequence of at most one partition is written to `out` directly.
+template <int DT, int BS, int WAVES, bool SPLIT = false>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(3)))
 void slotted_mfma_kernel(DecodeArgs a)
 {
@@ -814,10 +822,15 @@ void slotted_mfma_kernel(DecodeArgs a)
     __shared__ int32_t s_phys[kMaxRoundSubs];
     __shared__ int32_t s_rows[kMaxRoundSubs];  // first row << 8 | row count
     __shared__ int32_t s_total;
+    __shared__ int32_t s_run;   // positions covered by the rounds so far (see below)
+    __shared__ int32_t s_last;  // split mode: this work-group arrived last
 
     const int item = blockIdx.x;
-    const int g = item % a.num_kv_heads;
-    const int s = item / a.num_kv_heads;
+    const int parts = SPLIT ? a.parts_per_item : 1;
+    const int px0 = item % parts;
+    const int rest = item / parts;
+    const int g = rest % a.num_kv_heads;
+    const int s = rest / a.num_kv_heads;
     const int G = a.num_q_heads / a.num_kv_heads;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -832,6 +845,34 @@ void slotted_mfma_kernel(DecodeArgs a)
     const int nseg = min(max(a.num_segments[s], 0), a.max_segments);  // never past the row
     uint16_t *vlds = sm.v[w];
     uint16_t *klds = vlds + kSub * kVStride;
+    const int64_t row0 = (int64_t)s * a.num_q_heads + (int64_t)g * G;
+
+    // a segment never reaches outside its block, whatever the caller passed
+    auto clamped = [&](int i, int32_t &blk, int &off, int &len) {
+        blk = segs[3 * i];
+        off = min(max(segs[3 * i + 1], 0), BS);
+        len = min(max(segs[3 * i + 2], 0), BS - off);
+    };
+
+    // split mode: the sequence length n (the clamped lengths' sum, every wave)
+    int n = 0;
+    if constexpr (SPLIT) {
+        for (int base = 0; base < nseg; base += kSegRound) {
+            int32_t blk;
+            int off, len = 0;
+            if (base + lane < nseg)
+                clamped(base + lane, blk, off, len);
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1)
+                len += __shfl_xor(len, d, 64);
+            n += len;
+        }
+        n = __builtin_amdgcn_readfirstlane(n);
+    }
+    const int P = SPLIT ? a.partition_size : 0;
+    const int np = SPLIT ? (n + P - 1) / P : 1;
+    const bool direct = !SPLIT || np <= 1;
+    const int np_loop = direct ? (px0 == 0 ? 1 : 0) : np;
 
     u32x4 qop[4];
     {
@@ -842,112 +883,167 @@ void slotted_mfma_kernel(DecodeArgs a)
         for (int kk = 0; kk < 4; ++kk)
             qop[kk] = col < G ? *(const u32x4 *)(qrow + kk * 32) : (u32x4){0u, 0u, 0u, 0u};
     }
-    GqaState st;
-    st.m = kNegInf;
-    st.l = 0.f;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj)
-        st.acc[jj] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    for (int base = 0; base < nseg; base += kSegRound) {
-        if (w == 0) {
-            const int i = base + lane;
-            int32_t blk = 0, off = 0, len = 0;
-            if (i < nseg) {
-                blk = segs[3 * i];
-                // a segment never reaches outside its block, whatever the caller passed
-                off = min(max(segs[3 * i + 1], 0), BS);
-                len = min(max(segs[3 * i + 2], 0), BS - off);
-            }
-            const int c = (len + kSub - 1) / kSub;
-            int incl = c;  // inclusive prefix sum over the wave
+    for (int px = px0; px < np_loop; px += parts) {
+        // positions [t0, t1) of this partition (the whole sequence in one pass)
+        const int t0 = direct ? 0 : px * P;
+        const int t1 = direct ? INT32_MAX : min(n, t0 + P);
+        GqaState st;
+        st.m = kNegInf;
+        st.l = 0.f;
 #pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const int up = __shfl_up(incl, d, 64);
-                if (lane >= d)
-                    incl += up;
+        for (int jj = 0; jj < 8; ++jj)
+            st.acc[jj] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        if (px != px0)
+            __syncthreads();  // the previous partition's merge is done with LDS
+
+        // `run` (positions covered by the earlier rounds) is the same register
+        // value in every wave: wave 0 publishes the next one in s_run before the
+        // round's first barrier, and every wave reads it back after that barrier
+        // (s_run is rewritten only after the round's second barrier)
+        int run = 0;
+        for (int base = 0; base < nseg && run < t1; base += kSegRound) {
+            if (w == 0) {
+                const int i = base + lane;
+                int32_t blk = 0;
+                int off = 0, len = 0;
+                if (i < nseg)
+                    clamped(i, blk, off, len);
+                // running start of this segment among the sequence's positions
+                int incl_len = len;
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const int up = __shfl_up(incl_len, d, 64);
+                    if (lane >= d)
+                        incl_len += up;
+                }
+                const int start = run + incl_len - len;
+                // the part of the segment inside [t0, t1)
+                const int lo = max(start, t0), hi = min(start + len, t1);
+                const int rows = max(hi - lo, 0);
+                const int first = off + (lo - start);
+                const int c = (rows + kSub - 1) / kSub;
+                int incl = c;  // inclusive prefix sum over the wave
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const int up = __shfl_up(incl, d, 64);
+                    if (lane >= d)
+                        incl += up;
+                }
+                for (int k = 0; k < c; ++k) {
+                    s_phys[incl - c + k] = blk;
+                    s_rows[incl - c + k] = ((first + kSub * k) << 8) | min(kSub, rows - kSub * k);
+                }
+                if (lane == 63) {
+                    s_total = incl;
+                    s_run = run + incl_len;
+                }
             }
-            for (int k = 0; k < c; ++k) {
-                s_phys[incl - c + k] = blk;
-                s_rows[incl - c + k] = ((off + kSub * k) << 8) | min(kSub, len - kSub * k);
+            __syncthreads();
+            const int total = s_total;
+            run = __builtin_amdgcn_readfirstlane(s_run);
+            const int T = total > w ? (total - w + WAVES - 1) / WAVES : 0;
+            if (T > 0) {
+                int j = w;
+                KOp K;
+                VRows V;
+                {
+                    const SubRsrc r = slot_rsrc(s_phys, s_rows, j, kp, vp, head_off, blk_elems);
+                    load_k(K, r.k, lane);
+                    load_v(V, r.v, lane);
+                }
+                u32x2 pb;
+                float alpha;
+                bool rs;
+                for (int it = 0; it + 1 < T; ++it) {
+                    const int cnt = __builtin_amdgcn_readfirstlane(s_rows[j]) & 0xff;
+                    const SubRsrc rn =
+                        slot_rsrc(s_phys, s_rows, j + WAVES, kp, vp, head_off, blk_elems);
+                    const KOp KA = k_operand(K, klds, lane);
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_k(K, rn.k, lane);
+                    __builtin_amdgcn_sched_barrier(0);
+                    rs = qk_softmax<DT, true>(st, KA, qop, 0, 0, cnt, lane, a.scale_log2, pb,
+                                              alpha);
+                    __builtin_amdgcn_sched_barrier(0);
+                    stage_v(V, vlds, lane);
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_v(V, rn.v, lane);
+                    __builtin_amdgcn_sched_barrier(0);
+                    pv_mma<DT>(st, vlds, pb, rs, alpha, lane);
+                    __builtin_amdgcn_sched_barrier(0);
+                    j += WAVES;
+                }
+                const int cnt = __builtin_amdgcn_readfirstlane(s_rows[j]) & 0xff;
+                const KOp KA = k_operand(K, klds, lane);
+                rs = qk_softmax<DT, true>(st, KA, qop, 0, 0, cnt, lane, a.scale_log2, pb, alpha);
+                stage_v(V, vlds, lane);
+                pv_mma<DT>(st, vlds, pb, rs, alpha, lane);
             }
-            if (lane == 63)
-                s_total = incl;
+            __syncthreads();  // the descriptors of this round are no longer read
+        }
+        st.l = pair_sum32(pair_sum16(st.l));
+
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+            *(f32x4 *)&sm.o[w][col][16 * jj + 4 * grp] = st.acc[jj];
+        if (grp == 0) {
+            s_m[w][col] = st.m;
+            s_l[w][col] = st.l;
         }
         __syncthreads();
-        const int total = s_total;
-        const int T = total > w ? (total - w + WAVES - 1) / WAVES : 0;
-        if (T > 0) {
-            int j = w;
-            KOp K;
-            VRows V;
-            {
-                const SubRsrc r = slot_rsrc(s_phys, s_rows, j, kp, vp, head_off, blk_elems);
-                load_k(K, r.k, lane);
-                load_v(V, r.v, lane);
+        for (int e = tid; e < G * 32; e += WAVES * 64) {
+            const int qi = e >> 5, d0 = (e & 31) * 4;
+            float M = s_m[0][qi];
+#pragma unroll
+            for (int i = 1; i < WAVES; ++i)
+                M = fmaxf(M, s_m[i][qi]);
+            const float ref = safe_ref(M);
+            float L = 0.f;
+            f32x4 O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < WAVES; ++i) {
+                const float wgt = fexp2(s_m[i][qi] - ref);
+                L += s_l[i][qi] * wgt;
+                O += *(const f32x4 *)&sm.o[i][qi][d0] * wgt;
             }
-            u32x2 pb;
-            float alpha;
-            bool rs;
-            for (int it = 0; it + 1 < T; ++it) {
-                const int cnt = __builtin_amdgcn_readfirstlane(s_rows[j]) & 0xff;
-                const SubRsrc rn =
-                    slot_rsrc(s_phys, s_rows, j + WAVES, kp, vp, head_off, blk_elems);
-                const KOp KA = k_operand(K, klds, lane);
-                __builtin_amdgcn_sched_barrier(0);
-                load_k(K, rn.k, lane);
-                __builtin_amdgcn_sched_barrier(0);
-                rs = qk_softmax<DT, true>(st, KA, qop, 0, 0, cnt, lane, a.scale_log2, pb, alpha);
-                __builtin_amdgcn_sched_barrier(0);
-                stage_v(V, vlds, lane);
-                __builtin_amdgcn_sched_barrier(0);
-                load_v(V, rn.v, lane);
-                __builtin_amdgcn_sched_barrier(0);
-                pv_mma<DT>(st, vlds, pb, rs, alpha, lane);
-                __builtin_amdgcn_sched_barrier(0);
-                j += WAVES;
+            const int64_t row = row0 + qi;
+            if (direct) {
+                f32x4 o = {0.f, 0.f, 0.f, 0.f};
+                if (L > 0.f)
+                    o = O / L;
+                u32x2 packed;
+                packed.x = (uint32_t)to_bits<DT>(o[0]) | ((uint32_t)to_bits<DT>(o[1]) << 16);
+                packed.y = (uint32_t)to_bits<DT>(o[2]) | ((uint32_t)to_bits<DT>(o[3]) << 16);
+                *(u32x2 *)((uint16_t *)a.out + row * kHeadDim + d0) = packed;
+            } else {
+                // read by another work-group of the item (see arrive_last)
+                const Workspace ws = workspace_rsrc(a, (int64_t)a.num_seqs * a.num_q_heads);
+                st_ws4(ws.o, (int)((row * a.max_partitions + px) * kHeadDim + d0) * 4, O / L);
+                if (d0 == 0)
+                    st_ws1(ws.lse, (int)(row * a.max_partitions + px) * 4,
+                           (ref + flog2(L)) * kLn2);
             }
-            const int cnt = __builtin_amdgcn_readfirstlane(s_rows[j]) & 0xff;
-            const KOp KA = k_operand(K, klds, lane);
-            rs = qk_softmax<DT, true>(st, KA, qop, 0, 0, cnt, lane, a.scale_log2, pb, alpha);
-            stage_v(V, vlds, lane);
-            pv_mma<DT>(st, vlds, pb, rs, alpha, lane);
         }
-        __syncthreads();  // the descriptors of this round are no longer read
     }
-    st.l = pair_sum32(pair_sum16(st.l));
 
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj)
-        *(f32x4 *)&sm.o[w][col][16 * jj + 4 * grp] = st.acc[jj];
-    if (grp == 0) {
-        s_m[w][col] = st.m;
-        s_l[w][col] = st.l;
-    }
-    __syncthreads();
-    const int64_t row0 = (int64_t)s * a.num_q_heads + (int64_t)g * G;
-    for (int e = tid; e < G * 32; e += WAVES * 64) {
-        const int qi = e >> 5, d0 = (e & 31) * 4;
-        float M = s_m[0][qi];
-#pragma unroll
-        for (int i = 1; i < WAVES; ++i)
-            M = fmaxf(M, s_m[i][qi]);
-        const float ref = safe_ref(M);
-        float L = 0.f;
-        f32x4 O = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < WAVES; ++i) {
-            const float wgt = fexp2(s_m[i][qi] - ref);
-            L += s_l[i][qi] * wgt;
-            O += *(const f32x4 *)&sm.o[i][qi][d0] * wgt;
+    if constexpr (SPLIT) {
+        // the work-groups that wrote partials arrive; the last one merges them
+        if (direct || px0 >= np)
+            return;
+        if (!arrive_last(a.counters + rest, min(np, parts), &s_last))
+            return;
+        const Workspace ws = workspace_rsrc(a, (int64_t)a.num_seqs * a.num_q_heads);
+        for (int e = tid; e < G * 32; e += WAVES * 64) {
+            const int qi = e >> 5, d0 = (e & 31) * 4;
+            const int64_t row = row0 + qi;
+            const f32x4 o = merge_partials4(ws, (int)(row * a.max_partitions) * 4,
+                                            (int)(row * a.max_partitions * kHeadDim + d0) * 4, np);
+            u32x2 packed;
+            packed.x = (uint32_t)to_bits<DT>(o[0]) | ((uint32_t)to_bits<DT>(o[1]) << 16);
+            packed.y = (uint32_t)to_bits<DT>(o[2]) | ((uint32_t)to_bits<DT>(o[3]) << 16);
+            *(u32x2 *)((uint16_t *)a.out + row * kHeadDim + d0) = packed;
         }
-        f32x4 o = {0.f, 0.f, 0.f, 0.f};
-        if (L > 0.f)
-            o = O / L;
-        u32x2 packed;
-        packed.x = (uint32_t)to_bits<DT>(o[0]) | ((uint32_t)to_bits<DT>(o[1]) << 16);
-        packed.y = (uint32_t)to_bits<DT>(o[2]) | ((uint32_t)to_bits<DT>(o[3]) << 16);
-        *(u32x2 *)((uint16_t *)a.out + (row0 + qi) * kHeadDim + d0) = packed;
     }
 }
 
@@ -1778,8 +1874,12 @@ template <int DT, int BS>
 static hipError_t launch_slotted_t(const DecodeArgs &a, hipStream_t stream)
 {
     constexpr int W = PKV_MFMA_WAVES;
-    hipLaunchKernelGGL((slotted_mfma_kernel<DT, BS, W>), dim3(a.n_items), dim3(W * 64), 0, stream,
-                       a);
+    if (a.partition_size > 0)
+        hipLaunchKernelGGL((slotted_mfma_kernel<DT, BS, W, true>), dim3(a.n_items), dim3(W * 64),
+                           0, stream, a);
+    else
+        hipLaunchKernelGGL((slotted_mfma_kernel<DT, BS, W>), dim3(a.n_items), dim3(W * 64), 0,
+                           stream, a);
     return hipGetLastError();
 }
 

@@ -42,6 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
             "paged_attention_prefix_decode", "paged_attention_decode_slotted",
             "paged_attention_reduce", "paged_attention_split_decode",
             "paged_attention_split_decode_noalloc", "paged_kv_copy_slots",
+            "paged_attention_decode_slotted_split",
             "pkv_status_string", "pkv_max_partitions"} <= set(declared)
     assert pkv.exported_symbols() == declared
 
@@ -255,6 +256,26 @@ def test_slotted_argument_errors(lib):
     assert call(dt=2) == ENOTSUP
     assert call(scale=float("inf")) == EINVAL
     assert call(sg=P((1 << 20) + 2)) == EINVAL
+    assert call(S=0) == 0
+
+
+@host_only
+def test_slotted_split_argument_errors(lib):
+    f = lib.paged_attention_decode_slotted_split
+
+    def call(out=A, sg=A, ns=A, S=2, Hq=12, Hkv=2, B=16, MS=4, NB=64, P_=32, MP=2, po=A, pl=A,
+             ctr=A, dt=0):
+        return f(out, A, A, A, sg, ns, S, Hq, Hkv, 128, B, MS, NB, 0.088, P_, MP, po, pl, ctr,
+                 dt, None)
+
+    assert call(P_=0) == EINVAL
+    assert call(P_=24) == EINVAL              # not a multiple of 16
+    assert call(ctr=None) == EINVAL
+    assert call(out=None) == EINVAL
+    assert call(MP=1) == EWORKSPACE           # 4 segments x 16 positions need 2 partitions of 32
+    assert call(po=None) == EWORKSPACE
+    assert call(Hq=34) == ENOTSUP
+    assert call(ctr=P((1 << 20) + 2)) == EINVAL
     assert call(S=0) == 0
 
 

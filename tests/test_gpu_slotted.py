@@ -38,11 +38,34 @@ def _pools_both(runs, NB, Hkv, B, dtype):
 
 @pytest.fixture(params=["tiles", "per_sequence"])
 def mode(request, monkeypatch):
-    """Both kernels: tiles of sequences (the default wherever a tile's sub-tile
-    list fits in LDS) and one work-group per sequence (PKV_SLOTTED_TILES=0)."""
-    if request.param == "per_sequence":
-        monkeypatch.setenv("PKV_SLOTTED_TILES", "0")
+    """Both kernels: tiles of sequences (PKV_SLOTTED_TILES=1: taken whenever a
+    tile's sub-tile list fits in LDS) and one work-group per sequence
+    (PKV_SLOTTED_TILES=0)."""
+    monkeypatch.setenv("PKV_SLOTTED_TILES", "1" if request.param == "tiles" else "0")
     return request.param
+
+
+def tile_list_fits(Hq, Hkv, B, max_segments):
+    """The header's rule for the tiled kernel: 2 * floor(16 / G) sequences per
+    tile, each with up to max_segments * ceil(B / 16) sub-tiles, within 1,024."""
+    return 2 * (16 // (Hq // Hkv)) * max_segments * (-(-B // 16)) <= 1024
+
+
+def _gpu_split(q, gk, gv, segs, nsegs, dtype, scale, P, B):
+    """paged_attention_decode_slotted_split with a NaN-filled workspace; returns the
+    widened output and the arrival counters."""
+    S, Hq, _ = q.shape
+    Hkv = gk.shape[1]
+    mp = -(-segs.shape[1] * B // P)
+    out = torch.empty((S, Hq, 128), dtype=TDT[dtype], device=DEV)
+    out.view(torch.int16).fill_(0x5555)
+    po = torch.full((S, Hq, mp, 128), float("nan"), dtype=torch.float32, device=DEV)
+    pl = torch.full((S, Hq, mp), float("nan"), dtype=torch.float32, device=DEV)
+    ctr = torch.zeros((S, Hkv), dtype=torch.int32, device=DEV)
+    pkv.paged_attention_decode_slotted_split(out, to_dev(q, dtype, DEV), gk, gv, i32(segs, DEV),
+                                             i32(nsegs, DEV), P, po, pl, ctr, scale=scale)
+    torch.cuda.synchronize()
+    return widen_out(out), ctr
 
 
 def _gpu(q, gk, gv, segs, nsegs, dtype, scale):
@@ -134,7 +157,7 @@ NODE_CASES = [
     (3, 4, 16, 16, 32, "fp16", 70, 5),       # G 1 on the matrix-core path
     (4, 3, 32, 2, 64, "bf16", 150, 4),       # G 16
     (5, 4, 12, 4, 128, "fp16", 300, 3),      # G 3
-    (6, 3, 16, 8, 256, "bf16", 600, 3),      # G 2, the largest block
+    (6, 3, 16, 8, 256, "bf16", 250, 4),      # G 2, the largest block (a full tile list)
     (7, 3, 12, 2, 16, "fp16", 3, 150),       # ~150 short segments: three rounds of 64
 ]
 
@@ -160,6 +183,8 @@ def test_random_node_lists(case, mode):
     c = _node_case(seed, S, Hq, Hkv, B, dtype, hi, per, trunks=seed >= 11)
     print(f"[gpu] slotted ({mode}) seed={seed} S={S} Hq={Hq} Hkv={Hkv} B={B} {dtype} "
           f"max_segments={c['segs'].shape[1]}", flush=True)
+    # every case labelled "tiles" really runs the tiled kernel
+    assert mode != "tiles" or tile_list_fits(Hq, Hkv, B, c["segs"].shape[1])
     kp, vp, gk, gv = _pools_both(c["runs"], c["NB"], Hkv, B, dtype)
     scale = scale_for(128)
     ref = O.attention_slotted(c["q"], kp, vp, c["segs"], c["nsegs"], Hkv, B, c["NB"], scale,
@@ -168,6 +193,12 @@ def test_random_node_lists(case, mode):
     ok, err, nbad = tol_ok(got, ref)
     assert ok, (err, nbad)
     assert (got[-1 if seed >= 11 else 0] == 0).all()  # the empty sequence
+    # split mode (per-sequence kernel, partitions of 32 positions merged in the
+    # launch): segments straddle partition boundaries
+    got2, ctr = _gpu_split(c["q"], gk, gv, c["segs"], c["nsegs"], dtype, scale, 32, B)
+    ok, err, nbad = tol_ok(got2, ref)
+    assert ok, ("split", err, nbad)
+    assert not bool(ctr.any())
 
 
 def test_segment_counts_are_clamped_to_the_row(mode):
@@ -190,24 +221,109 @@ def test_segment_counts_are_clamped_to_the_row(mode):
     assert (got[2::5] == 0).all()
 
 
-@pytest.mark.parametrize("key", ["c1a", "c2", "c4"])
-def test_block_tables_as_segments(key):
-    """A block table as whole-block segments (plus the partly filled last block)
-    gives the oracle's ordinary attention."""
-    w = make_workload(get_config(key))
+_table_cache = {}
+
+
+def _tables_as_segments(key):
+    """A workload's block tables written as whole-block segments (plus the partly
+    filled last block), with the oracle's result (computed once per module)."""
+    if key not in _table_cache:
+        w = make_workload(get_config(key))
+        c = w.cfg
+        r = O.run_step(w, scale_for(c.head_dim))
+        B = c.block_size
+        nb = -(-w.lengths.astype(np.int64) // B)
+        segs = np.zeros((c.num_seqs, int(nb.max()), 3), np.int32)
+        for s in range(c.num_seqs):
+            for j in range(nb[s]):
+                segs[s, j] = (w.tables[s, j], 0, min(B, int(w.lengths[s]) - j * B))
+        _table_cache[key] = (w, r, segs, nb.astype(np.int32))
+    return _table_cache[key]
+
+
+# c4's tile list (8 sequences x 128 segments x 8 sub-tiles) does not fit: one
+# work-group per sequence only
+@pytest.mark.parametrize("key,mode", [("c1a", "tiles"), ("c1a", "per_sequence"),
+                                      ("c2", "tiles"), ("c2", "per_sequence"),
+                                      ("c4", "per_sequence")], indirect=["mode"])
+def test_block_tables_as_segments(key, mode):
+    """A block table as segments gives the oracle's ordinary attention."""
+    w, r, segs, nsegs = _tables_as_segments(key)
     c = w.cfg
-    print(f"[gpu] slotted from tables {key}", flush=True)
-    r = O.run_step(w, scale_for(c.head_dim))
-    B = c.block_size
-    nb = -(-w.lengths.astype(np.int64) // B)
-    segs = np.zeros((c.num_seqs, int(nb.max()), 3), np.int32)
-    for s in range(c.num_seqs):
-        for j in range(nb[s]):
-            segs[s, j] = (w.tables[s, j], 0, min(B, int(w.lengths[s]) - j * B))
+    print(f"[gpu] slotted from tables {key} ({mode})", flush=True)
+    assert mode != "tiles" or tile_list_fits(c.num_q_heads, c.num_kv_heads, c.block_size,
+                                             segs.shape[1])
     gk, gv = to_dev(r["k_pool"], c.dtype, DEV), to_dev(r["v_pool"], c.dtype, DEV)
-    got = _gpu(w.q, gk, gv, segs, nb.astype(np.int32), c.dtype, scale_for(c.head_dim))
+    got = _gpu(w.q, gk, gv, segs, nsegs, c.dtype, scale_for(c.head_dim))
     ok, err, nbad = tol_ok(got, r["out"])
     assert ok, (err, nbad)
+
+
+@pytest.mark.parametrize("key,P", [("c1a", 32), ("c2", 256), ("c2", 512), ("c4", 1024),
+                                   ("c4", 2048)])
+def test_block_tables_as_segments_split(key, P):
+    """Split mode on block tables written as segments: the oracle's attention, the
+    counters back at zero, and a second call on them giving the same bits."""
+    w, r, segs, nsegs = _tables_as_segments(key)
+    c = w.cfg
+    print(f"[gpu] slotted split from tables {key} P={P}", flush=True)
+    gk, gv = to_dev(r["k_pool"], c.dtype, DEV), to_dev(r["v_pool"], c.dtype, DEV)
+    got, ctr = _gpu_split(w.q, gk, gv, segs, nsegs, c.dtype, scale_for(c.head_dim), P,
+                          c.block_size)
+    ok, err, nbad = tol_ok(got, r["out"])
+    assert ok, (err, nbad)
+    assert not bool(ctr.any())
+    got2, _ = _gpu_split(w.q, gk, gv, segs, nsegs, c.dtype, scale_for(c.head_dim), P,
+                         c.block_size)
+    assert np.array_equal(got, got2)
+
+
+def test_long_leaves_split():
+    """A radix batch at the long-context shapes (32 query / 8 KV heads, blocks of
+    128, bf16) whose sequences share a 512-token root and short slotted nodes and
+    then own leaves of 16,000-20,000 tokens: split decode at 2,048 positions per
+    partition against the oracle."""
+    rng = np.random.default_rng(31)
+    S, Hq, Hkv, B, dt = 8, 32, 8, 128, "bf16"
+    lens = [512] + [int(x) for x in rng.integers(3, 40, size=4)] + \
+        [int(x) for x in rng.integers(16000, 20001, size=S)]
+    need = sum(-(-n // B) for n in lens)
+    NB = need + 9
+    free = [int(x) for x in rng.permutation(NB)]
+    node_segs = pack(lens, B, free)
+
+    def draw(*sh):
+        x = rng.standard_normal(sh).astype(np.float32)
+        return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+    node_k = [draw(n, Hkv, 128) for n in lens]
+    node_v = [draw(n, Hkv, 128) for n in lens]
+    paths = [[0, 1 + s % 4, 5 + s] for s in range(S)]
+    MS = max(sum(len(node_segs[i]) for i in p) for p in paths)
+    segs = np.zeros((S, MS, 3), np.int32)
+    nsegs = np.zeros(S, np.int32)
+    for s, p in enumerate(paths):
+        flat = [x for i in p for x in node_segs[i]]
+        segs[s, :len(flat)] = flat
+        nsegs[s] = len(flat)
+    rk, rv, st, tb, cu = [], [], [], [], [0]
+    for segs_i, k, v in zip(node_segs, node_k, node_v):
+        r = 0
+        for blk, off, ln in segs_i:
+            rk.append(k[r:r + ln]); rv.append(v[r:r + ln])
+            st.append(off); tb.append([blk]); cu.append(cu[-1] + ln)
+            r += ln
+    runs = (np.concatenate(rk), np.concatenate(rv), np.array(cu, np.int64),
+            np.array(st, np.int32), np.array(tb, np.int32))
+    print(f"[gpu] slotted split, long leaves: S={S} NB={NB} max_segments={MS}", flush=True)
+    kp, vp, gk, gv = _pools_both(runs, NB, Hkv, B, dt)
+    q = draw(S, Hq, 128)
+    scale = scale_for(128)
+    ref = O.attention_slotted(q, kp, vp, segs, nsegs, Hkv, B, NB, scale, dt)
+    got, ctr = _gpu_split(q, gk, gv, segs, nsegs, dt, scale, 2048, B)
+    ok, err, nbad = tol_ok(got, ref)
+    assert ok, (err, nbad)
+    assert not bool(ctr.any())
 
 
 def test_slotted_debug_check_rejects_bad_segments(monkeypatch):
