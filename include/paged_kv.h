@@ -361,6 +361,41 @@ int paged_attention_prefix_decode(void *out, const void *q, void *k_pool, void *
                                   float *part_lse, int dtype, void *stream);
 
 /*
+ * paged_attention_prefix_split_decode -- the two-pass shared-prefix decode with
+ * its second pass in split-context mode, for members whose own positions are
+ * long.
+ *
+ * Same result as paged_attention_prefix_decode with prefix_partition > 0: pass 1
+ * writes each group's prefix partitions (prefix_partition tokens each) to the
+ * workspace; pass 2 cuts each member's own positions -- from the last multiple
+ * of 16 at or below its prefix length to n-1 -- into partitions of
+ * suffix_partition tokens spread over several work-groups per (sequence, KV
+ * head), keeps their partials after the prefix partials in the same workspace
+ * row, and the last work-group of each (sequence, KV head) merges prefix and
+ * suffix partials as paged_attention_split_decode does (arrival counters; a
+ * suffix of at most one partition is merged by its own work-group).
+ *
+ *   prefix_partition, suffix_partition  > 0, multiples of 16
+ *   max_partitions  row stride of the workspace, at least
+ *                   ceil(ctx / prefix_partition) + ceil(ctx / suffix_partition)
+ *                   with ctx = max_blocks_per_seq * block_size, else
+ *                   PKV_EWORKSPACE; at most 2^31 - 1 bytes of part_o
+ *   counters        device int32 [num_seqs][num_kv_heads], all zero when the call
+ *                   starts and left zero, as for paged_attention_split_decode
+ * Other arguments and the caller contract as for paged_attention_prefix_decode.
+ */
+int paged_attention_prefix_split_decode(void *out, const void *q, void *k_pool, void *v_pool,
+                                        const void *k_new, const void *v_new, int64_t *slot_out,
+                                        const int32_t *block_tables, const int32_t *context_lens,
+                                        const int32_t *group_cu, const int32_t *prefix_lens,
+                                        int num_groups, int num_seqs, int num_q_heads,
+                                        int num_kv_heads, int head_dim, int block_size,
+                                        int max_blocks_per_seq, int64_t num_blocks, float scale,
+                                        int prefix_partition, int suffix_partition,
+                                        int max_partitions, float *part_o, float *part_lse,
+                                        int32_t *counters, int dtype, void *stream);
+
+/*
  * paged_attention_decode_slotted -- decode attention over slotted segments.
  *
  * Radix-tree prefix caches pack short nodes as slots of shared blocks: a node

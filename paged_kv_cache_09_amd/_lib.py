@@ -71,6 +71,10 @@ def load():
                                                 i32, i32, i32, i32, i64, f32, i32, i32, P, P,
                                                 i32, P]
     L.paged_attention_prefix_decode.restype = i32
+    L.paged_attention_prefix_split_decode.argtypes = [P, P, P, P, P, P, P, P, P, P, P, i32, i32,
+                                                      i32, i32, i32, i32, i32, i64, f32, i32,
+                                                      i32, i32, P, P, P, i32, P]
+    L.paged_attention_prefix_split_decode.restype = i32
     L.paged_attention_decode_slotted.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32,
                                                  i64, f32, i32, P]
     L.paged_attention_decode_slotted.restype = i32
@@ -475,6 +479,36 @@ def paged_attention_prefix_decode(out, q, k_pool, v_pool, block_tables, context_
         G, S, Hq, Hkv, D, B, W, NB, scale, int(prefix_partition), mp, _p(part_o),
         _p(part_lse), _dtype_code(q), _stream(dev))
     _check(rc, "paged_attention_prefix_decode")
+
+
+def paged_attention_prefix_split_decode(out, q, k_pool, v_pool, block_tables, context_lens,
+                                        group_cu, prefix_lens, prefix_partition: int,
+                                        suffix_partition: int, part_o, part_lse, counters,
+                                        k_new=None, v_new=None, slot_out=None,
+                                        scale: Optional[float] = None):
+    """Two-pass shared-prefix decode whose second pass splits each member's own
+    positions into partitions merged in the launch (counters: int32 [S][Hkv], zero
+    on entry and left zero)."""
+    NB, Hkv, B, D, S, Hq, W = _queries(out, q, k_pool, v_pool, block_tables, context_lens)
+    G = _dims(prefix_lens, 1, "prefix_lens")[0]
+    _expect(group_cu, (G + 1,), "group_cu")
+    _expect(k_new, (S, Hkv, D), "k_new")
+    _expect(v_new, (S, Hkv, D), "v_new")
+    _same_dtype(k_pool, (k_new, "k_new"), (v_new, "v_new"))
+    _expect(slot_out, (S,), "slot_out")
+    _expect(counters, (S, Hkv), "counters")
+    mp = _workspace(part_o, part_lse, S, Hq, D)
+    dev = _dev(out, q, k_pool, v_pool, block_tables, context_lens, group_cu, prefix_lens,
+               part_o, part_lse, k_new, v_new, slot_out, counters)
+    _ints((block_tables, "i32", "block_tables"), (context_lens, "i32", "context_lens"),
+          (group_cu, "i32", "group_cu"), (prefix_lens, "i32", "prefix_lens"),
+          (slot_out, "i64", "slot_out"), (counters, "i32", "counters"))
+    rc = load().paged_attention_prefix_split_decode(
+        _p(out), _p(q), _p(k_pool), _p(v_pool), _p(k_new), _p(v_new), _p(slot_out),
+        _p(block_tables), _p(context_lens), _p(group_cu), _p(prefix_lens),
+        G, S, Hq, Hkv, D, B, W, NB, _scale(scale), int(prefix_partition), int(suffix_partition),
+        mp, _p(part_o), _p(part_lse), _p(counters), _dtype_code(q), _stream(dev))
+    _check(rc, "paged_attention_prefix_split_decode")
 
 
 def paged_attention_decode_slotted(out, q, k_pool, v_pool, segments, num_segments,

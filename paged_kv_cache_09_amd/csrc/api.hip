@@ -495,6 +495,7 @@ struct PrefixGroups {
     const int32_t *group_cu = nullptr;
     const int32_t *prefix_lens = nullptr;
     int num_groups = 0;
+    int suffix_partition = 0;  // > 0: the suffix pass in split mode (counters required)
 };
 
 // Work-groups per (sequence, KV head) in split mode: enough for about
@@ -539,8 +540,11 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
         return PKV_EINVAL;
     if (k_new && (!aligned16(k_new) || !aligned16(v_new) || ((uintptr_t)slot_out & 7u)))
         return PKV_EINVAL;
-    if (counters && (prefix || partition_size <= 0 || !out || ((uintptr_t)out & 7u) ||
-                     ((uintptr_t)counters & 3u)))
+    if (counters && ((prefix && pg.suffix_partition <= 0) || partition_size <= 0 || !out ||
+                     ((uintptr_t)out & 7u) || ((uintptr_t)counters & 3u)))
+        return PKV_EINVAL;
+    if (prefix && pg.suffix_partition != 0 && (!counters || pg.suffix_partition < 0 ||
+                                                 pg.suffix_partition % 16 != 0))
         return PKV_EINVAL;
     int parts = 1;
     int prefix_part = 0, prefix_parts = 0;
@@ -558,13 +562,24 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
             return PKV_EINVAL;
         if (partition_size > 0) {
             // two passes: prefix partitions into the workspace, then the suffixes
+            // (in split mode their partitions follow the prefix partitions)
             prefix_part = partition_size;
             const int64_t need = (ctx + prefix_part - 1) / prefix_part;
-            if (!part_o || !part_lse || max_partitions < need || need <= 0)
+            const int64_t need_suffix =
+                pg.suffix_partition > 0 ? (ctx + pg.suffix_partition - 1) / pg.suffix_partition
+                                        : 0;
+            if (!part_o || !part_lse || max_partitions < need + need_suffix || need <= 0)
                 return PKV_EWORKSPACE;
             if (!aligned16(part_o) || ((uintptr_t)part_lse & 3u))
                 return PKV_EINVAL;
-            prefix_parts = max_partitions;
+            if (pg.suffix_partition > 0 &&
+                (int64_t)num_seqs * num_q_heads * max_partitions * head_dim * 4 > (int64_t)INT32_MAX)
+                return PKV_EWORKSPACE;
+            prefix_parts = (int)need;
+            if (pg.suffix_partition > 0)
+                parts = split_parts((int64_t)num_seqs * num_kv_heads, (int)need_suffix);
+        } else if (pg.suffix_partition > 0) {
+            return PKV_EINVAL;  // the suffix is split only in the two-pass form
         }
         if (!out || ((uintptr_t)out & 7u))
             return PKV_EINVAL;
@@ -643,7 +658,7 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
         // query heads; pass 2: each sequence's own positions, merged with the
         // prefix partials
         a.partition_size = 0;
-        a.max_partitions = prefix_parts;
+        a.max_partitions = max_partitions;  // the workspace's row stride
         a.group_cu = pg.group_cu;
         a.prefix_lens = pg.prefix_lens;
         a.num_groups = pg.num_groups;
@@ -653,9 +668,15 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
         const int64_t pitems = tiles * num_kv_heads * prefix_parts;
         if (pitems > INT32_MAX)
             return PKV_EINVAL;
+        a.parts_per_item = prefix_parts;  // prefix partitions per (tile, KV head)
         hipError_t e = pkv::launch_prefix_mfma(a, (int)pitems, dtype, block_size, st);
         if (e != hipSuccess)
             return PKV_ELAUNCH;
+        // the suffix pass: one work-group per (sequence, KV head), or `parts` of them
+        // over partitions of the suffix merged in the launch
+        a.parts_per_item = parts;
+        if (pg.suffix_partition > 0)
+            a.partition_size = pg.suffix_partition;
         return launch_status(pkv::launch_decode_mfma(a, dtype, block_size, st));
     }
     const hipError_t e = group == 1 ? pkv::launch_decode_g1(a, dtype, block_size, st)
@@ -845,6 +866,32 @@ int paged_attention_prefix_decode(void *out, const void *q, void *k_pool, void *
                        block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                        block_size, max_blocks_per_seq, num_blocks, scale, prefix_partition,
                        max_partitions, part_o, part_lse, dtype, stream, pg);
+}
+
+int paged_attention_prefix_split_decode(void *out, const void *q, void *k_pool, void *v_pool,
+                                        const void *k_new, const void *v_new, int64_t *slot_out,
+                                        const int32_t *block_tables, const int32_t *context_lens,
+                                        const int32_t *group_cu, const int32_t *prefix_lens,
+                                        int num_groups, int num_seqs, int num_q_heads,
+                                        int num_kv_heads, int head_dim, int block_size,
+                                        int max_blocks_per_seq, int64_t num_blocks, float scale,
+                                        int prefix_partition, int suffix_partition,
+                                        int max_partitions, float *part_o, float *part_lse,
+                                        int32_t *counters, int dtype, void *stream)
+{
+    if (!group_cu || !counters || prefix_partition <= 0 || suffix_partition <= 0)
+        return PKV_EINVAL;
+    if ((k_new == nullptr) != (v_new == nullptr))
+        return PKV_EINVAL;
+    PrefixGroups pg;
+    pg.group_cu = group_cu;
+    pg.prefix_lens = prefix_lens;
+    pg.num_groups = num_groups;
+    pg.suffix_partition = suffix_partition;
+    return decode_impl(out, q, k_pool, v_pool, k_new, v_new, k_new ? slot_out : nullptr,
+                       block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                       block_size, max_blocks_per_seq, num_blocks, scale, prefix_partition,
+                       max_partitions, part_o, part_lse, dtype, stream, pg, counters);
 }
 
 }  // extern "C"

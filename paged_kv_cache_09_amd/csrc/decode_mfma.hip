@@ -273,18 +273,25 @@ constexpr int kModeSuffix = 2;  // shared-prefix mode: positions prefix_len .. n
 constexpr int kModeMerge = 3;   // split mode whose last work-group per item merges the
                                 // partials into `out` (a context of one partition is
                                 // written to `out` directly)
+constexpr int kModeSuffixSplit = 4;  // shared-prefix mode with the positions after the
+                                     // prefix cut into partitions; the last work-group
+                                     // per item merges prefix and suffix partials
 
-// MODE kModeSplit / kModeMerge run a partition loop; the other modes one pass,
-// with the loop folded away at compile time.
+// MODE kModeSplit / kModeMerge / kModeSuffixSplit run a partition loop; the other
+// modes one pass, with the loop folded away at compile time.
 // The register budget is capped so that 4 waves (single pass) or 3 waves (split
 // modes, which keep more state live across their partition loop) fit on each SIMD
 // without spilling.
 template <int DT, int BS, int WAVES, int MODE>
 __global__ __launch_bounds__(WAVES * 64)
-__attribute__((amdgpu_waves_per_eu(MODE == kModeSplit || MODE == kModeMerge ? 3 : 4)))
+__attribute__((amdgpu_waves_per_eu(MODE == kModeSplit || MODE == kModeMerge ||
+                                           MODE == kModeSuffixSplit
+                                       ? 3
+                                       : 4)))
 void decode_mfma_kernel(DecodeArgs a)
 {
-    constexpr bool MERGE = MODE == kModeMerge;
+    constexpr bool SUFFIX = MODE == kModeSuffix || MODE == kModeSuffixSplit;
+    constexpr bool MERGE = MODE == kModeMerge || MODE == kModeSuffixSplit;
     constexpr bool SPLIT = MODE == kModeSplit || MERGE;
     // V staging during the token loop; the cross-wave merge afterwards
     __shared__ __attribute__((aligned(16))) union {
@@ -320,15 +327,17 @@ void decode_mfma_kernel(DecodeArgs a)
     const int64_t head_off = (int64_t)g * BS * kHeadDim;
     const int P = SPLIT ? a.partition_size : 0;
     // shared-prefix mode: this pass covers the positions after the group's prefix
-    const int start = MODE == kModeSuffix
+    const int start = SUFFIX
                           ? as_meta(a.prefix_lens)[group_of(as_meta(a.group_cu), a.num_groups, s)]
                           : 0;
     const int start_sub = start & ~(kSub - 1);  // sub-tiles stay aligned to 16 positions
+    // partitions start at position `base` (the suffix's first sub-tile, or 0)
+    const int base = SUFFIX ? start_sub : 0;
 
     // The first sub-tile's table entry (and the next one's) do not depend on the
     // context length: request them together with it, so the two scalar-load
     // latencies overlap instead of chaining.
-    const int tb_first = (P > 0 ? px0 * P : start_sub) + w * kSub;
+    const int tb_first = base + (P > 0 ? px0 * P : 0) + w * kSub;
     const int32_t e_first = sub_phys<BS>(trow, a.width, tb_first);
     const int32_t e_next = sub_phys<BS>(trow, a.width, tb_first + WAVES * kSub);
     const int n = as_meta(a.lens)[s];
@@ -356,7 +365,7 @@ void decode_mfma_kernel(DecodeArgs a)
     constexpr int kPre = 2;
     f32x4 pre_o[kPre];
     float pre_l[kPre];
-    if (MODE == kModeSuffix) {
+    if (SUFFIX) {
 #pragma unroll
         for (int k = 0; k < kPre; ++k) {
             const int e = tid + k * WAVES * 64;
@@ -374,15 +383,20 @@ void decode_mfma_kernel(DecodeArgs a)
     // Single pass: one iteration over the whole context (zeros when n = 0).
     // Merged split mode: a context of at most one partition is handled like a
     // single pass by the item's first work-group, which writes `out` itself.
-    const int np = SPLIT ? (n + P - 1) / P : 1;
+    // Suffix split mode: the positions base .. n-1 are cut into partitions, whose
+    // partials are kept after the group's prefix partials (index np_pre + p).
+    const int np = SPLIT ? (max(n - base, 0) + P - 1) / P : 1;
     const bool direct = MERGE && np <= 1;
     const int np_loop = direct ? (px0 == 0 ? 1 : 0) : np;
+    const int np_pre = SUFFIX && a.prefix_part > 0
+                           ? min((start + a.prefix_part - 1) / a.prefix_part, a.max_partitions)
+                           : 0;
     for (int px = px0; px < np_loop; px += parts) {
         if (px != px0)
             __syncthreads();  // the previous partition's merge is done with LDS
-        const int t0 = P > 0 ? px * P : start_sub;
+        const int t0 = P > 0 ? base + px * P : start_sub;
         const int t1 = P > 0 ? min(n, t0 + P) : n;
-        const int t_beg = MODE == kModeSuffix ? start : t0;  // positions below are masked
+        const int t_beg = SUFFIX ? start : t0;  // positions below are masked
         // With a fused append, position n-1 (in the item's last sub-tile) is not
         // read from the pool: it holds stale data until this kernel writes it.
         const bool owns_new = fused && t1 == n;
@@ -466,8 +480,8 @@ void decode_mfma_kernel(DecodeArgs a)
                 __builtin_amdgcn_sched_barrier(0);
                 load_k(K, rn.k, lane);  // the raw registers are free once staged
                 __builtin_amdgcn_sched_barrier(0);
-                rs = qk_softmax<DT, MODE == kModeSuffix>(st, KA, qop, tb, t_beg, t1, lane,
-                                                         a.scale_log2, pb, alpha);
+                rs = qk_softmax<DT, SUFFIX>(st, KA, qop, tb, t_beg, t1, lane, a.scale_log2, pb,
+                                            alpha);
                 __builtin_amdgcn_sched_barrier(0);
                 stage_v(V, vlds, lane);
                 __builtin_amdgcn_sched_barrier(0);
@@ -490,8 +504,8 @@ void decode_mfma_kernel(DecodeArgs a)
                     KA.k[kk] = s_new[0][4 * kk + grp];
             }
             if (tb + kSub <= t1)
-                rs = qk_softmax<DT, MODE == kModeSuffix>(st, KA, qop, tb, t_beg, t1, lane,
-                                                         a.scale_log2, pb, alpha);
+                rs = qk_softmax<DT, SUFFIX>(st, KA, qop, tb, t_beg, t1, lane, a.scale_log2, pb,
+                                            alpha);
             else
                 rs = qk_softmax<DT, true>(st, KA, qop, tb, t_beg, t1, lane, a.scale_log2, pb,
                                           alpha);
@@ -533,10 +547,8 @@ void decode_mfma_kernel(DecodeArgs a)
             const int64_t row = row0 + qi;
             if (MODE == kModeSuffix || P == 0 || direct) {
                 f32x4 o = {0.f, 0.f, 0.f, 0.f};
-                if (MODE == kModeSuffix) {
+                if (SUFFIX) {
                     // merge with the prefix partitions (normalised o, natural-log lse)
-                    const int np_pre =
-                        min((start + a.prefix_part - 1) / a.prefix_part, a.max_partitions);
                     const float *lse = a.part_lse + row * a.max_partitions;
                     const float *po = a.part_o + row * a.max_partitions * kHeadDim + d0;
                     float X = L > 0.f ? ref : kNegInf;
@@ -574,11 +586,13 @@ void decode_mfma_kernel(DecodeArgs a)
                 const f32x4 ov = O / L;
                 const float lse = (ref + flog2(L)) * kLn2;
                 if constexpr (MERGE) {
-                    // read by another work-group of the item (see arrive_last)
+                    // read by another work-group of the item (see arrive_last); suffix
+                    // partitions follow the prefix partitions
                     const Workspace ws = workspace_rsrc(a, (int64_t)a.num_seqs * a.num_q_heads);
-                    st_ws4(ws.o, (int)((row * a.max_partitions + px) * kHeadDim + d0) * 4, ov);
+                    const int pi = np_pre + px;
+                    st_ws4(ws.o, (int)((row * a.max_partitions + pi) * kHeadDim + d0) * 4, ov);
                     if (d0 == 0)
-                        st_ws1(ws.lse, (int)(row * a.max_partitions + px) * 4, lse);
+                        st_ws1(ws.lse, (int)(row * a.max_partitions + pi) * 4, lse);
                 } else {
                     *(f32x4 *)po = ov;
                     if (d0 == 0)
@@ -599,7 +613,8 @@ void decode_mfma_kernel(DecodeArgs a)
             const int qi = e >> 5, d0 = (e & 31) * 4;
             const int64_t row = row0 + qi;
             const f32x4 o = merge_partials4(ws, (int)(row * a.max_partitions) * 4,
-                                            (int)(row * a.max_partitions * kHeadDim + d0) * 4, np);
+                                            (int)(row * a.max_partitions * kHeadDim + d0) * 4,
+                                            np_pre + np);
             u32x2 packed;
             packed.x = (uint32_t)to_bits<DT>(o[0]) | ((uint32_t)to_bits<DT>(o[1]) << 16);
             packed.y = (uint32_t)to_bits<DT>(o[2]) | ((uint32_t)to_bits<DT>(o[3]) << 16);
@@ -637,9 +652,10 @@ void prefix_mfma_kernel(DecodeArgs a)
     __shared__ float s_m[WAVES][16], s_l[WAVES][16];
     __shared__ int64_t s_row[16];  // output row of each query column, -1 if inactive
 
-    // items: (tile, KV head, partition), partition fastest, then KV head
+    // items: (tile, KV head, partition), partition fastest, then KV head; the
+    // partials' row stride is max_partitions
     const int item = blockIdx.x;
-    const int npp = a.max_partitions;
+    const int npp = a.parts_per_item;
     const int pp = item % npp;
     const int g = (item / npp) % a.num_kv_heads;
     const int tile = item / (npp * a.num_kv_heads);
@@ -1799,7 +1815,10 @@ static hipError_t launch_mfma_t(const DecodeArgs &a, hipStream_t stream)
 {
     constexpr int W = PKV_MFMA_WAVES;
     constexpr int WS = PKV_SUFFIX_WAVES;
-    if (a.group_cu)
+    if (a.group_cu && a.counters)
+        hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, WS, kModeSuffixSplit>), dim3(a.n_items),
+                           dim3(WS * 64), 0, stream, a);
+    else if (a.group_cu)
         hipLaunchKernelGGL((decode_mfma_kernel<DT, BS, WS, kModeSuffix>), dim3(a.n_items),
                            dim3(WS * 64), 0, stream, a);
     else if (a.partition_size > 0 && a.counters)

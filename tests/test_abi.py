@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
             "paged_attention_prefix_decode", "paged_attention_decode_slotted",
             "paged_attention_reduce", "paged_attention_split_decode",
             "paged_attention_split_decode_noalloc", "paged_kv_copy_slots",
-            "paged_attention_decode_slotted_split",
+            "paged_attention_decode_slotted_split", "paged_attention_prefix_split_decode",
             "pkv_status_string", "pkv_max_partitions"} <= set(declared)
     assert pkv.exported_symbols() == declared
 
@@ -237,6 +237,26 @@ def test_prefix_decode_argument_errors(lib):
     assert call(B=8) == ENOTSUP
     assert call(cu=P((1 << 20) + 2)) == EINVAL  # misaligned group offsets
     assert call(S=0, G=1) == 0                  # nothing to do
+
+
+@host_only
+def test_prefix_split_decode_argument_errors(lib):
+    f = lib.paged_attention_prefix_split_decode
+
+    def call(out=A, cu=A, pl=A, G=1, S=2, Hq=12, Hkv=2, B=16, W=5, PP=16, SP=16, MP=10, po=A,
+             plse=A, ctr=A, dt=0):
+        return f(out, A, A, A, None, None, None, A, A, cu, pl, G, S, Hq, Hkv, 128, B, W, 64,
+                 0.088, PP, SP, MP, po, plse, ctr, dt, None)
+
+    assert call(ctr=None) == EINVAL
+    assert call(cu=None) == EINVAL
+    assert call(PP=0) == EINVAL               # the suffix is split only in the two-pass form
+    assert call(SP=0) == EINVAL
+    assert call(SP=24) == EINVAL              # not a multiple of 16
+    assert call(MP=9) == EWORKSPACE           # 80 positions: 5 prefix + 5 suffix partitions
+    assert call(out=None) == EINVAL
+    assert call(Hq=34) == ENOTSUP
+    assert call(S=0, G=1) == 0
 
 
 @host_only

@@ -27,23 +27,34 @@ SENTINEL = {"fp16": 0x7E00, "bf16": 0x7FC0}
 TDT = {"fp16": torch.float16, "bf16": torch.bfloat16}
 
 
-def _workspace(S, Hq, ctx, P):
-    mp = 1 if P == 0 else -(-ctx // P)
+def _workspace(S, Hq, ctx, P, SP=0):
+    mp = 1 if P == 0 else -(-ctx // P) + (-(-ctx // SP) if SP else 0)
     po = torch.full((S, Hq, mp, 128), float("nan"), dtype=torch.float32, device=DEV)
     pl = torch.full((S, Hq, mp), float("nan"), dtype=torch.float32, device=DEV)
     return po, pl
 
 
-def _run(g_or_pools, q, tables, lens, group_cu, prefix_lens, dtype, P=0, new=None, slots=None):
+def _run(g_or_pools, q, tables, lens, group_cu, prefix_lens, dtype, P=0, new=None, slots=None,
+         SP=0):
+    """paged_attention_prefix_decode, or with SP > 0 paged_attention_prefix_split_decode
+    (suffix partitions of SP positions; the arrival counters must end at zero)."""
     kp, vp = g_or_pools
     S, Hq, _ = q.shape
-    po, pl = _workspace(S, Hq, tables.shape[1] * kp.shape[2], P)
+    po, pl = _workspace(S, Hq, tables.shape[1] * kp.shape[2], P, SP)
     out = torch.empty((S, Hq, 128), dtype=TDT[dtype], device=DEV)
     out.view(torch.int16).fill_(0x5555)
     kn, vn = new if new is not None else (None, None)
-    pkv.paged_attention_prefix_decode(out, q, kp, vp, tables, lens, group_cu, prefix_lens, po, pl,
-                                      k_new=kn, v_new=vn, slot_out=slots,
-                                      scale=scale_for(128), prefix_partition=P)
+    if SP:
+        ctr = torch.zeros((S, kp.shape[1]), dtype=torch.int32, device=DEV)
+        pkv.paged_attention_prefix_split_decode(out, q, kp, vp, tables, lens, group_cu,
+                                                prefix_lens, P, SP, po, pl, ctr, k_new=kn,
+                                                v_new=vn, slot_out=slots, scale=scale_for(128))
+        torch.cuda.synchronize()
+        assert not bool(ctr.any()), "arrival counters not back at zero"
+    else:
+        pkv.paged_attention_prefix_decode(out, q, kp, vp, tables, lens, group_cu, prefix_lens, po,
+                                          pl, k_new=kn, v_new=vn, slot_out=slots,
+                                          scale=scale_for(128), prefix_partition=P)
     torch.cuda.synchronize()
     return out, po, pl
 
@@ -68,18 +79,20 @@ def _max_parts(w, P):
     return -(-(w.cfg.max_blocks_per_seq * w.cfg.block_size) // P)
 
 
-@pytest.mark.parametrize("P", [0, 128, 512])
+@pytest.mark.parametrize("P,SP", [(0, 0), (128, 0), (512, 0), (128, 32), (512, 64)])
 @pytest.mark.parametrize("fused", [False, True])
-def test_c5_prefix_decode_matches_oracle(P, fused):
+def test_c5_prefix_decode_matches_oracle(P, SP, fused):
+    """SP > 0: the suffix pass in split mode (members' own 5-128 positions in
+    partitions of 32 or 64, merged in the launch)."""
     w, r = c5_oracle()
     c = w.cfg
-    print(f"[gpu] prefix decode c5 P={P} fused={fused}", flush=True)
+    print(f"[gpu] prefix decode c5 P={P} SP={SP} fused={fused}", flush=True)
     g = GpuStep(w, append=not fused)
     cu = i32([0, c.num_seqs], DEV)
     plen = i32([c.prefix_tokens], DEV)
     new = (g.k_new, g.v_new) if fused else None
     out, po, pl = _run((g.k_pool, g.v_pool), g.q, g.tables, g.lens, cu, plen, c.dtype, P, new,
-                       g.slots if fused else None)
+                       g.slots if fused else None, SP=SP)
     ok, err, nbad = tol_ok(widen_out(out), r["out"])
     assert ok, (err, nbad)
     if fused:
@@ -169,11 +182,11 @@ GROUPED = [
 
 
 @pytest.mark.parametrize("case", GROUPED, ids=[f"seed{c[0]}" for c in GROUPED])
-@pytest.mark.parametrize("P", [0, 32])
-def test_grouped_prefix_decode(case, P):
+@pytest.mark.parametrize("P,SP", [(0, 0), (32, 0), (32, 16), (48, 32)])
+def test_grouped_prefix_decode(case, P, SP):
     seed, groups, Hq, Hkv, B, dtype = case
     print(f"[gpu] grouped prefix seed={seed} groups={groups} Hq={Hq} Hkv={Hkv} B={B} "
-          f"{dtype} P={P}", flush=True)
+          f"{dtype} P={P} SP={SP}", flush=True)
     c = _grouped_case(seed, groups, Hq, Hkv, B, dtype)
     kp_pre, vp_pre = c["kp"].copy(), c["vp"].copy()
     slots_ref = O.append(c["kp"], c["vp"], c["kn"], c["vn"], c["tables"], c["lens"], B, c["NB"])
@@ -183,16 +196,39 @@ def test_grouped_prefix_decode(case, P):
             i32(c["cu"], DEV), i32(c["plens"], DEV))
     # pools already holding the new token
     gk, gv = to_dev(c["kp"], dtype, DEV), to_dev(c["vp"], dtype, DEV)
-    out, _, _ = _run((gk, gv), *args, dtype, P)
+    out, _, _ = _run((gk, gv), *args, dtype, P, SP=SP)
     ok, err, nbad = tol_ok(widen_out(out), ref)
     assert ok, ("plain", err, nbad)
     # the fused append
     gk, gv = to_dev(kp_pre, dtype, DEV), to_dev(vp_pre, dtype, DEV)
     slots = torch.full((len(c["lens"]),), -7, dtype=torch.int64, device=DEV)
     out, _, _ = _run((gk, gv), *args, dtype, P,
-                     (to_dev(c["kn"], dtype, DEV), to_dev(c["vn"], dtype, DEV)), slots)
+                     (to_dev(c["kn"], dtype, DEV), to_dev(c["vn"], dtype, DEV)), slots, SP=SP)
     ok, err, nbad = tol_ok(widen_out(out), ref)
     assert ok, ("fused", err, nbad)
+    assert np.array_equal(slots.cpu().numpy(), slots_ref)
+    assert np.array_equal(bits_of(gk), c["kp"]) and np.array_equal(bits_of(gv), c["vp"])
+
+
+def test_long_suffixes_split():
+    """Members with 1-20,000 own positions after a 2,048-token prefix at the
+    long-context shapes (32 query / 8 KV heads, blocks of 128, bf16): prefix
+    partitions of 512, suffix partitions of 2,048, fused append; pools bit-exact,
+    output against the oracle."""
+    c = _grouped_case(41, [(6, 2048), (2, 300)], 32, 8, 128, "bf16", max_own=20000)
+    print(f"[gpu] prefix split, long suffixes: lens={c['lens'].tolist()}", flush=True)
+    dtype, B, Hkv = "bf16", 128, 8
+    kp_pre, vp_pre = c["kp"].copy(), c["vp"].copy()
+    slots_ref = O.append(c["kp"], c["vp"], c["kn"], c["vn"], c["tables"], c["lens"], B, c["NB"])
+    ref = O.attention(c["q"], c["kp"], c["vp"], c["tables"], c["lens"], Hkv, B, c["NB"],
+                      scale_for(128), dtype)
+    gk, gv = to_dev(kp_pre, dtype, DEV), to_dev(vp_pre, dtype, DEV)
+    slots = torch.full((len(c["lens"]),), -7, dtype=torch.int64, device=DEV)
+    out, _, _ = _run((gk, gv), to_dev(c["q"], dtype, DEV), i32(c["tables"], DEV),
+                     i32(c["lens"], DEV), i32(c["cu"], DEV), i32(c["plens"], DEV), dtype, 512,
+                     (to_dev(c["kn"], dtype, DEV), to_dev(c["vn"], dtype, DEV)), slots, SP=2048)
+    ok, err, nbad = tol_ok(widen_out(out), ref)
+    assert ok, (err, nbad)
     assert np.array_equal(slots.cpu().numpy(), slots_ref)
     assert np.array_equal(bits_of(gk), c["kp"]) and np.array_equal(bits_of(gv), c["vp"])
 
