@@ -1,7 +1,7 @@
 """Seeded radix-tree batch for slotted-segment decode.
 
-A tree of prompt nodes is laid out in a block pool the way the mhpq.cn page on
-Radix-Tree fragmentation describes its slotted allocator (section "物理内存管理器
+A tree of prompt nodes is laid out in a block pool by the slot-packing rule of the
+mhpq.cn page on Radix-Tree fragmentation (sections "核心设计原则" and "物理内存管理器
 核心逻辑实现"): a node shorter than a block is packed into the first partly filled
 block with enough free slots, at the block's first free offset, else at offset 0
 of the next block taken from the free list; a node of a block or more takes whole
@@ -92,26 +92,37 @@ class SlottedWorkload:
 
 
 def pack(node_lens, block_size: int, free_list: List[int]) -> List[List[Segment]]:
-    """The page's slotted allocation, node by node (see the module docstring)."""
-    free = list(free_list)
-    partial: List[List[int]] = []  # [block id, free slots]
+    """Lay out nodes (lengths >= 1) by the page's slot-packing rule: a node shorter
+    than a block goes into the first slotted block, in the order the blocks were
+    opened, that still has room for it, at that block's first free row; with no
+    such block, the next block of the free list is opened for it (offset 0).  A
+    node of a block or more takes whole blocks of its own from the free list.
+
+    Kept as two arrays over the opened slotted blocks (block id, rows in use), so
+    the first fit is a vectorised search over `used + n <= block_size`; a full
+    block never fits again."""
+    B = block_size
+    take = iter(free_list)  # blocks come from the head of the free list
+    ids = np.zeros(0, np.int64)    # slotted blocks in the order they were opened
+    used = np.zeros(0, np.int64)   # rows in use in each of them
     out: List[List[Segment]] = []
     for n in node_lens:
-        if n >= block_size:
-            nb = -(-n // block_size)
-            ids = [free.pop(0) for _ in range(nb)]
-            out.append([(ids[i], 0, min(block_size, n - i * block_size)) for i in range(nb)])
+        n = int(n)
+        assert n >= 1, "nodes hold at least one token"
+        if n >= B:
+            blocks = [next(take) for _ in range(-(-n // B))]
+            out.append([(int(b), 0, min(B, n - i * B)) for i, b in enumerate(blocks)])
             continue
-        for p in partial:
-            if p[1] >= n:
-                out.append([(p[0], block_size - p[1], n)])
-                p[1] -= n
-                break
+        fit = np.flatnonzero(used + n <= B)
+        if fit.size:
+            j = int(fit[0])
+            out.append([(int(ids[j]), int(used[j]), n)])
+            used[j] += n
         else:
-            b = free.pop(0)
-            out.append([(b, 0, n)])
-            partial.append([b, block_size - n])
-        partial = [p for p in partial if p[1] > 0]
+            b = next(take)
+            ids = np.append(ids, b)
+            used = np.append(used, n)
+            out.append([(int(b), 0, n)])
     return out
 
 
