@@ -97,10 +97,14 @@ def parse():
                          "or the per-sequence kernel (PKV_SLOTTED_TILES)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="approximate CPU time budget of the oracle sample")
+                    help="approximate CPU time budget of the oracle samples of the --op lines "
+                         "(the step's baseline runs exactly one whole step)")
     ap.add_argument("--copy-reference", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM "
                          "counter scaling and copy bandwidth) and print its rate")
+    ap.add_argument("--read-reference", action="store_true",
+                    help="only run the read-only HBM reference (a torch sum over 2 GiB) and "
+                         "print its rate")
     return ap.parse_args()
 
 
@@ -219,14 +223,47 @@ def copy_rate(reps: int = 10) -> dict:
             "gbps_read_plus_write": round(2 * n / ms / 1e6, 1)}
 
 
+def read_rate(reps: int = 10) -> dict:
+    """Read-only HBM reference: torch's row sums of a [131072, 4096] fp32 tensor
+    (2 GiB, 8x the MALL; the 512 KiB of sums written are negligible), timed with
+    HIP events over back-to-back reductions.  A plain library reduction, not a
+    tuned probe: the fastest of the plain torch reads tried on MI355X (a flat
+    sum, amax or matrix-vector product over the same bytes read at 3.5-4.0 TB/s)."""
+    import torch
+    n = 2 << 30
+    x = torch.ones((n // 4 // 4096, 4096), dtype=torch.float32, device="cuda:0")
+    for _ in range(3):
+        x.sum(dim=1)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        x.sum(dim=1)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del x
+    torch.cuda.empty_cache()
+    return {"bytes_read": n, "ms": round(ms, 4), "gbps_read": round(n / ms / 1e6, 1),
+            "method": "torch row sums of a [131072, 4096] fp32 tensor (2 GiB read), mean of "
+                      "%d back-to-back calls" % reps}
+
+
 def copy_reference():
     print(json.dumps({"copy_reference": True, **copy_rate()}))
+
+
+def read_reference():
+    print(json.dumps({"read_reference": True, **read_rate()}))
 
 
 def main():
     args = parse()
     if args.copy_reference:
         copy_reference()
+        return
+    if args.read_reference:
+        read_reference()
         return
     if args.gpus != 1:
         print(json.dumps({"error": "bench.py drives one GPU only; --gpus must be 1",
@@ -264,9 +301,11 @@ def bench_step(args):
     # ---- set-up: R distinct layers of pools, q, new rows (not timed) --------------
     t_setup = time.time()
     layers = []
+    hosts = []  # the R pool sets' host inputs (the CPU baseline runs the same step)
     w0 = None
     for d in range(R):
         w = make_workload(cfg, layer=d)
+        hosts.append(w)
         if w0 is None:
             w0 = w
         shape = w.pool_shape()
@@ -480,7 +519,7 @@ def bench_step(args):
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"], ref = cpu_baseline(w0, cfg, scale, args.cpu_seconds)
+        result["cpu_baseline"], ref = cpu_baseline(hosts, cfg, scale)
         # the oracle's layer-0 output (computed by that baseline run) against the
         # GPU's layer-0 output of the last timed step
         got = out[0].float().cpu().numpy().astype(np.float64)
@@ -492,8 +531,11 @@ def bench_step(args):
             "tolerance": "|gpu - oracle| <= 1e-2 + 1e-2 |oracle|, elementwise",
         }
     result["rocm"] = torch.version.hip
-    # context for the roofline: what a plain 1 GiB device copy moves on this GPU
+    # context for the roofline: what a plain 1 GiB device copy moves on this GPU, and
+    # what a plain library reduction reads (both far below the 8 TB/s vendor peak)
     result["copy_1gib_gbps_read_plus_write"] = copy_rate(5)["gbps_read_plus_write"]
+    rr = read_rate(5)
+    result["hbm_read_reference"] = {"gbps": rr["gbps_read"], "method": rr["method"]}
 
     print(json.dumps(result), flush=True)
 
@@ -780,46 +822,79 @@ def bench_slotted(args):
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, cfg, scale, budget_s):
-    """Time the fp64 oracle on one layer of the same workload (append + attention of
-    every sequence and head), repeated until about `budget_s` seconds of CPU time,
-    and scale to the whole step (all layers).  Returns the baseline record and the
-    oracle's output of that layer."""
+def _oracle_threads(O):
+    """OpenMP threads for the oracle: what OpenMP would use (OMP_NUM_THREADS), never
+    more than the CPUs this process may run on.  Returns (threads, affinity CPUs)."""
+    affinity = len(os.sched_getaffinity(0))
+    threads = max(1, min(O.max_threads(0), affinity))
+    O.max_threads(threads)
+    return threads, affinity
+
+
+def cpu_baseline(hosts, cfg, scale):
+    """The fp64 oracle on one whole step of the workload: for every layer, the
+    append of its new rows and attention of every sequence and head, over the
+    same R distinct pool sets the GPU cycles through (layer l uses set l % R).
+    Each set's pool is built once, untimed, and freed before the next; only the
+    layers' append + attention are timed.  Returns the baseline record and the
+    oracle's output of layer 0.  Single-threaded figures of the tiny (c1a) and
+    long-context (c4) workloads are added as context."""
     from oracle import oracle as O
     c = cfg
-    kp, vp = O.new_pools(w.num_blocks, c.num_kv_heads, c.block_size, c.head_dim, w.nan_bits)
-    O.append_tokens(kp, vp, w.k_src, w.v_src, w.seg_cu, w.seg_start, w.seg_tables,
-                    c.block_size, w.num_blocks)
-    threads = O.max_threads(0)
-    reps, spent = 0, 0.0
-    while reps == 0 or (spent < budget_s and reps < 50):
-        t = time.perf_counter()
-        O.append(kp, vp, w.k_new, w.v_new, w.tables, w.lengths, c.block_size, w.num_blocks)
-        ref = O.attention(w.q, kp, vp, w.tables, w.lengths, c.num_kv_heads, c.block_size,
-                          w.num_blocks, scale, c.dtype, threads)
-        spent += time.perf_counter() - t
-        reps += 1
-    per_layer = spent / reps
-    step_s = per_layer * c.num_layers
-    # the same layer once more on one thread (the append is idempotent: same rows,
-    # same slots)
-    t = time.perf_counter()
-    O.append(kp, vp, w.k_new, w.v_new, w.tables, w.lengths, c.block_size, w.num_blocks)
-    O.attention(w.q, kp, vp, w.tables, w.lengths, c.num_kv_heads, c.block_size, w.num_blocks,
-                scale, c.dtype, 1)
-    one_s = (time.perf_counter() - t) * c.num_layers
-    O.max_threads(threads)  # the thread count set for the run above persists
+    R = len(hosts)
+    threads, affinity = _oracle_threads(O)
+    spent, ref = 0.0, None
+    for d, w in enumerate(hosts):
+        kp, vp = O.new_pools(w.num_blocks, c.num_kv_heads, c.block_size, c.head_dim, w.nan_bits)
+        O.append_tokens(kp, vp, w.k_src, w.v_src, w.seg_cu, w.seg_start, w.seg_tables,
+                        c.block_size, w.num_blocks)
+        for li in range(d, c.num_layers, R):
+            t = time.perf_counter()
+            O.append(kp, vp, w.k_new, w.v_new, w.tables, w.lengths, c.block_size, w.num_blocks)
+            out = O.attention(w.q, kp, vp, w.tables, w.lengths, c.num_kv_heads, c.block_size,
+                              w.num_blocks, scale, c.dtype, threads)
+            spent += time.perf_counter() - t
+            if li == 0:
+                ref = out
+        del kp, vp
     return {
-        "value": round(c.num_seqs / step_s, 3),
+        "value": round(c.num_seqs / spent, 3),
         "unit": "tokens/s",
         "cores": threads,
+        "affinity_cpus": affinity,
         "kind": "oracle",
-        "sample": (f"layer 0 of {c.num_layers} ({c.num_seqs} sequences x {c.num_q_heads} heads, "
-                   f"append + fp64 attention), {reps} repetitions, {spent:.1f} s; "
-                   f"step time = per-layer time x {c.num_layers}"),
-        "single_thread_value": round(c.num_seqs / one_s, 3),
+        "sample": (f"one whole step: {c.num_layers} layer(s) of {c.num_seqs} sequences x "
+                   f"{c.num_q_heads} heads (append + fp64 attention), over {R} distinct pool "
+                   f"set(s), {spent:.1f} s on {threads} OpenMP threads"),
+        "single_thread": single_thread_oracle(scale),
         "cpu_model": _cpu_model(),
     }, ref
+
+
+def single_thread_oracle(scale):
+    """The oracle on one thread for one layer of the tiny batch (c1a) and of the
+    long-context batch (c4, 8 x 16,384 tokens): tokens/s and seconds."""
+    from oracle import oracle as O
+    from workloads import get_config, make_workload
+    res = {}
+    prev = O.max_threads(0)
+    for key in ("c1a", "c4"):
+        cfg = get_config(key)
+        w = make_workload(cfg)
+        kp, vp = O.new_pools(w.num_blocks, cfg.num_kv_heads, cfg.block_size, cfg.head_dim,
+                             w.nan_bits)
+        O.append_tokens(kp, vp, w.k_src, w.v_src, w.seg_cu, w.seg_start, w.seg_tables,
+                        cfg.block_size, w.num_blocks)
+        t = time.perf_counter()
+        O.append(kp, vp, w.k_new, w.v_new, w.tables, w.lengths, cfg.block_size, w.num_blocks)
+        O.attention(w.q, kp, vp, w.tables, w.lengths, cfg.num_kv_heads, cfg.block_size,
+                    w.num_blocks, scale, cfg.dtype, 1)
+        dt = time.perf_counter() - t
+        res[key] = {"tokens_per_s": round(cfg.num_seqs / dt, 3), "seconds": round(dt, 3),
+                    "sample": f"one layer, {cfg.num_seqs} sequences x {cfg.num_q_heads} heads"}
+        del kp, vp
+    O.max_threads(prev)
+    return res
 
 
 def _cpu_model() -> str:

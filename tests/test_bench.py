@@ -74,3 +74,5 @@ def test_bench_line_carries_the_contract_fields():
     cpu = b["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
     assert b["parity_vs_oracle"]["within_tolerance"] is True
+    assert set(cpu["single_thread"]) == {"c1a", "c4"} and cpu["affinity_cpus"] >= cpu["cores"]
+    assert b["hbm_read_reference"]["gbps"] > 0
