@@ -32,6 +32,8 @@
 //     log-sum-exp rule.
 // Masked positions (tokens >= n in the last block, stale data of reused blocks)
 // get score -inf and a zeroed V row, so a NaN there cannot reach the output.
+#include <type_traits>
+
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -263,6 +265,137 @@ __device__ __forceinline__ void pv_mma(GqaState &st, const uint16_t *vlds, const
     // the next sub-tile's LDS writes must not pass these reads
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---- sub-tiles staged in LDS by global-to-LDS loads ---------------------------
+// The shared-prefix and slotted-tile kernels keep two sub-tiles per wave in
+// flight without holding them in registers: gfx950's buffer loads can write
+// straight to LDS (16 bytes per lane).  Such a load writes the 16 bytes of lane L
+// at byte 16 L of its 1 KiB destination, and a lane outside the buffer's range
+// writes zeros (both checked on the GPU with an in-bounds probe), so a masked row
+// of a sub-tile is zero in LDS as it was in registers.
+//
+// A wave's staging area is two buffers, each a sub-tile's K rows then its V rows
+// (16 rows x 256 bytes each, no padding).  Since the destination is lane-linear,
+// the swizzle is applied on the global side: lane L of load i fetches chunk
+// (L % 16) ^ swz(r) of row r = 4 i + L / 16, so chunk c of row r sits at position
+// c ^ swz(r).  With swz(r) = (2 r + r / 8) % 16 the 16 lanes of a score-operand
+// read (rows 0..15, one chunk) and the 32 lanes of a transposing V read (rows
+// 0..7 or 8..15, two adjacent chunks) all fall on distinct banks.
+//
+// Ordering is explicit.  The compiler's own tracking of global-to-LDS loads is
+// kept out (the destination address passes through an empty asm statement, so no
+// LDS object is known to be written): it either waited for every such load in
+// flight, or for none, depending on the loop's shape.  Instead each read of a
+// buffer is preceded by a vector-memory wait whose count the caller derives from
+// its own fixed issue order, and each refill of a buffer by a wait for the LDS
+// reads of it.
+constexpr int kDmaSubBytes = kSub * kHeadDim * 2;  // K (or V) of a sub-tile: 4 KiB
+constexpr int kDmaBufBytes = 2 * kDmaSubBytes;     // K then V
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int dma_swz(int r) { return (2 * r + (r >> 3)) & 15; }
+
+// Per-lane byte offsets of the staged layout (constant for the whole kernel).
+struct DmaLanes {
+    int src[4];  // row / chunk of the sub-tile that lane fetches in load i
+    int ka[4];   // position of the A operand of score MFMA kk (row lane%16)
+    int va[8];   // position of the transposing V^T read jj
+};
+
+__device__ __forceinline__ DmaLanes dma_lanes(int lane)
+{
+    DmaLanes d;
+    const int col = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * i + grp;
+        d.src[i] = r * 256 + ((col ^ dma_swz(r)) << 4);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        d.ka[kk] = col * 256 + (((4 * kk + grp) ^ dma_swz(col)) << 4);
+    const int rv = 4 * grp + (col >> 2);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+        d.va[jj] = rv * 256 + (((2 * jj + ((col & 3) >> 1)) ^ dma_swz(rv)) << 4) + (col & 1) * 8;
+    return d;
+}
+
+// Issue the global-to-LDS loads of a sub-tile (K into buf, V into buf + 4 KiB):
+// 8 vector-memory operations.  `buf` must be wave-uniform.
+__device__ __forceinline__ void dma_sub(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                        char *buf, const DmaLanes &d)
+{
+    // the LDS byte address, hidden from the compiler's alias analysis
+    uint32_t base = (uint32_t)(uintptr_t)(lds_void *)buf;
+    asm volatile("" : "+s"(base));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(uintptr_t)(base + i * 1024), 16,
+                                                 d.src[i], 0, 0, kLoadReuse);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rv, (lds_void *)(uintptr_t)(base + kDmaSubBytes + i * 1024), 16, d.src[i], 0, 0,
+            kLoadReuse);
+}
+
+// The score A operand and the P.V A operand (V^T) of a staged sub-tile.
+__device__ __forceinline__ KOp dma_read_k(const char *buf, const DmaLanes &d)
+{
+    KOp a;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        a.k[kk] = *(const u32x4 *)(buf + d.ka[kk]);
+    return a;
+}
+
+__device__ __forceinline__ void dma_read_v(i16x4 (&va)[8], const char *buf, const DmaLanes &d)
+{
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+        va[jj] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4 *)(buf + kDmaSubBytes + d.va[jj]));
+}
+
+// acc = alpha * acc + V^T P^T for the halves that are live this sub-tile, from a
+// V^T operand already in registers.
+template <int DT, int NH>
+__device__ __forceinline__ void pv_mma_regs(GqaState (&st)[NH], const i16x4 (&va)[8],
+                                            const u32x2 (&pb)[NH], const bool (&rescale)[NH],
+                                            const float (&alpha)[NH], const bool (&live)[NH])
+{
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        if (!live[h])
+            continue;  // wave-uniform: a half with no active column this sub-tile
+        if (rescale[h]) {
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj)
+                st[h].acc[jj] *= alpha[h];
+        }
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+            st[h].acc[jj] = mfma_pv<DT>(__builtin_bit_cast(u32x2, va[jj]), pb[h], st[h].acc[jj]);
+    }
+}
+
+// s_waitcnt encodings (gfx9 family): wait until at most N vector-memory
+// operations are outstanding; until no LDS (or scalar) operation is.
+#define PKV_WAIT_VMCNT(N) __builtin_amdgcn_s_waitcnt(0x0F70 | ((N) & 15) | (((N) >> 4) << 14))
+#define PKV_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
+
+// A work-group barrier for data exchanged through LDS by ordinary LDS writes:
+// the wave's LDS (and scalar) operations complete first, and vector-memory
+// operations, global-to-LDS loads included, stay in flight (a fenced barrier
+// waits for every one of them).  The memory clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Work modes of the decode kernel.
@@ -1069,7 +1202,8 @@ void slotted_mfma_kernel(DecodeArgs a)
 template <int DT, int NH>
 __device__ __forceinline__ void pv_mma_halves(GqaState (&st)[NH], const uint16_t *vlds,
                                               const u32x2 (&pb)[NH], const bool (&rescale)[NH],
-                                              const float (&alpha)[NH], int lane)
+                                              const float (&alpha)[NH], int lane,
+                                              const bool (&live)[NH])
 {
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
     const int j = lane & 15, grp = lane >> 4;
@@ -1082,6 +1216,8 @@ __device__ __forceinline__ void pv_mma_halves(GqaState (&st)[NH], const uint16_t
         va[jj] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + 16 * jj));
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
+        if (!live[h])
+            continue;  // wave-uniform: a half with no active column this sub-tile
         if (rescale[h]) {
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj)
@@ -1120,11 +1256,17 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
 {
     constexpr int kCols = 16 * NH;   // query columns of a tile
     constexpr int kMembers = kCols;  // most member sequences of a tile (G = 1)
-    __shared__ __attribute__((aligned(16))) union {
-        uint16_t v[WAVES][kStageElems];
-        float o[WAVES][kCols][kOStride];
-    } sm;
+    // Each wave stages its sub-tiles in two buffers, one in each of two LDS arrays
+    // (even steps in stage_a, odd ones in stage_b): the compiler tracks the
+    // global-to-LDS loads into distinct arrays separately, so a read of one buffer
+    // waits only for that buffer's loads.  The cross-wave merge reuses both arrays
+    // (wave i's fp32 outputs [kCols][128] in stage_a for i < WAVES/2, else stage_b).
+    __shared__ __attribute__((aligned(16))) char stage_a[WAVES][kDmaBufBytes];
+    __shared__ __attribute__((aligned(16))) char stage_b[WAVES][kDmaBufBytes];
+    static_assert(kCols * kHeadDim * 4 * (WAVES / 2) <= WAVES * kDmaBufBytes,
+                  "the merge fits the staging arrays");
     __shared__ float s_m[WAVES][kCols], s_l[WAVES][kCols];
+    __shared__ float s_wgt[WAVES][kCols];    // merge weight of wave i's partial of a column
     __shared__ int64_t s_row[kCols];         // output row of each query column, -1 if inactive
     __shared__ int32_t s_cum[kMembers + 1];  // sub-tiles before member i's own ones (s_cum[0]: prefix)
     __shared__ int32_t s_len[kMembers];      // context length of member i (0 outside the group)
@@ -1148,16 +1290,47 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
     const meta_ptr tabs = as_meta(a.tables);
     const int64_t blk_elems = (int64_t)a.num_kv_heads * BS * kHeadDim;
     const int64_t head_off = (int64_t)g * BS * kHeadDim;
-    uint16_t *vlds = sm.v[w];
-    uint16_t *klds = vlds + kSub * kVStride;
     const int ch = g * G + col % G;  // query head of this lane's column
     int cm[NH];                      // member of this lane's column in each half
 #pragma unroll
     for (int h = 0; h < NH; ++h)
         cm[h] = h * sph + col / G;
 
+    // The query rows are requested first, before anything they do not depend on
+    // (each lane loads a valid row: a column outside the tile reads a neighbour's).
+    u32x4 qop[NH][4];
+    auto load_q = [&]() {
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            const uint16_t *qrow =
+                (const uint16_t *)a.q +
+                ((int64_t)min(s0 + cm[h], s_end - 1) * a.num_q_heads + ch) * kHeadDim + grp * 8;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                qop[h][kk] = *(const u32x4 *)(qrow + kk * 32);
+        }
+    };
+    load_q();
+
+    // A sub-tile of the work-group's list: its member (-1 for the prefix), first
+    // token, the positions it covers and the rows it loads, and its block.
+    struct Sub {
+        int seg, tb, t_beg, t_end, t_load;
+        int32_t phys;
+    };
+    // One cache policy for the whole list (the default one, which keeps the
+    // prefix in L2 for the group's other tiles).  Each sub-tile goes global ->
+    // LDS into one of the wave's two staging buffers: 8 vector-memory operations.
+    const DmaLanes dl = dma_lanes(lane);
+    char *const buf_a = stage_a[w];
+    char *const buf_b = stage_b[w];
+    auto dma = [&](const Sub &d, char *buf) {
+        const SubRsrc r = sub_rsrc<BS>(d.phys, kp, vp, d.tb, d.t_load, head_off, blk_elems);
+        dma_sub(r.k, r.v, buf, dl);
+    };
+
     int k = group_of(as_meta(a.group_cu), a.num_groups, s0);
-    for (bool more = true; more; ++k) {
+    for (bool more = true, first = true; more; ++k) {
         const int ga = as_meta(a.group_cu)[k], gb = as_meta(a.group_cu)[k + 1];
         more = gb < s_end;
         if (ga == gb)
@@ -1171,21 +1344,56 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
             active[h] = col < sph * G && cs < s_end && cs >= ga && cs < gb;
         }
 
+        // The list opens with a head of the first min(P, 2 WAVES) prefix sub-tiles.
+        // When the head holds both of each wave's first sub-tiles, their loads
+        // are issued here, before the members' set-up: they depend on the group's
+        // first row and prefix length only, and no appended row lies in the prefix
+        // (a member appends at its own position n - 1 >= prefix length).
+        const int n_pre = (plen + kSub - 1) / kSub;
+        const int head = min(n_pre, 2 * WAVES);
+        const bool early = n_pre >= 2 * WAVES;  // uniform
+        auto prefix_sub = [&](int j) {
+            Sub d;
+            d.seg = -1;
+            d.tb = j * kSub;
+            d.t_beg = 0;
+            d.t_end = plen;
+            d.t_load = plen;
+            d.phys = max(tabs[(int64_t)ga * a.width + min(d.tb / BS, a.width - 1)], 0);
+            return d;
+        };
+        // wave 0 requests the members' lengths first: the set-up below waits for
+        // them, and vector-memory results are counted in issue order
+        const int s_m0 = s0 + lane;
+        const bool in_m = w == 0 && lane < kMembers && lane < spt && s_m0 < s_end &&
+                          s_m0 >= ga && s_m0 < gb;
+        const int n_m = in_m ? a.lens[s_m0] : 0;
+        __builtin_amdgcn_sched_barrier(0);
+        // Without a long enough head the two loads are issued empty (zero-byte
+        // ranges), so that the count of loads in flight is the same on both paths;
+        // the real ones follow after the set-up.
+        Sub cur = prefix_sub(w), nxt = prefix_sub(w + WAVES);
+        if (!early) {
+            cur.t_load = 0;
+            nxt.t_load = 0;
+        }
+        dma(cur, buf_a);
+        dma(nxt, buf_b);
+        __builtin_amdgcn_sched_barrier(0);
+
         // per-member lengths and the cumulative sub-tile counts: lane i of wave 0
         // takes member i, and a wave prefix sum gives the running counts
         if (w == 0) {
-            const int s = s0 + lane;
-            const bool in = lane < kMembers && lane < spt && s < s_end && s >= ga && s < gb;
-            const int n = in ? a.lens[s] : 0;
-            if (in && fused && g == 0 && n <= 0 && a.slot_out)
-                a.slot_out[s] = -1;  // padding sequence: nothing appended
+            const int n = n_m;
+            if (in_m && fused && g == 0 && n <= 0 && a.slot_out)
+                a.slot_out[s_m0] = -1;  // padding sequence: nothing appended
             int incl = n > start_sub ? (n - start_sub + kSub - 1) / kSub : 0;
 #pragma unroll
             for (int d = 1; d < kMembers; d <<= 1) {
                 const int up = __shfl_up(incl, d, 64);
                 incl += lane >= d ? up : 0;
             }
-            const int base = (plen + kSub - 1) / kSub;
+            const int base = n_pre;
             if (lane < kMembers) {
                 s_len[lane] = n;
                 s_cum[lane + 1] = base + incl;
@@ -1193,7 +1401,167 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
             if (lane == 0)
                 s_cum[0] = base;
         }
-        __syncthreads();
+        lds_barrier();  // the global-to-LDS loads above stay in flight
+        const int total = __builtin_amdgcn_readfirstlane(s_cum[kMembers]);
+
+        // a column outside this group scores zeros (a later group of the tile
+        // reloads the rows zeroed by an earlier one)
+        if (!first)
+            load_q();
+        first = false;
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                qop[h][kk] = active[h] ? qop[h][kk] : (u32x4){0u, 0u, 0u, 0u};
+        }
+        GqaState st[NH];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            st[h].m = kNegInf;
+            st[h].l = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj)
+                st[h].acc[jj] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+
+        // Sub-tile j of the work-group's list: after the head, the list interleaves
+        // the remaining prefix sub-tiles (seg -1, read from L2 after their first
+        // use) evenly with the members' own ones (seg >= 0, mostly HBM reads), so
+        // that HBM is busy through the whole loop instead of only once the prefix
+        // is done.  With P' prefix sub-tiles among the T' positions after a head of
+        // H, position H + j is prefix sub-tile H + pi, pi = floor(j P' / T'), when
+        // floor((j+1) P' / T') exceeds pi, else the members' sub-tile j - pi,
+        // counted member after member.
+        //
+        // A wave takes positions w, w + WAVES, ...  Its lanes describe the next 64
+        // of them at once, each lane one position with its table entry, so the
+        // table reads of 64 steps cost one round trip; a step then takes its
+        // descriptor from the lanes with uniform lane reads.  A position past the
+        // list describes an empty sub-tile (seg -2, a zero-byte buffer range).
+        const int rest_pre = n_pre - head;
+        const int rest = max(total - head, 1);  // positions after the head (none: 1)
+        int d_seg, d_tb;                // this lane's position: member (or -1, -2), first token
+        int32_t d_phys;                 // and its table entry
+        auto describe_lanes = [&](int i0) {
+            const int j = w + (i0 + lane) * WAVES;
+            int row = ga;
+            d_seg = -2;
+            d_tb = 0;
+            if (j < head) {
+                d_seg = -1;
+                d_tb = j * kSub;
+            } else if (j < total) {
+                const int64_t jp = (int64_t)(j - head) * rest_pre;
+                const int pi = (int)(jp / rest), pi1 = (int)((jp + rest_pre) / rest);
+                if (pi1 > pi) {
+                    d_seg = -1;
+                    d_tb = (head + pi) * kSub;
+                } else {
+                    const int jm = n_pre + (j - head) - pi;  // s_cum coordinate of a member sub-tile
+                    int seg = 0;
+#pragma unroll
+                    for (int i = 1; i < kMembers; ++i)
+                        seg += s_cum[i] <= jm ? 1 : 0;
+                    d_seg = seg;
+                    d_tb = start_sub + (jm - s_cum[seg]) * kSub;
+                    row = s0 + seg;
+                }
+            }
+            d_phys = 0;
+            if (j < total)
+                d_phys = a.tables[(int64_t)row * a.width + min(d_tb / BS, a.width - 1)];
+        };
+        // the descriptor of the wave's position i (i % 64 is the lane holding it)
+        auto take = [&](int i) {
+            const int l = i & 63;
+            Sub d;
+            d.seg = __builtin_amdgcn_readlane(d_seg, l);
+            d.tb = __builtin_amdgcn_readlane(d_tb, l);
+            d.phys = __builtin_amdgcn_readlane(d_phys, l);
+            const bool own = d.seg >= 0;
+            const int n = own ? __builtin_amdgcn_readfirstlane(s_len[own ? d.seg : 0]) : plen;
+            d.t_beg = own ? plen : 0;
+            d.t_end = n;
+            d.t_load = d.seg == -2 ? 0 : n;
+            d.seg = max(d.seg, -1);
+            return d;
+        };
+        // The wave's k-th sub-tile is staged in buffer k % 2 (stage_a, stage_b).
+        // Step k reads both operands of sub-tile k from its buffer into registers,
+        // computes the scores and softmax, refills the buffer with sub-tile k + 2,
+        // and then runs P.V, so the loads of two sub-tiles are in flight behind the
+        // current one's work.  Steps -2 and -1 only issue the loads of sub-tiles 0
+        // and 1 (issued above already when the head holds them).  The loop is
+        // unrolled by two so that each step names its buffer.
+        //
+        // Vector-memory operations are issued in this order only (the scheduling
+        // barriers keep the compiler from moving them): step k issues the 8 loads
+        // of sub-tile k + 2, preceded every 64 steps by the table reads of the next
+        // 64 positions.  When step k reads sub-tile k, at least the 8 loads of
+        // sub-tile k + 1 were issued after that sub-tile's loads: waiting until at
+        // most 8 operations are outstanding covers it.
+        constexpr int kReadWait = 8;
+        auto step = [&](auto parity, auto run, Sub &cur, Sub &nxt, int k) {
+            constexpr bool RUN = decltype(run)::value;
+            char *const buf = decltype(parity)::value ? buf_b : buf_a;
+            i16x4 va[8];
+            u32x2 pb[NH];
+            float alpha[NH];
+            bool rs[NH];
+            // A member's own sub-tile has active columns only in the half holding
+            // the member: the other half's scores, softmax and P.V are skipped
+            // (wave-uniform), leaving its state as it was.
+            bool live[NH];
+#pragma unroll
+            for (int h = 0; h < NH; ++h)
+                live[h] = RUN && (cur.seg < 0 || (cur.seg >= h * sph && cur.seg < (h + 1) * sph));
+            if constexpr (RUN) {
+                __builtin_amdgcn_sched_barrier(0);
+                PKV_WAIT_VMCNT(kReadWait);  // this buffer's loads have landed
+                __builtin_amdgcn_sched_barrier(0);
+                const KOp KA = dma_read_k(buf, dl);
+                dma_read_v(va, buf, dl);
+                // a prefix sub-tile that the prefix fills needs no mask: its
+                // positions are all in range, and a column outside the tile only
+                // updates a state that is never written out
+                if (cur.seg < 0 && cur.tb + kSub <= cur.t_end) {
+#pragma unroll
+                    for (int h = 0; h < NH; ++h)
+                        rs[h] = qk_softmax<DT, false>(st[h], KA, qop[h], cur.tb, 0, cur.t_end,
+                                                      lane, a.scale_log2, pb[h], alpha[h]);
+                } else {
+#pragma unroll
+                    for (int h = 0; h < NH; ++h) {
+                        rs[h] = false;
+                        if (live[h]) {
+                            const bool on =
+                                cur.seg < 0 ? active[h] : (active[h] && cm[h] == cur.seg);
+                            rs[h] = qk_softmax<DT, true>(st[h], KA, qop[h], cur.tb, cur.t_beg,
+                                                         cur.t_end, lane, a.scale_log2, pb[h],
+                                                         alpha[h], on);
+                        }
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                PKV_WAIT_LGKM0();  // this buffer's reads are done: refill it
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (((k + 2) & 63) == 0 && k + 2 > 0)
+                describe_lanes(k + 2);
+            const Sub nxt2 = take(k + 2);
+            dma(nxt2, buf);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (RUN)
+                pv_mma_regs<DT, NH>(st, va, pb, rs, alpha, live);
+            __builtin_amdgcn_sched_barrier(0);
+            cur = nxt;
+            nxt = nxt2;
+        };
+        // the descriptors' table reads go out before the append, whose latency
+        // they share
+        if (w < total)
+            describe_lanes(0);
         // Fused append, spread over the work-group: each thread moves one 16-byte
         // chunk of a member's new K or V row to its slot.  The barrier below makes
         // the rows visible to the whole work-group, so the member's last sub-tile
@@ -1219,185 +1587,52 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
             }
         }
         __syncthreads();
-        const int total = __builtin_amdgcn_readfirstlane(s_cum[kMembers]);
 
-        // every lane loads a valid query row (inactive columns read a neighbour's
-        // and zero it): no load sits under a lane-dependent branch
-        u32x4 qop[NH][4];
-#pragma unroll
-        for (int h = 0; h < NH; ++h) {
-            const uint16_t *qrow =
-                (const uint16_t *)a.q +
-                ((int64_t)min(s0 + cm[h], s_end - 1) * a.num_q_heads + ch) * kHeadDim + grp * 8;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const u32x4 v = *(const u32x4 *)(qrow + kk * 32);
-                qop[h][kk] = active[h] ? v : (u32x4){0u, 0u, 0u, 0u};
-            }
-        }
-        GqaState st[NH];
-#pragma unroll
-        for (int h = 0; h < NH; ++h) {
-            st[h].m = kNegInf;
-            st[h].l = 0.f;
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj)
-                st[h].acc[jj] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        }
-
-        // Sub-tile j of the work-group's list: the list interleaves the prefix
-        // sub-tiles (seg -1, read from L2 after their first use) evenly with the
-        // members' own ones (seg >= 0, mostly HBM reads), so that HBM is busy
-        // through the whole loop instead of only once the prefix is done.  With P
-        // prefix sub-tiles among T, position j is prefix sub-tile pi = floor(j P / T)
-        // when floor((j+1) P / T) exceeds pi, else the members' sub-tile j - pi,
-        // counted member after member.  A wave describes positions w, w + WAVES, ...
-        // in order, so both quotients advance by a constant step with a carry (no
-        // division per sub-tile), and the member cursor only moves forward (one or
-        // two LDS reads per sub-tile).  A j past the list describes an empty sub-tile
-        // (a zero-byte buffer range), so that every step issues its loads
-        // unconditionally: the compiler's count of loads in flight then agrees on
-        // every path, and each wait covers only the sub-tile it needs.
-        const int n_pre = __builtin_amdgcn_readfirstlane(s_cum[0]);
-        struct Sub {
-            int seg, tb, t_beg, t_end, t_load;
-            int32_t phys;
-        };
-        // j P = q0 T + r0 and (j + 1) P = q1 T + r1 for the wave's next position j
-        const int tot = max(total, 1);  // no list (total 0) describes nothing
-        const int64_t wp = (int64_t)WAVES * n_pre;
-        const int dq = (int)(wp / tot), dr = (int)(wp % tot);
-        int q0 = (int)((int64_t)w * n_pre / tot), r0 = (int)((int64_t)w * n_pre % tot);
-        int q1 = (int)((int64_t)(w + 1) * n_pre / tot);
-        int r1 = (int)((int64_t)(w + 1) * n_pre % tot);
-        auto describe = [&](int j, int &seg) {
-            Sub d;
-            int row;
-            if (j >= total) {
-                // past the list: an empty sub-tile.  Its buffer range is empty, so no
-                // byte is fetched whatever the table entry; the entry is still read
-                // below, by the same load as on the other path, so that the compiler's
-                // count of loads in flight agrees on both
-                d.seg = -1;
-                d.tb = 0;
-                d.t_beg = 0;
-                d.t_end = plen;
-                d.t_load = 0;
-                row = ga;
-            } else {
-                const int pi = q0, pi1 = q1;  // prefix sub-tiles before positions j and j + 1
-                q0 += dq;
-                r0 += dr;
-                if (r0 >= total) {
-                    r0 -= total;
-                    ++q0;
-                }
-                q1 += dq;
-                r1 += dr;
-                if (r1 >= total) {
-                    r1 -= total;
-                    ++q1;
-                }
-                const bool pre = pi1 > pi;
-                const int jm = n_pre + j - pi;  // s_cum coordinate of a member sub-tile
-                if (!pre) {
-                    while (seg < kMembers - 1 &&
-                           jm >= __builtin_amdgcn_readfirstlane(s_cum[seg + 1]))
-                        ++seg;
-                }
-                d.seg = pre ? -1 : seg;
-                if (pre) {
-                    d.tb = pi * kSub;
-                    d.t_beg = 0;
-                    d.t_end = plen;
-                    d.t_load = plen;
-                    row = ga;
-                } else {
-                    const int n = __builtin_amdgcn_readfirstlane(s_len[seg]);
-                    d.tb = start_sub + (jm - __builtin_amdgcn_readfirstlane(s_cum[seg])) * kSub;
-                    d.t_beg = plen;
-                    d.t_end = n;
-                    d.t_load = n;
-                    row = s0 + seg;
-                }
-            }
-            // requested here, made uniform (and waited for) only when the sub-tile's
-            // loads are issued, one step later
-            const int32_t *trow_v =
-                a.tables + (int64_t)__builtin_amdgcn_readfirstlane(row) * a.width;
-            d.phys = table_entry_v(trow_v, a.width,
-                                   __builtin_amdgcn_readfirstlane(min(d.tb / BS, a.width - 1)));
-            return d;
-        };
-        // One cache policy for the whole list (the default one, which keeps the
-        // prefix in L2 for the group's other tiles): a policy chosen per sub-tile
-        // would split the loads over two code paths.
-        auto load_sub = [&](KOp &K, VRows &V, const Sub &d) {
-            // an empty sub-tile past the list may carry an unused (negative) table
-            // entry: the clamp keeps its base address inside the pool as well
-            const SubRsrc r = sub_rsrc<BS>(max(__builtin_amdgcn_readfirstlane(d.phys), 0), kp, vp,
-                                           d.tb, d.t_load, head_off, blk_elems);
-            load_k<kLoadReuse>(K, r.k, lane);
-            load_v<kLoadReuse>(V, r.v, lane);
-        };
-        // Sub-tiles w, w + WAVES, ... belong to this wave: the scores of the current
-        // one are computed, then the next one's loads are issued into the same
-        // registers, overlapping the softmax and P.V of the current sub-tile.  The
-        // table entry of the sub-tile after next is requested at the same time, so
-        // that its latency (a member's own blocks miss the caches) never sits
-        // between a sub-tile's description and its loads.
-        auto step = [&](KOp &K, VRows &V, Sub &cur, Sub &nxt, int jn2, int &seg) {
-            const Sub nxt2 = describe(jn2, seg);
-            u32x2 pb[NH];
-            float alpha[NH];
-            bool rs[NH];
-            const KOp KA = k_operand(K, klds, lane);
-            // a prefix sub-tile that the prefix fills needs no mask: its positions
-            // are all in range, and a column outside the tile only updates a state
-            // that is never written out
-            if (cur.seg < 0 && cur.tb + kSub <= cur.t_end) {
-#pragma unroll
-                for (int h = 0; h < NH; ++h)
-                    rs[h] = qk_softmax<DT, false>(st[h], KA, qop[h], cur.tb, 0, cur.t_end, lane,
-                                                  a.scale_log2, pb[h], alpha[h]);
-            } else {
-#pragma unroll
-                for (int h = 0; h < NH; ++h) {
-                    const bool on = cur.seg < 0 ? active[h] : (active[h] && cm[h] == cur.seg);
-                    rs[h] = qk_softmax<DT, true>(st[h], KA, qop[h], cur.tb, cur.t_beg, cur.t_end,
-                                                 lane, a.scale_log2, pb[h], alpha[h], on);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            stage_v(V, vlds, lane);
-            __builtin_amdgcn_sched_barrier(0);
-            load_sub(K, V, nxt);
-            __builtin_amdgcn_sched_barrier(0);
-            pv_mma_halves<DT, NH>(st, vlds, pb, rs, alpha, lane);
-            __builtin_amdgcn_sched_barrier(0);
-            cur = nxt;
-            nxt = nxt2;
-        };
         if (w < total) {
-            int seg = -1;
-            Sub cur = describe(w, seg);
-            Sub nxt = describe(w + WAVES, seg);
-            KOp K;
-            VRows V;
-            load_sub(K, V, cur);
-            for (int j = w; j < total; j += WAVES)
-                step(K, V, cur, nxt, j + 2 * WAVES, seg);
+            using even = std::integral_constant<int, 0>;
+            using odd = std::integral_constant<int, 1>;
+            using warm = std::false_type;
+            using full = std::true_type;
+            if (!early) {
+                step(even(), warm(), cur, nxt, -2);
+                step(odd(), warm(), cur, nxt, -1);
+            }
+            const int steps = (total - w + WAVES - 1) / WAVES;
+            for (int k = 0;;) {
+                step(even(), full(), cur, nxt, k);
+                if (++k >= steps)
+                    break;
+                step(odd(), full(), cur, nxt, k);
+                if (++k >= steps)
+                    break;
+            }
         }
+        // the loads of the sub-tiles past the list still write this wave's buffers
+        PKV_WAIT_VMCNT(0);
 #pragma unroll
         for (int h = 0; h < NH; ++h)
             st[h].l = pair_sum32(pair_sum16(st[h].l));
 
-        __syncthreads();  // all waves are done with their V staging area
+        __syncthreads();  // every wave is done with its staging buffers
+        // wave i's outputs: 16-byte chunk q of column r at chunk q ^ (r % 16) of
+        // the column's 512-byte row, so that the 16 columns one write (or read)
+        // instruction covers fall in different banks
+        auto o_area = [&](int i) -> float * {
+            char *const base = i < WAVES / 2 ? &stage_a[0][0] : &stage_b[0][0];
+            return (float *)base + (i % (WAVES / 2)) * (kCols * kHeadDim);
+        };
+        {
+            float *const ow = o_area(w);
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+                const int r = 16 * h + col;
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj)
+                    *(f32x4 *)&ow[r * kHeadDim + 4 * ((4 * jj + grp) ^ (r & 15))] = st[h].acc[jj];
+            }
+        }
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj)
-                *(f32x4 *)&sm.o[w][16 * h + col][16 * jj + 4 * grp] = st[h].acc[jj];
             if (grp == 0) {
                 s_m[w][16 * h + col] = st[h].m;
                 s_l[w][16 * h + col] = st[h].l;
@@ -1410,33 +1645,40 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
             s_row[tid] = act ? (int64_t)cs * a.num_q_heads + g * G + c % G : -1;
         }
         __syncthreads();
+        // the weight of wave i's partial of column qi: exp2(m_i - M) / L, with M
+        // the column's largest reference max and L its merged denominator (0 for
+        // an empty column)
+        if (tid < WAVES * kCols) {
+            const int i = tid / kCols, qi = tid % kCols;
+            float M = s_m[0][qi];
+#pragma unroll
+            for (int v = 1; v < WAVES; ++v)
+                M = fmaxf(M, s_m[v][qi]);
+            const float ref = safe_ref(M);
+            float L = 0.f;
+#pragma unroll
+            for (int v = 0; v < WAVES; ++v)
+                L += s_l[v][qi] * fexp2(s_m[v][qi] - ref);
+            s_wgt[i][qi] = L > 0.f ? fexp2(s_m[i][qi] - ref) / L : 0.f;
+        }
+        __syncthreads();
         for (int e = tid; e < kCols * 32; e += WAVES * 64) {
             const int qi = e >> 5, d0 = (e & 31) * 4;
             const int64_t row = s_row[qi];
+            f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < WAVES; ++i)
+                o += *(const f32x4 *)&o_area(i)[qi * kHeadDim + 4 * ((d0 / 4) ^ (qi & 15))] *
+                     s_wgt[i][qi];
             if (row < 0)
                 continue;
-            float M = s_m[0][qi];
-#pragma unroll
-            for (int i = 1; i < WAVES; ++i)
-                M = fmaxf(M, s_m[i][qi]);
-            const float ref = safe_ref(M);
-            float L = 0.f;
-            f32x4 O = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int i = 0; i < WAVES; ++i) {
-                const float wgt = fexp2(s_m[i][qi] - ref);
-                L += s_l[i][qi] * wgt;
-                O += *(const f32x4 *)&sm.o[i][qi][d0] * wgt;
-            }
-            f32x4 o = {0.f, 0.f, 0.f, 0.f};
-            if (L > 0.f)
-                o = O / L;
             u32x2 packed;
             packed.x = (uint32_t)to_bits<DT>(o[0]) | ((uint32_t)to_bits<DT>(o[1]) << 16);
             packed.y = (uint32_t)to_bits<DT>(o[2]) | ((uint32_t)to_bits<DT>(o[3]) << 16);
             *(u32x2 *)((uint16_t *)a.out + row * kHeadDim + d0) = packed;
         }
-        __syncthreads();  // LDS is reused by the next group of the tile
+        if (more)
+            __syncthreads();  // LDS is reused by the next group of the tile
     }
 }
 
@@ -1711,6 +1953,12 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
         const int rows = (cur.desc >> 8) & 0xff;
         const int owner = (cur.desc >> 16) - 1;  // -1: common
         const KOp KA = k_operand(K, klds, lane);
+        // a member's own sub-tile has active columns only in the half holding the
+        // member: the other half's scores, softmax and P.V are skipped (uniform)
+        bool live[NH];
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+            live[h] = owner < 0 || (owner >= h * sph && owner < (h + 1) * sph);
         // a full common sub-tile needs no mask: a column outside the tile only
         // updates a state that is never written out
         if (owner < 0 && rows == kSub) {
@@ -1721,9 +1969,12 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
         } else {
 #pragma unroll
             for (int h = 0; h < NH; ++h) {
-                const bool on = owner < 0 ? active[h] : (active[h] && cm[h] == owner);
-                rs[h] = qk_softmax<DT, true>(st[h], KA, qop[h], 0, 0, rows, lane, a.scale_log2,
-                                             pb[h], alpha[h], on);
+                rs[h] = false;
+                if (live[h]) {
+                    const bool on = owner < 0 ? active[h] : (active[h] && cm[h] == owner);
+                    rs[h] = qk_softmax<DT, true>(st[h], KA, qop[h], 0, 0, rows, lane,
+                                                 a.scale_log2, pb[h], alpha[h], on);
+                }
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -1731,7 +1982,7 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
         __builtin_amdgcn_sched_barrier(0);
         load_sub(K, V, nxt);
         __builtin_amdgcn_sched_barrier(0);
-        pv_mma_halves<DT, NH>(st, vlds, pb, rs, alpha, lane);
+        pv_mma_halves<DT, NH>(st, vlds, pb, rs, alpha, lane, live);
         __builtin_amdgcn_sched_barrier(0);
         cur = nxt;
         nxt = nxt2;
