@@ -733,7 +733,12 @@ def bench_slotted(args):
             kr, vr, cu, st, tb = w.k_src, w.v_src, w.seg_cu, w.seg_start, w.seg_tables
             segs, nsegs = _tables_as_segments(w)
             NB = w.num_blocks
-            info = dict(unique=int(w.lengths.sum()), logical=int(w.lengths.sum()),
+            # rows that several tables share (a shared prefix) count once
+            held = np.zeros(NB * cfg.block_size, bool)
+            for si in range(cfg.num_seqs):
+                for b, o, ln in segs[si, :nsegs[si]]:
+                    held[b * cfg.block_size + o:b * cfg.block_size + o + ln] = True
+            info = dict(unique=int(held.sum()), logical=int(w.lengths.sum()),
                         mean=float(w.lengths.mean()), nodes=None, S=cfg.num_seqs)
         kp = torch.zeros((NB, cfg.num_kv_heads, cfg.block_size, cfg.head_dim), dtype=tdt,
                          device=dev)

@@ -1719,10 +1719,12 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
 {
     constexpr int kCols = 16 * NH;   // query columns of a tile
     constexpr int kMembers = kCols;  // most member sequences of a tile (G = 1)
-    __shared__ __attribute__((aligned(16))) union {
-        uint16_t v[WAVES][kStageElems];
-        float o[WAVES][kCols][kOStride];
-    } sm;
+    // two staging buffers per wave in two LDS arrays, as in the one-pass
+    // shared-prefix kernel; the cross-wave merge reuses them
+    __shared__ __attribute__((aligned(16))) char stage_a[WAVES][kDmaBufBytes];
+    __shared__ __attribute__((aligned(16))) char stage_b[WAVES][kDmaBufBytes];
+    static_assert(kCols * kHeadDim * 4 * (WAVES / 2) <= WAVES * kDmaBufBytes,
+                  "the merge fits the staging arrays");
     __shared__ float s_m[WAVES][kCols], s_l[WAVES][kCols];
     __shared__ int32_t s_phys[kTileSubs];
     __shared__ int32_t s_desc[kTileSubs];
@@ -1748,8 +1750,6 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
     const uint16_t *__restrict__ vp = (const uint16_t *)a.v_pool;
     const int64_t blk_elems = (int64_t)a.num_kv_heads * BS * kHeadDim;
     const int64_t head_off = (int64_t)g * BS * kHeadDim;
-    uint16_t *vlds = sm.v[w];
-    uint16_t *klds = vlds + kSub * kVStride;
     // segments of member i, and how many are in use (clamped to the row)
     auto seg_row = [&](int i) { return a.segments + (int64_t)(s0 + i) * ms * 3; };
     auto seg_count = [&](int i) { return min(max(a.num_segments[s0 + i], 0), ms); };
@@ -1759,6 +1759,30 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
         len = min(max(len, 0), BS - off);
     };
 
+    const int ch = g * G + col % G;  // query head of this lane's column
+    int cm[NH];                      // member of this lane's column in each half
+    bool active[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        cm[h] = h * sph + col / G;
+        active[h] = col < sph * G && cm[h] < m;
+    }
+    // every lane loads a valid query row (inactive columns read a neighbour's and
+    // zero it): no load sits under a lane-dependent branch.  The rows are
+    // requested first, so that they have landed long before the loop starts.
+    u32x4 qop[NH][4];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        const uint16_t *qrow = (const uint16_t *)a.q +
+                               ((int64_t)(s0 + min(cm[h], m - 1)) * a.num_q_heads + ch) *
+                                   kHeadDim +
+                               grp * 8;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const u32x4 v = *(const u32x4 *)(qrow + kk * 32);
+            qop[h][kk] = active[h] ? v : (u32x4){0u, 0u, 0u, 0u};
+        }
+    }
     // 1. Common segments: lane k compares segment k of every member with member
     // 0's; each wave takes members 1 + w, 1 + w + WAVES, ...
     const int n0 = seg_count(0);
@@ -1867,29 +1891,6 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
     }
     __syncthreads();
 
-    const int ch = g * G + col % G;  // query head of this lane's column
-    int cm[NH];                      // member of this lane's column in each half
-    bool active[NH];
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-        cm[h] = h * sph + col / G;
-        active[h] = col < sph * G && cm[h] < m;
-    }
-    // every lane loads a valid query row (inactive columns read a neighbour's and
-    // zero it): no load sits under a lane-dependent branch
-    u32x4 qop[NH][4];
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-        const uint16_t *qrow = (const uint16_t *)a.q +
-                               ((int64_t)(s0 + min(cm[h], m - 1)) * a.num_q_heads + ch) *
-                                   kHeadDim +
-                               grp * 8;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const u32x4 v = *(const u32x4 *)(qrow + kk * 32);
-            qop[h][kk] = active[h] ? v : (u32x4){0u, 0u, 0u, 0u};
-        }
-    }
     GqaState st[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
@@ -1938,74 +1939,117 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
         d.desc = past ? 0 : __builtin_amdgcn_readfirstlane(s_desc[idx]);
         return d;
     };
-    auto load_sub = [&](KOp &K, VRows &V, const Sub &d) {
+    // Sub-tile k of the wave goes global -> LDS into buffer k % 2 (stage_a,
+    // stage_b): 8 vector-memory operations.  Step k reads sub-tile k's operands,
+    // computes its scores and softmax, refills the buffer with sub-tile k + 2 and
+    // runs P.V; steps -2 and -1 only issue the first two sub-tiles' loads.  The
+    // loop issues no other vector-memory operation (the descriptors come from
+    // LDS), so when step k reads, the 8 loads of sub-tile k + 1 were issued after
+    // sub-tile k's: waiting until at most 8 are outstanding covers them.
+    const DmaLanes dl = dma_lanes(lane);
+    char *const buf_a = stage_a[w];
+    char *const buf_b = stage_b[w];
+    auto dma = [&](const Sub &d, char *buf) {
         const int64_t b = (int64_t)d.phys * blk_elems + head_off +
                           (int64_t)(d.desc & 0xff) * kHeadDim;
         const int bytes = ((d.desc >> 8) & 0xff) * kHeadDim * 2;
-        load_k<kLoadReuse>(K, make_rsrc(kp + b, bytes), lane);
-        load_v<kLoadReuse>(V, make_rsrc(vp + b, bytes), lane);
+        dma_sub(make_rsrc(kp + b, bytes), make_rsrc(vp + b, bytes), buf, dl);
     };
-    auto step = [&](KOp &K, VRows &V, Sub &cur, Sub &nxt, int jn) {
+    constexpr int kReadWait = 8;
+    auto step = [&](auto parity, auto run, Sub &cur, Sub &nxt, int jn) {
+        constexpr bool RUN = decltype(run)::value;
+        char *const buf = decltype(parity)::value ? buf_b : buf_a;
         const Sub nxt2 = describe(jn);
+        i16x4 va[8];
         u32x2 pb[NH];
         float alpha[NH];
         bool rs[NH];
         const int rows = (cur.desc >> 8) & 0xff;
         const int owner = (cur.desc >> 16) - 1;  // -1: common
-        const KOp KA = k_operand(K, klds, lane);
         // a member's own sub-tile has active columns only in the half holding the
         // member: the other half's scores, softmax and P.V are skipped (uniform)
         bool live[NH];
 #pragma unroll
         for (int h = 0; h < NH; ++h)
-            live[h] = owner < 0 || (owner >= h * sph && owner < (h + 1) * sph);
-        // a full common sub-tile needs no mask: a column outside the tile only
-        // updates a state that is never written out
-        if (owner < 0 && rows == kSub) {
+            live[h] = RUN && (owner < 0 || (owner >= h * sph && owner < (h + 1) * sph));
+        if constexpr (RUN) {
+            __builtin_amdgcn_sched_barrier(0);
+            PKV_WAIT_VMCNT(kReadWait);  // this buffer's loads have landed
+            __builtin_amdgcn_sched_barrier(0);
+            const KOp KA = dma_read_k(buf, dl);
+            dma_read_v(va, buf, dl);
+            // a full common sub-tile needs no mask: a column outside the tile
+            // only updates a state that is never written out
+            if (owner < 0 && rows == kSub) {
 #pragma unroll
-            for (int h = 0; h < NH; ++h)
-                rs[h] = qk_softmax<DT, false>(st[h], KA, qop[h], 0, 0, kSub, lane, a.scale_log2,
-                                              pb[h], alpha[h]);
-        } else {
+                for (int h = 0; h < NH; ++h)
+                    rs[h] = qk_softmax<DT, false>(st[h], KA, qop[h], 0, 0, kSub, lane,
+                                                  a.scale_log2, pb[h], alpha[h]);
+            } else {
 #pragma unroll
-            for (int h = 0; h < NH; ++h) {
-                rs[h] = false;
-                if (live[h]) {
-                    const bool on = owner < 0 ? active[h] : (active[h] && cm[h] == owner);
-                    rs[h] = qk_softmax<DT, true>(st[h], KA, qop[h], 0, 0, rows, lane,
-                                                 a.scale_log2, pb[h], alpha[h], on);
+                for (int h = 0; h < NH; ++h) {
+                    rs[h] = false;
+                    if (live[h]) {
+                        const bool on = owner < 0 ? active[h] : (active[h] && cm[h] == owner);
+                        rs[h] = qk_softmax<DT, true>(st[h], KA, qop[h], 0, 0, rows, lane,
+                                                     a.scale_log2, pb[h], alpha[h], on);
+                    }
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
+            PKV_WAIT_LGKM0();  // this buffer's reads are done: refill it
         }
         __builtin_amdgcn_sched_barrier(0);
-        stage_v(V, vlds, lane);
+        dma(nxt2, buf);
         __builtin_amdgcn_sched_barrier(0);
-        load_sub(K, V, nxt);
-        __builtin_amdgcn_sched_barrier(0);
-        pv_mma_halves<DT, NH>(st, vlds, pb, rs, alpha, lane, live);
+        if constexpr (RUN)
+            pv_mma_regs<DT, NH>(st, va, pb, rs, alpha, live);
         __builtin_amdgcn_sched_barrier(0);
         cur = nxt;
         nxt = nxt2;
     };
     if (w < total) {
-        Sub cur = describe(w);
-        Sub nxt = describe(w + WAVES);
-        KOp K;
-        VRows V;
-        load_sub(K, V, cur);
-        for (int j = w; j < total; j += WAVES)
-            step(K, V, cur, nxt, j + 2 * WAVES);
+        using even = std::integral_constant<int, 0>;
+        using odd = std::integral_constant<int, 1>;
+        Sub cur{}, nxt{};
+        step(even(), std::false_type(), cur, nxt, w);
+        step(odd(), std::false_type(), cur, nxt, w + WAVES);
+        for (int j = w;;) {
+            step(even(), std::true_type(), cur, nxt, j + 2 * WAVES);
+            j += WAVES;
+            if (j >= total)
+                break;
+            step(odd(), std::true_type(), cur, nxt, j + 2 * WAVES);
+            j += WAVES;
+            if (j >= total)
+                break;
+        }
     }
+    // the loads of the sub-tiles past the list still write this wave's buffers
+    PKV_WAIT_VMCNT(0);
 #pragma unroll
     for (int h = 0; h < NH; ++h)
         st[h].l = pair_sum32(pair_sum16(st[h].l));
 
-    __syncthreads();  // all waves are done with their V staging area
+    __syncthreads();  // every wave is done with its staging buffers
+    // wave i's outputs: 16-byte chunk q of column r at chunk q ^ (r % 16) of the
+    // column's 512-byte row
+    auto o_area = [&](int i) -> float * {
+        char *const base = i < WAVES / 2 ? &stage_a[0][0] : &stage_b[0][0];
+        return (float *)base + (i % (WAVES / 2)) * (kCols * kHeadDim);
+    };
+    {
+        float *const ow = o_area(w);
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            const int r = 16 * h + col;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj)
+                *(f32x4 *)&ow[r * kHeadDim + 4 * ((4 * jj + grp) ^ (r & 15))] = st[h].acc[jj];
+        }
+    }
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-            *(f32x4 *)&sm.o[w][16 * h + col][16 * jj + 4 * grp] = st[h].acc[jj];
         if (grp == 0) {
             s_m[w][16 * h + col] = st[h].m;
             s_l[w][16 * h + col] = st[h].l;
@@ -2030,7 +2074,7 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
         for (int i = 0; i < WAVES; ++i) {
             const float wgt = fexp2(s_m[i][qi] - ref);
             L += s_l[i][qi] * wgt;
-            O += *(const f32x4 *)&sm.o[i][qi][d0] * wgt;
+            O += *(const f32x4 *)&o_area(i)[qi * kHeadDim + 4 * ((d0 / 4) ^ (qi & 15))] * wgt;
         }
         f32x4 o = {0.f, 0.f, 0.f, 0.f};
         if (L > 0.f)
