@@ -412,14 +412,17 @@ constexpr int kModeSuffixSplit = 4;  // shared-prefix mode with the positions af
 
 // MODE kModeSplit / kModeMerge / kModeSuffixSplit run a partition loop; the other
 // modes one pass, with the loop folded away at compile time.
-// The register budget is capped so that 4 waves (single pass) or 3 waves (split
-// modes, which keep more state live across their partition loop) fit on each SIMD
-// without spilling.
+// The register budget is capped so that 4 waves (single pass) or PKV_SPLIT_OCC
+// waves (split modes, which keep two sub-tiles in registers and more state live
+// across their partition loop) fit on each SIMD without spilling.
+#ifndef PKV_SPLIT_OCC
+#define PKV_SPLIT_OCC 2
+#endif
 template <int DT, int BS, int WAVES, int MODE>
 __global__ __launch_bounds__(WAVES * 64)
 __attribute__((amdgpu_waves_per_eu(MODE == kModeSplit || MODE == kModeMerge ||
                                            MODE == kModeSuffixSplit
-                                       ? 3
+                                       ? PKV_SPLIT_OCC
                                        : 4)))
 void decode_mfma_kernel(DecodeArgs a)
 {
@@ -561,24 +564,14 @@ void decode_mfma_kernel(DecodeArgs a)
         }
         const int T = nsub > w ? (nsub - w + WAVES - 1) / WAVES : 0;
         if (T > 0) {
-            // Single register buffer per operand, pipelined: the next sub-tile's K
-            // loads are issued once the scores are done, its V loads once the
-            // current V rows are staged in LDS, so they overlap softmax and P.V.
             int tb = t0 + w * kSub;
             const int step = WAVES * kSub;
             const bool first = px == px0;
-            KOp K;
-            VRows V;
-            {
-                const int32_t ef = first ? e_first : sub_phys<BS>(trow, a.width, tb);
-                const SubRsrc r = sub_rsrc<BS>(ef, kp, vp, tb, t_load, head_off, blk_elems);
-                load_k(K, r.k, lane);
-                load_v(V, r.v, lane);
-            }
-            if (new_here) {
-                // write the new rows to their slot now: stores share the in-order
-                // vmcnt counter with loads, so issuing them here lets their latency
-                // overlap the loop instead of the end of the work-group
+            // write the new rows to their slot once the first loads are out:
+            // stores share the in-order vmcnt counter with loads, so issuing them
+            // here lets their latency overlap the loop instead of the end of the
+            // work-group
+            auto store_new = [&]() {
                 const int tn = n - 1;
                 const int64_t dst =
                     phys_n * blk_elems + head_off + (int64_t)(tn % BS) * kHeadDim;
@@ -599,16 +592,40 @@ void decode_mfma_kernel(DecodeArgs a)
                 }
                 if (g == 0 && lane == 0 && a.slot_out)
                     a.slot_out[s] = phys_n * BS + tn % BS;
-            }
-            // table entries are looked up one sub-tile ahead of the loads that use them
-            int32_t pn = first ? e_next : sub_phys<BS>(trow, a.width, tb + step);
+            };
             u32x2 pb;
             float alpha;
             bool rs;
-            for (int j = 0; j + 1 < T; ++j) {  // every sub-tile here is full
-                const int32_t pn2 = sub_phys<BS>(trow, a.width, tb + 2 * step);
+            // The last sub-tile: position n-1, if it lies here, takes the new rows in
+            // place of the (unfetched) pool row; a partial sub-tile is masked.
+            auto last_step = [&](KOp &K, VRows &V) {
+                const bool here = new_here && tb + kSub >= n;
+                const int row = n - 1 - tb;  // 0..15 when `here`
+                KOp KA = k_operand(K, klds, lane);
+                if (here && (lane & 15) == row) {
+                    // the four lanes of row `row` take the new key into the A operand
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        KA.k[kk] = s_new[0][4 * kk + grp];
+                }
+                if (tb + kSub <= t1)
+                    rs = qk_softmax<DT, SUFFIX>(st, KA, qop, tb, t_beg, t1, lane, a.scale_log2,
+                                                pb, alpha);
+                else
+                    rs = qk_softmax<DT, true>(st, KA, qop, tb, t_beg, t1, lane, a.scale_log2,
+                                              pb, alpha);
+                stage_v(V, vlds, lane);
+                if (here && lane < 16)
+                    *(u32x4 *)(vlds + row * kVStride + lane * 8) = s_new[1][lane];
+                pv_mma<DT>(st, vlds, pb, rs, alpha, lane);
+            };
+            // A full sub-tile, consumed from (K, V); the loads of the sub-tile `ahead`
+            // steps later (table entry pn) go into the same registers once they are
+            // free: the K loads once the scores' operand is staged, the V loads once
+            // the V rows are, so they overlap softmax and P.V.
+            auto full_step = [&](KOp &K, VRows &V, int32_t pn, int ahead) {
                 const SubRsrc rn =
-                    sub_rsrc<BS>(pn, kp, vp, tb + step, t_load, head_off, blk_elems);
+                    sub_rsrc<BS>(pn, kp, vp, tb + ahead * step, t_load, head_off, blk_elems);
                 const KOp KA = k_operand(K, klds, lane);
                 __builtin_amdgcn_sched_barrier(0);
                 load_k(K, rn.k, lane);  // the raw registers are free once staged
@@ -622,30 +639,65 @@ void decode_mfma_kernel(DecodeArgs a)
                 __builtin_amdgcn_sched_barrier(0);
                 pv_mma<DT>(st, vlds, pb, rs, alpha, lane);
                 __builtin_amdgcn_sched_barrier(0);
-                pn = pn2;
                 tb += step;
+            };
+            if constexpr (SPLIT) {
+                // Split modes (3 waves per SIMD, registers to spare): two register
+                // buffers, so the loads of the next two sub-tiles are in flight
+                // behind the current one.  Step j consumes buffer j % 2 and refills
+                // it with sub-tile j + 2; sub-tiles past the wave's last one have an
+                // empty buffer range (zeros, no fetch).  Table entries are looked up
+                // a step before the loads that use them.
+                KOp K0, K1;
+                VRows V0, V1;
+                {
+                    const int32_t ef = first ? e_first : sub_phys<BS>(trow, a.width, tb);
+                    const int32_t en = first ? e_next : sub_phys<BS>(trow, a.width, tb + step);
+                    const SubRsrc r0 = sub_rsrc<BS>(ef, kp, vp, tb, t_load, head_off, blk_elems);
+                    const SubRsrc r1 =
+                        sub_rsrc<BS>(en, kp, vp, tb + step, t_load, head_off, blk_elems);
+                    load_k(K0, r0.k, lane);
+                    load_v(V0, r0.v, lane);
+                    load_k(K1, r1.k, lane);
+                    load_v(V1, r1.v, lane);
+                }
+                if (new_here)
+                    store_new();
+                int32_t pa = sub_phys<BS>(trow, a.width, tb + 2 * step);
+                int j = 0;
+                for (; j + 2 < T; j += 2) {  // steps j and j + 1 are full
+                    const int32_t pb2 = sub_phys<BS>(trow, a.width, tb + 3 * step);
+                    full_step(K0, V0, pa, 2);
+                    pa = sub_phys<BS>(trow, a.width, tb + 3 * step);
+                    full_step(K1, V1, pb2, 2);
+                }
+                if (j + 1 < T) {
+                    full_step(K0, V0, pa, 2);
+                    last_step(K1, V1);
+                } else {
+                    last_step(K0, V0);
+                }
+            } else {
+                // Single pass: one register buffer per operand (4 waves per SIMD).
+                KOp K;
+                VRows V;
+                {
+                    const int32_t ef = first ? e_first : sub_phys<BS>(trow, a.width, tb);
+                    const SubRsrc r = sub_rsrc<BS>(ef, kp, vp, tb, t_load, head_off, blk_elems);
+                    load_k(K, r.k, lane);
+                    load_v(V, r.v, lane);
+                }
+                if (new_here)
+                    store_new();
+                // table entries are looked up one sub-tile ahead of the loads that use them
+                int32_t pn = first ? e_next : sub_phys<BS>(trow, a.width, tb + step);
+                for (int j = 0; j + 1 < T; ++j) {  // every sub-tile here is full
+                    const int32_t pn2 = sub_phys<BS>(trow, a.width, tb + 2 * step);
+                    full_step(K, V, pn, 1);
+                    pn = pn2;
+                }
+                last_step(K, V);
             }
-            // position n-1 in this sub-tile: put the new rows in place of the
-            // (unfetched) pool row
-            const bool here = new_here && tb + kSub >= n;
-            const int row = n - 1 - tb;  // 0..15 when `here`
-            KOp KA = k_operand(K, klds, lane);
-            if (here && (lane & 15) == row) {
-                // the four lanes of row `row` take the new key into the A operand
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    KA.k[kk] = s_new[0][4 * kk + grp];
-            }
-            if (tb + kSub <= t1)
-                rs = qk_softmax<DT, SUFFIX>(st, KA, qop, tb, t_beg, t1, lane, a.scale_log2, pb,
-                                            alpha);
-            else
-                rs = qk_softmax<DT, true>(st, KA, qop, tb, t_beg, t1, lane, a.scale_log2, pb,
-                                          alpha);
-            stage_v(V, vlds, lane);
-            if (here && lane < 16)
-                *(u32x4 *)(vlds + row * kVStride + lane * 8) = s_new[1][lane];
-            pv_mma<DT>(st, vlds, pb, rs, alpha, lane);
         }
 
         // sum of the four lane groups' shares of l (m is already uniform across them)
