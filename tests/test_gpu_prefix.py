@@ -210,6 +210,35 @@ def test_grouped_prefix_decode(case, P, SP):
     assert np.array_equal(bits_of(gk), c["kp"]) and np.array_equal(bits_of(gv), c["vp"])
 
 
+@pytest.mark.parametrize("groups,max_own", [([(8, 4096)], 4000), ([(3, 200), (5, 2500)], 6000)])
+def test_one_pass_long_lists(groups, max_own):
+    """One-pass shared-prefix decode on tiles whose sub-tile lists give each wave
+    well over 64 steps (a 4,096-token prefix with members of up to 4,000 own
+    positions; a short-prefix group beside a long one), so the per-lane
+    descriptors are renewed several times in a launch; plain and fused."""
+    dtype, Hq, Hkv, B = "fp16", 32, 8, 16
+    c = _grouped_case(53, groups, Hq, Hkv, B, dtype, max_own=max_own)
+    print(f"[gpu] one-pass long lists groups={groups} lens={c['lens'].tolist()}", flush=True)
+    kp_pre, vp_pre = c["kp"].copy(), c["vp"].copy()
+    slots_ref = O.append(c["kp"], c["vp"], c["kn"], c["vn"], c["tables"], c["lens"], B, c["NB"])
+    ref = O.attention(c["q"], c["kp"], c["vp"], c["tables"], c["lens"], Hkv, B, c["NB"],
+                      scale_for(128), dtype)
+    args = (to_dev(c["q"], dtype, DEV), i32(c["tables"], DEV), i32(c["lens"], DEV),
+            i32(c["cu"], DEV), i32(c["plens"], DEV))
+    gk, gv = to_dev(c["kp"], dtype, DEV), to_dev(c["vp"], dtype, DEV)
+    out, _, _ = _run((gk, gv), *args, dtype, 0)
+    ok, err, nbad = tol_ok(widen_out(out), ref)
+    assert ok, ("plain", err, nbad)
+    gk, gv = to_dev(kp_pre, dtype, DEV), to_dev(vp_pre, dtype, DEV)
+    slots = torch.full((len(c["lens"]),), -7, dtype=torch.int64, device=DEV)
+    out, _, _ = _run((gk, gv), *args, dtype, 0,
+                     (to_dev(c["kn"], dtype, DEV), to_dev(c["vn"], dtype, DEV)), slots)
+    ok, err, nbad = tol_ok(widen_out(out), ref)
+    assert ok, ("fused", err, nbad)
+    assert np.array_equal(slots.cpu().numpy(), slots_ref)
+    assert np.array_equal(bits_of(gk), c["kp"]) and np.array_equal(bits_of(gv), c["vp"])
+
+
 def test_long_suffixes_split():
     """Members with 1-20,000 own positions after a 2,048-token prefix at the
     long-context shapes (32 query / 8 KV heads, blocks of 128, bf16): prefix
