@@ -1248,42 +1248,6 @@ void slotted_mfma_kernel(DecodeArgs a)
     }
 }
 
-// P.V of one staged sub-tile for NH column halves: the V^T operand is read from
-// LDS once (eight transposing reads into separate registers) and multiplied with
-// each half's probabilities.
-template <int DT, int NH>
-__device__ __forceinline__ void pv_mma_halves(GqaState (&st)[NH], const uint16_t *vlds,
-                                              const u32x2 (&pb)[NH], const bool (&rescale)[NH],
-                                              const float (&alpha)[NH], int lane,
-                                              const bool (&live)[NH])
-{
-    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    const int j = lane & 15, grp = lane >> 4;
-    const uint16_t *base = vlds + (4 * grp + (j >> 2)) * kVStride + 4 * (j & 3);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    i16x4 va[8];
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj)
-        va[jj] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + 16 * jj));
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-        if (!live[h])
-            continue;  // wave-uniform: a half with no active column this sub-tile
-        if (rescale[h]) {
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj)
-                st[h].acc[jj] *= alpha[h];
-        }
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-            st[h].acc[jj] = mfma_pv<DT>(__builtin_bit_cast(u32x2, va[jj]), pb[h], st[h].acc[jj]);
-    }
-    // the next sub-tile's LDS writes must not pass these reads
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Shared-prefix decode in one pass.  One work-group per (query tile, KV head).  A
 // tile is NH halves of 16 MFMA columns; each half holds the G query heads of
 // floor(16/G) consecutive member sequences of a group.  The work-group's

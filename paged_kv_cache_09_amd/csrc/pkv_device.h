@@ -98,19 +98,6 @@ __device__ __forceinline__ u32x4 ldbuf(__amdgpu_buffer_rsrc_t r, int off)
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL);
 }
 
-// Table entry `idx` of a row of `width` entries, read with a vector load.  Loops
-// that also wait on LDS use this instead of a scalar load: scalar loads and LDS
-// accesses share one wait counter and scalar results return out of order, so the
-// next LDS wait would also wait for the scalar load and expose its latency on
-// every step; a vector load is counted in order with the tile loads.  The value
-// stays in a VGPR (identical in every lane) until the caller makes it uniform,
-// which is where the wait for it lands.  An index past the row reads 0.
-__device__ __forceinline__ int32_t table_entry_v(const int32_t *row, int width, int idx)
-{
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(row, width * 4);
-    return (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r, idx * 4, 0, 0);
-}
-
 // ---- cross-lane -------------------------------------------------------------
 // DPP row operations act inside rows of 16 lanes.  The four steps below give
 // every lane of a row the same sum (each step adds a value and its mirror, and
