@@ -79,6 +79,11 @@ def parse():
                     help="for a split workload, run the split decode and the standalone merge "
                          "(paged_attention_reduce) as two launches per layer instead of "
                          "paged_attention_split_decode, which merges in the same launch")
+    ap.add_argument("--order", default="long", choices=["long", "natural"],
+                    help="dispatch order of the single-pass decode: long (the default) puts "
+                         "the sequences longer than twice the batch mean first, computed on the "
+                         "host from the batch's lengths (paged_attention_decode_ordered); "
+                         "natural keeps the batch order")
     ap.add_argument("--no-prefix", action="store_true",
                     help="for a shared-prefix workload, run the plain fused decode instead of "
                          "paged_attention_prefix_decode")
@@ -335,6 +340,17 @@ def bench_step(args):
 
     fused = not args.separate
     prefix = cfg.prefix_tokens > 0 and not args.no_prefix
+    # Single-pass decode: dispatch the long sequences first (a host-side plan from
+    # the lengths the caller already has; the results do not depend on the order).
+    order_dev = None
+    order_rule = "natural (batch order)"
+    if not P and not prefix and args.order == "long":
+        n_host = np.asarray(w0.lengths, np.int64)
+        longs = [i for i in range(S) if n_host[i] > 2 * n_host.mean()]
+        rest = [i for i in range(S) if n_host[i] <= 2 * n_host.mean()]
+        order_dev = torch.tensor(longs + rest, dtype=torch.int32, device=dev)
+        order_rule = ("sequences longer than twice the batch mean first (%d of %d), then the "
+                      "rest in batch order" % (len(longs), S))
     # split workloads merge their partitions in the decode launch itself, with one
     # zeroed arrival counter per (sequence, KV head) that every launch leaves zero
     merged = bool(P) and not args.no_merge and not prefix
@@ -370,6 +386,10 @@ def bench_step(args):
                                              part_o, part_lse, counters,
                                              k_new=L["kn"] if fused else None,
                                              v_new=L["vn"] if fused else None, scale=scale)
+        elif order_dev is not None:
+            pkv.paged_attention_decode_ordered(o, L["q"], L["k"], L["v"], tables, lens, order_dev,
+                                               k_new=L["kn"] if fused else None,
+                                               v_new=L["vn"] if fused else None, scale=scale)
         elif fused:
             pkv.paged_attention_append_decode(o, L["q"], L["k"], L["v"], L["kn"], L["vn"],
                                               tables, lens, scale=scale, partition_size=P,
@@ -487,9 +507,12 @@ def bench_step(args):
                      else ("paged_attention_split_decode (merged in launch)" +
                            (" with the fused append" if fused else " after paged_kv_append"))
                      if merged
-                     else ("paged_attention_append_decode" if fused else
-                           "paged_kv_append + paged_attention_decode") +
+                     else ("paged_attention_decode_ordered (fused append)" if fused and order_dev
+                           is not None else "paged_attention_append_decode" if fused else
+                           "paged_kv_append + paged_attention_decode_ordered" if order_dev
+                           is not None else "paged_kv_append + paged_attention_decode") +
                      (" + paged_attention_reduce" if P else "")),
+            "dispatch_order": order_rule,
             "accumulate": "fp32",
         },
         "hbm_gbps": round(gbps, 1),
@@ -500,7 +523,10 @@ def bench_step(args):
                         "paged_attention_prefix_decode (one pass)") if prefix
                        else "paged_attention_split_decode (partitions merged in launch)"
                        if merged
+                       else "paged_attention_decode_ordered (fused append)" if fused and
+                       order_dev is not None
                        else "paged_attention_append_decode" if fused
+                       else "paged_attention_decode_ordered" if order_dev is not None
                        else "paged_attention_decode"),
             "bound": "hbm",
             "achieved": round(dec_gbps, 1),

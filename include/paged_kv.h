@@ -273,6 +273,38 @@ int paged_attention_split_decode(void *out, const void *q, void *k_pool, void *v
                                  void *stream);
 
 /*
+ * paged_attention_decode_ordered -- the single-pass decode (with the append
+ * fused when k_new / v_new are given) with a caller-chosen dispatch order.
+ *
+ * Work items are one per (sequence, KV head), launched in grid order; the
+ * sequences of a batch are otherwise dispatched in batch order, so a long
+ * sequence near the end of the batch finishes last and the launch waits for it.
+ * A caller that keeps its lengths on the host (any serving engine does) can put
+ * the longest sequences first: the work items of sequence seq_order[i] take the
+ * place of sequence i's.  The output, pools and slots are the same, bit for bit,
+ * for every order (each item's arithmetic does not depend on where it runs).
+ * The address walk and attention are those of paged_attention_decode
+ * ("显存虚拟化革命：PagedAttention 内存池管理与显存碎片终结", blog.llmgo.top, §五.1).
+ *
+ *   seq_order      device int32 [num_seqs], 4-byte aligned, a permutation of
+ *                  0 .. num_seqs-1 (entries are clamped to that range on the
+ *                  device; PKV_DEBUG_CHECK=1 rejects any entry out of range or
+ *                  repeated with PKV_EDEVICE).  Null gives PKV_EINVAL.
+ *   k_new, v_new   optional, both or neither (PKV_EINVAL otherwise): the fused
+ *                  append of paged_attention_append_decode, with slot_out
+ *   out            [num_seqs][num_q_heads][head_dim], dtype; required
+ * Other arguments, layouts and errors as for paged_attention_append_decode in
+ * single-pass mode (partition_size 0).
+ */
+int paged_attention_decode_ordered(void *out, const void *q, void *k_pool, void *v_pool,
+                                   const void *k_new, const void *v_new, int64_t *slot_out,
+                                   const int32_t *block_tables, const int32_t *context_lens,
+                                   const int32_t *seq_order, int num_seqs, int num_q_heads,
+                                   int num_kv_heads, int head_dim, int block_size,
+                                   int max_blocks_per_seq, int64_t num_blocks, float scale,
+                                   int dtype, void *stream);
+
+/*
  * paged_attention_split_decode_noalloc -- paged_attention_split_decode with no
  * workspace argument and no allocation, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that

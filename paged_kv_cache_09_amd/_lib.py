@@ -64,6 +64,9 @@ def load():
     L.paged_attention_split_decode.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32,
                                                i32, i32, i64, f32, i32, i32, P, P, P, i32, P]
     L.paged_attention_split_decode.restype = i32
+    L.paged_attention_decode_ordered.argtypes = [P, P, P, P, P, P, P, P, P, P, i32, i32, i32,
+                                                 i32, i32, i32, i64, f32, i32, P]
+    L.paged_attention_decode_ordered.restype = i32
     L.paged_attention_split_decode_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32,
                                                        i32, i32, i32, i64, f32, i32, i32, P]
     L.paged_attention_split_decode_noalloc.restype = i32
@@ -403,6 +406,30 @@ def paged_attention_append_decode(out, q, k_pool, v_pool, k_new, v_new, block_ta
         scale, int(partition_size), mp, _p(part_o), _p(part_lse), _dtype_code(q),
         _stream(dev))
     _check(rc, "paged_attention_append_decode")
+
+
+def paged_attention_decode_ordered(out, q, k_pool, v_pool, block_tables, context_lens,
+                                   seq_order, k_new=None, v_new=None, slot_out=None,
+                                   scale: Optional[float] = None):
+    """Single-pass decode (the append fused when k_new / v_new are given) whose work
+    items are dispatched in the order seq_order (int32 [S], a permutation of
+    0..S-1): the same results, bit for bit, as the natural order."""
+    NB, Hkv, B, D, S, Hq, W = _queries(out, q, k_pool, v_pool, block_tables, context_lens)
+    _expect(k_new, (S, Hkv, D), "k_new")
+    _expect(v_new, (S, Hkv, D), "v_new")
+    _same_dtype(k_pool, (k_new, "k_new"), (v_new, "v_new"))
+    _expect(slot_out, (S,), "slot_out")
+    _expect(seq_order, (S,), "seq_order")
+    dev = _dev(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens, slot_out,
+               seq_order)
+    _ints((block_tables, "i32", "block_tables"), (context_lens, "i32", "context_lens"),
+          (slot_out, "i64", "slot_out"), (seq_order, "i32", "seq_order"))
+    scale = _scale(scale)
+    rc = load().paged_attention_decode_ordered(
+        _p(out), _p(q), _p(k_pool), _p(v_pool), _p(k_new), _p(v_new), _p(slot_out),
+        _p(block_tables), _p(context_lens), _p(seq_order), S, Hq, Hkv, D, B, W, NB, scale,
+        _dtype_code(q), _stream(dev))
+    _check(rc, "paged_attention_decode_ordered")
 
 
 def paged_attention_split_decode(out, q, k_pool, v_pool, block_tables, context_lens,

@@ -133,6 +133,23 @@ __global__ void debug_copies_kernel(const int32_t *src, const int32_t *dst, int 
             atomicOr(&g_debug_flag, 16);
 }
 
+// A dispatch order: every entry inside the batch and no sequence twice (so it is
+// a permutation of 0 .. num_seqs-1).
+__global__ void debug_order_kernel(const int32_t *order, int num_seqs)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= num_seqs)
+        return;
+    const int32_t v = order[i];
+    if (v < 0 || v >= num_seqs) {
+        atomicOr(&g_debug_flag, 2);
+        return;
+    }
+    for (int j = 0; j < i; ++j)
+        if (order[j] == v)
+            atomicOr(&g_debug_flag, 16);
+}
+
 // Slot copies: blocks inside the pool, both row ranges inside their block, and no
 // destination row that is a source row of any copy or a destination row of
 // another (the result would depend on copy order).
@@ -230,6 +247,16 @@ int debug_check_copies(const int32_t *src, const int32_t *dst, int num_pairs,
     hipLaunchKernelGGL(debug_clear_kernel, dim3(1), dim3(1), 0, stream);
     hipLaunchKernelGGL(debug_copies_kernel, dim3((num_pairs + 255) / 256), dim3(256), 0, stream,
                        src, dst, num_pairs, num_blocks);
+    if (hipGetLastError() != hipSuccess)
+        return PKV_ELAUNCH;
+    return read_debug_flag(stream);
+}
+
+int debug_check_order(const int32_t *order, int num_seqs, hipStream_t stream)
+{
+    hipLaunchKernelGGL(debug_clear_kernel, dim3(1), dim3(1), 0, stream);
+    hipLaunchKernelGGL(debug_order_kernel, dim3((num_seqs + 255) / 256), dim3(256), 0, stream,
+                       order, num_seqs);
     if (hipGetLastError() != hipSuccess)
         return PKV_ELAUNCH;
     return read_debug_flag(stream);
@@ -518,9 +545,11 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
                 int max_blocks_per_seq, int64_t num_blocks, float scale, int partition_size,
                 int max_partitions, float *part_o, float *part_lse, int dtype, void *stream,
                 const PrefixGroups &pg = PrefixGroups(), int32_t *counters = nullptr,
-                bool validate_only = false)
+                bool validate_only = false, const int32_t *seq_order = nullptr)
 {
     const bool prefix = pg.group_cu != nullptr;
+    if (seq_order && (((uintptr_t)seq_order & 3u) || prefix))
+        return PKV_EINVAL;
     if (!q || !k_pool || !v_pool || !block_tables || !context_lens)
         return PKV_EINVAL;
     if (num_seqs < 0 || num_q_heads <= 0 || partition_size < 0)
@@ -612,6 +641,8 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
         if (rc == PKV_OK && prefix)
             rc = pkv::debug_check_groups(pg.group_cu, pg.prefix_lens, context_lens,
                                          pg.num_groups, num_seqs, k_new ? 1 : 0, st);
+        if (rc == PKV_OK && seq_order)
+            rc = pkv::debug_check_order(seq_order, num_seqs, st);
         if (rc)
             return rc;
     }
@@ -638,6 +669,7 @@ int decode_impl(void *out, const void *q, const void *k_pool, const void *v_pool
     a.slot_out = slot_out;
     a.block_size = block_size;
     a.counters = counters;
+    a.seq_order = seq_order;
     if (prefix && partition_size == 0) {
         // one pass: each work-group streams its tile's prefix, then each member's
         // own positions, and writes `out`
@@ -734,6 +766,24 @@ int paged_attention_split_decode(void *out, const void *q, void *k_pool, void *v
                        block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                        block_size, max_blocks_per_seq, num_blocks, scale, partition_size,
                        max_partitions, part_o, part_lse, dtype, stream, PrefixGroups(), counters);
+}
+
+int paged_attention_decode_ordered(void *out, const void *q, void *k_pool, void *v_pool,
+                                   const void *k_new, const void *v_new, int64_t *slot_out,
+                                   const int32_t *block_tables, const int32_t *context_lens,
+                                   const int32_t *seq_order, int num_seqs, int num_q_heads,
+                                   int num_kv_heads, int head_dim, int block_size,
+                                   int max_blocks_per_seq, int64_t num_blocks, float scale,
+                                   int dtype, void *stream)
+{
+    if (!seq_order || !out)
+        return PKV_EINVAL;
+    if ((k_new == nullptr) != (v_new == nullptr))
+        return PKV_EINVAL;
+    return decode_impl(out, q, k_pool, v_pool, k_new, v_new, k_new ? slot_out : nullptr,
+                       block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                       block_size, max_blocks_per_seq, num_blocks, scale, 0, 0, nullptr, nullptr,
+                       dtype, stream, PrefixGroups(), nullptr, false, seq_order);
 }
 
 }  // extern "C"

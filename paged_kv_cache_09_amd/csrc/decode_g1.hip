@@ -264,7 +264,7 @@ void decode_g1_kernel(DecodeArgs a)
     const int px0 = item % parts;
     const int rest = item / parts;
     const int h = rest % a.num_kv_heads;  // query head == kv head
-    const int s = rest / a.num_kv_heads;
+    const int s = ordered_seq(a, rest / a.num_kv_heads);
 
     const int tid = threadIdx.x;
     // wave index, made explicitly uniform so that tile indices and table lookups

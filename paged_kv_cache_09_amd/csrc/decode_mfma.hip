@@ -447,7 +447,7 @@ void decode_mfma_kernel(DecodeArgs a)
     const int px0 = item % parts;
     const int rest = item / parts;
     const int g = rest % a.num_kv_heads;  // kv head
-    const int s = rest / a.num_kv_heads;
+    const int s = ordered_seq(a, rest / a.num_kv_heads);
     const int G = a.num_q_heads / a.num_kv_heads;
     const int tid = threadIdx.x;
     // wave index, made explicitly uniform so that tile indices and table lookups

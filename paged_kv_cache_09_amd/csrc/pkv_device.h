@@ -219,7 +219,17 @@ struct DecodeArgs {
     // head); the last work-group of an item to finish merges its partitions into
     // `out` and puts the counter back to 0
     int32_t *counters;
+    // optional dispatch order (null: natural): the work items of sequence
+    // seq_order[i] take the place of sequence i's in the grid; entries are
+    // clamped to [0, num_seqs) so that a bad order cannot reach outside the batch
+    const int32_t *seq_order;
 };
+
+// The sequence whose work items sit at position i of the grid's sequence order.
+__device__ __forceinline__ int ordered_seq(const DecodeArgs &a, int i)
+{
+    return a.seq_order ? min(max(as_meta(a.seq_order)[i], 0), a.num_seqs - 1) : i;
+}
 
 // ---- merged split mode --------------------------------------------------------
 // The work-groups of one item exchange their partials through the workspace.

@@ -75,5 +75,6 @@ int debug_check_copies(const int32_t *src, const int32_t *dst, int num_pairs,
                        int64_t num_blocks, hipStream_t stream);
 int debug_check_slot_copies(const int32_t *copies, int num_copies, int block_size,
                             int64_t num_blocks, hipStream_t stream);
+int debug_check_order(const int32_t *order, int num_seqs, hipStream_t stream);
 
 }  // namespace pkv

@@ -43,7 +43,8 @@ def test_every_declared_symbol_is_exported(lib):
             "paged_attention_reduce", "paged_attention_split_decode",
             "paged_attention_split_decode_noalloc", "paged_kv_copy_slots",
             "paged_attention_decode_slotted_split", "paged_attention_prefix_split_decode",
-            "pkv_status_string", "pkv_max_partitions"} <= set(declared)
+            "paged_attention_decode_ordered", "pkv_status_string",
+            "pkv_max_partitions"} <= set(declared)
     assert pkv.exported_symbols() == declared
 
 
@@ -168,6 +169,25 @@ def test_split_decode_argument_errors(lib):
     assert call(MP=2) == EWORKSPACE              # 80 positions need 3 partitions of 32
     assert call(po=None) == EWORKSPACE
     assert call(Hq=34) == ENOTSUP
+    assert call(scale=float("inf")) == EINVAL
+    assert call(S=0) == 0
+
+
+@host_only
+def test_decode_ordered_argument_errors(lib):
+    f = lib.paged_attention_decode_ordered
+
+    def call(out=A, kn=None, vn=None, order=A, S=2, Hq=12, Hkv=2, B=16, W=5, scale=0.088,
+             dt=0):
+        return f(out, A, A, A, kn, vn, None, A, A, order, S, Hq, Hkv, 128, B, W, 64, scale, dt,
+                 None)
+
+    assert call(order=None) == EINVAL               # the order is required
+    assert call(order=P((1 << 20) + 2)) == EINVAL   # misaligned order
+    assert call(out=None) == EINVAL
+    assert call(kn=A) == EINVAL                     # k_new without v_new
+    assert call(Hq=34) == ENOTSUP
+    assert call(B=24) == ENOTSUP
     assert call(scale=float("inf")) == EINVAL
     assert call(S=0) == 0
 

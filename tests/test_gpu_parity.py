@@ -18,8 +18,8 @@ torch = pytest.importorskip("torch")
 
 from workloads import get_config, make_workload  # noqa: E402
 from oracle import oracle as O  # noqa: E402
-from gpu_harness import (GpuStep, bits_of, fused_step, merged_step, scale_for, tol_ok,  # noqa: E402
-                         widen_out)
+from gpu_harness import (GpuStep, bits_of, fused_step, i32, merged_step, scale_for,  # noqa: E402
+                         tol_ok, widen_out)
 import paged_kv_cache_09_amd as pkv  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -131,6 +131,61 @@ def test_fused_append_decode(key, P):
     assert np.array_equal(bits_of(g.v_pool[idx]), r["v_pool"][ref])
     ok, err, nbad = tol_ok(widen_out(out), r["out"])
     assert ok, f"{key} P={P}: max err {err}, {nbad} bad"
+
+
+# ---------------------------------------------------------------------------
+def _orders(n, seed):
+    """Dispatch orders to try: sequences above twice the mean length first, the
+    reverse of the batch, and a seeded random permutation."""
+    S = len(n)
+    big = [i for i in range(S) if n[i] > 2 * n.mean()]
+    long_first = big + [i for i in range(S) if i not in set(big)]
+    rng = np.random.default_rng(seed)
+    return {"long_first": np.array(long_first), "reversed": np.arange(S)[::-1].copy(),
+            "random": rng.permutation(S)}
+
+
+@pytest.mark.parametrize("key", ["c1a", "c2", "c3", "c4"])
+def test_decode_ordered_equals_natural_order(key):
+    """paged_attention_decode_ordered (fused append): pools and slots bit-exact
+    against the oracle and the output within tolerance, for several dispatch
+    orders; the output is also bit for bit the natural order's."""
+    w, r = oracle_for(key)
+    ref_blocks = referenced_blocks(w)
+    idx = None
+    natural = None
+    for name, order in _orders(w.lengths, 7).items():
+        print(f"[gpu] ordered decode {key} order={name}", flush=True)
+        g = GpuStep(w, append=False)
+        if natural is None:
+            natural = fused_step(g, 0).cpu()
+            g = GpuStep(w, append=False)
+        out = torch.empty_like(g.q)
+        pkv.paged_attention_decode_ordered(out, g.q, g.k_pool, g.v_pool, g.tables, g.lens,
+                                           i32(order, g.device), k_new=g.k_new,
+                                           v_new=g.v_new, slot_out=g.slots)
+        torch.cuda.synchronize()
+        assert np.array_equal(g.slots.cpu().numpy(), r["slots"])
+        idx = torch.from_numpy(ref_blocks.astype(np.int64)).to(g.device)
+        assert np.array_equal(bits_of(g.k_pool[idx]), r["k_pool"][ref_blocks])
+        assert np.array_equal(bits_of(g.v_pool[idx]), r["v_pool"][ref_blocks])
+        ok, err, nbad = tol_ok(widen_out(out), r["out"])
+        assert ok, f"{key} {name}: max err {err}, {nbad} bad"
+        assert torch.equal(out.cpu().view(torch.int16), natural.view(torch.int16)), name
+
+
+def test_decode_ordered_debug_check_rejects_bad_orders(monkeypatch):
+    w = _small(block_size=16, num_q_heads=12, num_kv_heads=2, lengths=(5, 40, 17))
+    g = GpuStep(w)
+    monkeypatch.setenv("PKV_DEBUG_CHECK", "1")
+    out = torch.empty_like(g.q)
+    good = i32(np.array([2, 0, 1]), g.device)
+    pkv.paged_attention_decode_ordered(out, g.q, g.k_pool, g.v_pool, g.tables, g.lens, good)
+    for bad in ([0, 0, 1], [0, 1, 3], [-1, 1, 2]):  # a repeat, past the batch, negative
+        with pytest.raises(pkv.PagedKVError) as e:
+            pkv.paged_attention_decode_ordered(out, g.q, g.k_pool, g.v_pool, g.tables, g.lens,
+                                               i32(np.array(bad), g.device))
+        assert e.value.status == -5
 
 
 # ---------------------------------------------------------------------------
