@@ -78,6 +78,8 @@ def lib():
         L.oracle_append_tokens.restype = C.c_int
         L.oracle_locate_slotted.argtypes = [P, i64, i64, i64, i64, P, P]
         L.oracle_locate_slotted.restype = C.c_int
+        L.oracle_append_slotted.argtypes = [P, P, P, P, P, P, P] + [i64] * 6
+        L.oracle_append_slotted.restype = C.c_int
         L.oracle_attention_slotted.argtypes = [P, P, P, P, P, P] + [i64] * 7 + [C.c_double,
                                                                                 C.c_int, C.c_int]
         L.oracle_attention_slotted.restype = C.c_int
@@ -211,6 +213,22 @@ def locate_slotted(segs, block_size: int, num_blocks: int, t: int):
                                      C.byref(phys), C.byref(off))
     _check(rc, "locate_slotted")
     return phys.value, off.value
+
+
+def append_slotted(k_pool, v_pool, k_new, v_new, segs, num_segs, block_size, num_blocks):
+    """In-place append of each sequence's new token at position n-1 of its segment
+    list (n = sum of its segment lengths); returns slot ids (int64 [S], -1 for
+    n = 0)."""
+    assert k_pool.flags.c_contiguous and v_pool.flags.c_contiguous
+    S, Hkv, D = k_new.shape
+    segs = _c(segs, np.int32)
+    slots = np.empty(S, dtype=np.int64)
+    rc = lib().oracle_append_slotted(_p(k_pool), _p(v_pool), _p(_c(k_new, np.uint16)),
+                                     _p(_c(v_new, np.uint16)), _p(segs),
+                                     _p(_c(num_segs, np.int32)), _p(slots), S, segs.shape[1],
+                                     Hkv, D, block_size, num_blocks)
+    _check(rc, "append_slotted")
+    return slots
 
 
 def attention_slotted(q, k_pool, v_pool, segs, num_segs, num_kv_heads, block_size, num_blocks,

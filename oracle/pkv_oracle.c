@@ -50,6 +50,11 @@
  *    rows move from (block, slot offset) to offset 0 of the dedicated block,
  *    every head, in K and in V; the source rows are left as they are.  Written
  *    here for any destination offset.
+ *  - Slotted append: a decode step's new token goes to the sequence's last
+ *    position n-1, n being the sum of its segment lengths (the lengths count the
+ *    new token, as for block tables); the walk over the segments gives its (block,
+ *    offset), which must be the node's own slot (a shared one is split first, as
+ *    above).  Bit copy, every head, K and V.
  *  - Partials and merge: attention over the token range of one partition, its
  *    log-sum-exp, and the exact log-sum-exp combination of partitions.  The
  *    pages do not describe partitions; the merge is the algebraic identity
@@ -546,6 +551,63 @@ int oracle_locate_slotted(const int32_t *segs, int64_t num_segs, int64_t block_s
         start += len;
     }
     return OR_ETABLE;  /* t is past the sequence */
+}
+
+/* Append of each sequence's new token to its slotted segments: position n-1 of the
+ * concatenated segments (n = sum of the first num_segs[s] lengths), every head,
+ * K and V; slot_out[s] = block * block_size + offset, or -1 when n = 0.  Two
+ * sequences writing one slot is an error (OR_EDUP).  segs: [num_seqs][max_segs][3]. */
+int oracle_append_slotted(uint16_t *k_pool, uint16_t *v_pool, const uint16_t *k_new,
+                          const uint16_t *v_new, const int32_t *segs, const int32_t *num_segs,
+                          int64_t *slot_out, int64_t num_seqs, int64_t max_segs,
+                          int64_t num_kv_heads, int64_t head_dim, int64_t block_size,
+                          int64_t num_blocks)
+{
+    int rc = check_dims(num_kv_heads, head_dim, block_size, 1, num_blocks);
+    if (rc)
+        return rc;
+    if (num_seqs < 0 || max_segs < 0)
+        return OR_EARG;
+    unsigned char *map = calloc((size_t)(num_blocks * block_size), 1);
+    if (!map)
+        return OR_ENOMEM;
+    for (int64_t s = 0; s < num_seqs && rc == OR_OK; ++s) {
+        const int32_t *row = segs + s * max_segs * 3;
+        const int64_t ns = num_segs[s];
+        if (ns < 0 || ns > max_segs) {
+            rc = OR_EARG;
+            break;
+        }
+        int64_t n = 0;
+        for (int64_t i = 0; i < ns; ++i)
+            n += row[3 * i + 2];
+        if (n <= 0) {
+            if (slot_out)
+                slot_out[s] = -1;
+            continue;
+        }
+        int64_t phys, off;
+        rc = oracle_locate_slotted(row, ns, block_size, num_blocks, n - 1, &phys, &off);
+        if (rc)
+            break;
+        rc = mark_slot(map, phys * block_size + off);
+        if (rc)
+            break;
+        for (int64_t h = 0; h < num_kv_heads; ++h) {
+            const uint16_t *kn = k_new + (s * num_kv_heads + h) * head_dim;
+            const uint16_t *vn = v_new + (s * num_kv_heads + h) * head_dim;
+            for (int64_t d = 0; d < head_dim; ++d) {
+                const int64_t at =
+                    oracle_elem_offset(phys, h, off, d, num_kv_heads, block_size, head_dim);
+                k_pool[at] = kn[d];
+                v_pool[at] = vn[d];
+            }
+        }
+        if (slot_out)
+            slot_out[s] = phys * block_size + off;
+    }
+    free(map);
+    return rc;
 }
 
 /* Decode attention over slotted segments: out[s][h] = softmax(scale q.K^T) V over

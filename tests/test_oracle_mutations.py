@@ -68,6 +68,12 @@ MUTANTS = {
                                "block_size, head_dim);\n                    k_pool[to] = k_pool[from];"),
     "slot_offset_dropped": ("*off = so + (t - start);", "*off = (t - start);"),
     "segment_end_inclusive": ("if (t < start + len) {", "if (t <= start + len) {"),
+    "slotted_append_at_n": ("rc = oracle_locate_slotted(row, ns, block_size, num_blocks, n - 1, &phys, &off);",
+                            "rc = oracle_locate_slotted(row, ns, block_size, num_blocks, n, &phys, &off);"),
+    "slotted_append_skips_values": ("                k_pool[at] = kn[d];\n                v_pool[at] = vn[d];",
+                                    "                k_pool[at] = kn[d];"),
+    "slotted_append_value_head_zero": ("const uint16_t *vn = v_new + (s * num_kv_heads + h) * head_dim;",
+                                       "const uint16_t *vn = v_new + (s * num_kv_heads) * head_dim;"),
     "segment_start_not_advanced": ("        start += len;\n    }\n    return OR_ETABLE;",
                                    "    }\n    return OR_ETABLE;"),
 }

@@ -132,3 +132,91 @@ def test_order_dependent_or_out_of_range_copies_are_rejected(oracle_lib, copies)
     kp = kp[:16]
     with pytest.raises(Exception):
         oracle_lib.copy_slots(np.ascontiguousarray(kp), np.ascontiguousarray(vp), copies)
+
+
+# ---------------------------------------------------------------------------
+# the append of a decode step's token to a slotted sequence
+# ---------------------------------------------------------------------------
+def test_slotted_append_of_the_page_example(oracle_lib):
+    """After the split, path Y = A, B lists B as (4, 0, 9): the token counted by its
+    grown length lands at the fixture's append slot (4, 8), in every head, K and
+    V.  A sequence with no segments (n = 0) gets slot -1 and writes nothing.
+    Nothing else in the pool changes."""
+    g = _golden()
+    B, NB, a = g["block_size"], g["pool_blocks"], g["append"]
+    Hkv, D = 2, 128
+    kp, vp = _marked_pools(NB, Hkv, B, D, seed=21)
+    k0, v0 = kp.copy(), vp.copy()
+    rng = np.random.default_rng(22)
+    kn = (rng.standard_normal((2, Hkv, D)) * 0.5).astype(np.float16).view(np.uint16)
+    vn = (rng.standard_normal((2, Hkv, D)) * 0.5).astype(np.float16).view(np.uint16)
+    b_after = g["after"]["B"][0]
+    segs = np.zeros((2, 2, 3), np.int32)
+    segs[1] = [g["before"]["A"][0], [b_after[0], b_after[1], b_after[2] + 1]]
+    nseg = np.array([0, 2], np.int32)
+    slots = oracle_lib.append_slotted(kp, vp, kn, vn, segs, nseg, B, NB)
+    assert slots.tolist() == [-1, a["block"] * B + a["offset"]]
+    want_k, want_v = k0.copy(), v0.copy()
+    want_k[a["block"], :, a["offset"]] = kn[1]
+    want_v[a["block"], :, a["offset"]] = vn[1]
+    assert np.array_equal(kp, want_k) and np.array_equal(vp, want_v)
+
+
+def test_slotted_append_then_attention_is_brute_force(oracle_lib):
+    """Random node lists, each sequence's last segment a private slot: after the
+    append, attention over the segments equals brute force over each sequence's
+    logical rows with the new row last; zero-length segments and empty
+    sequences included."""
+    rng = np.random.default_rng(5)
+    B, Hkv, Hq, D, NB = 16, 2, 6, 128, 40
+    S, MS = 6, 5
+    kp, vp = _marked_pools(NB, Hkv, B, D, seed=8)
+    free = list(rng.permutation(NB))
+    segs = np.zeros((S, MS, 3), np.int32)
+    nseg = np.zeros(S, np.int32)
+    for s in range(S):
+        ns = int(rng.integers(0, MS + 1)) if s else 0
+        for i in range(ns):
+            blk = int(free.pop())
+            off = int(rng.integers(0, B))
+            ln = int(rng.integers(0, B - off + 1)) if i < ns - 1 else int(rng.integers(1, B - off + 1))
+            segs[s, i] = (blk, off, ln)
+        nseg[s] = ns
+    logical = []
+    for s in range(S):
+        rows = [(kp[b, :, o:o + ln].transpose(1, 0, 2), vp[b, :, o:o + ln].transpose(1, 0, 2))
+                for b, o, ln in segs[s, :nseg[s]]]
+        logical.append(rows)
+    kn = (rng.standard_normal((S, Hkv, D)) * 0.5).astype(np.float16).view(np.uint16)
+    vn = (rng.standard_normal((S, Hkv, D)) * 0.5).astype(np.float16).view(np.uint16)
+    slots = oracle_lib.append_slotted(kp, vp, kn, vn, segs, nseg, B, NB)
+    q = (rng.standard_normal((S, Hq, D)) * 0.5).astype(np.float16).view(np.uint16)
+    out = oracle_lib.attention_slotted(q, kp, vp, segs, nseg, Hkv, B, NB, SCALE, "fp16")
+    G = Hq // Hkv
+    qd = brute.widen(q, "fp16")
+    for s in range(S):
+        n = int(segs[s, :nseg[s], 2].sum())
+        if n == 0:
+            assert slots[s] == -1
+            assert np.all(out[s] == 0.0)
+            continue
+        lk = np.concatenate([r[0] for r in logical[s]]) if logical[s] else np.zeros((0, Hkv, D), np.uint16)
+        lv = np.concatenate([r[1] for r in logical[s]]) if logical[s] else np.zeros((0, Hkv, D), np.uint16)
+        # the last logical row is the new token's
+        lk = np.concatenate([lk[:n - 1], kn[s:s + 1]])
+        lv = np.concatenate([lv[:n - 1], vn[s:s + 1]])
+        b, o, ln = [x for x in segs[s, :nseg[s]] if x[2] > 0][-1]
+        assert slots[s] == b * B + o + ln - 1
+        K, V = brute.widen(lk, "fp16"), brute.widen(lv, "fp16")
+        for h in range(Hq):
+            ref = brute.attention_one(qd[s, h], K[:, h // G], V[:, h // G], SCALE)
+            assert np.abs(out[s, h] - ref).max() <= 1e-12
+
+
+def test_slotted_append_rejects_two_writes_to_one_slot(oracle_lib):
+    B, Hkv, D, NB = 16, 1, 128, 4
+    kp, vp = _marked_pools(NB, Hkv, B, D, seed=9)
+    segs = np.array([[[2, 0, 5]], [[2, 0, 5]]], np.int32)   # both end on (2, 4)
+    kn = np.zeros((2, Hkv, D), np.uint16)
+    with pytest.raises(Exception):
+        oracle_lib.append_slotted(kp, vp, kn, kn, segs, np.array([1, 1], np.int32), B, NB)
