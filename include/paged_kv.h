@@ -468,6 +468,38 @@ int paged_attention_decode_slotted(void *out, const void *q, const void *k_pool,
                                    void *stream);
 
 /*
+ * paged_attention_append_decode_slotted -- the step's cache append fused into the
+ * slotted decode: each sequence's new K/V row is written to its position n-1 and
+ * then attended to with the rest, in one launch.
+ *
+ * The lengths of a sequence's segments count its new token, as block-table
+ * lengths do (n = the sum of its segment lengths, clamped to their blocks):
+ * position n-1 is the last row of its last non-empty segment, and the new rows
+ * k_new[s] / v_new[s] are written there for every KV head, bit for bit.  That
+ * row must be the node's own slot: a node held in a shared slot is split into a
+ * block of its own first (paged_kv_copy_slots), since an append must not touch
+ * the shared slots ("碎片化的双重绞杀…" mhpq.cn Radix-Tree page, "核心设计原则";
+ * the append at the sequence's current position: blog.llmgo.top PagedAttention
+ * page, §三).  Attention is that of paged_attention_decode_slotted.
+ *
+ *   k_new, v_new   [num_seqs][num_kv_heads][head_dim], dtype, 16-byte aligned;
+ *                  required (PKV_EINVAL otherwise)
+ *   slot_out       optional int64 [num_seqs]: block * block_size + offset of the
+ *                  written row, -1 for a sequence with n = 0 (nothing written)
+ * Other arguments, limits and errors as for paged_attention_decode_slotted
+ * (PKV_DEBUG_CHECK=1 validates the segments as there).  Two sequences whose
+ * position n-1 is the same slot are a caller error: the row written is then
+ * either's.
+ */
+int paged_attention_append_decode_slotted(void *out, const void *q, void *k_pool, void *v_pool,
+                                          const void *k_new, const void *v_new,
+                                          int64_t *slot_out, const int32_t *segments,
+                                          const int32_t *num_segments, int num_seqs,
+                                          int num_q_heads, int num_kv_heads, int head_dim,
+                                          int block_size, int max_segments, int64_t num_blocks,
+                                          float scale, int dtype, void *stream);
+
+/*
  * paged_attention_decode_slotted_split -- slotted decode in split-context mode,
  * the partitions merged in the same launch.
  *

@@ -955,8 +955,13 @@ int slotted_impl(void *out, const void *q, const void *k_pool, const void *v_poo
                  int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                  int max_segments, int64_t num_blocks, float scale, int partition_size,
                  int max_partitions, float *part_o, float *part_lse, int32_t *counters, int dtype,
-                 void *stream)
+                 void *stream, const void *k_new = nullptr, const void *v_new = nullptr,
+                 int64_t *slot_out = nullptr)
 {
+    if ((k_new == nullptr) != (v_new == nullptr) || (k_new && partition_size > 0))
+        return PKV_EINVAL;
+    if (k_new && (!aligned16(k_new) || !aligned16(v_new) || ((uintptr_t)slot_out & 7u)))
+        return PKV_EINVAL;
     if (!out || !q || !k_pool || !v_pool || !segments || !num_segments)
         return PKV_EINVAL;
     if (num_seqs < 0 || num_q_heads <= 0 || max_segments <= 0 || partition_size < 0)
@@ -1018,6 +1023,9 @@ int slotted_impl(void *out, const void *q, const void *k_pool, const void *v_poo
     a.segments = segments;
     a.num_segments = num_segments;
     a.max_segments = max_segments;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.slot_out = k_new ? slot_out : nullptr;
     if (partition_size > 0) {
         a.partition_size = partition_size;
         a.max_partitions = max_partitions;
@@ -1066,6 +1074,21 @@ int paged_attention_decode_slotted(void *out, const void *q, const void *k_pool,
     return slotted_impl(out, q, k_pool, v_pool, segments, num_segments, num_seqs, num_q_heads,
                         num_kv_heads, head_dim, block_size, max_segments, num_blocks, scale, 0, 0,
                         nullptr, nullptr, nullptr, dtype, stream);
+}
+
+int paged_attention_append_decode_slotted(void *out, const void *q, void *k_pool, void *v_pool,
+                                          const void *k_new, const void *v_new,
+                                          int64_t *slot_out, const int32_t *segments,
+                                          const int32_t *num_segments, int num_seqs,
+                                          int num_q_heads, int num_kv_heads, int head_dim,
+                                          int block_size, int max_segments, int64_t num_blocks,
+                                          float scale, int dtype, void *stream)
+{
+    if (!k_new || !v_new)
+        return PKV_EINVAL;
+    return slotted_impl(out, q, k_pool, v_pool, segments, num_segments, num_seqs, num_q_heads,
+                        num_kv_heads, head_dim, block_size, max_segments, num_blocks, scale, 0, 0,
+                        nullptr, nullptr, nullptr, dtype, stream, k_new, v_new, slot_out);
 }
 
 int paged_attention_decode_slotted_split(void *out, const void *q, const void *k_pool,

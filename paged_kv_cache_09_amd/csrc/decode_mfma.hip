@@ -988,6 +988,52 @@ void prefix_mfma_kernel(DecodeArgs a)
 constexpr int kSegRound = 64;
 constexpr int kMaxRoundSubs = kSegRound * 16;  // a 256-row segment gives 16 sub-tiles
 
+// Fused append for slotted segments (one whole wave per call): sequence s's new K
+// and V rows of KV head g go to its position n-1, which is the last row of its
+// last non-empty segment (lengths clamped to the block, as the decode reads
+// them); with head 0 the wave also writes the slot id, or -1 when n = 0.  The
+// caller's next fenced barrier makes the rows visible to every wave's loads.
+template <int BS>
+__device__ __forceinline__ void slotted_append_wave(const DecodeArgs &a, int s, int g, int lane)
+{
+    const int32_t *segs = a.segments + (int64_t)s * a.max_segments * 3;
+    const int nseg = min(max(a.num_segments[s], 0), a.max_segments);
+    int last = -1, lblk = 0, lrow = 0;  // this lane's last non-empty segment
+    for (int base = 0; base < nseg; base += 64) {
+        const int i = base + lane;
+        if (i < nseg) {
+            const int off = min(max(segs[3 * i + 1], 0), BS);
+            const int len = min(max(segs[3 * i + 2], 0), BS - off);
+            if (len > 0) {
+                last = i;
+                lblk = segs[3 * i];
+                lrow = off + len - 1;
+            }
+        }
+    }
+    int best = last;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1)
+        best = max(best, __shfl_xor(best, d, 64));
+    if (best < 0) {
+        if (g == 0 && lane == 0 && a.slot_out)
+            a.slot_out[s] = -1;
+        return;
+    }
+    const int blk = __shfl(lblk, best & 63, 64), row = __shfl(lrow, best & 63, 64);
+    const int64_t dst = ((int64_t)blk * a.num_kv_heads + g) * BS * kHeadDim +
+                        (int64_t)row * kHeadDim;
+    const int64_t src = ((int64_t)s * a.num_kv_heads + g) * kHeadDim;
+    if (lane < 32) {
+        const int kv = lane >> 4, c = lane & 15;
+        const u32x4 val =
+            *(const u32x4 *)((const uint16_t *)(kv ? a.v_new : a.k_new) + src + 8 * c);
+        *(u32x4 *)((uint16_t *)(kv ? a.v_pool : a.k_pool) + dst + 8 * c) = val;
+    }
+    if (g == 0 && lane == 0 && a.slot_out)
+        a.slot_out[s] = (int64_t)blk * BS + row;
+}
+
 // Buffer resources of slotted sub-tile jx: its block, first row and row count
 // come from the LDS descriptors (made uniform for the scalar descriptor).
 __device__ __forceinline__ SubRsrc slot_rsrc(const int32_t *s_phys, const int32_t *s_rows, int jx,
@@ -1083,6 +1129,13 @@ void slotted_mfma_kernel(DecodeArgs a)
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
             qop[kk] = col < G ? *(const u32x4 *)(qrow + kk * 32) : (u32x4){0u, 0u, 0u, 0u};
+    }
+
+    // fused append (single pass only): wave 0 writes the new rows; the round's
+    // first barrier below completes the stores before any wave loads a sub-tile
+    if constexpr (!SPLIT) {
+        if (a.k_new && w == 0)
+            slotted_append_wave<BS>(a, s, g, lane);
     }
 
     for (int px = px0; px < np_loop; px += parts) {
@@ -1799,6 +1852,13 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
             qop[h][kk] = active[h] ? v : (u32x4){0u, 0u, 0u, 0u};
         }
     }
+    // 0. Fused append: each wave writes the new rows of members w, w + WAVES, ...;
+    // the fenced barrier after step 1 completes the stores before any load
+    if (a.k_new) {
+        for (int i = w; i < m; i += WAVES)
+            slotted_append_wave<BS>(a, s0 + i, g, lane);
+    }
+
     // 1. Common segments: lane k compares segment k of every member with member
     // 0's; each wave takes members 1 + w, 1 + w + WAVES, ...
     const int n0 = seg_count(0);

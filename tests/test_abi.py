@@ -43,7 +43,8 @@ def test_every_declared_symbol_is_exported(lib):
             "paged_attention_reduce", "paged_attention_split_decode",
             "paged_attention_split_decode_noalloc", "paged_kv_copy_slots",
             "paged_attention_decode_slotted_split", "paged_attention_prefix_split_decode",
-            "paged_attention_decode_ordered", "pkv_status_string",
+            "paged_attention_decode_ordered", "paged_attention_append_decode_slotted",
+            "pkv_status_string",
             "pkv_max_partitions"} <= set(declared)
     assert pkv.exported_symbols() == declared
 
@@ -300,6 +301,25 @@ def test_slotted_argument_errors(lib):
 
 
 @host_only
+def test_append_decode_slotted_argument_errors(lib):
+    f = lib.paged_attention_append_decode_slotted
+
+    def call(out=A, kn=A, vn=A, so=None, sg=A, S=2, Hq=12, Hkv=2, B=16, MS=4, dt=0):
+        return f(out, A, A, A, kn, vn, so, sg, A, S, Hq, Hkv, 128, B, MS, 64, 0.088, dt, None)
+
+    assert call(kn=None, vn=None) == EINVAL          # the new rows are required
+    assert call(vn=None) == EINVAL                   # k_new without v_new
+    assert call(kn=P((1 << 20) + 8)) == EINVAL       # k_new not 16-byte aligned
+    assert call(so=P((1 << 20) + 4)) == EINVAL       # slot_out not 8-byte aligned
+    assert call(sg=None) == EINVAL
+    assert call(out=None) == EINVAL
+    assert call(Hq=34) == ENOTSUP
+    assert call(B=24) == ENOTSUP
+    assert call(dt=2) == ENOTSUP
+    assert call(S=0) == 0
+
+
+@host_only
 def test_slotted_split_argument_errors(lib):
     f = lib.paged_attention_decode_slotted_split
 
@@ -400,3 +420,11 @@ def test_binding_rejects_mismatched_workspace_and_new_rows():
     with pytest.raises(ValueError):                      # slotted: segments for 3 sequences
         pkv.paged_attention_decode_slotted(a["out"], a["q"], a["k_pool"], a["v_pool"],
                                            _t(3, 4, 3, dtype="i32"), _t(2, dtype="i32"))
+    with pytest.raises(ValueError):                      # slotted append: no V rows
+        pkv.paged_attention_append_decode_slotted(a["out"], a["q"], a["k_pool"], a["v_pool"],
+                                                  _t(2, 2, 128), None, _t(2, 4, 3, dtype="i32"),
+                                                  _t(2, dtype="i32"))
+    with pytest.raises(ValueError):                      # slotted append: rows of one sequence
+        pkv.paged_attention_append_decode_slotted(a["out"], a["q"], a["k_pool"], a["v_pool"],
+                                                  _t(1, 2, 128), _t(1, 2, 128),
+                                                  _t(2, 4, 3, dtype="i32"), _t(2, dtype="i32"))

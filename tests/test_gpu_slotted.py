@@ -11,7 +11,7 @@ from workloads import get_config, make_workload  # noqa: E402
 from workloads.gen import NAN_BITS  # noqa: E402
 from workloads.slotted import make_slotted_workload, pack  # noqa: E402
 from oracle import oracle as O  # noqa: E402
-from gpu_harness import i32, i64, scale_for, to_dev, tol_ok, widen_out  # noqa: E402
+from gpu_harness import bits_of, i32, i64, scale_for, to_dev, tol_ok, widen_out  # noqa: E402
 import paged_kv_cache_09_amd as pkv  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -93,29 +93,37 @@ def test_radix_batch_matches_oracle(mode):
     assert ok, (err, nbad)
 
 
-def _node_case(seed, S, Hq, Hkv, B, dtype, node_len_hi, nodes_per_path, trunks=False):
+def _node_case(seed, S, Hq, Hkv, B, dtype, node_len_hi, nodes_per_path, trunks=False,
+               leaves=False):
     """Random tree-less node sets: every sequence walks its own random list of
     nodes (shared ones included), some paths empty, some nodes of length 0.
     With trunks, runs of consecutive sequences first walk a common random list
-    of nodes (cut short for some), as the paths of a radix tree do."""
+    of nodes (cut short for some), as the paths of a radix tree do.  With
+    leaves, every sequence but the empty one also ends in a private node of its
+    own (every third one followed by a zero-length node), whose last row is the
+    sequence's position n-1, and the case holds new K/V rows for the append."""
     rng = np.random.default_rng(seed)
+    lrng = np.random.default_rng(seed + 1000)  # leaves and new rows: the rest is unchanged
     nn = max(3 * S + 8, 2 * nodes_per_path)
     lens = [int(x) for x in rng.integers(0, node_len_hi + 1, size=nn)]
     free = [int(x) for x in rng.permutation(10 * nn + 16)]
+    if leaves:
+        lens += [int(x) for x in lrng.integers(1, node_len_hi + 2, size=S)]
+        free += list(range(10 * nn + 16, 10 * nn + 16 + S * (node_len_hi // B + 2)))
     node_segs = pack([max(n, 1) for n in lens], B, free)
     # zero-length nodes keep a (block, offset, 0) segment
     node_segs = [[(segs[0][0], segs[0][1], 0)] if lens[i] == 0 else segs
                  for i, segs in enumerate(node_segs)]
     NB = max(x[0] for segs in node_segs for x in segs) + 1
 
-    def draw(*sh):
-        x = rng.standard_normal(sh).astype(np.float32)
+    def draw(*sh, gen=rng):
+        x = gen.standard_normal(sh).astype(np.float32)
         if dtype == "fp16":
             return x.astype(np.float16).view(np.uint16)
         return (x.view(np.uint32) >> 16).astype(np.uint16)
 
-    node_k = [draw(n, Hkv, 128) for n in lens]
-    node_v = [draw(n, Hkv, 128) for n in lens]
+    node_k = [draw(n, Hkv, 128) for n in lens[:nn]]
+    node_v = [draw(n, Hkv, 128) for n in lens[:nn]]
     paths = [[int(x) for x in rng.choice(nn, size=rng.integers(0, nodes_per_path + 1),
                                          replace=False)] for _ in range(S)]
     if trunks:
@@ -130,6 +138,15 @@ def _node_case(seed, S, Hq, Hkv, B, dtype, node_len_hi, nodes_per_path, trunks=F
                 paths[t] = trunk[:cut] + own
             s += run
     paths[-1 if trunks else 0] = []
+    extra = {}
+    if leaves:
+        node_k += [draw(n, Hkv, 128, gen=lrng) for n in lens[nn:]]
+        node_v += [draw(n, Hkv, 128, gen=lrng) for n in lens[nn:]]
+        zero = [i for i in range(nn) if lens[i] == 0]
+        for t in range(S):
+            if t != (S - 1 if trunks else 0):
+                paths[t] = paths[t] + [nn + t] + (zero[:1] if t % 3 == 0 else [])
+        extra = dict(k_new=draw(S, Hkv, 128, gen=lrng), v_new=draw(S, Hkv, 128, gen=lrng))
     MS = max(1, max(sum(len(node_segs[i]) for i in p) for p in paths))
     segs = np.zeros((S, MS, 3), np.int32)
     nsegs = np.zeros(S, np.int32)
@@ -147,7 +164,7 @@ def _node_case(seed, S, Hq, Hkv, B, dtype, node_len_hi, nodes_per_path, trunks=F
             r += ln
     runs = (np.concatenate(rk), np.concatenate(rv), np.array(cu, np.int64),
             np.array(st, np.int32), np.array(tb, np.int32))
-    return dict(NB=NB, segs=segs, nsegs=nsegs, runs=runs, q=draw(S, Hq, 128))
+    return dict(NB=NB, segs=segs, nsegs=nsegs, runs=runs, q=draw(S, Hq, 128), **extra)
 
 
 NODE_CASES = [
@@ -276,6 +293,77 @@ def test_block_tables_as_segments_split(key, P):
     got2, _ = _gpu_split(w.q, gk, gv, segs, nsegs, c.dtype, scale_for(c.head_dim), P,
                          c.block_size)
     assert np.array_equal(got, got2)
+
+
+def _gpu_append(q, gk, gv, k_new, v_new, segs, nsegs, dtype, scale):
+    """paged_attention_append_decode_slotted on the device pools (written in
+    place); returns the widened output and the slot ids."""
+    S, Hq, _ = q.shape
+    out = torch.empty((S, Hq, 128), dtype=TDT[dtype], device=DEV)
+    out.view(torch.int16).fill_(0x5555)
+    slots = torch.full((S,), -2, dtype=torch.int64, device=DEV)
+    pkv.paged_attention_append_decode_slotted(
+        out, to_dev(q, dtype, DEV), gk, gv, to_dev(k_new, dtype, DEV), to_dev(v_new, dtype, DEV),
+        i32(segs, DEV), i32(nsegs, DEV), slot_out=slots, scale=scale)
+    torch.cuda.synchronize()
+    return widen_out(out), slots.cpu().numpy()
+
+
+def _check_append(q, kp, vp, gk, gv, k_new, v_new, segs, nsegs, Hkv, B, NB, dtype):
+    """The fused call against the oracle's append followed by its attention: the
+    pools bit for bit, the slot ids exactly, the output within the tolerance;
+    then a plain slotted decode over the written pools gives the same output bit
+    for bit (the rows were in place before any wave read them)."""
+    scale = scale_for(128)
+    ref_slots = O.append_slotted(kp, vp, k_new, v_new, segs, nsegs, B, NB)
+    ref = O.attention_slotted(q, kp, vp, segs, nsegs, Hkv, B, NB, scale, dtype)
+    got, slots = _gpu_append(q, gk, gv, k_new, v_new, segs, nsegs, dtype, scale)
+    assert np.array_equal(slots, ref_slots)
+    assert np.array_equal(bits_of(gk), kp) and np.array_equal(bits_of(gv), vp)
+    ok, err, nbad = tol_ok(got, ref)
+    assert ok, (err, nbad)
+    assert np.array_equal(_gpu(q, gk, gv, segs, nsegs, dtype, scale), got)
+    return slots
+
+
+def test_append_radix_batch_matches_oracle(mode):
+    """The radix-tree batch with each sequence's new token written to the last
+    row of its private leaf (the lengths count it) and attended in one launch."""
+    cfg = get_config("c5")
+    w = make_slotted_workload(cfg)
+    S, Hkv = len(w.paths), cfg.num_kv_heads
+    print(f"[gpu] slotted append radix batch ({mode}) S={S} NB={w.num_blocks}", flush=True)
+    kp, vp, gk, gv = _pools_both(w.runs(), w.num_blocks, Hkv, cfg.block_size, cfg.dtype)
+    rng = np.random.default_rng(4242)
+    new = [_bits_like(rng.standard_normal((S, Hkv, 128)).astype(np.float32), cfg.dtype)
+           for _ in range(2)]
+    slots = _check_append(w.q, kp, vp, gk, gv, new[0], new[1], w.segments, w.num_segments,
+                          Hkv, cfg.block_size, w.num_blocks, cfg.dtype)
+    assert (slots >= 0).all() and len(set(slots.tolist())) == S
+
+
+def _bits_like(x, dtype):
+    if dtype == "fp16":
+        return x.astype(np.float16).view(np.uint16)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+APPEND_CASES = [NODE_CASES[i] for i in (0, 2, 3, 4, 6)] + [TRUNK_CASES[i] for i in (0, 1, 5, 7)]
+
+
+@pytest.mark.parametrize("case", APPEND_CASES, ids=[f"seed{c[0]}" for c in APPEND_CASES])
+def test_append_random_node_lists(case, mode):
+    """Random node lists, each ending in a private leaf (some followed by an empty
+    segment, one sequence empty: slot -1, nothing written)."""
+    seed, S, Hq, Hkv, B, dtype, hi, per = case
+    c = _node_case(seed, S, Hq, Hkv, B, dtype, hi, per, trunks=seed >= 11, leaves=True)
+    print(f"[gpu] slotted append ({mode}) seed={seed} S={S} Hq={Hq} Hkv={Hkv} B={B} {dtype} "
+          f"max_segments={c['segs'].shape[1]}", flush=True)
+    assert mode != "tiles" or tile_list_fits(Hq, Hkv, B, c["segs"].shape[1])
+    kp, vp, gk, gv = _pools_both(c["runs"], c["NB"], Hkv, B, dtype)
+    slots = _check_append(c["q"], kp, vp, gk, gv, c["k_new"], c["v_new"], c["segs"],
+                          c["nsegs"], Hkv, B, c["NB"], dtype)
+    assert slots[-1 if seed >= 11 else 0] == -1
 
 
 def test_long_leaves_split():
