@@ -97,6 +97,10 @@ def parse():
                          "shared-prefix workload) or the workload's block tables written as "
                          "segments (tables; the default otherwise, in split mode when the "
                          "workload's partition size is set)")
+    ap.add_argument("--slotted-append", default="on", choices=["on", "off"],
+                    help="--op slotted, single pass: each launch also appends the step's new "
+                         "K/V rows to every sequence's last position (the default), or decode "
+                         "only")
     ap.add_argument("--slotted-kernel", default="auto", choices=["auto", "tiles", "per_sequence"],
                     help="--op slotted, single pass: the library's choice, or force the tiled "
                          "or the per-sequence kernel (PKV_SLOTTED_TILES)")
@@ -720,11 +724,13 @@ def bench_slotted(args):
     """Decode over slotted (block, slot offset, length) segments, one launch per
     step, cycling through R distinct batches.  The batch is the radix tree at the
     workload's shapes (a shared 512-token root, shared short nodes packed as
-    slots, a private leaf per sequence; paged_attention_decode_slotted), or the
-    workload's own block tables written as segments (whole blocks; in split mode
-    with the workload's partition size, paged_attention_decode_slotted_split).
-    value = sequences / step time; the roofline counts each node's K/V rows once
-    (unique bytes)."""
+    slots, a private leaf per sequence), or the workload's own block tables
+    written as segments (whole blocks; in split mode with the workload's
+    partition size, paged_attention_decode_slotted_split).  In single pass the
+    launch also writes each sequence's new K/V rows to its last position
+    (paged_attention_append_decode_slotted) unless --slotted-append off
+    (paged_attention_decode_slotted).  value = sequences / step time; the
+    roofline counts each node's K/V rows once (unique bytes)."""
     import torch
     import paged_kv_cache_09_amd as pkv
     from workloads import get_config, make_workload
@@ -740,6 +746,7 @@ def bench_slotted(args):
     R = args.distinct or (4 if kind == "radix" else cfg.bench_distinct_layers)
     if args.slotted_kernel != "auto":
         os.environ["PKV_SLOTTED_TILES"] = "1" if args.slotted_kernel == "tiles" else "0"
+    append = not P and args.slotted_append == "on"
     dev = torch.device("cuda:0")
     tdt = {"fp16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
 
@@ -775,7 +782,8 @@ def bench_slotted(args):
             # the step's own token, so that every position holds data
             pkv.paged_kv_append(kp, vp, up(w.k_new), up(w.v_new), torch.from_numpy(w.tables).to(dev),
                                 torch.from_numpy(w.lengths).to(dev))
-        batches.append(dict(w=w, k=kp, v=vp, q=up(w.q), info=info,
+        batches.append(dict(w=w, k=kp, v=vp, q=up(w.q), info=info, kn=up(w.k_new),
+                            vn=up(w.v_new),
                             segs=torch.from_numpy(segs).to(dev),
                             ns=torch.from_numpy(nsegs).to(dev)))
     torch.cuda.synchronize()
@@ -797,6 +805,9 @@ def bench_slotted(args):
         if P:
             pkv.paged_attention_decode_slotted_split(out, b["q"], b["k"], b["v"], b["segs"],
                                                      b["ns"], P, po, pl, ctr, scale=scale)
+        elif append:
+            pkv.paged_attention_append_decode_slotted(out, b["q"], b["k"], b["v"], b["kn"],
+                                                      b["vn"], b["segs"], b["ns"], scale=scale)
         else:
             pkv.paged_attention_decode_slotted(out, b["q"], b["k"], b["v"], b["segs"], b["ns"],
                                                scale=scale)
@@ -808,10 +819,12 @@ def bench_slotted(args):
     e, Hkv = cfg.elem_bytes, cfg.num_kv_heads
     row = 2 * Hkv * D * e                                   # K and V of one token, all heads
     nseg = int(b0["ns"].sum())
-    unique = info["unique"] * row + 2 * S * Hq * D * e + 12 * nseg + 4 * S
-    logical = info["logical"] * row + 2 * S * Hq * D * e + 12 * nseg + 4 * S
+    new_rows = 2 * S * row if append else 0                # new rows read + written
+    unique = info["unique"] * row + 2 * S * Hq * D * e + 12 * nseg + 4 * S + new_rows
+    logical = info["logical"] * row + 2 * S * Hq * D * e + 12 * nseg + 4 * S + new_rows
     name = "slotted_split" if P else "slotted"
     roof = roofline("paged_attention_decode_slotted_split" if P else
+                    "paged_attention_append_decode_slotted" if append else
                     "paged_attention_decode_slotted", unique, ms,
                     measured_traffic(f"{name}_{cfg.key}" if kind == "tables" else
                                      f"slotted_{cfg.key}", "slotted"))
@@ -823,7 +836,7 @@ def bench_slotted(args):
               "block_size": cfg.block_size, "mean_context": round(info["mean"], 1),
               "unique_tokens": info["unique"], "nodes": info["nodes"],
               "max_segments": MS, "partition_size": P, "distinct_batches": R, "launches": 1,
-              "kernel_choice": args.slotted_kernel}
+              "append_fused": append, "kernel_choice": args.slotted_kernel}
     line = _side_line("slotted-segment decode tokens/s and unique-byte HBM GB/s, 1 GPU",
                       S / (ms * 1e-3), "tokens/s", args, cfg, cfg.dtype, config, roof,
                       {"logical_bytes_per_launch": logical})
@@ -842,13 +855,16 @@ def bench_slotted(args):
         reps, spent = 0, 0.0
         while reps == 0 or (spent < args.cpu_seconds and reps < 20):
             t = time.perf_counter()
+            if append:
+                O.append_slotted(kp, vp, w0.k_new, w0.v_new, segs, nsegs, cfg.block_size, NB)
             O.attention_slotted(w0.q, kp, vp, segs, nsegs, Hkv, cfg.block_size, NB, scale,
                                 cfg.dtype, threads)
             spent += time.perf_counter() - t
             reps += 1
         line["cpu_baseline"] = {"value": round(S * reps / spent, 3), "unit": "tokens/s",
                                 "cores": threads, "kind": "oracle",
-                                "sample": f"the whole batch ({S} sequences x {Hq} heads, fp64), "
+                                "sample": f"the whole batch ({S} sequences x {Hq} heads, fp64"
+                                          f"{', append + attention' if append else ''}), "
                                           f"{reps} repetitions, {spent:.1f} s"}
     print(json.dumps(line), flush=True)
 

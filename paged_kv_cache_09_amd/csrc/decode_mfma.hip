@@ -988,29 +988,57 @@ void prefix_mfma_kernel(DecodeArgs a)
 constexpr int kSegRound = 64;
 constexpr int kMaxRoundSubs = kSegRound * 16;  // a 256-row segment gives 16 sub-tiles
 
-// Fused append for slotted segments (one whole wave per call): sequence s's new K
-// and V rows of KV head g go to its position n-1, which is the last row of its
+// Fused append for slotted segments, one whole wave per sequence: sequence s's new
+// K and V rows of KV head g go to its position n-1, which is the last row of its
 // last non-empty segment (lengths clamped to the block, as the decode reads
-// them); with head 0 the wave also writes the slot id, or -1 when n = 0.  The
-// caller's next fenced barrier makes the rows visible to every wave's loads.
-template <int BS>
-__device__ __forceinline__ void slotted_append_wave(const DecodeArgs &a, int s, int g, int lane)
+// them); with head 0 the wave also writes the slot id, or -1 when n = 0.  Split
+// in two so that a wave can have the loads of several sequences in flight at
+// once: slot_append_load issues every load (the segment count, lane k's segment
+// k < 64, and lanes 0-31's 16 bytes of the new K (lanes 0-15) or V row), none
+// depending on another; slot_append_store finds the row (a longer list's later
+// segments are read there) and writes it.  The caller's next fenced barrier
+// makes the rows visible to every wave's loads.
+struct SlotAppend {
+    int nseg;           // segment count as passed
+    int32_t blk, off, len;  // this lane's segment of the first 64
+    u32x4 val;          // lanes 0-31: their 16 bytes of the new rows
+};
+
+__device__ __forceinline__ SlotAppend slot_append_load(const DecodeArgs &a, int s, int g,
+                                                       int lane)
 {
-    const int32_t *segs = a.segments + (int64_t)s * a.max_segments * 3;
-    const int nseg = min(max(a.num_segments[s], 0), a.max_segments);
+    SlotAppend r;
+    const int32_t *seg = a.segments + ((int64_t)s * a.max_segments + min(lane, a.max_segments - 1)) * 3;
+    r.nseg = a.num_segments[s];
+    r.blk = seg[0];
+    r.off = seg[1];
+    r.len = seg[2];
+    const int kv = (lane >> 4) & 1, c = lane & 15;
+    r.val = *(const u32x4 *)((const uint16_t *)(kv ? a.v_new : a.k_new) +
+                             ((int64_t)s * a.num_kv_heads + g) * kHeadDim + 8 * c);
+    return r;
+}
+
+template <int BS>
+__device__ __forceinline__ void slot_append_store(const DecodeArgs &a, const SlotAppend &r, int s,
+                                                  int g, int lane)
+{
+    const int nseg = min(max(r.nseg, 0), a.max_segments);
     int last = -1, lblk = 0, lrow = 0;  // this lane's last non-empty segment
-    for (int base = 0; base < nseg; base += 64) {
-        const int i = base + lane;
-        if (i < nseg) {
-            const int off = min(max(segs[3 * i + 1], 0), BS);
-            const int len = min(max(segs[3 * i + 2], 0), BS - off);
-            if (len > 0) {
-                last = i;
-                lblk = segs[3 * i];
-                lrow = off + len - 1;
-            }
+    auto take = [&](int i, int32_t blk, int off, int len) {
+        off = min(max(off, 0), BS);
+        len = min(max(len, 0), BS - off);
+        if (len > 0) {
+            last = i;
+            lblk = blk;
+            lrow = off + len - 1;
         }
-    }
+    };
+    if (lane < nseg)
+        take(lane, r.blk, r.off, r.len);
+    const int32_t *segs = a.segments + (int64_t)s * a.max_segments * 3;
+    for (int i = 64 + lane; i < nseg; i += 64)
+        take(i, segs[3 * i], segs[3 * i + 1], segs[3 * i + 2]);
     int best = last;
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1)
@@ -1023,13 +1051,8 @@ __device__ __forceinline__ void slotted_append_wave(const DecodeArgs &a, int s, 
     const int blk = __shfl(lblk, best & 63, 64), row = __shfl(lrow, best & 63, 64);
     const int64_t dst = ((int64_t)blk * a.num_kv_heads + g) * BS * kHeadDim +
                         (int64_t)row * kHeadDim;
-    const int64_t src = ((int64_t)s * a.num_kv_heads + g) * kHeadDim;
-    if (lane < 32) {
-        const int kv = lane >> 4, c = lane & 15;
-        const u32x4 val =
-            *(const u32x4 *)((const uint16_t *)(kv ? a.v_new : a.k_new) + src + 8 * c);
-        *(u32x4 *)((uint16_t *)(kv ? a.v_pool : a.k_pool) + dst + 8 * c) = val;
-    }
+    if (lane < 32)
+        *(u32x4 *)((uint16_t *)(lane >> 4 ? a.v_pool : a.k_pool) + dst + 8 * (lane & 15)) = r.val;
     if (g == 0 && lane == 0 && a.slot_out)
         a.slot_out[s] = (int64_t)blk * BS + row;
 }
@@ -1121,6 +1144,14 @@ void slotted_mfma_kernel(DecodeArgs a)
     const bool direct = !SPLIT || np <= 1;
     const int np_loop = direct ? (px0 == 0 ? 1 : 0) : np;
 
+    // fused append (single pass only): wave 0 issues its loads with the query's
+    // and writes the new rows before the partition loop; the round's first
+    // barrier completes the stores before any wave loads a sub-tile
+    SlotAppend ap;
+    if constexpr (!SPLIT) {
+        if (a.k_new && w == 0)
+            ap = slot_append_load(a, s, g, lane);
+    }
     u32x4 qop[4];
     {
         const uint16_t *qrow = (const uint16_t *)a.q +
@@ -1131,11 +1162,9 @@ void slotted_mfma_kernel(DecodeArgs a)
             qop[kk] = col < G ? *(const u32x4 *)(qrow + kk * 32) : (u32x4){0u, 0u, 0u, 0u};
     }
 
-    // fused append (single pass only): wave 0 writes the new rows; the round's
-    // first barrier below completes the stores before any wave loads a sub-tile
     if constexpr (!SPLIT) {
         if (a.k_new && w == 0)
-            slotted_append_wave<BS>(a, s, g, lane);
+            slot_append_store<BS>(a, ap, s, g, lane);
     }
 
     for (int px = px0; px < np_loop; px += parts) {
@@ -1852,11 +1881,16 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
             qop[h][kk] = active[h] ? v : (u32x4){0u, 0u, 0u, 0u};
         }
     }
-    // 0. Fused append: each wave writes the new rows of members w, w + WAVES, ...;
-    // the fenced barrier after step 1 completes the stores before any load
+    // 0. Fused append: each wave takes members w, w + WAVES, ...; their loads are
+    // in flight with step 1's, the stores with step 2's, and the fenced barrier
+    // after step 2 completes the stores before any sub-tile load
+    constexpr int kPer = (kMembers + WAVES - 1) / WAVES;
+    SlotAppend ap[kPer];
     if (a.k_new) {
-        for (int i = w; i < m; i += WAVES)
-            slotted_append_wave<BS>(a, s0 + i, g, lane);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            if (w + j * WAVES < m)
+                ap[j] = slot_append_load(a, s0 + w + j * WAVES, g, lane);
     }
 
     // 1. Common segments: lane k compares segment k of every member with member
@@ -1892,6 +1926,12 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
         for (int i = 0; i < WAVES; ++i)
             d |= s_diff[i];
         ncom = d ? __builtin_ctzll(d) : kCommonScan;
+    }
+    if (a.k_new) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            if (w + j * WAVES < m)
+                slot_append_store<BS>(a, ap[j], s0 + w + j * WAVES, g, lane);
     }
 
     // 2. The common sub-tiles (wave 0, from member 0's segments) at the head of

@@ -334,18 +334,9 @@ def test_append_radix_batch_matches_oracle(mode):
     S, Hkv = len(w.paths), cfg.num_kv_heads
     print(f"[gpu] slotted append radix batch ({mode}) S={S} NB={w.num_blocks}", flush=True)
     kp, vp, gk, gv = _pools_both(w.runs(), w.num_blocks, Hkv, cfg.block_size, cfg.dtype)
-    rng = np.random.default_rng(4242)
-    new = [_bits_like(rng.standard_normal((S, Hkv, 128)).astype(np.float32), cfg.dtype)
-           for _ in range(2)]
-    slots = _check_append(w.q, kp, vp, gk, gv, new[0], new[1], w.segments, w.num_segments,
+    slots = _check_append(w.q, kp, vp, gk, gv, w.k_new, w.v_new, w.segments, w.num_segments,
                           Hkv, cfg.block_size, w.num_blocks, cfg.dtype)
     assert (slots >= 0).all() and len(set(slots.tolist())) == S
-
-
-def _bits_like(x, dtype):
-    if dtype == "fp16":
-        return x.astype(np.float16).view(np.uint16)
-    return (x.view(np.uint32) >> 16).astype(np.uint16)
 
 
 APPEND_CASES = [NODE_CASES[i] for i in (0, 2, 3, 4, 6)] + [TRUNK_CASES[i] for i in (0, 1, 5, 7)]

@@ -33,7 +33,7 @@ LEVEL2 = (64, 3, 15)
 LEAF = (5, 128)            # private tail of each sequence
 
 # stream ids (disjoint from the decode generator's)
-S_LENS, S_FREE, S_NODE_K, S_NODE_V, S_Q = range(20, 25)
+S_LENS, S_FREE, S_NODE_K, S_NODE_V, S_Q, S_NEW_K, S_NEW_V = range(20, 27)
 
 Segment = Tuple[int, int, int]
 
@@ -58,6 +58,8 @@ class SlottedWorkload:
     segments: np.ndarray            # int32 [S][max_segments][3]
     num_segments: np.ndarray        # int32 [S]
     nan_bits: int
+    k_new: np.ndarray = None        # [S][Hkv][D] bits: the step's new rows, which an
+    v_new: np.ndarray = None        # append writes to the last row of each leaf
 
     def logical_kv(self, s: int):
         p = self.paths[s]
@@ -156,6 +158,11 @@ def make_slotted_workload(cfg: Config, num_seqs: int = None, seed_id: int = None
         segments[s, :len(flat)] = flat
         num_segments[s] = len(flat)
     q = _bits(_rng(cid, S_Q).standard_normal((S, Hq, D), dtype=np.float32) * scale, c.dtype)
+    k_new = _bits(_rng(cid, S_NEW_K).standard_normal((S, Hkv, D), dtype=np.float32) * scale,
+                  c.dtype)
+    v_new = _bits(_rng(cid, S_NEW_V).standard_normal((S, Hkv, D), dtype=np.float32) * scale,
+                  c.dtype)
     return SlottedWorkload(cfg=c, num_blocks=num_blocks, node_segments=node_segs, node_k=node_k,
                            node_v=node_v, paths=paths, q=q, segments=segments,
-                           num_segments=num_segments, nan_bits=NAN_BITS[c.dtype])
+                           num_segments=num_segments, nan_bits=NAN_BITS[c.dtype], k_new=k_new,
+                           v_new=v_new)
