@@ -201,7 +201,7 @@ __device__ __forceinline__ bool qk_softmax(GqaState &st, const KOp &K, const u32
         if (PARTIAL && (t < t_beg || t >= t_end || !col_on))
             sc[r] = kNegInf;
     }
-    float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    float mt = vmax(vmax3(sc[0], sc[1], sc[2]), sc[3]);
     mt = pair_max32(pair_max16(mt));
     const bool grow = mt > st.m + kRescaleSlack;  // always true for the first scores
     const bool rescale = __ballot(grow) != 0;     // wave-uniform
@@ -2019,40 +2019,35 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
 
     // Position j of the list is common sub-tile pi = floor(j P / T) when
     // floor((j+1) P / T) exceeds pi, else the members' sub-tile j - pi (entry
-    // P + j - pi); the quotients advance by a constant step with a carry.  A j past
-    // the list describes an empty sub-tile (zero rows, so its buffer range is
-    // empty and nothing is fetched), so every step issues its loads the same way.
+    // P + j - pi).  A j past the list describes an empty sub-tile (zero rows, so
+    // its buffer range is empty and nothing is fetched), so every step issues its
+    // loads the same way.  A wave takes positions w, w + WAVES, ...: its lanes
+    // hold the descriptors of the next 64 of them (lane l: the wave's position
+    // i0 + l), read from the LDS list once per 64 steps, and a step takes its own
+    // with two lane reads.  The list holds at most kTileSubs entries, so j P fits
+    // in 32 bits.
     struct Sub {
         int32_t phys, desc;
     };
+    static_assert((int64_t)kTileSubs * kTileSubs < ((int64_t)1 << 31), "32-bit quotients");
     const int tot = max(total, 1);
-    const int64_t wp = (int64_t)WAVES * n_pre;
-    const int dq = (int)(wp / tot), dr = (int)(wp % tot);
-    int q0 = (int)((int64_t)w * n_pre / tot), r0 = (int)((int64_t)w * n_pre % tot);
-    int q1 = (int)((int64_t)(w + 1) * n_pre / tot);
-    int r1 = (int)((int64_t)(w + 1) * n_pre % tot);
-    auto describe = [&](int j) {
+    int d_phys = 0, d_desc = 0;  // this lane's position of the wave's current 64
+    auto describe_lanes = [&](int i0) {
+        const int j = w + (i0 + lane) * WAVES;
         int idx = 0;
         const bool past = j >= total;
         if (!past) {
-            const int pi = q0, pi1 = q1;
-            q0 += dq;
-            r0 += dr;
-            if (r0 >= total) {
-                r0 -= total;
-                ++q0;
-            }
-            q1 += dq;
-            r1 += dr;
-            if (r1 >= total) {
-                r1 -= total;
-                ++q1;
-            }
+            const int pi = j * n_pre / tot, pi1 = (j + 1) * n_pre / tot;
             idx = pi1 > pi ? pi : n_pre + j - pi;
         }
+        d_phys = s_phys[idx];
+        d_desc = past ? 0 : s_desc[idx];
+    };
+    // the descriptor of the wave's position i (i % 64 is the lane holding it)
+    auto take = [&](int i) {
         Sub d;
-        d.phys = __builtin_amdgcn_readfirstlane(s_phys[idx]);
-        d.desc = past ? 0 : __builtin_amdgcn_readfirstlane(s_desc[idx]);
+        d.phys = __builtin_amdgcn_readlane(d_phys, i & 63);
+        d.desc = __builtin_amdgcn_readlane(d_desc, i & 63);
         return d;
     };
     // Sub-tile k of the wave goes global -> LDS into buffer k % 2 (stage_a,
@@ -2072,10 +2067,12 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
         dma_sub(make_rsrc(kp + b, bytes), make_rsrc(vp + b, bytes), buf, dl);
     };
     constexpr int kReadWait = 8;
-    auto step = [&](auto parity, auto run, Sub &cur, Sub &nxt, int jn) {
+    auto step = [&](auto parity, auto run, Sub &cur, Sub &nxt, int kn) {
         constexpr bool RUN = decltype(run)::value;
         char *const buf = decltype(parity)::value ? buf_b : buf_a;
-        const Sub nxt2 = describe(jn);
+        if (kn > 0 && (kn & 63) == 0)
+            describe_lanes(kn);
+        const Sub nxt2 = take(kn);
         i16x4 va[8];
         u32x2 pb[NH];
         float alpha[NH];
@@ -2128,16 +2125,17 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
         using even = std::integral_constant<int, 0>;
         using odd = std::integral_constant<int, 1>;
         Sub cur{}, nxt{};
-        step(even(), std::false_type(), cur, nxt, w);
-        step(odd(), std::false_type(), cur, nxt, w + WAVES);
-        for (int j = w;;) {
-            step(even(), std::true_type(), cur, nxt, j + 2 * WAVES);
-            j += WAVES;
-            if (j >= total)
+        describe_lanes(0);
+        step(even(), std::false_type(), cur, nxt, 0);
+        step(odd(), std::false_type(), cur, nxt, 1);
+        // step k consumes the wave's sub-tile k (position w + k WAVES) and issues
+        // the loads of sub-tile k + 2
+        for (int k = 0;;) {
+            step(even(), std::true_type(), cur, nxt, k + 2);
+            if (w + ++k * WAVES >= total)
                 break;
-            step(odd(), std::true_type(), cur, nxt, j + 2 * WAVES);
-            j += WAVES;
-            if (j >= total)
+            step(odd(), std::true_type(), cur, nxt, k + 2);
+            if (w + ++k * WAVES >= total)
                 break;
         }
     }

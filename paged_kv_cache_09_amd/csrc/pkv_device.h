@@ -118,6 +118,24 @@ __device__ __forceinline__ float row_sum16(float x)
 
 __device__ __forceinline__ float xor_lane(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
+// Maximum of scores and running maxima, which are never signalling NaNs: the
+// hardware max directly.  fmaxf makes the compiler quiet every operand it cannot
+// prove canonical (a lane-swapped or selected value) with an extra v_max_f32
+// x, x, x first, which cost 12 VALU operations per 16-token step of the GQA
+// kernels' softmax.
+__device__ __forceinline__ float vmax(float a, float b)
+{
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c)
+{
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // Max / sum over lanes l and l^16 (or l^32), the same bits in both lanes of the
 // pair.  The gfx950 lane-swap instructions hand every lane both values of its
 // pair in one VALU operation (lane layout checked on the GPU with an in-bounds
@@ -127,13 +145,13 @@ __device__ __forceinline__ float pair_max16(float x)
 {
     const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                     false);
-    return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+    return vmax(__uint_as_float(t[0]), __uint_as_float(t[1]));
 }
 __device__ __forceinline__ float pair_max32(float x)
 {
     const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                     false);
-    return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+    return vmax(__uint_as_float(t[0]), __uint_as_float(t[1]));
 }
 __device__ __forceinline__ float pair_sum16(float x)
 {
