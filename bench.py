@@ -101,6 +101,10 @@ def parse():
                     help="--op slotted, single pass: each launch also appends the step's new "
                          "K/V rows to every sequence's last position (the default), or decode "
                          "only")
+    ap.add_argument("--slotted-order", default="tree", choices=["tree", "drawn"],
+                    help="--op slotted, radix batch: sequences in tree order (sorted by their "
+                         "node paths, so that a tile's consecutive sequences share nodes), or "
+                         "in the order the workload draws them")
     ap.add_argument("--slotted-kernel", default="auto", choices=["auto", "tiles", "per_sequence"],
                     help="--op slotted, single pass: the library's choice, or force the tiled "
                          "or the per-sequence kernel (PKV_SLOTTED_TILES)")
@@ -720,6 +724,18 @@ def _tables_as_segments(w):
     return segs, nb.astype(np.int32)
 
 
+def tree_ordered(w):
+    """The radix batch with its sequences sorted by node path (a depth-first order
+    of the tree): sequences under one node become neighbours, as a scheduler that
+    batches requests by prefix would submit them.  Only the order of the
+    per-sequence arrays changes; every sequence keeps its nodes and rows."""
+    import dataclasses
+    perm = sorted(range(len(w.paths)), key=lambda s: w.paths[s])
+    return dataclasses.replace(w, paths=[w.paths[s] for s in perm], q=w.q[perm],
+                               segments=w.segments[perm], num_segments=w.num_segments[perm],
+                               k_new=w.k_new[perm], v_new=w.v_new[perm])
+
+
 def bench_slotted(args):
     """Decode over slotted (block, slot offset, length) segments, one launch per
     step, cycling through R distinct batches.  The batch is the radix tree at the
@@ -757,6 +773,8 @@ def bench_slotted(args):
     for d in range(R):
         if kind == "radix":
             w = make_slotted_workload(cfg, seed_id=1000 * cfg.cfg_id + d)
+            if args.slotted_order == "tree":
+                w = tree_ordered(w)
             kr, vr, cu, st, tb = w.runs()
             segs, nsegs, NB = w.segments, w.num_segments, w.num_blocks
             info = dict(unique=w.unique_tokens(), logical=int(w.lengths().sum()),
@@ -836,7 +854,8 @@ def bench_slotted(args):
               "block_size": cfg.block_size, "mean_context": round(info["mean"], 1),
               "unique_tokens": info["unique"], "nodes": info["nodes"],
               "max_segments": MS, "partition_size": P, "distinct_batches": R, "launches": 1,
-              "append_fused": append, "kernel_choice": args.slotted_kernel}
+              "append_fused": append, "kernel_choice": args.slotted_kernel,
+              "batch_order": args.slotted_order if kind == "radix" else "batch"}
     line = _side_line("slotted-segment decode tokens/s and unique-byte HBM GB/s, 1 GPU",
                       S / (ms * 1e-3), "tokens/s", args, cfg, cfg.dtype, config, roof,
                       {"logical_bytes_per_launch": logical})
