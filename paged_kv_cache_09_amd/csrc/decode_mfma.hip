@@ -1787,9 +1787,12 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
 // consecutive sequences start with the same segments.  The tile's common segments
 // -- the leading triples that every member lists identically, found by comparing
 // the first kCommonScan of them -- become sub-tiles read once for the whole tile
-// with every column active; each member's remaining segments become sub-tiles
-// with only its G columns active (the others score -inf and keep their state).
-// The whole list of descriptors sits in LDS: the host takes this path only when
+// with every column active.  Of the remaining segments, one that a run of
+// consecutive members lists at the same index (a node under the common path that
+// part of the tile shares; in a batch in tree order, the sequences under one node
+// are neighbours) becomes sub-tiles read once for the run, with the run's columns
+// active; the others, sub-tiles of one member (the other columns score -inf and
+// keep their state).  The whole list of descriptors sits in LDS: the host takes this path only when
 // a tile's sub-tiles fit (members x max_segments x ceil(B/16) <= kTileSubs).  The
 // waves take the list round-robin with the common sub-tiles spread evenly among
 // the members' ones, as in the shared-prefix kernel.
@@ -1804,11 +1807,12 @@ __device__ __forceinline__ int wave_sum_i(int x)
     return x;
 }
 
-// Sub-tile descriptor: physical block, and first row | row count << 8 | owner << 16,
-// where owner is the member index + 1, or 0 for a common sub-tile.
-__device__ __forceinline__ int32_t slot_desc(int first_row, int rows, int owner)
+// Sub-tile descriptor: physical block, and first row | row count << 8 | lo << 16 |
+// hi << 21: the sub-tile belongs to members lo..hi of the tile (0..31 for a common
+// sub-tile).
+__device__ __forceinline__ int32_t slot_desc(int first_row, int rows, int lo, int hi)
 {
-    return first_row | (rows << 8) | (owner << 16);
+    return first_row | (rows << 8) | (lo << 16) | (hi << 21);
 }
 
 template <int DT, int BS, int WAVES, int NH>
@@ -1827,6 +1831,7 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
     __shared__ int32_t s_phys[kTileSubs];
     __shared__ int32_t s_desc[kTileSubs];
     __shared__ uint64_t s_diff[WAVES];  // per wave: segment indices where a member differs
+    __shared__ uint64_t s_same[kMembers];  // member i: segment indices equal to member i-1's
     __shared__ int32_t s_cnt[kMembers];  // each member's own sub-tiles
     __shared__ int32_t s_ncom;          // common sub-tiles
 
@@ -1893,27 +1898,32 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
                 ap[j] = slot_append_load(a, s0 + w + j * WAVES, g, lane);
     }
 
-    // 1. Common segments: lane k compares segment k of every member with member
-    // 0's; each wave takes members 1 + w, 1 + w + WAVES, ...
+    // 1. Lane k compares segment k (k < 64) of every member with member 0's (the
+    // segments common to the tile) and with the previous member's (runs of
+    // members that share a segment, such as a node under the tile's common path);
+    // each wave takes members w, w + WAVES, ...  Every lane reads an entry of its
+    // own row (segment min(k, max_segments - 1)), so the segment loads go out with
+    // the counts' instead of after them; the counts mask the comparisons.
+    const int kseg = min(lane, ms - 1);
     const int n0 = seg_count(0);
-    int b0 = 0, o0 = 0, l0 = 0;
-    if (lane < n0) {
-        const int32_t *r = seg_row(0) + 3 * lane;
-        b0 = r[0];
-        o0 = r[1];
-        l0 = r[2];
-    }
+    const int32_t *r0 = seg_row(0) + 3 * kseg;
+    const int b0 = r0[0], o0 = r0[1], l0 = r0[2];  // used for lanes below n0 only
     {
         bool diff = lane >= n0;
-        for (int i = 1 + w; i < m; i += WAVES) {
-            const int ni = seg_count(i);
-            if (lane < ni && lane < n0) {
-                const int32_t *r = seg_row(i) + 3 * lane;
-                diff |= r[0] != b0 || r[1] != o0 || r[2] != l0;
-            } else {
-                diff = true;
-            }
+        for (int i = w; i < m; i += WAVES) {
+            if (i == 0)
+                continue;
+            const int ni = seg_count(i), np = seg_count(i - 1);
+            const int32_t *r = seg_row(i) + 3 * kseg, *rp = seg_row(i - 1) + 3 * kseg;
+            const int bi = r[0], oi = r[1], li = r[2];
+            diff |= lane >= ni || bi != b0 || oi != o0 || li != l0;
+            const bool same = lane < ni && lane < np && bi == rp[0] && oi == rp[1] && li == rp[2];
+            const uint64_t sm = __ballot(same);
+            if (lane == 0)
+                s_same[i] = sm;
         }
+        if (w == 0 && lane == 0)
+            s_same[0] = 0;
         const uint64_t d = __ballot(diff);
         if (lane == 0)
             s_diff[w] = d;
@@ -1935,7 +1945,8 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
     }
 
     // 2. The common sub-tiles (wave 0, from member 0's segments) at the head of
-    // the list, and each member's count of own sub-tiles
+    // the list, and each member's count of the other sub-tiles it starts: those
+    // of its segments that do not repeat the previous member's
     if (w == 0) {
         int off = o0, len = l0;
         clamp_seg(off, len);
@@ -1948,7 +1959,8 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
         }
         for (int k = 0; k < c; ++k) {
             s_phys[incl - c + k] = b0;
-            s_desc[incl - c + k] = slot_desc(off + kSub * k, min(kSub, len - kSub * k), 0);
+            s_desc[incl - c + k] =
+                slot_desc(off + kSub * k, min(kSub, len - kSub * k), 0, kMembers - 1);
         }
         if (lane == 63)
             s_ncom = incl;
@@ -1956,11 +1968,13 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
     for (int i = w; i < m; i += WAVES) {
         const int ni = seg_count(i);
         const int32_t *r = seg_row(i);
+        const uint64_t same = s_same[i];
         int cnt = 0;
         for (int base = ncom; base < ni; base += 64) {
+            const int k = base + lane;
             int c = 0;
-            if (base + lane < ni) {
-                int off = r[3 * (base + lane) + 1], len = r[3 * (base + lane) + 2];
+            if (k < ni && !(k < 64 && ((same >> k) & 1))) {
+                int off = r[3 * k + 1], len = r[3 * k + 2];
                 clamp_seg(off, len);
                 c = (len + kSub - 1) / kSub;
             }
@@ -1971,7 +1985,9 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
     }
     __syncthreads();
 
-    // 3. Each member's own sub-tiles, member after member, after the common ones
+    // 3. The sub-tiles each member starts, member after member, after the common
+    // ones; a segment shared by members i..j (each repeating the previous one's)
+    // is read once, for all of them
     const int n_pre = __builtin_amdgcn_readfirstlane(s_ncom);
     int total = n_pre;
     for (int i = 0; i < m; ++i)
@@ -1982,14 +1998,20 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
             pos += __builtin_amdgcn_readfirstlane(s_cnt[k]);
         const int ni = seg_count(i);
         const int32_t *r = seg_row(i);
+        const uint64_t same = s_same[i];
         for (int base = ncom; base < ni; base += 64) {
-            int blk = 0, off = 0, len = 0, c = 0;
-            if (base + lane < ni) {
-                blk = r[3 * (base + lane)];
-                off = r[3 * (base + lane) + 1];
-                len = r[3 * (base + lane) + 2];
+            const int kk = base + lane;
+            int blk = 0, off = 0, len = 0, c = 0, hi = i;
+            if (kk < ni && !(kk < 64 && ((same >> kk) & 1))) {
+                blk = r[3 * kk];
+                off = r[3 * kk + 1];
+                len = r[3 * kk + 2];
                 clamp_seg(off, len);
                 c = (len + kSub - 1) / kSub;
+                // the run of following members that repeat this segment
+                if (kk < 64)
+                    while (hi + 1 < m && ((s_same[hi + 1] >> kk) & 1))
+                        ++hi;
             }
             int incl = c;
 #pragma unroll
@@ -2000,7 +2022,7 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
             for (int k = 0; k < c; ++k) {
                 s_phys[pos + incl - c + k] = blk;
                 s_desc[pos + incl - c + k] =
-                    slot_desc(off + kSub * k, min(kSub, len - kSub * k), i + 1);
+                    slot_desc(off + kSub * k, min(kSub, len - kSub * k), i, hi);
             }
             pos += __builtin_amdgcn_readlane(incl, 63);
         }
@@ -2078,22 +2100,22 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
         float alpha[NH];
         bool rs[NH];
         const int rows = (cur.desc >> 8) & 0xff;
-        const int owner = (cur.desc >> 16) - 1;  // -1: common
-        // a member's own sub-tile has active columns only in the half holding the
-        // member: the other half's scores, softmax and P.V are skipped (uniform)
+        const int lo = (cur.desc >> 16) & 31, hi = (cur.desc >> 21) & 31;  // its members
+        // a half that holds none of the sub-tile's members skips its scores,
+        // softmax and P.V (uniform)
         bool live[NH];
 #pragma unroll
         for (int h = 0; h < NH; ++h)
-            live[h] = RUN && (owner < 0 || (owner >= h * sph && owner < (h + 1) * sph));
+            live[h] = RUN && hi >= h * sph && lo < (h + 1) * sph;
         if constexpr (RUN) {
             __builtin_amdgcn_sched_barrier(0);
             PKV_WAIT_VMCNT(kReadWait);  // this buffer's loads have landed
             __builtin_amdgcn_sched_barrier(0);
             const KOp KA = dma_read_k(buf, dl);
             dma_read_v(va, buf, dl);
-            // a full common sub-tile needs no mask: a column outside the tile
-            // only updates a state that is never written out
-            if (owner < 0 && rows == kSub) {
+            // a full sub-tile of every member needs no mask: a column outside the
+            // tile only updates a state that is never written out
+            if (lo == 0 && hi >= m - 1 && rows == kSub) {
 #pragma unroll
                 for (int h = 0; h < NH; ++h)
                     rs[h] = qk_softmax<DT, false>(st[h], KA, qop[h], 0, 0, kSub, lane,
@@ -2103,7 +2125,7 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
                 for (int h = 0; h < NH; ++h) {
                     rs[h] = false;
                     if (live[h]) {
-                        const bool on = owner < 0 ? active[h] : (active[h] && cm[h] == owner);
+                        const bool on = active[h] && cm[h] >= lo && cm[h] <= hi;
                         rs[h] = qk_softmax<DT, true>(st[h], KA, qop[h], 0, 0, rows, lane,
                                                      a.scale_log2, pb[h], alpha[h], on);
                     }

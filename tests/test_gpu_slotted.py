@@ -93,6 +93,124 @@ def test_radix_batch_matches_oracle(mode):
     assert ok, (err, nbad)
 
 
+def _tree_order(w):
+    """The radix batch with its sequences sorted by node path (depth-first order):
+    a tile's consecutive sequences share the root, a level-1 node and, in runs of
+    four, level-2 nodes."""
+    import dataclasses
+    perm = sorted(range(len(w.paths)), key=lambda t: w.paths[t])
+    return dataclasses.replace(w, paths=[w.paths[t] for t in perm], q=w.q[perm],
+                               segments=w.segments[perm], num_segments=w.num_segments[perm],
+                               k_new=w.k_new[perm], v_new=w.v_new[perm])
+
+
+def test_radix_batch_tree_order_matches_oracle(mode):
+    """The radix batch in tree order: runs of members within a tile share nodes
+    below the common path, read once per run by the tiled kernel."""
+    cfg = get_config("c5")
+    w = _tree_order(make_slotted_workload(cfg))
+    print(f"[gpu] slotted radix batch in tree order ({mode})", flush=True)
+    kp, vp, gk, gv = _pools_both(w.runs(), w.num_blocks, cfg.num_kv_heads, cfg.block_size,
+                                 cfg.dtype)
+    scale = scale_for(128)
+    ref = O.attention_slotted(w.q, kp, vp, w.segments, w.num_segments, cfg.num_kv_heads,
+                              cfg.block_size, w.num_blocks, scale, cfg.dtype)
+    got = _gpu(w.q, gk, gv, w.segments, w.num_segments, cfg.dtype, scale)
+    ok, err, nbad = tol_ok(got, ref)
+    assert ok, (err, nbad)
+    slots = _check_append(w.q, kp, vp, gk, gv, w.k_new, w.v_new, w.segments, w.num_segments,
+                          cfg.num_kv_heads, cfg.block_size, w.num_blocks, cfg.dtype)
+    assert (slots >= 0).all()
+
+
+def _tree_case(seed, S, Hq, Hkv, B, dtype, fanout, depth, node_len_hi):
+    """A random tree of prompt nodes (each internal node has 1..fanout children,
+    some nodes empty) whose leaves, listed depth-first, are the sequences: runs of
+    consecutive sequences share nodes at every depth, cut where the tree
+    branches.  Paths are truncated at random for some sequences, and a few
+    sequences repeat their neighbour's path with their own leaf."""
+    rng = np.random.default_rng(seed)
+    lens, paths = [], []
+
+    def node(n):
+        lens.append(n)
+        return len(lens) - 1
+
+    def grow(prefix, d):
+        if len(paths) >= S:
+            return
+        if d == depth:
+            paths.append(prefix + [node(int(rng.integers(1, node_len_hi + 1)))])
+            return
+        for _ in range(int(rng.integers(1, fanout + 1))):
+            ln = int(rng.integers(0, node_len_hi + 1)) if rng.random() < 0.9 else 0
+            grow(prefix + [node(ln)], d + 1)
+
+    root = node(int(rng.integers(1, 4 * node_len_hi)))
+    while len(paths) < S:
+        grow([root], 1)
+    for t in range(S):
+        if rng.random() < 0.1:  # a shorter path: the leaf hangs higher up
+            cut = int(rng.integers(1, len(paths[t])))
+            paths[t] = paths[t][:cut] + [paths[t][-1]]
+    free = [int(x) for x in rng.permutation(20 * len(lens) + 16)]
+    node_segs = pack([max(n, 1) for n in lens], B, free)
+    node_segs = [[(sg[0][0], sg[0][1], 0)] if lens[i] == 0 else sg for i, sg in enumerate(node_segs)]
+    NB = max(x[0] for sg in node_segs for x in sg) + 1
+
+    def draw(*sh):
+        x = rng.standard_normal(sh).astype(np.float32)
+        if dtype == "fp16":
+            return x.astype(np.float16).view(np.uint16)
+        return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+    node_k = [draw(n, Hkv, 128) for n in lens]
+    node_v = [draw(n, Hkv, 128) for n in lens]
+    MS = max(sum(len(node_segs[i]) for i in p) for p in paths)
+    segs = np.zeros((S, MS, 3), np.int32)
+    nsegs = np.zeros(S, np.int32)
+    for t, p in enumerate(paths):
+        flat = [x for i in p for x in node_segs[i]]
+        segs[t, :len(flat)] = flat
+        nsegs[t] = len(flat)
+    rk, rv, st, tb, cu = [], [], [], [], [0]
+    for sg, k, v in zip(node_segs, node_k, node_v):
+        r = 0
+        for blk, off, ln in sg:
+            rk.append(k[r:r + ln]); rv.append(v[r:r + ln])
+            st.append(off); tb.append([blk]); cu.append(cu[-1] + ln)
+            r += ln
+    runs = (np.concatenate(rk), np.concatenate(rv), np.array(cu, np.int64),
+            np.array(st, np.int32), np.array(tb, np.int32))
+    return dict(NB=NB, segs=segs, nsegs=nsegs, runs=runs, q=draw(S, Hq, 128))
+
+
+TREE_CASES = [
+    # (seed, S, Hq, Hkv, B, dtype, fanout, depth, max node length)
+    (41, 40, 32, 8, 16, "fp16", 3, 3, 20),    # G 4: 8 per tile
+    (42, 70, 16, 16, 16, "bf16", 4, 3, 12),   # G 1: 32 per tile, runs across the halves
+    (43, 30, 12, 2, 16, "fp16", 2, 4, 10),    # G 6: 4 per tile
+    (44, 50, 24, 8, 32, "bf16", 3, 3, 40),    # G 3, blocks of 32
+    (45, 20, 32, 2, 64, "fp16", 2, 2, 90),    # G 16: 2 per tile
+]
+
+
+@pytest.mark.parametrize("case", TREE_CASES, ids=[f"seed{c[0]}" for c in TREE_CASES])
+def test_random_trees_in_tree_order(case, mode):
+    seed, S, Hq, Hkv, B, dtype, fan, depth, hi = case
+    c = _tree_case(seed, S, Hq, Hkv, B, dtype, fan, depth, hi)
+    print(f"[gpu] slotted tree ({mode}) seed={seed} S={S} Hq={Hq} Hkv={Hkv} B={B} {dtype} "
+          f"max_segments={c['segs'].shape[1]}", flush=True)
+    assert mode != "tiles" or tile_list_fits(Hq, Hkv, B, c["segs"].shape[1])
+    kp, vp, gk, gv = _pools_both(c["runs"], c["NB"], Hkv, B, dtype)
+    scale = scale_for(128)
+    ref = O.attention_slotted(c["q"], kp, vp, c["segs"], c["nsegs"], Hkv, B, c["NB"], scale,
+                              dtype)
+    got = _gpu(c["q"], gk, gv, c["segs"], c["nsegs"], dtype, scale)
+    ok, err, nbad = tol_ok(got, ref)
+    assert ok, (err, nbad)
+
+
 def _node_case(seed, S, Hq, Hkv, B, dtype, node_len_hi, nodes_per_path, trunks=False,
                leaves=False):
     """Random tree-less node sets: every sequence walks its own random list of
