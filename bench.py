@@ -81,9 +81,9 @@ def parse():
                          "paged_attention_split_decode, which merges in the same launch")
     ap.add_argument("--order", default="long", choices=["long", "natural"],
                     help="dispatch order of the single-pass decode: long (the default) puts "
-                         "the sequences longer than twice the batch mean first, computed on the "
-                         "host from the batch's lengths (paged_attention_decode_ordered); "
-                         "natural keeps the batch order")
+                         "the sequences longer than twice the batch mean first and the shortest "
+                         "last, computed on the host from the batch's lengths "
+                         "(paged_attention_decode_ordered); natural keeps the batch order")
     ap.add_argument("--no-prefix", action="store_true",
                     help="for a shared-prefix workload, run the plain fused decode instead of "
                          "paged_attention_prefix_decode")
@@ -353,12 +353,21 @@ def bench_step(args):
     order_dev = None
     order_rule = "natural (batch order)"
     if not P and not prefix and args.order == "long":
+        # The sequences above twice the batch mean go first, so that they do not
+        # finish last; the shortest go last, as many as give one work-group per
+        # compute unit (at most an eighth of the batch), so that the launch's last
+        # partial wave of work-groups is its shortest; the rest keep batch order.
         n_host = np.asarray(w0.lengths, np.int64)
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
         longs = [i for i in range(S) if n_host[i] > 2 * n_host.mean()]
         rest = [i for i in range(S) if n_host[i] <= 2 * n_host.mean()]
-        order_dev = torch.tensor(longs + rest, dtype=torch.int32, device=dev)
-        order_rule = ("sequences longer than twice the batch mean first (%d of %d), then the "
-                      "rest in batch order" % (len(longs), S))
+        k = min(-(-cus // cfg.num_kv_heads), S // 8, len(rest))
+        shorts = sorted(sorted(rest, key=lambda i: n_host[i])[:k], key=lambda i: -n_host[i])
+        mid = [i for i in rest if i not in set(shorts)]
+        order_dev = torch.tensor(longs + mid + shorts, dtype=torch.int32, device=dev)
+        order_rule = ("sequences longer than twice the batch mean first (%d of %d), the %d "
+                      "shortest last (longest of them first), the rest in batch order"
+                      % (len(longs), S, len(shorts)))
     # split workloads merge their partitions in the decode launch itself, with one
     # zeroed arrival counter per (sequence, KV head) that every launch leaves zero
     merged = bool(P) and not args.no_merge and not prefix
