@@ -33,10 +33,12 @@
  *   n = 0 marks a padding sequence.
  * Caller contract (not checked unless PKV_DEBUG_CHECK=1 is set in the
  *   environment): 0 <= n <= max_blocks_per_seq * block_size; table entries of
- *   blocks 0 .. ceil(n/block_size)-1 lie in [0, num_blocks); no two sequences
- *   append to the same slot in one call.  With PKV_DEBUG_CHECK=1 each call first
- *   runs a device-side check of these, synchronises `stream`, and returns
- *   PKV_EDEVICE if one fails.  The check keeps its verdict in one flag per device:
+ *   blocks 0 .. ceil(n/block_size)-1 lie in [0, num_blocks).  With
+ *   PKV_DEBUG_CHECK=1 each call first runs a device-side check of these,
+ *   synchronises `stream`, and returns PKV_EDEVICE if one fails.  Also the
+ *   caller's, and never checked: no two sequences append to the same slot in one
+ *   call (the row left in the slot is then either sequence's).  The check keeps
+ *   its verdict in one flag per device:
  *   checked calls that run at the same time on one device (from several threads)
  *   may report each other's violations.
  * Supported shapes: head_dim = 128; block_size in {16, 32, 64, 128, 256};
