@@ -540,3 +540,62 @@ def test_slotted_debug_check_rejects_bad_segments(monkeypatch):
         _gpu(q, gk, gk, np.array([[[0, 0, 1]], [[1, 0, 3]]], np.int32),
              np.array([2, 1], np.int32), "fp16", 0.1)
     assert ei.value.status == -5
+
+
+def test_append_debug_check_rejects_bad_segments_and_writes_nothing(monkeypatch):
+    """The fused slotted append validates the segments before any kernel runs:
+    a rejected call leaves the pools and the slot ids untouched."""
+    gk = torch.zeros((8, 2, 16, 128), dtype=torch.float16, device=DEV)
+    gv = torch.zeros_like(gk)
+    q = np.zeros((2, 4, 128), np.uint16)
+    new = np.full((2, 2, 128), 0x3C00, np.uint16)  # 1.0 in fp16
+    monkeypatch.setenv("PKV_DEBUG_CHECK", "1")
+    print("[gpu] slotted append debug rejections", flush=True)
+    for segs, ns in (([[[0, 12, 5]], [[1, 0, 3]]], [1, 1]),   # slot past its block
+                     ([[[9, 0, 5]], [[1, 0, 3]]], [1, 1]),    # block outside the pool
+                     ([[[0, 0, 1]], [[1, 0, 3]]], [2, 1])):   # count above the row
+        slots = torch.full((2,), -7, dtype=torch.int64, device=DEV)
+        out = torch.empty((2, 4, 128), dtype=torch.float16, device=DEV)
+        with pytest.raises(pkv.PagedKVError) as ei:
+            pkv.paged_attention_append_decode_slotted(
+                out, to_dev(q, "fp16", DEV), gk, gv, to_dev(new, "fp16", DEV),
+                to_dev(new, "fp16", DEV), i32(np.array(segs, np.int32), DEV),
+                i32(np.array(ns, np.int32), DEV), slot_out=slots, scale=0.1)
+        assert ei.value.status == -5
+        torch.cuda.synchronize()
+        assert not bool(gk.any()) and not bool(gv.any())
+        assert (slots.cpu().numpy() == -7).all()
+
+
+def test_append_single_row_segments_and_block_edges(mode):
+    """Segments of one row, and new rows landing on a block's first and last row
+    (offsets 0 and B - 1) at every block size, against the oracle."""
+    for B in (16, 32, 64, 128, 256):
+        Hq, Hkv, S = 8, 2, 6
+        rng = np.random.default_rng(500 + B)
+        # sequence t: a shared one-row segment, then a private segment ending at
+        # offset B-1 (t even) or a one-row segment at offset 0 of its own block
+        NB = 2 * S + 2
+        segs = np.zeros((S, 2, 3), np.int32)
+        for t in range(S):
+            segs[t, 0] = (0, 0, 1)
+            segs[t, 1] = (1 + t, 3, B - 3) if t % 2 == 0 else (1 + t, 0, 1)
+        nsegs = np.full(S, 2, np.int32)
+        kr = (rng.standard_normal((1 + S * B, Hkv, 128)).astype(np.float16)).view(np.uint16)
+        vr = (rng.standard_normal((1 + S * B, Hkv, 128)).astype(np.float16)).view(np.uint16)
+        runs_k, runs_v, cu, st, tb = [kr[:1]], [vr[:1]], [0, 1], [0], [[0]]
+        r = 1
+        for t in range(S):
+            off, ln = int(segs[t, 1, 1]), int(segs[t, 1, 2])
+            runs_k.append(kr[r:r + ln]); runs_v.append(vr[r:r + ln])
+            cu.append(cu[-1] + ln); st.append(off); tb.append([1 + t]); r += ln
+        runs = (np.concatenate(runs_k), np.concatenate(runs_v), np.array(cu, np.int64),
+                np.array(st, np.int32), np.array(tb, np.int32))
+        print(f"[gpu] slotted append edges ({mode}) B={B}", flush=True)
+        kp, vp, gk, gv = _pools_both(runs, NB, Hkv, B, "fp16")
+        q = (rng.standard_normal((S, Hq, 128)).astype(np.float16)).view(np.uint16)
+        kn = (rng.standard_normal((S, Hkv, 128)).astype(np.float16)).view(np.uint16)
+        vn = (rng.standard_normal((S, Hkv, 128)).astype(np.float16)).view(np.uint16)
+        slots = _check_append(q, kp, vp, gk, gv, kn, vn, segs, nsegs, Hkv, B, NB, "fp16")
+        want = [(1 + t) * B + (B - 1 if t % 2 == 0 else 0) for t in range(S)]
+        assert slots.tolist() == want
