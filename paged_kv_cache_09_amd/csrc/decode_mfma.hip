@@ -997,7 +997,8 @@ constexpr int kMaxRoundSubs = kSegRound * 16;  // a 256-row segment gives 16 sub
 // k < 64, and lanes 0-31's 16 bytes of the new K (lanes 0-15) or V row), none
 // depending on another; slot_append_store finds the row (a longer list's later
 // segments are read there) and writes it.  The caller's next fenced barrier
-// makes the rows visible to every wave's loads.
+// (workgroup-scope release and acquire) orders the stores before every later
+// load of the work-group's waves.
 struct SlotAppend {
     int nseg;           // segment count as passed
     int32_t blk, off, len;  // this lane's segment of the first 64
@@ -1008,7 +1009,8 @@ __device__ __forceinline__ SlotAppend slot_append_load(const DecodeArgs &a, int 
                                                        int lane)
 {
     SlotAppend r;
-    const int32_t *seg = a.segments + ((int64_t)s * a.max_segments + min(lane, a.max_segments - 1)) * 3;
+    const int32_t *seg =
+        a.segments + ((int64_t)s * a.max_segments + min(lane, a.max_segments - 1)) * 3;
     r.nseg = a.num_segments[s];
     r.blk = seg[0];
     r.off = seg[1];
@@ -1146,7 +1148,7 @@ void slotted_mfma_kernel(DecodeArgs a)
 
     // fused append (single pass only): wave 0 issues its loads with the query's
     // and writes the new rows before the partition loop; the round's first
-    // barrier completes the stores before any wave loads a sub-tile
+    // barrier orders the stores before any wave's sub-tile loads
     SlotAppend ap;
     if constexpr (!SPLIT) {
         if (a.k_new && w == 0)
@@ -1792,10 +1794,10 @@ void prefix_fused_mfma_kernel(DecodeArgs a)
 // part of the tile shares; in a batch in tree order, the sequences under one node
 // are neighbours) becomes sub-tiles read once for the run, with the run's columns
 // active; the others, sub-tiles of one member (the other columns score -inf and
-// keep their state).  The whole list of descriptors sits in LDS: the host takes this path only when
-// a tile's sub-tiles fit (members x max_segments x ceil(B/16) <= kTileSubs).  The
-// waves take the list round-robin with the common sub-tiles spread evenly among
-// the members' ones, as in the shared-prefix kernel.
+// keep their state).  The whole list of descriptors sits in LDS: the host takes
+// this path only when a tile's sub-tiles fit (members x max_segments x ceil(B/16)
+// <= kTileSubs).  The waves take the list round-robin with the common sub-tiles
+// spread evenly among the members' ones, as in the shared-prefix kernel.
 constexpr int kTileSubs = kSlottedTileSubs;  // descriptor capacity of one tile's list
 constexpr int kCommonScan = 64;              // leading segments compared across a tile
 
@@ -1887,8 +1889,8 @@ void slotted_tiled_mfma_kernel(DecodeArgs a)
         }
     }
     // 0. Fused append: each wave takes members w, w + WAVES, ...; their loads are
-    // in flight with step 1's, the stores with step 2's, and the fenced barrier
-    // after step 2 completes the stores before any sub-tile load
+    // in flight with step 1's, the stores go out after step 1's barrier, and the
+    // barriers that follow order them before any wave's sub-tile loads
     constexpr int kPer = (kMembers + WAVES - 1) / WAVES;
     SlotAppend ap[kPer];
     if (a.k_new) {
