@@ -486,8 +486,9 @@ int paged_attention_decode_slotted(void *out, const void *q, const void *k_pool,
  *
  *   k_new, v_new   [num_seqs][num_kv_heads][head_dim], dtype, 16-byte aligned;
  *                  required (PKV_EINVAL otherwise)
- *   slot_out       optional int64 [num_seqs]: block * block_size + offset of the
- *                  written row, -1 for a sequence with n = 0 (nothing written)
+ *   slot_out       optional int64 [num_seqs], 8-byte aligned: block * block_size +
+ *                  offset of the written row, -1 for a sequence with n = 0
+ *                  (nothing written)
  * Other arguments, limits and errors as for paged_attention_decode_slotted
  * (PKV_DEBUG_CHECK=1 validates the segments as there).  Two sequences whose
  * position n-1 is the same slot are a caller error: the row written is then
