@@ -135,14 +135,19 @@ def test_fused_append_decode(key, P):
 
 # ---------------------------------------------------------------------------
 def _orders(n, seed):
-    """Dispatch orders to try: sequences above twice the mean length first, the
-    reverse of the batch, and a seeded random permutation."""
+    """Dispatch orders to try: sequences above twice the mean length first; the
+    same with the shortest eighth of the batch last, longest of them first (the
+    shape of the bench's plan); the reverse of the batch; and a seeded random
+    permutation."""
     S = len(n)
     big = [i for i in range(S) if n[i] > 2 * n.mean()]
-    long_first = big + [i for i in range(S) if i not in set(big)]
+    rest = [i for i in range(S) if i not in set(big)]
+    shorts = sorted(sorted(rest, key=lambda i: n[i])[:S // 8], key=lambda i: -n[i])
     rng = np.random.default_rng(seed)
-    return {"long_first": np.array(long_first), "reversed": np.arange(S)[::-1].copy(),
-            "random": rng.permutation(S)}
+    return {"long_first": np.array(big + rest),
+            "long_first_short_last": np.array(big + [i for i in rest if i not in set(shorts)]
+                                              + shorts),
+            "reversed": np.arange(S)[::-1].copy(), "random": rng.permutation(S)}
 
 
 @pytest.mark.parametrize("key", ["c1a", "c2", "c3", "c4"])
