@@ -599,3 +599,48 @@ def test_append_single_row_segments_and_block_edges(mode):
         slots = _check_append(q, kp, vp, gk, gv, kn, vn, segs, nsegs, Hkv, B, NB, "fp16")
         want = [(1 + t) * B + (B - 1 if t % 2 == 0 else 0) for t in range(S)]
         assert slots.tolist() == want
+
+
+_big_cache = {}
+
+
+def _big_radix():
+    """A 1,024-sequence radix batch in tree order (1,024 tiles of the tiled
+    kernel across 8 KV heads), with the oracle's append over the whole batch and
+    its attention on 128 sampled sequences (computed once per module)."""
+    if "w" not in _big_cache:
+        cfg = get_config("c5")
+        w = _tree_order(make_slotted_workload(cfg, num_seqs=1024))
+        kp, vp = O.new_pools(w.num_blocks, cfg.num_kv_heads, cfg.block_size, 128,
+                             NAN_BITS[cfg.dtype])
+        kr, vr, cu, st, tb = w.runs()
+        O.append_tokens(kp, vp, kr, vr, cu, st, tb, cfg.block_size, w.num_blocks)
+        kp0, vp0 = kp.copy(), vp.copy()
+        slots = O.append_slotted(kp, vp, w.k_new, w.v_new, w.segments, w.num_segments,
+                                 cfg.block_size, w.num_blocks)
+        sample = np.random.default_rng(77).choice(1024, size=128, replace=False)
+        ref = O.attention_slotted(w.q[sample], kp, vp, w.segments[sample],
+                                  w.num_segments[sample], cfg.num_kv_heads, cfg.block_size,
+                                  w.num_blocks, scale_for(128), cfg.dtype)
+        _big_cache.update(w=w, cfg=cfg, pools0=(kp0, vp0), pools=(kp, vp), slots=slots,
+                          sample=sample, ref=ref)
+    return _big_cache
+
+
+def test_append_large_radix_batch(mode):
+    """1,024 sequences in tree order, fused append: pools and slot ids bit for bit
+    over the whole batch, outputs of 128 sampled sequences against the oracle."""
+    c = _big_radix()
+    w, cfg = c["w"], c["cfg"]
+    print(f"[gpu] slotted append large radix batch ({mode}) S=1024 NB={w.num_blocks}",
+          flush=True)
+    assert mode != "tiles" or tile_list_fits(cfg.num_q_heads, cfg.num_kv_heads, cfg.block_size,
+                                             w.segments.shape[1])
+    gk = to_dev(c["pools0"][0], cfg.dtype, DEV)
+    gv = to_dev(c["pools0"][1], cfg.dtype, DEV)
+    got, slots = _gpu_append(w.q, gk, gv, w.k_new, w.v_new, w.segments, w.num_segments,
+                             cfg.dtype, scale_for(128))
+    assert np.array_equal(slots, c["slots"])
+    assert np.array_equal(bits_of(gk), c["pools"][0]) and np.array_equal(bits_of(gv), c["pools"][1])
+    ok, err, nbad = tol_ok(got[c["sample"]], c["ref"])
+    assert ok, (err, nbad)
