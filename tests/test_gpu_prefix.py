@@ -276,3 +276,30 @@ def test_prefix_decode_debug_check_rejects_short_members(monkeypatch):
         _run((gk, gv), to_dev(c["q"], "fp16", DEV), i32(c["tables"], DEV),
              i32(c["lens"], DEV), i32([0, 3], DEV), i32(c["plens"], DEV), "fp16")
     assert ei.value.status == -5
+
+
+def test_large_grouped_batch_fused():
+    """1,024 sequences in five groups (prefixes of 512, 100, 64, 1,000 tokens and
+    an empty one; a one-member group), one pass with the fused append: pools and
+    slot ids bit for bit over the whole batch, outputs of 128 sampled sequences
+    against the oracle."""
+    dtype, Hq, Hkv, B = "fp16", 32, 8, 16
+    groups = [(300, 512), (1, 100), (400, 64), (200, 1000), (123, 0)]
+    c = _grouped_case(61, groups, Hq, Hkv, B, dtype, max_own=128)
+    S = len(c["lens"])
+    print(f"[gpu] large grouped prefix batch S={S} NB={c['NB']}", flush=True)
+    kp_pre, vp_pre = c["kp"].copy(), c["vp"].copy()
+    slots_ref = O.append(c["kp"], c["vp"], c["kn"], c["vn"], c["tables"], c["lens"], B, c["NB"])
+    sample = np.random.default_rng(62).choice(S, size=128, replace=False)
+    ref = O.attention(c["q"][sample], c["kp"], c["vp"], c["tables"][sample], c["lens"][sample],
+                      Hkv, B, c["NB"], scale_for(128), dtype)
+    args = (to_dev(c["q"], dtype, DEV), i32(c["tables"], DEV), i32(c["lens"], DEV),
+            i32(c["cu"], DEV), i32(c["plens"], DEV))
+    gk, gv = to_dev(kp_pre, dtype, DEV), to_dev(vp_pre, dtype, DEV)
+    slots = torch.full((S,), -7, dtype=torch.int64, device=DEV)
+    out, _, _ = _run((gk, gv), *args, dtype, 0,
+                     (to_dev(c["kn"], dtype, DEV), to_dev(c["vn"], dtype, DEV)), slots)
+    ok, err, nbad = tol_ok(widen_out(out)[sample], ref)
+    assert ok, (err, nbad)
+    assert np.array_equal(slots.cpu().numpy(), slots_ref)
+    assert np.array_equal(bits_of(gk), c["kp"]) and np.array_equal(bits_of(gv), c["vp"])
