@@ -71,3 +71,33 @@ def test_fused_decode_beyond_65535_work_groups(Hq, Hkv):
     assert np.array_equal(bits_of(gk), c["kp"]) and np.array_equal(bits_of(gv), c["vp"])
     ok, err, nbad = tol_ok(widen_out(out)[sample], ref)
     assert ok, (err, nbad)
+
+
+def test_merged_split_decode_beyond_65535_work_groups():
+    """The split decode with the in-kernel merge over 131,072 (sequence, KV head)
+    items: partitions of 16 positions, so most items merge two partitions; the
+    arrival counters are left zero."""
+    S, Hq, Hkv, B, dtype, P = 16384, 32, 8, 16, "fp16", 16
+    c = _case(95, S, Hq, Hkv, B, dtype, 32)
+    print(f"[gpu] scale merged split S={S} Hq={Hq} Hkv={Hkv} P={P}", flush=True)
+    gk, gv = to_dev(c["kp"], dtype, DEV), to_dev(c["vp"], dtype, DEV)
+    slots_ref = O.append(c["kp"], c["vp"], c["kn"], c["vn"], c["tables"], c["n"], B, c["NB"])
+    sample = np.random.default_rng(96).choice(S, size=256, replace=False)
+    ref = O.attention(c["q"][sample], c["kp"], c["vp"], c["tables"][sample], c["n"][sample], Hkv,
+                      B, c["NB"], scale_for(128), dtype)
+    mp = -(-c["tables"].shape[1] * B // P)
+    out = torch.empty((S, Hq, 128), dtype=torch.float16, device=DEV)
+    po = torch.empty((S, Hq, mp, 128), dtype=torch.float32, device=DEV)
+    pl = torch.empty((S, Hq, mp), dtype=torch.float32, device=DEV)
+    ctr = torch.zeros((S, Hkv), dtype=torch.int32, device=DEV)
+    slots = torch.full((S,), -7, dtype=torch.int64, device=DEV)
+    pkv.paged_attention_split_decode(out, to_dev(c["q"], dtype, DEV), gk, gv, i32(c["tables"], DEV),
+                                     i32(c["n"], DEV), P, po, pl, ctr,
+                                     k_new=to_dev(c["kn"], dtype, DEV),
+                                     v_new=to_dev(c["vn"], dtype, DEV), slot_out=slots)
+    torch.cuda.synchronize()
+    assert not bool(ctr.any())
+    assert np.array_equal(slots.cpu().numpy(), slots_ref)
+    assert np.array_equal(bits_of(gk), c["kp"]) and np.array_equal(bits_of(gv), c["vp"])
+    ok, err, nbad = tol_ok(widen_out(out)[sample], ref)
+    assert ok, (err, nbad)
