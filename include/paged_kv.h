@@ -537,6 +537,28 @@ int paged_attention_decode_slotted_split(void *out, const void *q, const void *k
                                          int dtype, void *stream);
 
 /*
+ * paged_attention_append_decode_slotted_split -- the slotted split decode with
+ * the step's append fused: each sequence's new K/V rows are written to its
+ * position n-1 (as in paged_attention_append_decode_slotted, the same contract on
+ * that row) by the one work-group that reads it, the one whose partitions
+ * include the last, before any of its loads; the others never read that row.
+ *
+ *   k_new, v_new   [num_seqs][num_kv_heads][head_dim], dtype, 16-byte aligned;
+ *                  required
+ *   slot_out       optional int64 [num_seqs], 8-byte aligned, as for
+ *                  paged_attention_append_decode_slotted
+ *   partition_size > 0 (PKV_EINVAL otherwise)
+ * Other arguments, workspace and counters as for
+ * paged_attention_decode_slotted_split.
+ */
+int paged_attention_append_decode_slotted_split(
+    void *out, const void *q, void *k_pool, void *v_pool, const void *k_new, const void *v_new,
+    int64_t *slot_out, const int32_t *segments, const int32_t *num_segments, int num_seqs,
+    int num_q_heads, int num_kv_heads, int head_dim, int block_size, int max_segments,
+    int64_t num_blocks, float scale, int partition_size, int max_partitions, float *part_o,
+    float *part_lse, int32_t *counters, int dtype, void *stream);
+
+/*
  * paged_attention_reduce -- log-sum-exp merge of split-context partitions.
  *
  * For each (s, h) with P = partition_size and np = ceil(n/P) partitions:

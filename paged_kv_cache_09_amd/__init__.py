@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     paged_attention_decode_ordered,
     paged_attention_decode_slotted,
     paged_attention_append_decode_slotted,
+    paged_attention_append_decode_slotted_split,
     paged_attention_decode_slotted_split,
     paged_attention_prefix_decode,
     paged_attention_prefix_split_decode,

@@ -88,6 +88,10 @@ def load():
                                                        i32, i32, i64, f32, i32, i32, P, P, P,
                                                        i32, P]
     L.paged_attention_decode_slotted_split.restype = i32
+    L.paged_attention_append_decode_slotted_split.argtypes = [P, P, P, P, P, P, P, P, P, i32,
+                                                              i32, i32, i32, i32, i32, i64, f32,
+                                                              i32, i32, P, P, P, i32, P]
+    L.paged_attention_append_decode_slotted_split.restype = i32
     L.paged_attention_reduce.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, P]
     L.paged_attention_reduce.restype = i32
     _lib = L
@@ -623,6 +627,42 @@ def paged_attention_decode_slotted_split(out, q, k_pool, v_pool, segments, num_s
         B, ss[1], NB, _scale(scale), int(partition_size), mp, _p(part_o), _p(part_lse),
         _p(counters), _dtype_code(q), _stream(dev))
     _check(rc, "paged_attention_decode_slotted_split")
+
+
+def paged_attention_append_decode_slotted_split(out, q, k_pool, v_pool, k_new, v_new, segments,
+                                                num_segments, partition_size: int, part_o,
+                                                part_lse, counters, slot_out=None,
+                                                scale: Optional[float] = None):
+    """The slotted split decode with the step's K/V rows written first to each
+    sequence's position n-1, by the work-group that reads it, in one launch."""
+    NB, Hkv, B, D = _pools(k_pool, v_pool)
+    S, Hq, Dq = _dims(q, 3, "q")
+    if Dq != D:
+        raise ValueError(f"q has head_dim {Dq}, the pools {D}")
+    _same_dtype(k_pool, (q, "q"), (out, "out"))
+    _expect(out, (S, Hq, D), "out")
+    if k_new is None or v_new is None:
+        raise ValueError("k_new and v_new are required")
+    _expect(k_new, (S, Hkv, D), "k_new")
+    _expect(v_new, (S, Hkv, D), "v_new")
+    _same_dtype(k_pool, (k_new, "k_new"), (v_new, "v_new"))
+    _expect(slot_out, (S,), "slot_out")
+    ss = segments.shape
+    if len(ss) != 3 or ss[0] != S or ss[2] != 3:
+        raise ValueError(f"segments must be [{S}][max_segments][3], got {tuple(ss)}")
+    _expect(num_segments, (S,), "num_segments")
+    _expect(counters, (S, Hkv), "counters")
+    mp = _workspace(part_o, part_lse, S, Hq, D)
+    dev = _dev(out, q, k_pool, v_pool, k_new, v_new, segments, num_segments, part_o, part_lse,
+               counters, slot_out)
+    _ints((segments, "i32", "segments"), (num_segments, "i32", "num_segments"),
+          (counters, "i32", "counters"), (slot_out, "i64", "slot_out"))
+    rc = load().paged_attention_append_decode_slotted_split(
+        _p(out), _p(q), _p(k_pool), _p(v_pool), _p(k_new), _p(v_new), _p(slot_out),
+        _p(segments), _p(num_segments), S, Hq, Hkv, D, B, ss[1], NB, _scale(scale),
+        int(partition_size), mp, _p(part_o), _p(part_lse), _p(counters), _dtype_code(q),
+        _stream(dev))
+    _check(rc, "paged_attention_append_decode_slotted_split")
 
 
 def paged_attention_reduce(out, part_o, part_lse, context_lens, partition_size: int):

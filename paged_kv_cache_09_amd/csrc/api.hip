@@ -958,7 +958,7 @@ int slotted_impl(void *out, const void *q, const void *k_pool, const void *v_poo
                  void *stream, const void *k_new = nullptr, const void *v_new = nullptr,
                  int64_t *slot_out = nullptr)
 {
-    if ((k_new == nullptr) != (v_new == nullptr) || (k_new && partition_size > 0))
+    if ((k_new == nullptr) != (v_new == nullptr))
         return PKV_EINVAL;
     if (k_new && (!aligned16(k_new) || !aligned16(v_new) || ((uintptr_t)slot_out & 7u)))
         return PKV_EINVAL;
@@ -1089,6 +1089,21 @@ int paged_attention_append_decode_slotted(void *out, const void *q, void *k_pool
     return slotted_impl(out, q, k_pool, v_pool, segments, num_segments, num_seqs, num_q_heads,
                         num_kv_heads, head_dim, block_size, max_segments, num_blocks, scale, 0, 0,
                         nullptr, nullptr, nullptr, dtype, stream, k_new, v_new, slot_out);
+}
+
+int paged_attention_append_decode_slotted_split(
+    void *out, const void *q, void *k_pool, void *v_pool, const void *k_new, const void *v_new,
+    int64_t *slot_out, const int32_t *segments, const int32_t *num_segments, int num_seqs,
+    int num_q_heads, int num_kv_heads, int head_dim, int block_size, int max_segments,
+    int64_t num_blocks, float scale, int partition_size, int max_partitions, float *part_o,
+    float *part_lse, int32_t *counters, int dtype, void *stream)
+{
+    if (!k_new || !v_new || partition_size <= 0)
+        return PKV_EINVAL;
+    return slotted_impl(out, q, k_pool, v_pool, segments, num_segments, num_seqs, num_q_heads,
+                        num_kv_heads, head_dim, block_size, max_segments, num_blocks, scale,
+                        partition_size, max_partitions, part_o, part_lse, counters, dtype, stream,
+                        k_new, v_new, slot_out);
 }
 
 int paged_attention_decode_slotted_split(void *out, const void *q, const void *k_pool,

@@ -1146,14 +1146,14 @@ void slotted_mfma_kernel(DecodeArgs a)
     const bool direct = !SPLIT || np <= 1;
     const int np_loop = direct ? (px0 == 0 ? 1 : 0) : np;
 
-    // fused append (single pass only): wave 0 issues its loads with the query's
+    // fused append: wave 0 of the work-group that takes the partition holding
+    // position n-1 (the only one that reads it) issues its loads with the query's
     // and writes the new rows before the partition loop; the round's first
     // barrier orders the stores before any wave's sub-tile loads
     SlotAppend ap;
-    if constexpr (!SPLIT) {
-        if (a.k_new && w == 0)
-            ap = slot_append_load(a, s, g, lane);
-    }
+    const bool appends = a.k_new && w == 0 && px0 == (direct ? 0 : (np - 1) % parts);
+    if (appends)
+        ap = slot_append_load(a, s, g, lane);
     u32x4 qop[4];
     {
         const uint16_t *qrow = (const uint16_t *)a.q +
@@ -1164,10 +1164,8 @@ void slotted_mfma_kernel(DecodeArgs a)
             qop[kk] = col < G ? *(const u32x4 *)(qrow + kk * 32) : (u32x4){0u, 0u, 0u, 0u};
     }
 
-    if constexpr (!SPLIT) {
-        if (a.k_new && w == 0)
-            slot_append_store<BS>(a, ap, s, g, lane);
-    }
+    if (appends)
+        slot_append_store<BS>(a, ap, s, g, lane);
 
     for (int px = px0; px < np_loop; px += parts) {
         // positions [t0, t1) of this partition (the whole sequence in one pass)

@@ -44,6 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
             "paged_attention_split_decode_noalloc", "paged_kv_copy_slots",
             "paged_attention_decode_slotted_split", "paged_attention_prefix_split_decode",
             "paged_attention_decode_ordered", "paged_attention_append_decode_slotted",
+            "paged_attention_append_decode_slotted_split",
             "pkv_status_string",
             "pkv_max_partitions"} <= set(declared)
     assert pkv.exported_symbols() == declared
@@ -317,6 +318,24 @@ def test_append_decode_slotted_argument_errors(lib):
     assert call(B=24) == ENOTSUP
     assert call(dt=2) == ENOTSUP
     assert call(S=0) == 0
+
+
+@host_only
+def test_append_decode_slotted_split_argument_errors(lib):
+    f = lib.paged_attention_append_decode_slotted_split
+
+    def call(kn=A, vn=A, so=None, P_=32, MP=2, ctr=A, dt=0):
+        return f(A, A, A, A, kn, vn, so, A, A, 2, 12, 2, 128, 16, 4, 64, 0.088, P_, MP, A, A,
+                 ctr, dt, None)
+
+    assert call(kn=None, vn=None) == EINVAL          # the new rows are required
+    assert call(vn=None) == EINVAL
+    assert call(P_=0) == EINVAL                      # split mode only
+    assert call(P_=24) == EINVAL                     # not a multiple of 16
+    assert call(so=P((1 << 20) + 4)) == EINVAL       # slot_out not 8-byte aligned
+    assert call(ctr=None) == EINVAL
+    assert call(MP=1) == EWORKSPACE
+    assert call(dt=2) == ENOTSUP
 
 
 @host_only

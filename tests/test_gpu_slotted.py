@@ -644,3 +644,76 @@ def test_append_large_radix_batch(mode):
     assert np.array_equal(bits_of(gk), c["pools"][0]) and np.array_equal(bits_of(gv), c["pools"][1])
     ok, err, nbad = tol_ok(got[c["sample"]], c["ref"])
     assert ok, (err, nbad)
+
+
+def _gpu_split_append(q, gk, gv, k_new, v_new, segs, nsegs, dtype, scale, P, B):
+    """paged_attention_append_decode_slotted_split (pools written in place); returns
+    the widened output, the slot ids and the arrival counters."""
+    S, Hq, _ = q.shape
+    Hkv = gk.shape[1]
+    mp = -(-segs.shape[1] * B // P)
+    out = torch.empty((S, Hq, 128), dtype=TDT[dtype], device=DEV)
+    out.view(torch.int16).fill_(0x5555)
+    po = torch.full((S, Hq, mp, 128), float("nan"), dtype=torch.float32, device=DEV)
+    pl = torch.full((S, Hq, mp), float("nan"), dtype=torch.float32, device=DEV)
+    ctr = torch.zeros((S, Hkv), dtype=torch.int32, device=DEV)
+    slots = torch.full((S,), -2, dtype=torch.int64, device=DEV)
+    pkv.paged_attention_append_decode_slotted_split(
+        out, to_dev(q, dtype, DEV), gk, gv, to_dev(k_new, dtype, DEV), to_dev(v_new, dtype, DEV),
+        i32(segs, DEV), i32(nsegs, DEV), P, po, pl, ctr, slot_out=slots, scale=scale)
+    torch.cuda.synchronize()
+    return widen_out(out), slots.cpu().numpy(), ctr
+
+
+@pytest.mark.parametrize("key,P", [("c1a", 32), ("c2", 256), ("c2", 512), ("c4", 2048)])
+def test_append_split_block_tables_as_segments(key, P):
+    """The split decode with the fused append on block tables written as segments:
+    the new token's slot (the table append's) starts as the NaN sentinel and ends
+    with the new rows; pools and slot ids bit for bit, the oracle's attention, the
+    counters back at zero."""
+    w, r, segs, nsegs = _tables_as_segments(key)
+    c = w.cfg
+    B = c.block_size
+    print(f"[gpu] slotted split append from tables {key} P={P}", flush=True)
+    kp0, vp0 = r["k_pool"].copy(), r["v_pool"].copy()
+    for t, slot in enumerate(r["slots"]):
+        if slot >= 0:
+            kp0[slot // B, :, slot % B, :] = w.nan_bits
+            vp0[slot // B, :, slot % B, :] = w.nan_bits
+    gk, gv = to_dev(kp0, c.dtype, DEV), to_dev(vp0, c.dtype, DEV)
+    got, slots, ctr = _gpu_split_append(w.q, gk, gv, w.k_new, w.v_new, segs, nsegs, c.dtype,
+                                        scale_for(c.head_dim), P, B)
+    assert np.array_equal(slots, r["slots"])
+    assert not bool(ctr.any())
+    ref_blocks = np.unique(segs[:, :, 0][segs[:, :, 2] > 0])
+    idx = torch.from_numpy(ref_blocks.astype(np.int64)).to(DEV)
+    assert np.array_equal(bits_of(gk[idx]), r["k_pool"][ref_blocks])
+    assert np.array_equal(bits_of(gv[idx]), r["v_pool"][ref_blocks])
+    ok, err, nbad = tol_ok(got, r["out"])
+    assert ok, (err, nbad)
+
+
+@pytest.mark.parametrize("case", APPEND_CASES, ids=[f"seed{c[0]}" for c in APPEND_CASES])
+@pytest.mark.parametrize("P", [16, 48])
+def test_append_split_random_node_lists(case, P):
+    """Random node lists ending in private leaves, split mode with the fused append
+    at partitions of 16 and 48 positions (the row n-1 in every position of its
+    partition across the cases), against the oracle's slotted append and
+    attention; the empty sequence gets slot -1."""
+    seed, S, Hq, Hkv, B, dtype, hi, per = case
+    c = _node_case(seed, S, Hq, Hkv, B, dtype, hi, per, trunks=seed >= 11, leaves=True)
+    print(f"[gpu] slotted split append seed={seed} P={P} S={S} B={B}", flush=True)
+    kp, vp, gk, gv = _pools_both(c["runs"], c["NB"], Hkv, B, dtype)
+    scale = scale_for(128)
+    ref_slots = O.append_slotted(kp, vp, c["k_new"], c["v_new"], c["segs"], c["nsegs"], B,
+                                 c["NB"])
+    ref = O.attention_slotted(c["q"], kp, vp, c["segs"], c["nsegs"], Hkv, B, c["NB"], scale,
+                              dtype)
+    got, slots, ctr = _gpu_split_append(c["q"], gk, gv, c["k_new"], c["v_new"], c["segs"],
+                                        c["nsegs"], dtype, scale, P, B)
+    assert np.array_equal(slots, ref_slots)
+    assert slots[-1 if seed >= 11 else 0] == -1
+    assert not bool(ctr.any())
+    assert np.array_equal(bits_of(gk), kp) and np.array_equal(bits_of(gv), vp)
+    ok, err, nbad = tol_ok(got, ref)
+    assert ok, (err, nbad)
