@@ -9,7 +9,10 @@
  *      that row sits in the pool at (block table[0], offset 0);
  *   2. scale 0: every score is 0, so the output is the plain mean of the n value
  *      rows of the sequence (walked through its block table), within 1e-2;
- *   3. argument errors come back as status codes without touching the device.
+ *   3. the same one-token case through slotted segments: each sequence's one
+ *      segment (block, offset, length 1) is the slot the fused append writes,
+ *      and the output equals that value row, bit for bit;
+ *   4. argument errors come back as status codes without touching the device.
  * Prints one line per check and exits 0 when all pass.
  */
 #include <math.h>
@@ -159,7 +162,48 @@ int main(void)
            bad ? "FAIL" : "ok");
     failures += bad;
 
-    /* 3. argument errors */
+    /* 3. one-token slotted segments, fused append: output = appended value row */
+    {
+        int32_t segs_h[S * 3], nsegs_h[S];
+        int64_t slots_h[S];
+        for (int s = 0; s < S; ++s) {
+            segs_h[3 * s] = (7 * s + 1) % NB; /* block */
+            segs_h[3 * s + 1] = 2 * s + 1;    /* slot offset */
+            segs_h[3 * s + 2] = 1;            /* length: the new token */
+            nsegs_h[s] = 1;
+        }
+        void *segs = dev_copy(segs_h, sizeof segs_h), *nsegs = dev_copy(nsegs_h, sizeof nsegs_h);
+        void *slots = NULL;
+        CHECK_HIP(hipMalloc(&slots, sizeof slots_h));
+        rc = paged_attention_append_decode_slotted(out, q, k_pool, v_pool, kn, vn, slots, segs,
+                                                   nsegs, S, HQ, HKV, D, B, 1, NB,
+                                                   PKV_DEFAULT_SCALE, PKV_FP16, NULL);
+        CHECK_HIP(hipDeviceSynchronize());
+        CHECK_HIP(hipMemcpy(out_h, out, sizeof out_h, hipMemcpyDeviceToHost));
+        CHECK_HIP(hipMemcpy(v_pool_h, v_pool, pool_elems * 2, hipMemcpyDeviceToHost));
+        CHECK_HIP(hipMemcpy(slots_h, slots, sizeof slots_h, hipMemcpyDeviceToHost));
+        bad = rc != PKV_OK;
+        for (int s = 0; s < S; ++s) {
+            if (slots_h[s] != (int64_t)segs_h[3 * s] * B + segs_h[3 * s + 1])
+                bad = 1;
+            for (int h = 0; h < HQ; ++h)
+                if (memcmp(out_h + (s * HQ + h) * D, vn_h + (s * HKV + h / G) * D, D * 2) != 0)
+                    bad = 1;
+            for (int g = 0; g < HKV; ++g) {
+                const size_t at = (((size_t)segs_h[3 * s] * HKV + g) * B + segs_h[3 * s + 1]) * D;
+                if (memcmp(v_pool_h + at, vn_h + (s * HKV + g) * D, D * 2) != 0)
+                    bad = 1;
+            }
+        }
+        printf("one-token slotted segments: the row lands at the segment's slot and is the "
+               "output: %s\n", bad ? "FAIL" : "ok");
+        failures += bad;
+        hipFree(segs);
+        hipFree(nsegs);
+        hipFree(slots);
+    }
+
+    /* 4. argument errors */
     bad = 0;
     if (paged_attention_decode(out, NULL, k_pool, v_pool, tables, lens, S, HQ, HKV, D, B, W, NB,
                                1.0f, 0, 0, NULL, NULL, PKV_FP16, NULL) != PKV_EINVAL)
