@@ -498,19 +498,24 @@ void decode_mfma_kernel(DecodeArgs a)
     // Shared-prefix mode: the first prefix partition's partials of the elements
     // this thread merges at the end (element e = (query row e/32, dims 4(e%32)..))
     // are requested now, so their latency overlaps the token loop.
+    // Two rounds cover a group (G <= 16: 512 elements, 256 threads).  The merge's
+    // loop counts rounds at run time, so the two are held as named values and
+    // picked by select (an array indexed by the round would live in scratch).
     constexpr int kPre = 2;
-    f32x4 pre_o[kPre];
-    float pre_l[kPre];
+    static_assert(kPre * WAVES * 64 >= 16 * 32, "two rounds cover a group of 16 heads");
+    f32x4 pre_o0 = {0.f, 0.f, 0.f, 0.f}, pre_o1 = {0.f, 0.f, 0.f, 0.f};
+    float pre_l0 = 0.f, pre_l1 = 0.f;
     if (SUFFIX) {
-#pragma unroll
-        for (int k = 0; k < kPre; ++k) {
-            const int e = tid + k * WAVES * 64;
-            if (e < G * 32) {
-                const int64_t row = row0 + (e >> 5);
-                pre_l[k] = a.part_lse[row * a.max_partitions];
-                pre_o[k] = *(const f32x4 *)(a.part_o + row * a.max_partitions * kHeadDim +
-                                            (e & 31) * 4);
-            }
+        const int e0 = tid, e1 = tid + WAVES * 64;
+        if (e0 < G * 32) {
+            const int64_t row = row0 + (e0 >> 5);
+            pre_l0 = a.part_lse[row * a.max_partitions];
+            pre_o0 = *(const f32x4 *)(a.part_o + row * a.max_partitions * kHeadDim + (e0 & 31) * 4);
+        }
+        if (e1 < G * 32) {
+            const int64_t row = row0 + (e1 >> 5);
+            pre_l1 = a.part_lse[row * a.max_partitions];
+            pre_o1 = *(const f32x4 *)(a.part_o + row * a.max_partitions * kHeadDim + (e1 & 31) * 4);
         }
     }
 
@@ -738,7 +743,7 @@ void decode_mfma_kernel(DecodeArgs a)
                     const float *po = a.part_o + row * a.max_partitions * kHeadDim + d0;
                     float X = L > 0.f ? ref : kNegInf;
                     for (int p = 0; p < np_pre; ++p)
-                        X = fmaxf(X, (p == 0 && k < kPre ? pre_l[k] : lse[p]) * kLog2e);
+                        X = fmaxf(X, (p == 0 && k < kPre ? (k == 0 ? pre_l0 : pre_l1) : lse[p]) * kLog2e);
                     float den = 0.f;
                     f32x4 num = {0.f, 0.f, 0.f, 0.f};
                     if (X != kNegInf) {
@@ -749,10 +754,10 @@ void decode_mfma_kernel(DecodeArgs a)
                         }
                         for (int p = 0; p < np_pre; ++p) {
                             const bool pf = p == 0 && k < kPre;
-                            const float lp = (pf ? pre_l[k] : lse[p]) * kLog2e;
+                            const float lp = (pf ? (k == 0 ? pre_l0 : pre_l1) : lse[p]) * kLog2e;
                             if (lp != kNegInf) {
                                 const float wp = fexp2(lp - X);
-                                num += (pf ? pre_o[k] : *(const f32x4 *)(po + p * kHeadDim)) * wp;
+                                num += (pf ? (k == 0 ? pre_o0 : pre_o1) : *(const f32x4 *)(po + p * kHeadDim)) * wp;
                                 den += wp;
                             }
                         }
