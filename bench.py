@@ -359,15 +359,13 @@ def bench_step(args):
         # partial wave of work-groups is its shortest; the rest keep batch order.
         n_host = np.asarray(w0.lengths, np.int64)
         cus = torch.cuda.get_device_properties(dev).multi_processor_count
-        longs = [i for i in range(S) if n_host[i] > 2 * n_host.mean()]
-        rest = [i for i in range(S) if n_host[i] <= 2 * n_host.mean()]
-        k = min(-(-cus // cfg.num_kv_heads), S // 8, len(rest))
-        shorts = sorted(sorted(rest, key=lambda i: n_host[i])[:k], key=lambda i: -n_host[i])
-        mid = [i for i in rest if i not in set(shorts)]
-        order_dev = torch.tensor(longs + mid + shorts, dtype=torch.int32, device=dev)
+        order = pkv.long_first_order(n_host, cfg.num_kv_heads, cus)
+        n_long = int((n_host > 2 * n_host.mean()).sum())
+        n_short = min(-(-cus // cfg.num_kv_heads), S // 8, S - n_long)
+        order_dev = torch.from_numpy(order).to(dev)
         order_rule = ("sequences longer than twice the batch mean first (%d of %d), the %d "
                       "shortest last (longest of them first), the rest in batch order"
-                      % (len(longs), S, len(shorts)))
+                      % (n_long, S, n_short))
     # split workloads merge their partitions in the decode launch itself, with one
     # zeroed arrival counter per (sequence, KV head) that every launch leaves zero
     merged = bool(P) and not args.no_merge and not prefix

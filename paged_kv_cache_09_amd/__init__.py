@@ -32,3 +32,4 @@ from ._lib import (  # noqa: F401
     paged_kv_copy_slots,
     status_string,
 )
+from .plan import long_first_order  # noqa: F401
