@@ -134,17 +134,19 @@ def test_fused_append_decode(key, P):
 
 
 # ---------------------------------------------------------------------------
-def _orders(n, seed):
-    """Dispatch orders to try: sequences above twice the mean length first; the
-    same with the shortest eighth of the batch last, longest of them first (the
-    shape of the bench's plan); the reverse of the batch; and a seeded random
-    permutation."""
+def _orders(n, seed, num_kv_heads):
+    """Dispatch orders to try: the package's plan (long_first_order, the order the
+    bench dispatches); sequences above twice the mean length first; the same with
+    the shortest eighth of the batch last, longest of them first; the reverse of
+    the batch; and a seeded random permutation."""
     S = len(n)
     big = [i for i in range(S) if n[i] > 2 * n.mean()]
     rest = [i for i in range(S) if i not in set(big)]
     shorts = sorted(sorted(rest, key=lambda i: n[i])[:S // 8], key=lambda i: -n[i])
     rng = np.random.default_rng(seed)
-    return {"long_first": np.array(big + rest),
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return {"plan": pkv.long_first_order(n, num_kv_heads, cus),
+            "long_first": np.array(big + rest),
             "long_first_short_last": np.array(big + [i for i in rest if i not in set(shorts)]
                                               + shorts),
             "reversed": np.arange(S)[::-1].copy(), "random": rng.permutation(S)}
@@ -159,7 +161,7 @@ def test_decode_ordered_equals_natural_order(key):
     ref_blocks = referenced_blocks(w)
     idx = None
     natural = None
-    for name, order in _orders(w.lengths, 7).items():
+    for name, order in _orders(w.lengths, 7, w.cfg.num_kv_heads).items():
         print(f"[gpu] ordered decode {key} order={name}", flush=True)
         g = GpuStep(w, append=False)
         if natural is None:
